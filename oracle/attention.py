@@ -1,0 +1,192 @@
+"""fp64 CPU oracle for exact softmax attention, forward and analytic backward.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline may import this module.  It shares no code with the HIP library and
+must never be used as a fallback for it.
+
+What it computes (the definition the flash kernels reach up to rounding order):
+
+* scores  s_ij = scale * <q_i, k_j> + bias_h(i, j).  The scale is applied to the
+  dot product and the score_mod is added afterwards, without scaling
+  (attnax ``pallas_flash_attention`` page, kernel body: scores are formed as
+  ``q k^T * scale`` and then passed through ``score_mod`` with global query and
+  key indices).
+* a key (i, j) is *allowed* when the key-padding mask keeps key j of that batch
+  row (flash-attention-jax page, "Use flash_attention": mask of shape
+  (batch, seq); nonzero = keep, as in the attnax kernel body's
+  ``where(mask, scores, min)``) and, for causal attention, j <= i
+  (flash-attention-jax page, "Use causal_flash_attention").
+* lse_i = log sum_{j allowed} exp(s_ij), P_ij = exp(s_ij - lse_i) on allowed
+  pairs and 0 elsewhere, O_i = sum_j P_ij v_j.  This is the exact result the
+  online softmax of the attnax kernel body (running max, running sum, rescaled
+  accumulator, final division by the sum) arrives at.
+* a query row with no allowed key is an empty sum: O_i = 0, lse_i = -inf, and
+  its gradients are zero.  (The pages leave this open; the attnax kernel's
+  finite ``min`` fill would instead average V.)
+* backward, by calculus on the definition (the bias does not depend on the
+  scores, so it adds no term):
+  dP = dO V^T, D_i = sum_j P_ij dP_ij (= <dO_i, O_i>), dS = P * (dP - D),
+  dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
+
+score_mod kinds (the pages name them but do not define them; the readings
+are the workloads' own definitions):
+
+* ALiBi (flaxattention page, example: ``generate_alibi_bias(num_heads)``):
+  bias = -slope_h * (q_idx - kv_idx) with slope_h = 2^(-8 (h+1) / H).
+* checkerboard (flaxattention page, autograd example and benchmark):
+  bias = +even when (q_idx + kv_idx) is even, +odd otherwise
+  (defaults +0.5 / -0.5).
+
+Query rows may be restricted to a subset ``rows`` (global indices).  Then the
+forward returns those rows, and the backward returns dQ for those rows and the
+dK, dV that a dO which is zero outside those rows produces (the backward is
+linear in dO, so these are exact).
+
+Every function here is pinned by tests that do not use this module's
+arithmetic: closed forms, finite differences, hand-worked values and a
+library attention routine.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD = 0, 1, 2
+
+
+def as_f64(x) -> np.ndarray:
+    """Upcast a numpy array or a CPU torch tensor (any float dtype) to fp64."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def default_alibi_slopes(num_heads: int) -> np.ndarray:
+    """slope_h = 2^(-8 (h+1) / H), h = 0..H-1."""
+    h = np.arange(num_heads, dtype=np.float64)
+    return np.exp2(-8.0 * (h + 1.0) / num_heads)
+
+
+def score_bias(mod: int, h: int, q_idx: np.ndarray, kv_idx: np.ndarray, num_heads: int,
+               alibi_slopes: Optional[Sequence[float]] = None,
+               checker: Tuple[float, float] = (0.5, -0.5)) -> np.ndarray:
+    """Additive bias of shape (len(q_idx), len(kv_idx)) for head h."""
+    qi = np.asarray(q_idx, dtype=np.int64)[:, None]
+    kj = np.asarray(kv_idx, dtype=np.int64)[None, :]
+    if mod == MOD_NONE:
+        return np.zeros((qi.shape[0], kj.shape[1]))
+    if mod == MOD_ALIBI:
+        slopes = default_alibi_slopes(num_heads) if alibi_slopes is None else np.asarray(
+            alibi_slopes, dtype=np.float64)
+        return -slopes[h] * (qi - kj).astype(np.float64)
+    if mod == MOD_CHECKERBOARD:
+        even = ((qi + kj) % 2) == 0
+        return np.where(even, float(checker[0]), float(checker[1]))
+    raise ValueError(f"unknown score_mod kind {mod}")
+
+
+def allowed_pairs(q_idx: np.ndarray, seq_kv: int, causal: bool,
+                  key_mask_row: Optional[np.ndarray]) -> np.ndarray:
+    """Boolean (len(q_idx), seq_kv): key kept by the mask and, if causal, j <= i."""
+    kj = np.arange(seq_kv)[None, :]
+    ok = np.ones((len(q_idx), seq_kv), dtype=bool)
+    if key_mask_row is not None:
+        ok &= (np.asarray(key_mask_row) != 0)[None, :]
+    if causal:
+        ok &= kj <= np.asarray(q_idx)[:, None]
+    return ok
+
+
+def _probabilities(qb: np.ndarray, kb: np.ndarray, scale: float, bias: np.ndarray,
+                   ok: np.ndarray):
+    """Scores, lse and P for one (batch, head) and a block of query rows."""
+    s = scale * (qb @ kb.T) + bias
+    s_allowed = np.where(ok, s, -np.inf)
+    m = s_allowed.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    any_ok = np.isfinite(m)
+    m_safe = np.where(any_ok, m, 0.0)
+    e = np.where(ok, np.exp(s_allowed - m_safe[:, None]), 0.0)
+    tot = e.sum(axis=1)
+    with np.errstate(divide="ignore"):
+        lse = np.where(any_ok, m_safe + np.log(tot), -np.inf)
+    p = np.where(any_ok[:, None], e / np.where(any_ok, tot, 1.0)[:, None], 0.0)
+    return s, lse, p
+
+
+def _setup(q, k, v, rows, key_mask):
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    if (q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape[:3] != v.shape[:3]
+            or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]):
+        raise ValueError("q (B,H,Sq,D), k (B,H,Skv,D) and v (B,H,Skv,Dv) expected")
+    seq_q = q.shape[2]
+    rows = np.arange(seq_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    km = None if key_mask is None else as_f64(key_mask)
+    return q, k, v, rows, km
+
+
+def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
+            mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
+            rows: Optional[Sequence[int]] = None):
+    """Exact attention output and log-sum-exp.
+
+    Returns ``(o, lse)``: o (B, H, R, D), lse (B, H, R) in fp64, where R are the
+    requested query rows (all rows by default).
+    """
+    q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
+    B, H = q.shape[:2]
+    seq_kv = k.shape[2]
+    o = np.zeros((B, H, len(rows), v.shape[3]))
+    lse = np.zeros((B, H, len(rows)))
+    kv_idx = np.arange(seq_kv)
+    for b in range(B):
+        ok = allowed_pairs(rows, seq_kv, causal, None if km is None else km[b])
+        for h in range(H):
+            bias = score_bias(mod, h, rows, kv_idx, H, alibi_slopes, checker)
+            _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, ok)
+            o[b, h] = p @ v[b, h]
+    return o, lse
+
+
+def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None,
+             mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
+             rows: Optional[Sequence[int]] = None):
+    """Analytic gradients of sum(dout * O) with respect to q, k and v.
+
+    Returns ``(dq, dk, dv)``: dq (B, H, R, D) for the requested rows; dk and dv
+    (B, H, Skv, D) are the gradients for a dout that is zero outside those rows
+    (with all rows, the ordinary full gradient).
+    """
+    q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
+    do = as_f64(dout)
+    if do.shape != q.shape[:3] + v.shape[3:]:
+        raise ValueError("dout must have shape (B, H, Sq, Dv)")
+    B, H, _, D = q.shape
+    seq_kv = k.shape[2]
+    dq = np.zeros((B, H, len(rows), D))
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    kv_idx = np.arange(seq_kv)
+    for b in range(B):
+        ok = allowed_pairs(rows, seq_kv, causal, None if km is None else km[b])
+        for h in range(H):
+            bias = score_bias(mod, h, rows, kv_idx, H, alibi_slopes, checker)
+            qb, dob = q[b, h, rows], do[b, h, rows]
+            _, _, p = _probabilities(qb, k[b, h], scale, bias, ok)
+            dp = dob @ v[b, h].T
+            d_row = (p * dp).sum(axis=1)
+            ds = p * (dp - d_row[:, None])
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ qb)
+            dv[b, h] = p.T @ dob
+    return dq, dk, dv
+
+
+def decode(q, k, v, *, scale: float, key_mask=None, mod: int = MOD_NONE, alibi_slopes=None,
+           checker=(0.5, -0.5)):
+    """Single-query attention (seq_q = 1, query index 0): the forward at Sq = 1."""
+    q = as_f64(q)
+    if q.shape[2] != 1:
+        raise ValueError("decode takes seq_q = 1")
+    return forward(q, k, v, scale=scale, causal=False, key_mask=key_mask, mod=mod,
+                   alibi_slopes=alibi_slopes, checker=checker)

@@ -1,0 +1,427 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the definition or mathematics
+fixes: hand-worked values, closed forms (uniform scores, geometric series for
+ALiBi, parity counts for the checkerboard), central finite differences of the
+analytic backward, invariants, and an independent library attention routine
+(torch's fp64 CPU ``scaled_dot_product_attention`` with autograd).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import MOD_ALIBI, MOD_CHECKERBOARD, MOD_NONE
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _eval_expr(s):
+    env = {"e": math.e, "exp": math.exp, "log": math.log, "__builtins__": {}}
+    return float(eval(str(s), env))  # expressions from the hand-worked fixture only
+
+
+def _eval_tree(x):
+    if isinstance(x, list):
+        return [_eval_tree(y) for y in x]
+    return _eval_expr(x)
+
+
+# --------------------------------------------------------------------------- golden
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"][:40])
+def test_hand_worked_examples(case):
+    q, k, v = (np.array(case[n], dtype=np.float64) for n in ("q", "k", "v"))
+    km = None if case["key_mask"] is None else np.array(case["key_mask"])
+    kw = dict(scale=case["scale"], causal=case["causal"], key_mask=km, mod=case["mod"])
+    o, lse = oracle.forward(q, k, v, **kw)
+    np.testing.assert_allclose(o, np.array(_eval_tree(case["o"])), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.array(_eval_tree(case["lse"])), rtol=0, atol=1e-14)
+    if "dout" in case:
+        dq, dk, dv = oracle.backward(q, k, v, np.array(case["dout"], dtype=np.float64), **kw)
+        np.testing.assert_allclose(dq, np.array(_eval_tree(case["dq"])), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(dk, np.array(_eval_tree(case["dk"])), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(dv, np.array(_eval_tree(case["dv"])), rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- closed forms
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_uniform_scores_give_mean_of_v():
+    B, H, Sq, Skv, D = 2, 3, 7, 11, 5
+    q = np.zeros((B, H, Sq, D))
+    k, v = _rand((B, H, Skv, D), 1), _rand((B, H, Skv, D), 2)
+    o, lse = oracle.forward(q, k, v, scale=0.37)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(Skv), atol=1e-14)
+
+
+def test_uniform_scores_with_key_mask_give_mean_of_kept_v():
+    B, H, Sq, Skv, D = 2, 2, 4, 9, 3
+    q = np.zeros((B, H, Sq, D))
+    k, v = _rand((B, H, Skv, D), 3), _rand((B, H, Skv, D), 4)
+    km = np.array([[1, 0, 1, 1, 0, 0, 1, 0, 1], [0, 0, 0, 1, 0, 0, 0, 0, 0]], dtype=np.uint8)
+    o, lse = oracle.forward(q, k, v, scale=1.0, key_mask=km)
+    for b in range(B):
+        kept = km[b] != 0
+        np.testing.assert_allclose(o[b], np.broadcast_to(v[b][:, kept].mean(axis=1, keepdims=True), o[b].shape), atol=1e-14)
+        np.testing.assert_allclose(lse[b], math.log(kept.sum()), atol=1e-14)
+
+
+def test_causal_uniform_scores_give_cumulative_mean():
+    B, H, S, D = 1, 2, 13, 4
+    q = np.zeros((B, H, S, D))
+    k, v = _rand((B, H, S, D), 5), _rand((B, H, S, D), 6)
+    o, lse = oracle.forward(q, k, v, scale=0.5, causal=True)
+    cum = np.cumsum(v, axis=2) / np.arange(1, S + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, cum, atol=1e-14)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, S + 1))[None, None, :].repeat(H, 1), atol=1e-14)
+
+
+def test_causal_row_zero_is_single_key():
+    q, k, v = _rand((1, 1, 6, 4), 7), _rand((1, 1, 6, 4), 8), _rand((1, 1, 6, 4), 9)
+    o, lse = oracle.forward(q, k, v, scale=0.3, causal=True)
+    np.testing.assert_allclose(o[0, 0, 0], v[0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0, 0], 0.3 * q[0, 0, 0] @ k[0, 0, 0], atol=1e-15)
+
+
+@pytest.mark.parametrize("mod", [MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD])
+def test_single_kept_key(mod):
+    B, H, Sq, Skv, D = 1, 2, 5, 8, 3
+    q, k, v = _rand((B, H, Sq, D), 10), _rand((B, H, Skv, D), 11), _rand((B, H, Skv, D), 12)
+    do = _rand((B, H, Sq, D), 13)
+    j = 5
+    km = np.zeros((B, Skv), dtype=np.uint8)
+    km[0, j] = 1
+    o, lse = oracle.forward(q, k, v, scale=0.4, key_mask=km, mod=mod)
+    dq, dk, dv = oracle.backward(q, k, v, do, scale=0.4, key_mask=km, mod=mod)
+    for h in range(H):
+        np.testing.assert_allclose(o[0, h], np.broadcast_to(v[0, h, j], (Sq, D)), atol=1e-15)
+        bias = oracle.score_bias(mod, h, np.arange(Sq), np.array([j]), H)[:, 0]
+        np.testing.assert_allclose(lse[0, h], 0.4 * q[0, h] @ k[0, h, j] + bias, atol=1e-14)
+    np.testing.assert_allclose(dq, 0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0, atol=1e-15)
+    exp_dv = np.zeros_like(dv)
+    exp_dv[:, :, j] = do.sum(axis=2)
+    np.testing.assert_allclose(dv, exp_dv, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_alibi_geometric_series(causal):
+    """q = 0: s_ij = -slope (i - j); weights are powers of r = exp(-slope)."""
+    H, S = 4, 37
+    q = np.zeros((1, H, S, 2))
+    k = _rand((1, H, S, 2), 14)
+    j = np.arange(S, dtype=np.float64)
+    v = np.zeros((1, H, S, 2))
+    v[..., 0] = 1.0
+    v[..., 1] = j
+    o, lse = oracle.forward(q, k, v, scale=1.0, causal=causal, mod=MOD_ALIBI)
+    for h in range(H):
+        slope = 2.0 ** (-8.0 * (h + 1) / H)
+        r = math.exp(-slope)
+        for i in range(S):
+            n_back = i + 1                      # keys j <= i: weights r^0 .. r^i
+            z_back = (1 - r ** n_back) / (1 - r)
+            m_back = r * (1 - n_back * r ** (n_back - 1) + (n_back - 1) * r ** n_back) / (1 - r) ** 2
+            z, num = z_back, i * z_back - m_back  # sum_j j w_j with j = i - t
+            if not causal:
+                n_fwd = S - 1 - i               # keys j > i: weights (1/r)^1 .. (1/r)^n_fwd
+                g = 1.0 / r
+                z_fwd = g * (g ** n_fwd - 1) / (g - 1) if n_fwd else 0.0
+                # sum_{t=1}^{n} t g^t = g (1 - (n+1) g^n + n g^(n+1)) / (1-g)^2
+                m_fwd = g * (1 - (n_fwd + 1) * g ** n_fwd + n_fwd * g ** (n_fwd + 1)) / (1 - g) ** 2
+                z += z_fwd
+                num += i * z_fwd + m_fwd
+            assert abs(lse[0, h, i] - math.log(z)) < 1e-12
+            assert abs(o[0, h, i, 1] - num / z) < 1e-9 * max(1.0, abs(num / z))
+            assert abs(o[0, h, i, 0] - 1.0) < 1e-14
+
+
+def test_alibi_row_shift_invariance():
+    """The -slope*q_idx part is constant along a row: O is unchanged and lse
+    moves by exactly that constant when it is dropped."""
+    B, H, S, D = 1, 3, 9, 4
+    q, k, v = _rand((B, H, S, D), 15), _rand((B, H, S, D), 16), _rand((B, H, S, D), 17)
+    o1, lse1 = oracle.forward(q, k, v, scale=0.5, mod=MOD_ALIBI)
+    o0, lse0 = oracle.forward(q, k, v, scale=0.5)
+    slopes = oracle.default_alibi_slopes(H)
+    # reference: add slope*j through the key side by augmenting q, k with one extra dim
+    qa = np.concatenate([q, np.ones((B, H, S, 1))], axis=-1)
+    ka = np.concatenate([k, (slopes[None, :, None, None] / 0.5) * np.arange(S)[None, None, :, None]], axis=-1)
+    o2, lse2 = oracle.forward(qa, ka, v, scale=0.5)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    i = np.arange(S)
+    np.testing.assert_allclose(lse1, lse2 - slopes[None, :, None] * i[None, None, :], atol=1e-12)
+    assert np.abs(o1 - o0).max() > 1e-3  # the bias does change the result
+
+
+@pytest.mark.parametrize("Skv", [10, 11])
+def test_checkerboard_counts(Skv):
+    """q = 0, non-causal: s_ij = +0.5 on even (i+j), -0.5 on odd."""
+    Sq = 6
+    q = np.zeros((1, 1, Sq, 1))
+    k = _rand((1, 1, Skv, 1), 18)
+    v = ((-1.0) ** np.arange(Skv)).reshape(1, 1, Skv, 1)
+    o, lse = oracle.forward(q, k, v, scale=1.0, mod=MOD_CHECKERBOARD)
+    n_even_j = (Skv + 1) // 2
+    n_odd_j = Skv // 2
+    for i in range(Sq):
+        # keys with (i+j) even: j even when i is even, j odd when i is odd
+        n_plus = n_even_j if i % 2 == 0 else n_odd_j
+        n_minus = Skv - n_plus
+        z = n_plus * math.exp(0.5) + n_minus * math.exp(-0.5)
+        assert abs(lse[0, 0, i] - math.log(z)) < 1e-14
+        sign_plus = 1.0 if i % 2 == 0 else -1.0   # v_j = (-1)^j, and (-1)^j = (-1)^i on the + keys
+        expect = sign_plus * (n_plus * math.exp(0.5) - n_minus * math.exp(-0.5)) / z
+        assert abs(o[0, 0, i, 0] - expect) < 1e-14
+
+
+# --------------------------------------------------------------------------- invariants
+
+
+COMBOS = [(c, m, km) for c in (False, True) for m in (MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD)
+          for km in (False, True)]
+
+
+def _case(seed, B=2, H=2, Sq=6, Skv=6, D=3, key_mask=False, keep_all_first=True):
+    q, k, v = _rand((B, H, Sq, D), seed), _rand((B, H, Skv, D), seed + 1), _rand((B, H, Skv, D), seed + 2)
+    do = _rand((B, H, Sq, D), seed + 3)
+    km = None
+    if key_mask:
+        km = (np.random.default_rng(seed + 4).random((B, Skv)) < 0.6).astype(np.uint8)
+        km[:, 0] = 1 if keep_all_first else km[:, 0]
+    return q, k, v, do, km
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
+def test_ones_v_gives_ones(causal, mod, use_mask):
+    q, k, _, _, km = _case(20, key_mask=use_mask)
+    v = np.ones((2, 2, 6, 3))
+    o, _ = oracle.forward(q, k, v, scale=0.7, causal=causal, key_mask=km, mod=mod)
+    np.testing.assert_allclose(o, 1.0, atol=1e-14)
+
+
+def test_masked_key_with_garbage_is_ignored():
+    B, H, Sq, Skv, D = 1, 2, 5, 9, 4
+    q, k, v = _rand((B, H, Sq, D), 21), _rand((B, H, Skv, D), 22), _rand((B, H, Skv, D), 23)
+    km = np.ones((B, Skv), dtype=np.uint8)
+    km[0, 3] = 0
+    km[0, 7] = 0
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, [3, 7]] = 1e4
+    v2[:, :, [3, 7]] = -3e5
+    o, lse = oracle.forward(q, k2, v2, scale=0.5, key_mask=km)
+    keep = [j for j in range(Skv) if km[0, j]]
+    o_ref, lse_ref = oracle.forward(q, k[:, :, keep], v[:, :, keep], scale=0.5)
+    np.testing.assert_allclose(o, o_ref, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
+def test_backward_invariants(causal, mod, use_mask):
+    q, k, v, do, km = _case(30, key_mask=use_mask)
+    o, _ = oracle.forward(q, k, v, scale=0.6, causal=causal, key_mask=km, mod=mod)
+    dq, dk, dv = oracle.backward(q, k, v, do, scale=0.6, causal=causal, key_mask=km, mod=mod)
+    # every row keeps key 0 here, so every row has an allowed key
+    np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-13)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-13)
+    assert np.isfinite(o).all()
+
+
+def test_fully_masked_row_is_empty_sum():
+    B, H, S, D = 1, 1, 4, 3
+    q, k, v, do = (_rand((B, H, S, D), 40 + i) for i in range(4))
+    km = np.array([[0, 1, 1, 1]], dtype=np.uint8)   # row 0 (causal) sees only key 0, which is masked
+    o, lse = oracle.forward(q, k, v, scale=1.0, causal=True, key_mask=km)
+    assert np.all(o[0, 0, 0] == 0.0) and lse[0, 0, 0] == -np.inf
+    dq, dk, dv = oracle.backward(q, k, v, do, scale=1.0, causal=True, key_mask=km)
+    assert np.all(dq[0, 0, 0] == 0.0)
+    # rows 1..3 are unaffected by row 0's empty sum: compare with the row subset
+    o_r, lse_r = oracle.forward(q, k, v, scale=1.0, causal=True, key_mask=km, rows=[1, 2, 3])
+    np.testing.assert_allclose(o[0, 0, 1:], o_r[0, 0], atol=0)
+    assert np.isfinite(lse[0, 0, 1:]).all()
+
+
+# --------------------------------------------------------------------------- calculus
+
+
+def _loss(q, k, v, do, kw):
+    o, _ = oracle.forward(q, k, v, **kw)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
+def test_gradients_match_central_differences(causal, mod, use_mask):
+    B, H, S, D = 1, 2, 5, 3
+    q, k, v, do, km = _case(50, B=B, H=H, Sq=S, Skv=S, D=D, key_mask=use_mask)
+    kw = dict(scale=0.8, causal=causal, key_mask=km, mod=mod)
+    dq, dk, dv = oracle.backward(q, k, v, do, **kw)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = {"q": q, "k": k, "v": v}
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (_loss(args_p["q"], args_p["k"], args_p["v"], do, kw)
+                        - _loss(args_m["q"], args_m["k"], args_m["v"], do, kw)) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=1e-8, err_msg=f"d{name}")
+
+
+def _torch_bias(mod, B, H, Sq, Skv, causal, km):
+    """Additive float mask for torch SDPA, written independently of the oracle."""
+    i = torch.arange(Sq, dtype=torch.float64)[:, None]
+    j = torch.arange(Skv, dtype=torch.float64)[None, :]
+    bias = torch.zeros(B, H, Sq, Skv, dtype=torch.float64)
+    if mod == MOD_ALIBI:
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float64)
+        bias = bias + (slopes[:, None, None] * (j - i))[None]
+    elif mod == MOD_CHECKERBOARD:
+        bias = bias + torch.where(((i + j) % 2) == 0, 0.5, -0.5)[None, None]
+    neg = torch.zeros(B, 1, Sq, Skv, dtype=torch.float64)
+    if causal:
+        neg = neg.masked_fill(j > i, float("-inf"))
+    if km is not None:
+        neg = neg.masked_fill(torch.from_numpy(km == 0)[:, None, None, :], float("-inf"))
+    return bias + neg
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
+@pytest.mark.parametrize("shape", [(2, 3, 33, 33, 16), (1, 2, 17, 40, 8)])
+def test_against_torch_sdpa_fp64(causal, mod, use_mask, shape):
+    B, H, Sq, Skv, D = shape
+    if causal and Sq != Skv:
+        pytest.skip("causal attention is defined here for seq_q == seq_kv")
+    q, k, v, do, km = _case(60, B=B, H=H, Sq=Sq, Skv=Skv, D=D, key_mask=use_mask)
+    scale = 1.0 / math.sqrt(D)
+    kw = dict(scale=scale, causal=causal, key_mask=km, mod=mod)
+    o, lse = oracle.forward(q, k, v, **kw)
+    dq, dk, dv = oracle.backward(q, k, v, do, **kw)
+
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = _torch_bias(mod, B, H, Sq, Skv, causal, km)
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-13)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+    # lse against torch's logsumexp of the masked, biased scores
+    s = torch.matmul(torch.from_numpy(q), torch.from_numpy(k).transpose(-1, -2)) * scale + mask
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+# --------------------------------------------------------------------------- row subsets
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", [(True, MOD_ALIBI, False), (False, MOD_CHECKERBOARD, True)])
+def test_row_subset_matches_full_and_sparse_dout(causal, mod, use_mask):
+    q, k, v, do, km = _case(70, B=1, H=2, Sq=24, Skv=24, D=4, key_mask=use_mask)
+    kw = dict(scale=0.5, causal=causal, key_mask=km, mod=mod)
+    rows = [0, 3, 11, 23]
+    o, lse = oracle.forward(q, k, v, **kw)
+    o_r, lse_r = oracle.forward(q, k, v, rows=rows, **kw)
+    np.testing.assert_allclose(o_r, o[:, :, rows], atol=1e-15)
+    np.testing.assert_allclose(lse_r, lse[:, :, rows], atol=1e-15)
+    dq, _, _ = oracle.backward(q, k, v, do, **kw)
+    do_sparse = np.zeros_like(do)
+    do_sparse[:, :, rows] = do[:, :, rows]
+    _, dk_s, dv_s = oracle.backward(q, k, v, do_sparse, **kw)
+    dq_r, dk_r, dv_r = oracle.backward(q, k, v, do, rows=rows, **kw)
+    np.testing.assert_allclose(dq_r, dq[:, :, rows], atol=1e-14)
+    np.testing.assert_allclose(dk_r, dk_s, atol=1e-14)
+    np.testing.assert_allclose(dv_r, dv_s, atol=1e-14)
+
+
+def test_decode_is_forward_at_one_query():
+    q, k, v = _rand((2, 3, 1, 8), 80), _rand((2, 3, 50, 8), 81), _rand((2, 3, 50, 8), 82)
+    o, lse = oracle.decode(q, k, v, scale=0.25)
+    qa = np.zeros((2, 3, 1, 8)) + q
+    tq, tk, tv = (torch.from_numpy(x) for x in (qa, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.25)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-14)
+
+
+# --------------------------------------------------------------------------- planted mistakes
+
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible mistakes in the oracle (on the CPU) and check that the
+    pins above reject each of them."""
+    import oracle.attention as A
+    case = json.load(open(GOLDEN))["cases"]
+
+    def run_golden():
+        for c in case:
+            test_hand_worked_examples(c)
+
+    # 1) ALiBi sign flipped
+    orig_bias = A.score_bias
+
+    def flipped(mod, *a, **kw):
+        b = orig_bias(mod, *a, **kw)
+        return -b if mod == MOD_ALIBI else b
+    monkeypatch.setattr(A, "score_bias", flipped)
+    with pytest.raises(AssertionError):
+        test_alibi_geometric_series(True)
+    monkeypatch.setattr(A, "score_bias", orig_bias)
+
+    # 2) scale applied to the bias as well as the dot product
+    orig_probs = A._probabilities
+
+    def scaled_bias(qb, kb, scale, bias, ok):
+        return orig_probs(qb, kb, scale, scale * bias, ok)
+    monkeypatch.setattr(A, "_probabilities", scaled_bias)
+    with pytest.raises(AssertionError):
+        run_golden()
+    monkeypatch.setattr(A, "_probabilities", orig_probs)
+
+    # 3) causal mask transposed (j >= i instead of j <= i)
+    orig_allowed = A.allowed_pairs
+
+    def transposed(q_idx, seq_kv, causal, km):
+        ok = orig_allowed(q_idx, seq_kv, False, km)
+        if causal:
+            ok &= np.arange(seq_kv)[None, :] >= np.asarray(q_idx)[:, None]
+        return ok
+    monkeypatch.setattr(A, "allowed_pairs", transposed)
+    with pytest.raises(AssertionError):
+        test_causal_uniform_scores_give_cumulative_mean()
+    monkeypatch.setattr(A, "allowed_pairs", orig_allowed)
+
+    # 4) backward without the D_i term
+    def bad_backward(q, k, v, dout, *, scale, causal=False, key_mask=None, mod=0,
+                     alibi_slopes=None, checker=(0.5, -0.5), rows=None):
+        q, k, v, rows, km = A._setup(q, k, v, rows, key_mask)
+        do = A.as_f64(dout)
+        B, H, _, D = q.shape
+        dq = np.zeros((B, H, len(rows), D))
+        dk, dv = np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            ok = A.allowed_pairs(rows, k.shape[2], causal, None if km is None else km[b])
+            for h in range(H):
+                bias = A.score_bias(mod, h, rows, np.arange(k.shape[2]), H, alibi_slopes, checker)
+                _, _, p = A._probabilities(q[b, h, rows], k[b, h], scale, bias, ok)
+                ds = p * (do[b, h, rows] @ v[b, h].T)
+                dq[b, h] = scale * ds @ k[b, h]
+                dk[b, h] = scale * ds.T @ q[b, h, rows]
+                dv[b, h] = p.T @ do[b, h, rows]
+        return dq, dk, dv
+    monkeypatch.setattr(oracle, "backward", bad_backward)
+    with pytest.raises(AssertionError):
+        test_gradients_match_central_differences(False, MOD_NONE, False)
