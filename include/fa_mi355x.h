@@ -1,0 +1,142 @@
+/*
+ * fa_mi355x.h - C ABI of the tiled online-softmax attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes exact attention
+ *
+ *     O = softmax(scale * Q K^T + score_mod + mask) V
+ *
+ * tile by tile with an online softmax (running row max m, running row sum l,
+ * accumulator rescaled by exp(m_old - m_new)), so the seq_q x seq_kv score
+ * matrix is never written to memory.  This is the computation of the attnax
+ * ``pallas_flash_attention`` page (kernel body: per query block, a loop over
+ * key/value blocks that forms scores, applies score_mod with global indices,
+ * applies the mask, then updates max, sum and accumulator and divides at the
+ * end), with the input layout of the flash-attention-jax page ("Use
+ * flash_attention": q, k, v as (batch, heads, seq, dim), key mask as
+ * (batch, seq)), its causal variant ("Use causal_flash_attention"), and the
+ * score_mods named on the flaxattention page (ALiBi in the example,
+ * checkerboard in the autograd example and benchmark).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, contiguous, row-major:
+ *     q, out, dout, dq          (batch, heads, seq_q,  head_dim)
+ *     k, v, dk, dv              (batch, heads, seq_kv, head_dim)
+ *     lse                       (batch, heads, seq_q)  float32, natural log
+ *     key_mask                  (batch, seq_kv) uint8, nonzero = keep the key
+ *   q, k, v, out, dout, dq, dk, dv all have the element type ``dtype``.
+ * - Every pointer named as a tensor is a DEVICE pointer on the current HIP
+ *   device, 16-byte aligned.  The ``fa_problem`` struct itself is a host
+ *   pointer read only during the call.
+ * - The caller owns all memory.  The library allocates nothing, keeps no
+ *   state between calls and only enqueues work on ``stream`` (a hipStream_t;
+ *   NULL means the legacy default stream).  Results are ready when the stream
+ *   reaches them; device faults surface at the caller's synchronisation.
+ * - Outputs must not alias inputs.  Calls on different streams may run
+ *   concurrently when their outputs and workspaces are disjoint.
+ * - Arguments are validated on the host before anything is enqueued; a
+ *   non-zero fa_status means nothing was launched (except FA_ERR_HIP, which
+ *   reports a failed launch).  There is no fallback path.
+ *
+ * Semantics
+ * ---------
+ * s_ij = scale * <q_i, k_j> + bias_h(i, j), where i and j are global 0-based
+ * query and key positions and the bias is NOT multiplied by scale.  Key j is
+ * allowed for query i when key_mask[b][j] != 0 (or key_mask == NULL) and, if
+ * causal, j <= i.  lse_i = log sum_{allowed j} exp(s_ij); out_i =
+ * sum_{allowed j} exp(s_ij - lse_i) v_j.  A row with no allowed key gets
+ * out_i = 0, lse_i = -inf and zero gradients.  Score, softmax and
+ * accumulation arithmetic is float32; probabilities are rounded to ``dtype``
+ * before the probability-times-V product for the 16-bit types.
+ */
+#ifndef FA_MI355X_H_
+#define FA_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum, bad shape */
+  FA_ERR_UNSUPPORTED = 2,        /* valid request outside what the kernels implement */
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,
+  FA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/* score_mod kinds (flaxattention page: example and benchmark).
+ *  FA_MOD_ALIBI:        bias = -slope_h * (i - j).  slope_h comes from
+ *                       alibi_slopes[h] (device float[heads]) or, when that is
+ *                       NULL, slope_h = 2^(-8 (h + 1) / heads).
+ *  FA_MOD_CHECKERBOARD: bias = checker_even when (i + j) is even, otherwise
+ *                       checker_odd (the workloads use +0.5 / -0.5). */
+typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2 } fa_mod_kind;
+
+typedef struct {
+  int64_t batch, heads, seq_q, seq_kv, head_dim;
+  int32_t dtype;             /* fa_dtype */
+  int32_t causal;            /* 0 or 1; 1 requires seq_q == seq_kv (key j <= query i) */
+  float scale;               /* multiplies q.k; pass 1/sqrt(head_dim) for the usual scaling */
+  int32_t mod_kind;          /* fa_mod_kind */
+  const float* alibi_slopes; /* device float[heads] or NULL (FA_MOD_ALIBI only) */
+  float checker_even;        /* FA_MOD_CHECKERBOARD only */
+  float checker_odd;
+  const uint8_t* key_mask;   /* device uint8 (batch, seq_kv), nonzero = keep; NULL = keep all */
+} fa_problem;
+
+/* Supported: dtype f16 or bf16 with head_dim 64 or 128; dtype f32 with
+ * head_dim 64, 128 or 512.  Any seq_q, seq_kv >= 1 (ragged tails are masked
+ * inside the kernels).  Sizes must keep every tensor under 2^31 elements per
+ * (batch, head) slice and batch * heads under 2^31. */
+
+/* Forward (attnax kernel body: online-softmax loop, final acc / l).
+ * Writes out (dtype) and, when lse != NULL, lse (float32, natural log).  The
+ * backward needs lse. */
+fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const void* v,
+                     void* out, float* lse, void* stream);
+
+/* Bytes of device workspace fa_backward needs for problem p (written to *bytes). */
+fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes);
+
+/* Backward: gradients of sum(dout * out) with respect to q, k and v, with the
+ * probabilities recomputed from the saved lse (no score matrix is stored).
+ * out and lse must be the values fa_forward produced for the same inputs.
+ * The workspace (>= fa_backward_workspace_size bytes, 256-byte aligned) is
+ * scratch: its contents on entry are ignored and on exit undefined.  Every
+ * kernel is deterministic: repeated calls give bitwise-equal results. */
+fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, const void* dout,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Bytes of device workspace fa_decode needs for problem p (seq_q must be 1). */
+fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
+
+/* Decode: one query per (batch, head) (seq_q == 1, query position 0,
+ * causal == 0) against seq_kv keys, split over the key axis into chunks whose
+ * partial (max, sum, accumulator) are merged exactly.  The flaxattention page
+ * (decoding benchmark and TODO list) singles this case out.  f16, bf16 and
+ * f32 with head_dim 64 or 128.  Same outputs as fa_forward at seq_q = 1. */
+fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H_ */

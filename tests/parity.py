@@ -1,0 +1,130 @@
+"""Helpers shared by the GPU parity tests: run the HIP library and the fp64
+oracle on the same seeded inputs and measure the difference."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import tiled_online_softmax_flashattention_amd as fa
+import workloads as W
+
+MOD_NAME = {W.MOD_NONE: None, W.MOD_ALIBI: "alibi", W.MOD_CHECKERBOARD: "checkerboard"}
+
+# Tolerances (fp32: max-abs-err; 16-bit: max-abs-err / max|ref|).
+TOL_F32 = {"o": 1e-4, "grad": 1e-5}
+TOL_16 = {"o": 2e-2, "grad": 5e-2}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def err(gpu: torch.Tensor, ref: np.ndarray, dtype: str) -> float:
+    g = gpu.detach().double().cpu().numpy()
+    d = np.abs(g - ref).max() if ref.size else 0.0
+    if dtype == "f32":
+        return float(d)
+    scale = np.abs(ref).max() if ref.size else 1.0
+    return float(d / max(scale, 1e-30))
+
+
+def check(name: str, gpu: torch.Tensor, ref: np.ndarray, dtype: str, kind: str) -> float:
+    tol = (TOL_F32 if dtype == "f32" else TOL_16)[kind]
+    e = err(gpu, ref, dtype)
+    assert np.isfinite(gpu.detach().double().cpu().numpy()).all(), f"{name}: non-finite values"
+    assert e <= tol, f"{name}: error {e:.3e} > {tol:.1e}"
+    return e
+
+
+def check_lse(gpu: torch.Tensor, ref: np.ndarray) -> None:
+    g = gpu.detach().double().cpu().numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(g), fin), "lse: empty rows differ"
+    assert np.all(g[~fin] == -np.inf)
+    if fin.any():
+        d = np.abs(g[fin] - ref[fin])
+        assert (d <= 1e-3 + 1e-5 * np.abs(ref[fin])).all(), f"lse: max error {d.max():.3e}"
+
+
+def kw_of(w: W.Workload) -> dict:
+    return dict(causal=w.causal, score_mod=MOD_NAME[w.mod], scale=w.scale)
+
+
+def oracle_kw(w: W.Workload, inputs: dict) -> dict:
+    return dict(scale=w.scale, causal=w.causal, mod=w.mod,
+                key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+
+
+def to_dev(inputs: dict) -> dict:
+    return {k: (None if v is None else v.cuda()) for k, v in inputs.items()}
+
+
+def run_forward(w: W.Workload, dev: dict):
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], key_mask=dev.get("key_mask"), **kw_of(w))
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_backward(w: W.Workload, dev: dict, out, lse, dout):
+    g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dout, key_mask=dev.get("key_mask"), **kw_of(w))
+    torch.cuda.synchronize()
+    return g
+
+
+def full_parity(w: W.Workload, backward: bool = True, inputs=None) -> dict:
+    """Every output element against the oracle (sizes the oracle finishes quickly)."""
+    say(f"[parity] {w.name} B{w.batch} H{w.heads} Sq{w.seq_q} Skv{w.seq_kv} D{w.head_dim} {w.dtype} "
+        f"causal={w.causal} mod={w.mod} mask={w.key_mask}")
+    inputs = inputs or w.make(with_dout=backward)
+    dev = to_dev(inputs)
+    out, lse = run_forward(w, dev)
+    okw = oracle_kw(w, inputs)
+    o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
+    res = {"o": check("o", out, o_ref, w.dtype, "o")}
+    check_lse(lse, lse_ref)
+    if backward:
+        dq, dk, dv = run_backward(w, dev, out, lse, dev["dout"])
+        dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
+        res["dq"] = check("dq", dq, dq_r, w.dtype, "grad")
+        res["dk"] = check("dk", dk, dk_r, w.dtype, "grad")
+        res["dv"] = check("dv", dv, dv_r, w.dtype, "grad")
+    say(f"[parity] ok {res}")
+    return res
+
+
+def sampled_parity(w: W.Workload, n_rows: int, backward: bool = True) -> dict:
+    """Large shapes: O, lse and dQ on sampled query rows; all dK, dV rows from
+    a second backward whose dO is zero outside the sampled rows (exact, since
+    the backward is linear in dO)."""
+    say(f"[sampled] {w.name}: generating inputs")
+    inputs = w.make(with_dout=backward)
+    rows = W.sample_rows(w.seq_q, n_rows, w.workload_id)
+    dev = to_dev(inputs)
+    say(f"[sampled] {w.name}: forward on GPU")
+    out, lse = run_forward(w, dev)
+    okw = oracle_kw(w, inputs)
+    say(f"[sampled] {w.name}: oracle forward on {len(rows)} rows")
+    o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], rows=rows, **okw)
+    r = torch.from_numpy(rows).cuda()
+    res = {"o": check("o", out[:, :, r], o_ref, w.dtype, "o")}
+    check_lse(lse[:, :, r], lse_ref)
+    if backward:
+        say(f"[sampled] {w.name}: backward on GPU (dense dO)")
+        dq, _, _ = run_backward(w, dev, out, lse, dev["dout"])
+        dq_s = dq[:, :, r].cpu()
+        del dq
+        sparse = torch.zeros_like(dev["dout"])
+        sparse[:, :, r] = dev["dout"][:, :, r]
+        say(f"[sampled] {w.name}: backward on GPU (dO zero outside sampled rows)")
+        _, dk, dv = run_backward(w, dev, out, lse, sparse)
+        say(f"[sampled] {w.name}: oracle backward on {len(rows)} rows")
+        dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], rows=rows, **okw)
+        res["dq"] = check("dq", dq_s, dq_r, w.dtype, "grad")
+        res["dk"] = check("dk", dk, dk_r, w.dtype, "grad")
+        res["dv"] = check("dv", dv, dv_r, w.dtype, "grad")
+    say(f"[sampled] ok {res}")
+    return res

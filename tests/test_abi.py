@@ -1,0 +1,135 @@
+"""The C ABI loads, exports every symbol the header declares, and rejects bad
+arguments on the host before anything reaches the GPU (no compute calls here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from tiled_online_softmax_flashattention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Fake, 256-byte aligned device addresses: validation must reject the call
+# before any of them could be dereferenced.
+A = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(12)]
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fa_[a-z0-9_]+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("fa_forward", "fa_backward", "fa_decode", "fa_backward_workspace_size",
+               "fa_decode_workspace_size", "fa_status_string", "fa_abi_version"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_lib.SIGNATURES) == declared_functions()
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.fa_abi_version() == 1
+    for s in range(5):
+        assert lib.fa_status_string(s)
+    assert lib.fa_status_string(99) == b"unknown status"
+
+
+def prob(**kw):
+    p = _lib.FaProblem()
+    p.batch, p.heads, p.seq_q, p.seq_kv, p.head_dim = 2, 4, 100, 100, 64
+    p.dtype, p.causal, p.scale, p.mod_kind = _lib.FA_F16, 0, 0.125, 0
+    p.checker_even, p.checker_odd = 0.5, -0.5
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def fwd(p, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4]):
+    return _lib.load().fa_forward(ctypes.byref(p) if p is not None else None, q, k, v, o, lse, None)
+
+
+def bwd(p, ws_bytes=1 << 30, ws=A[11], **override):
+    ptrs = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8])
+    ptrs.update(override)
+    return _lib.load().fa_backward(ctypes.byref(p), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["lse"],
+                                   ptrs["do"], ptrs["dq"], ptrs["dk"], ptrs["dv"], ws, ws_bytes, None)
+
+
+def dec(p, ws_bytes=1 << 30, ws=A[11]):
+    return _lib.load().fa_decode(ctypes.byref(p), A[0], A[1], A[2], A[3], A[4], ws, ws_bytes, None)
+
+
+INVALID, UNSUP, WS = _lib.FA_ERR_INVALID_ARGUMENT, _lib.FA_ERR_UNSUPPORTED, _lib.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("heads", -1), ("seq_q", 0), ("seq_kv", 0),
+                                         ("head_dim", 0), ("dtype", 7), ("causal", 2), ("mod_kind", 3),
+                                         ("scale", float("nan")), ("scale", float("inf"))])
+def test_invalid_problem_fields(field, value):
+    assert fwd(prob(**{field: value})) == INVALID
+
+
+def test_null_problem_and_pointers():
+    assert fwd(None) == INVALID
+    assert fwd(prob(), q=None) == INVALID
+    assert fwd(prob(), o=None) == INVALID
+    assert fwd(prob(), k=ctypes.c_void_p(0x10008)) == INVALID       # not 16-byte aligned
+    assert fwd(prob(), lse=ctypes.c_void_p(0x10002)) == INVALID
+
+
+def test_causal_needs_square():
+    assert fwd(prob(causal=1, seq_kv=101)) == INVALID
+
+
+def test_unsupported_head_dims():
+    assert fwd(prob(head_dim=96)) == UNSUP
+    assert fwd(prob(head_dim=512)) == UNSUP                      # 512 is fp32-only
+    assert fwd(prob(head_dim=256, dtype=_lib.FA_F32)) == UNSUP
+
+
+def test_checkerboard_needs_finite_values():
+    assert fwd(prob(mod_kind=2, checker_even=float("nan"))) == INVALID
+
+
+def test_oversized_problem():
+    assert fwd(prob(seq_q=1 << 26, seq_kv=1 << 26)) == UNSUP
+
+
+def test_backward_workspace_rules():
+    lib = _lib.load()
+    p = prob(seq_q=300, seq_kv=300)
+    n = ctypes.c_size_t(0)
+    assert lib.fa_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.FA_OK
+    rows = 2 * 4 * 300
+    assert n.value >= 2 * rows * 4 and n.value % 256 == 0
+    assert bwd(p, ws_bytes=n.value - 1) == WS
+    assert bwd(p, ws=None) == INVALID
+    assert bwd(p, ws=ctypes.c_void_p(0x10010)) == INVALID            # workspace must be 256-byte aligned
+    assert bwd(p, lse=None) == INVALID
+    assert bwd(p, dk=None) == INVALID
+    assert lib.fa_backward_workspace_size(ctypes.byref(p), None) == INVALID
+
+
+def test_decode_rules():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=2, seq_kv=4096)), ctypes.byref(n)) == INVALID
+    p = prob(seq_q=1, seq_kv=32768)
+    assert lib.fa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.FA_OK
+    assert n.value > 0 and n.value % 256 == 0
+    assert dec(p, ws_bytes=n.value - 1) == WS
+    assert dec(prob(seq_q=2)) == INVALID
+    assert dec(prob(seq_q=1, head_dim=512, dtype=_lib.FA_F32)) == UNSUP

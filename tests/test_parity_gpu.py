@@ -1,0 +1,180 @@
+"""GPU parity: the HIP library against the fp64 oracle on identical seeded inputs.
+
+Bars: fp32 max-abs-err <= 1e-4 on O and <= 1e-5 on dQ/dK/dV; f16/bf16
+max-abs-err / max|ref| <= 2e-2 on O and <= 5e-2 on each gradient; lse within
+1e-3 + 1e-5 |lse|.  Small cases compare every element; the five workloads at
+their full sizes compare sampled rows (and all dK/dV rows through a sparse dO).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_online_softmax_flashattention_amd as fa
+import workloads as W
+from parity import check, check_lse, full_parity, oracle_kw, sampled_parity, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+MODS = [W.MOD_NONE, W.MOD_ALIBI, W.MOD_CHECKERBOARD]
+
+
+def small(dtype, D, causal, mod, mask, Sq=200, Skv=333, B=2, H=2, wid=100):
+    if causal:
+        Skv = Sq
+    return W.Workload(f"small {dtype} D{D}", wid, B, H, Sq, Skv, D, dtype, causal=causal, mod=mod, key_mask=mask)
+
+
+INSTANCES = [(dt, D, c, m, k) for dt, Ds in (("f16", (64, 128)), ("bf16", (64, 128)), ("f32", (64, 128)))
+             for D in Ds for c in (False, True) for m in MODS for k in (False, True)]
+
+
+@pytest.mark.parametrize("dtype,D,causal,mod,mask", INSTANCES)
+def test_every_instance_small(gpu_lib, dtype, D, causal, mod, mask):
+    full_parity(small(dtype, D, causal, mod, mask))
+
+
+@pytest.mark.parametrize("causal,mod,mask", [(c, m, k) for c in (False, True) for m in MODS for k in (False, True)])
+def test_f32_d512_small(gpu_lib, causal, mod, mask):
+    full_parity(small("f32", 512, causal, mod, mask, Sq=80, Skv=130, B=1, H=2))
+
+
+@pytest.mark.parametrize("S", [1, 17, 63, 64, 65, 127, 129, 255, 257])
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 512)])
+def test_ragged_causal_lengths(gpu_lib, S, dtype, D):
+    full_parity(small(dtype, D, True, W.MOD_ALIBI, False, Sq=S, B=1, H=3, wid=101))
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (1, 300), (300, 1), (5, 70), (129, 64), (64, 129)])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_ragged_noncausal_shapes(gpu_lib, Sq, Skv, dtype):
+    full_parity(small(dtype, 64, False, W.MOD_CHECKERBOARD, True, Sq=Sq, Skv=Skv, B=2, H=1, wid=102))
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 512)])
+def test_fully_masked_rows_are_empty(gpu_lib, dtype, D):
+    """Causal with the first keys masked: the first rows have no allowed key,
+    so O = 0, lse = -inf and dQ = 0 there (the empty-sum reading)."""
+    w = small(dtype, D, True, W.MOD_NONE, True, Sq=70, B=1, H=2, wid=103)
+    inputs = w.make()
+    km = torch.ones(1, 70, dtype=torch.uint8)
+    km[0, :3] = 0
+    inputs["key_mask"] = km
+    res = full_parity(w, inputs=inputs)
+    dev = to_dev(inputs)
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True, key_mask=dev["key_mask"])
+    assert torch.all(out[:, :, :3] == 0) and torch.all(lse[:, :, :3] == float("-inf"))
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], causal=True, key_mask=dev["key_mask"])
+    assert torch.all(dq[:, :, :3] == 0)
+    assert res
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_masked_keys_with_garbage_are_ignored(gpu_lib, dtype):
+    w = small(dtype, 64, False, W.MOD_NONE, True, Sq=90, Skv=150, B=2, H=2, wid=104)
+    inputs = w.make()
+    km = inputs["key_mask"]
+    bad = (km == 0)
+    for name in ("k", "v"):
+        t = inputs[name].clone()
+        t.permute(0, 2, 1, 3)[bad] = 300.0   # finite, huge values in masked rows
+        inputs[name] = t
+    full_parity(w, inputs=inputs)
+
+
+def test_backward_is_deterministic(gpu_lib):
+    for dtype, D, causal in (("f16", 64, True), ("bf16", 128, False), ("f32", 512, True)):
+        w = small(dtype, D, causal, W.MOD_ALIBI, False, Sq=150, B=1, H=2, wid=105)
+        say(f"[determinism] {dtype} D{D} causal={causal}")
+        dev = to_dev(w.make())
+        out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, score_mod="alibi")
+        g1 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], causal=causal, score_mod="alibi")
+        out2, lse2 = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, score_mod="alibi")
+        g2 = fa.backward(dev["q"], dev["k"], dev["v"], out2, lse2, dev["dout"], causal=causal, score_mod="alibi")
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
+def test_uniform_scores_full_shape_invariants(gpu_lib):
+    """q = 0 at a long causal shape: O_i is the running mean of V and
+    lse_i = log(i+1), checkable for every row without the oracle."""
+    S, D = 4096, 64
+    v = W.normal((1, 2, S, D), "f32", 106, W.V).cuda()
+    q = torch.zeros_like(v)
+    k = W.normal((1, 2, S, D), "f32", 106, W.K).cuda()
+    out, lse = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    vd = v.double().cpu()
+    cum = torch.cumsum(vd, dim=2) / torch.arange(1, S + 1, dtype=torch.float64)[None, None, :, None]
+    assert (out.double().cpu() - cum).abs().max().item() < 3e-5
+    ref = torch.log(torch.arange(1, S + 1, dtype=torch.float64))
+    assert (lse.double().cpu() - ref).abs().max().item() < 3e-5
+
+
+# ------------------------------------------------------------------ decode
+
+
+def decode_case(dtype, D, Skv, mod, mask, B=3, H=2, wid=110):
+    w = W.Workload(f"decode {dtype}", wid, B, H, 1, Skv, D, dtype, mod=mod, key_mask=mask, backward=False)
+    say(f"[decode] {dtype} D{D} Skv{Skv} mod={mod} mask={mask}")
+    inputs = w.make()
+    dev = to_dev(inputs)
+    out, lse = fa.decode(dev["q"], dev["k"], dev["v"], key_mask=dev.get("key_mask"),
+                         score_mod={0: None, 1: "alibi", 2: "checkerboard"}[mod], scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(inputs["q"], inputs["k"], inputs["v"], **{k: v for k, v in oracle_kw(w, inputs).items() if k != "causal"})
+    check("decode o", out, o_ref, dtype, "o")
+    check_lse(lse, lse_ref)
+    return dev, out, lse, w
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("f16", 128), ("bf16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("Skv", [1, 77, 2053])
+@pytest.mark.parametrize("mod,mask", [(W.MOD_NONE, False), (W.MOD_ALIBI, True), (W.MOD_CHECKERBOARD, False)])
+def test_decode_small(gpu_lib, dtype, D, Skv, mod, mask):
+    decode_case(dtype, D, Skv, mod, mask)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_decode_matches_forward_at_one_query(gpu_lib, dtype):
+    dev, out, lse, w = decode_case(dtype, 64, 4100, W.MOD_CHECKERBOARD, True)
+    out2, lse2 = fa.forward(dev["q"], dev["k"], dev["v"], key_mask=dev["key_mask"], score_mod="checkerboard")
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert (out.float() - out2.float()).abs().max().item() <= tol * max(1.0, out2.float().abs().max().item())
+    assert (lse - lse2).abs().max().item() < 1e-4
+
+
+# ------------------------------------------------------------- the workloads
+
+
+def test_workload_tiny_f32_exact(gpu_lib):
+    full_parity(W.TINY_F32)
+
+
+def test_workload_prefill_f16_causal_alibi(gpu_lib):
+    sampled_parity(W.PREFILL_F16, 128)
+
+
+def test_workload_keypad_bf16_checkerboard(gpu_lib):
+    sampled_parity(W.KEYPAD_BF16, 64)
+
+
+@pytest.mark.parametrize("w", [W.DECODE_F16_2K, W.DECODE_F16_32K], ids=["2k", "32k"])
+def test_workload_decode_f16(gpu_lib, w):
+    inputs = w.make()
+    dev = to_dev(inputs)
+    say(f"[workload] {w.name}")
+    out, lse = fa.decode(dev["q"], dev["k"], dev["v"], scale=w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(inputs["q"], inputs["k"], inputs["v"], scale=w.scale)
+    check("decode o", out, o_ref, "f16", "o")
+    check_lse(lse, lse_ref)
+
+
+def test_workload_long_f32_d512_causal(gpu_lib):
+    sampled_parity(W.LONG_F32, 256)

@@ -1,0 +1,144 @@
+"""Tiled online-softmax attention for AMD Instinct MI355X (gfx950).
+
+Thin binding over the C ABI in ``include/fa_mi355x.h``: it only marshals
+torch tensors (device memory) and the current HIP stream into the library
+calls.  Every step of the computation runs in the library's HIP kernels; there
+is no CPU or PyTorch fallback, and a missing library raises.
+
+    out, lse = forward(q, k, v, causal=..., key_mask=..., score_mod=...)
+    dq, dk, dv = backward(q, k, v, out, lse, dout, ...)
+    out, lse = decode(q, k, v, ...)              # seq_q == 1, split over keys
+
+q, k, v: (batch, heads, seq, head_dim) contiguous cuda tensors of one dtype
+(float32, float16 or bfloat16); key_mask: (batch, seq_kv) uint8/bool,
+nonzero = keep; score_mod: None, "alibi" or "checkerboard".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FaError
+
+__all__ = ["forward", "backward", "decode", "backward_workspace_bytes", "decode_workspace_bytes",
+           "FaError", "problem"]
+
+_DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
+_MOD = {None: _lib.FA_MOD_NONE, "none": _lib.FA_MOD_NONE, "alibi": _lib.FA_MOD_ALIBI,
+        "checkerboard": _lib.FA_MOD_CHECKERBOARD}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
+            key_mask: Optional[torch.Tensor] = None, score_mod: Optional[str] = None,
+            scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
+            checker: Tuple[float, float] = (0.5, -0.5)) -> _lib.FaProblem:
+    """The C-ABI problem descriptor for these tensors."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be (batch, heads, seq, head_dim)")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if score_mod not in _MOD:
+        raise ValueError(f"unknown score_mod {score_mod!r}")
+    B, H, Sq, D = q.shape
+    p = _lib.FaProblem()
+    p.batch, p.heads, p.seq_q, p.seq_kv, p.head_dim = B, H, Sq, k.shape[2], D
+    p.dtype = _DTYPE[q.dtype]
+    p.causal = int(bool(causal))
+    p.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
+    p.mod_kind = _MOD[score_mod]
+    p.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
+    p.checker_even, p.checker_odd = float(checker[0]), float(checker[1])
+    p.key_mask = None if key_mask is None else key_mask.data_ptr()
+    return p
+
+
+def _check_tensors(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same cuda device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _mask_u8(key_mask):
+    if key_mask is None:
+        return None
+    return key_mask.to(torch.uint8).contiguous() if key_mask.dtype != torch.uint8 else key_mask.contiguous()
+
+
+def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
+            checker=(0.5, -0.5), out=None, lse=None):
+    """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, key_mask, alibi_slopes)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = _lib.load()
+    _lib.check(lib.fa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q)),
+               "fa_forward")
+    return out, lse
+
+
+def backward_workspace_bytes(p: _lib.FaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().fa_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)), "fa_backward_workspace_size")
+    return int(n.value)
+
+
+def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
+             alibi_slopes=None, checker=(0.5, -0.5), workspace=None, grads=None):
+    """Gradients (dq, dk, dv) of sum(dout * out)."""
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    need = backward_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    lib = _lib.load()
+    _lib.check(lib.fa_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)),
+               "fa_backward")
+    return dq, dk, dv
+
+
+def decode_workspace_bytes(p: _lib.FaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().fa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)), "fa_decode_workspace_size")
+    return int(n.value)
+
+
+def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5),
+           workspace=None, out=None, lse=None):
+    """Single-query attention (seq_q == 1), split over the key axis."""
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, key_mask, alibi_slopes)
+    p = problem(q, k, causal=False, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    need = decode_workspace_bytes(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = _lib.load()
+    _lib.check(lib.fa_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                             workspace.numel(), _stream(q)), "fa_decode")
+    return out, lse

@@ -1,0 +1,224 @@
+// C ABI of the attention library: argument validation on the host, choice of
+// kernel instance, workspace sizing and launches on the caller's stream.
+//
+// Validation touches no HIP API, so every error path can be exercised on a
+// machine without a GPU.  Nothing here allocates device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa_mi355x.h"
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool head_dim_supported(int32_t dtype, int64_t d) {
+  if (dtype == FA_F32) return d == 64 || d == 128 || d == 512;
+  return d == 64 || d == 128;
+}
+
+// Checks shared by every entry point.  Pure host logic.
+fa_status validate_problem(const fa_problem* p) {
+  if (!p) return FA_ERR_INVALID_ARGUMENT;
+  if (p->batch <= 0 || p->heads <= 0 || p->seq_q <= 0 || p->seq_kv <= 0 || p->head_dim <= 0)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
+  if (p->causal != 0 && p->causal != 1) return FA_ERR_INVALID_ARGUMENT;
+  if (p->mod_kind != FA_MOD_NONE && p->mod_kind != FA_MOD_ALIBI && p->mod_kind != FA_MOD_CHECKERBOARD)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(p->scale)) return FA_ERR_INVALID_ARGUMENT;
+  if (p->mod_kind == FA_MOD_CHECKERBOARD && (!isfinite(p->checker_even) || !isfinite(p->checker_odd)))
+    return FA_ERR_INVALID_ARGUMENT;
+  if (p->causal && p->seq_q != p->seq_kv) return FA_ERR_INVALID_ARGUMENT;
+  if (p->alibi_slopes && ((uintptr_t)p->alibi_slopes & 3u)) return FA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
+  // index arithmetic inside the kernels is 32-bit per (batch, head) slice
+  if (p->batch * p->heads > kMaxI32 / 8) return FA_ERR_UNSUPPORTED;
+  if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;
+  if (p->batch > kMaxI32 / p->seq_kv) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+bool tensors_ok(std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (!x || !aligned16(x)) return false;
+  return true;
+}
+
+int block_q_fwd(const fa_problem* p) {
+  return p->dtype == FA_F32 ? fa::fwd32_block_q((int)p->head_dim) : fa::fwd16_block_q();
+}
+
+fa::AttnArgs make_args(const fa_problem* p) {
+  fa::AttnArgs a = {};
+  a.B = (int)p->batch;
+  a.H = (int)p->heads;
+  a.Sq = (int)p->seq_q;
+  a.Skv = (int)p->seq_kv;
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * fa::kLog2e;
+  a.key_mask = p->key_mask;
+  a.alibi_slopes = p->mod_kind == FA_MOD_ALIBI ? p->alibi_slopes : nullptr;
+  a.even_nat = p->checker_even;
+  a.odd_nat = p->checker_odd;
+  a.even_log2 = p->checker_even * fa::kLog2e;
+  a.odd_log2 = p->checker_odd * fa::kLog2e;
+  a.causal = p->causal;
+  return a;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct BwdLayout {
+  size_t delta_off, lse2_off, total;
+};
+
+BwdLayout bwd_layout(const fa_problem* p) {
+  const size_t rows = (size_t)p->batch * p->heads * p->seq_q;
+  BwdLayout l;
+  l.delta_off = 0;
+  l.lse2_off = round_up(rows * sizeof(float), 256);
+  l.total = l.lse2_off + round_up(rows * sizeof(float), 256);
+  return l;
+}
+
+size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
+  const int BH = (int)(p->batch * p->heads);
+  *n_split = fa::decode_choose_split(BH, (int)p->seq_kv, chunk);
+  return round_up((size_t)BH * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const void* v, void* out,
+                     float* lse, void* stream) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
+  const int64_t nqb = ceil_div(p->seq_q, block_q_fwd(p));
+  if (nqb * p->batch * p->heads > kMaxI32) return FA_ERR_UNSUPPORTED;
+
+  fa::AttnArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.n_qblocks = (int)nqb;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err;
+  if (p->dtype == FA_F32)
+    err = fa::launch_fwd32(a, (int)p->head_dim, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
+  else
+    err = fa::launch_fwd16(a, p->dtype == FA_BF16, (int)p->head_dim, p->mod_kind, p->causal != 0,
+                           p->key_mask != nullptr, st);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (!bytes) return FA_ERR_INVALID_ARGUMENT;
+  *bytes = bwd_layout(p).total;
+  return FA_OK;
+}
+
+fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (!tensors_ok({q, k, v, out, dout, dq, dk, dv})) return FA_ERR_INVALID_ARGUMENT;
+  if (!lse || ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
+  const BwdLayout lay = bwd_layout(p);
+  if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const int D = (int)p->head_dim;
+  const bool f32 = p->dtype == FA_F32;
+  const int64_t nkb = ceil_div(p->seq_kv, f32 ? fa::bwd32_block_kv(D) : fa::bwd16_block_kv());
+  const int64_t nqb = ceil_div(p->seq_q, f32 ? fa::bwd32_block_q(D) : fa::bwd16_block_q());
+  if ((nkb > nqb ? nkb : nqb) * p->batch * p->heads > kMaxI32) return FA_ERR_UNSUPPORTED;
+
+  fa::AttnArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void*>(out);
+  a.lse = const_cast<float*>(lse);
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = (float*)((char*)workspace + lay.delta_off);
+  a.lse2 = (float*)((char*)workspace + lay.lse2_off);
+  a.n_qblocks = (int)nqb;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err = fa::launch_bwd_pre(a, p->dtype, D, st);
+  if (err != hipSuccess) return FA_ERR_HIP;
+  if (f32)
+    err = fa::launch_bwd32(a, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
+  else
+    err = fa::launch_bwd16(a, p->dtype == FA_BF16, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (!bytes) return FA_ERR_INVALID_ARGUMENT;
+  if (p->seq_q != 1 || p->causal) return FA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
+  int n_split, chunk;
+  *bytes = decode_ws(p, &n_split, &chunk);
+  return FA_OK;
+}
+
+fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (p->seq_q != 1 || p->causal) return FA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
+  if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
+  int n_split, chunk;
+  const size_t need = decode_ws(p, &n_split, &chunk);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+
+  fa::AttnArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.partial = (float*)workspace;
+  a.n_split = n_split;
+  a.chunk = chunk;
+  hipError_t err = fa::launch_decode(a, p->dtype, (int)p->head_dim, p->mod_kind, p->key_mask != nullptr,
+                                     (hipStream_t)stream);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported problem (dtype, head_dim or size)";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+}  // extern "C"

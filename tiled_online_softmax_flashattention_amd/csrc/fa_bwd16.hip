@@ -1,0 +1,533 @@
+// Backward attention for 16-bit inputs (f16, bf16), head_dim 64 or 128.
+//
+// Gradients of sum(dO * O) by calculus on the attention definition:
+//   P = exp(S - lse) recomputed from the forward's saved log-sum-exp,
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta) with delta_i = <dO_i, O_i>,
+//   dK = scale * dS^T Q,  dQ = scale * dS K.
+// The pages obtain their gradient by tracing the kernel (attnax
+// pallas_flash_attention docstring) and time it (flaxattention benchmark
+// table); this is the hand-written counterpart.
+//
+// Two deterministic passes, no atomics:
+//  * dkdv16_kernel: key-stationary.  Each wave keeps 32 keys' K and V rows in
+//    registers and their dK^T, dV^T accumulators, and loops over 64-query
+//    tiles whose Q and dO are staged through LDS in both the natural and the
+//    transposed layout.  S and dP are formed with queries as rows, so the
+//    lane holds one key and the probabilities feed dV^T = dO^T P and
+//    dK^T = Q^T dS directly as MFMA B operands.
+//  * dq16_kernel: query-stationary, like the forward.  Each wave keeps 32
+//    queries' Q and dO rows in registers; K tiles are staged natural and
+//    transposed, V natural; S^T and dP^T are formed with keys as rows so the
+//    lane holds one query, and dQ^T = K^T dS^T accumulates in registers.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// ---------------------------------------------------------------- preprocess
+
+// delta_i = sum_d dO_id * O_id; lse2_i = lse_i * log2(e), +inf for an empty
+// row (so that exp2(s - lse2) = 0 there).
+template <int ES, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtype) {
+  constexpr int EPL = 16 / ES;                        // elements per 16-byte load
+  constexpr int LPR = (D * ES / 16) < 64 ? (D * ES / 16) : 64;  // lanes per row
+  constexpr int IT = D * ES / 16 / LPR;               // loads per lane
+  constexpr int RPB = 256 / LPR;                      // rows per block
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const char* O = (const char*)a.o + row * D * ES;
+    const char* dO = (const char*)a.dout + row * D * ES;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int off = (it * LPR + sub) * 16;
+      const u32x4 x = *(const u32x4*)(O + off);
+      const u32x4 y = *(const u32x4*)(dO + off);
+      if (ES == 4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc += __builtin_bit_cast(float, x[c]) * __builtin_bit_cast(float, y[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint16_t x0 = x[c] & 0xffffu, x1 = x[c] >> 16, y0 = y[c] & 0xffffu, y1 = y[c] >> 16;
+          if (dtype == 2) acc += to_f32<BF16>(x0) * to_f32<BF16>(y0) + to_f32<BF16>(x1) * to_f32<BF16>(y1);
+          else acc += to_f32<F16>(x0) * to_f32<F16>(y0) + to_f32<F16>(x1) * to_f32<F16>(y1);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
+  if (row < rows && sub == 0) {
+    a.delta[row] = acc;
+    const float l = a.lse[row];
+    a.lse2[row] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+  }
+  (void)EPL;
+}
+
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+  const int es = dtype == 0 ? 4 : 2;
+  const int lpr = (D * es / 16) < 64 ? (D * es / 16) : 64;
+  const int rpb = 256 / lpr;
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  if (es == 4) {
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<4, 64>), grid, block, 0, st, a, dtype);
+    else if (D == 128) hipLaunchKernelGGL((bwd_pre_kernel<4, 128>), grid, block, 0, st, a, dtype);
+    else hipLaunchKernelGGL((bwd_pre_kernel<4, 512>), grid, block, 0, st, a, dtype);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<2, 64>), grid, block, 0, st, a, dtype);
+    else hipLaunchKernelGGL((bwd_pre_kernel<2, 128>), grid, block, 0, st, a, dtype);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ shared helpers
+
+// Stage a 64-row tile of a (rows, D) 16-bit tensor into LDS twice: natural
+// rows with pitch D + 8, and transposed (D rows of 64 positions) with the
+// swap23 column order and 16-byte chunks XOR-swizzled by row.  Each thread
+// owns 4 consecutive rows x 8 dims.
+template <int D>
+struct Stage2 {
+  static constexpr int NG = 16 * (D / 8);   // (4-row group, 8-dim chunk) pairs
+  u32x4 r[4];
+  bool active;
+  __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
+    active = tid < NG;
+    const int rg = tid / (D / 8), ch = tid % (D / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + 4 * rg + i;
+      r[i] = (active && row < nrows) ? *(const u32x4*)(g + (size_t)row * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* nat, uint16_t* tr, int tid) const {
+    if (!active) return;
+    const int rg = tid / (D / 8), ch = tid % (D / 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_write16(&nat[(4 * rg + i) * (D + 8) + 8 * ch], r[i]);
+    const int col = swap23(4 * rg);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d = 8 * ch + c, word = c >> 1, sh = (c & 1) * 16;
+      const uint32_t e0 = (r[0][word] >> sh) & 0xffffu, e1 = (r[1][word] >> sh) & 0xffffu;
+      const uint32_t e2 = (r[2][word] >> sh) & 0xffffu, e3 = (r[3][word] >> sh) & 0xffffu;
+      const int phys = (((col >> 3) ^ (d & 7)) << 3) + (col & 7);
+      lds_write8(&tr[d * 64 + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
+    }
+  }
+};
+
+// Natural-layout staging of a 64-row tile (pitch D + 8).
+template <int D>
+struct Stage1 {
+  static constexpr int N = 64 * D / 8 / 256;   // 16-byte chunks per thread
+  u32x4 r[N];
+  __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
+      r[i] = (row0 + row < nrows) ? *(const u32x4*)(g + (size_t)(row0 + row) * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* nat, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
+      lds_write16(&nat[row * (D + 8) + 8 * ch], r[i]);
+    }
+  }
+};
+
+// Read the A fragment of a transposed tile: lane (row d, group hi), 16-wide step st.
+__device__ __forceinline__ u32x4 read_tr(const uint16_t* tr, int d, int st, int hi) {
+  return lds_read16(&tr[d * 64 + (((2 * st + hi) ^ (d & 7)) << 3)]);
+}
+
+template <class T>
+__device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
+  return u32x4{pack2<T>(x[8 * u + 0], x[8 * u + 1]), pack2<T>(x[8 * u + 2], x[8 * u + 3]),
+               pack2<T>(x[8 * u + 4], x[8 * u + 5]), pack2<T>(x[8 * u + 6], x[8 * u + 7])};
+}
+
+// ------------------------------------------------------------- dK / dV pass
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
+  static constexpr int BQ = 64;     // queries per tile
+  static constexpr int QP = D + 8;
+  static constexpr size_t lds = (size_t)2 * (BQ * QP + D * BQ) * 2 + 2 * BQ * 4;
+};
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void dkdv16_kernel(const AttnArgs a) {
+  using C = DkdvCfg<D>;
+  constexpr int BKV = C::BKV, BQ = C::BQ, QP = C::QP;
+  constexpr int KS = D / 16, DT = D / 32;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
+  uint16_t* sQ = smem16;
+  uint16_t* sQt = sQ + BQ * QP;
+  uint16_t* sO = sQt + D * BQ;
+  uint16_t* sOt = sO + BQ * QP;
+  float* sL = (float*)(sOt + D * BQ);
+  float* sDl = sL + BQ;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = blockIdx.x / BH;     // low kb = most query tiles under causal: dispatched first
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int k0 = kb * BKV;
+  const int kw = k0 + 32 * wave;
+  const int kj = kw + l32;            // this lane's key
+
+  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
+  const uint16_t* dOg = (const uint16_t*)a.dout + (size_t)bh * Sq * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + (size_t)bh * Skv * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (size_t)bh * Skv * D;
+  const float* lse2g = a.lse2 + (size_t)bh * Sq;
+  const float* deltag = a.delta + (size_t)bh * Sq;
+
+  // K and V rows of this lane's key as B operands (dims 16kk + 8hi .. +7).
+  u32x4 kf[KS], vf[KS];
+  {
+    const bool ok = kj < Skv;
+    const size_t off = (size_t)(ok ? kj : 0) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4 x = *(const u32x4*)(Kg + off + 16 * kk);
+      const u32x4 y = *(const u32x4*)(Vg + off + 16 * kk);
+      kf[kk] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+      vf[kk] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  bool key_ok = kj < Skv;
+  if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + (key_ok ? kj : 0)] != 0;
+
+  float slope2 = 0.f, cbe = 0.f, cbo = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MOD == MOD_CHECKERBOARD) {
+    // query tiles start at even positions, so register r holds a query of parity (r & 1)
+    const bool keven = (kj & 1) == 0;
+    cbe = keven ? a.even_log2 : a.odd_log2;   // even query
+    cbo = keven ? a.odd_log2 : a.even_log2;   // odd query
+  }
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  const int nqt = (Sq + BQ - 1) / BQ;
+  Stage2<D> stq, sto;
+  float lreg = 0.f, dreg = 0.f;
+  auto load_tile = [&](int q0) {
+    stq.load(Qg, q0, Sq, tid);
+    sto.load(dOg, q0, Sq, tid);
+    if (tid < BQ) {
+      const bool ok = q0 + tid < Sq;
+      lreg = ok ? lse2g[q0 + tid] : __builtin_inff();
+      dreg = ok ? deltag[q0 + tid] : 0.f;
+    }
+  };
+
+  if (qt0 < nqt) load_tile(qt0 * BQ);
+  for (int it = qt0; it < nqt; ++it) {
+    const int q0 = it * BQ;
+    if (it > qt0) __syncthreads();
+    stq.store(sQ, sQt, tid);
+    sto.store(sO, sOt, tid);
+    if (tid < BQ) {
+      sL[tid] = lreg;
+      sDl[tid] = dreg;
+    }
+    __syncthreads();
+    if (it + 1 < nqt) load_tile(q0 + BQ);
+    if (CAUSAL && q0 + BQ - 1 < kw) continue;  // every query of the tile precedes every key of this wave
+
+    // S = Q K^T and dP = dO V^T, queries as rows.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = zero16();
+      dp[mt] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int off = (32 * mt + l32) * QP + 16 * kk + 8 * hi;
+        s[mt] = mma16<T>(lds_read16(&sQ[off]), kf[kk], s[mt]);
+        dp[mt] = mma16<T>(lds_read16(&sO[off]), vf[kk], dp[mt]);
+      }
+    }
+
+    const bool diag = CAUSAL && (q0 < kw + 31);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 l4 = *(const f32x4*)&sL[32 * mt + 8 * u + 4 * hi];
+        const f32x4 d4 = *(const f32x4*)&sDl[32 * mt + 8 * u + 4 * hi];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * u + c;
+          const int qi = q0 + 32 * mt + acc_row(r, hi);
+          float x = s[mt][r] * a.scale_log2;
+          if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi);
+          if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cbo : cbe;
+          float p = exp2_hw(x - l4[c]);
+          if (!key_ok) p = 0.f;
+          if (diag && kj > qi) p = 0.f;
+          s[mt][r] = p;
+          dp[mt][r] = p * (dp[mt][r] - d4[c]);
+        }
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries.
+#pragma unroll
+    for (int st = 0; st < BQ / 16; ++st) {
+      const int mt = st >> 1, u = st & 1;
+      const u32x4 pb = pack8<T>(s[mt], u);
+      const u32x4 db = pack8<T>(dp[mt], u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + l32;
+        dv[dt] = mma16<T>(read_tr(sOt, d, st, hi), pb, dv[dt]);
+        dk[dt] = mma16<T>(read_tr(sQt, d, st, hi), db, dk[dt]);
+      }
+    }
+  }
+
+  if (kj < Skv) {
+    uint16_t* dKg = (uint16_t*)a.dk + ((size_t)bh * Skv + kj) * D;
+    uint16_t* dVg = (uint16_t*)a.dv + ((size_t)bh * Skv + kj) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int col = 32 * dt + 8 * u + 4 * hi;
+        *(u32x2*)(dKg + col) = u32x2{pack2<T>(dk[dt][4 * u] * sc, dk[dt][4 * u + 1] * sc),
+                                     pack2<T>(dk[dt][4 * u + 2] * sc, dk[dt][4 * u + 3] * sc)};
+        *(u32x2*)(dVg + col) = u32x2{pack2<T>(dv[dt][4 * u], dv[dt][4 * u + 1]),
+                                     pack2<T>(dv[dt][4 * u + 2], dv[dt][4 * u + 3])};
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- dQ pass
+
+template <int D>
+struct Dq16Cfg {
+  static constexpr int BM = 128;   // queries per workgroup
+  static constexpr int BN = 64;    // keys per tile
+  static constexpr int KP = D + 8;
+  static constexpr size_t lds = (size_t)(2 * BN * KP + D * BN) * 2 + 64;
+};
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void dq16_kernel(const AttnArgs a) {
+  using C = Dq16Cfg<D>;
+  constexpr int BM = C::BM, BN = C::BN, KP = C::KP;
+  constexpr int KS = D / 16, DT = D / 32;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
+  uint16_t* sK = smem16;
+  uint16_t* sKt = sK + BN * KP;
+  uint16_t* sV = sKt + D * BN;
+  uint8_t* sM = (uint8_t*)(sV + BN * KP);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int q0 = qb * BM;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + l32;
+
+  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
+  const uint16_t* dOg = (const uint16_t*)a.dout + (size_t)bh * Sq * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + (size_t)bh * Skv * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (size_t)bh * Skv * D;
+
+  u32x4 qf[KS], of[KS];
+  float lse2 = __builtin_inff(), delta = 0.f;
+  {
+    const bool ok = qi < Sq;
+    const size_t off = (size_t)(ok ? qi : 0) * D + 8 * hi;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4 x = *(const u32x4*)(Qg + off + 16 * kk);
+      const u32x4 y = *(const u32x4*)(dOg + off + 16 * kk);
+      qf[kk] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+      of[kk] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (ok) {
+      lse2 = a.lse2[(size_t)bh * Sq + qi];
+      delta = a.delta[(size_t)bh * Sq + qi];
+    }
+  }
+
+  float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MOD == MOD_CHECKERBOARD) {
+    const bool qeven = (qi & 1) == 0;
+    cb0 = qeven ? a.even_log2 : a.odd_log2;
+    cb1 = qeven ? a.odd_log2 : a.even_log2;
+  }
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
+
+  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  Stage2<D> stk;
+  Stage1<D> stv;
+  uint8_t mreg = 0;
+  auto load_tile = [&](int kv0) {
+    stk.load(Kg, kv0, Skv, tid);
+    stv.load(Vg, kv0, Skv, tid);
+    if constexpr (MASK) {
+      if (tid < BN) mreg = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+    }
+  };
+
+  load_tile(0);
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * BN;
+    if (j > 0) __syncthreads();
+    stk.store(sK, sKt, tid);
+    stv.store(sV, tid);
+    if constexpr (MASK) {
+      if (tid < BN) sM[tid] = mreg;
+    }
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile(kv0 + BN);
+    if (CAUSAL && kv0 > qw + 31) continue;
+
+    // S^T = K Q^T and dP^T = V dO^T, keys as rows.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = zero16();
+      dp[t] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int off = (32 * t + l32) * KP + 16 * kk + 8 * hi;
+        s[t] = mma16<T>(lds_read16(&sK[off]), qf[kk], s[t]);
+        dp[t] = mma16<T>(lds_read16(&sV[off]), of[kk], dp[t]);
+      }
+    }
+
+    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
+    const bool tail = kv0 + BN > Skv;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t mw = 0xffffffffu;
+        if constexpr (MASK) mw = *(const uint32_t*)&sM[32 * t + 8 * u + 4 * hi];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * u + c;
+          const int kv = kv0 + 32 * t + acc_row(r, hi);
+          float x = s[t][r] * a.scale_log2;
+          if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
+          if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
+          float p = exp2_hw(x - lse2);
+          if constexpr (MASK) {
+            if (((mw >> (8 * c)) & 0xffu) == 0u) p = 0.f;
+          } else {
+            if (tail && kv >= Skv) p = 0.f;
+          }
+          if (diag && kv > qi) p = 0.f;
+          dp[t][r] = p * (dp[t][r] - delta);
+        }
+      }
+    }
+
+    // dQ^T += K^T dS^T over the tile's 64 keys.
+#pragma unroll
+    for (int st = 0; st < BN / 16; ++st) {
+      const int t = st >> 1, u = st & 1;
+      const u32x4 db = pack8<T>(dp[t], u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_tr(sKt, 32 * dt + l32, st, hi), db, dq[dt]);
+    }
+  }
+
+  if (qi < Sq) {
+    uint16_t* dQg = (uint16_t*)a.dq + ((size_t)bh * Sq + qi) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        *(u32x2*)(dQg + 32 * dt + 8 * u + 4 * hi) =
+            u32x2{pack2<T>(dq[dt][4 * u] * sc, dq[dt][4 * u + 1] * sc), pack2<T>(dq[dt][4 * u + 2] * sc, dq[dt][4 * u + 3] * sc)};
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- launchers
+
+template <class K>
+static hipError_t launch_dyn(K kern, unsigned grid, size_t lds, hipStream_t st, const AttnArgs& a) {
+  if (lds > 65536) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_bwd16_inst(const AttnArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  const unsigned nkb = (unsigned)((a.Skv + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
+  hipError_t err = launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
+  if (err != hipSuccess) return err;
+  return launch_dyn(dq16_kernel<T, D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, Dq16Cfg<D>::lds, st, a);
+}
+
+template <class T, int D, int MOD>
+static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
+  if (causal) return mask ? launch_bwd16_inst<T, D, MOD, true, true>(a, st) : launch_bwd16_inst<T, D, MOD, true, false>(a, st);
+  return mask ? launch_bwd16_inst<T, D, MOD, false, true>(a, st) : launch_bwd16_inst<T, D, MOD, false, false>(a, st);
+}
+
+template <class T, int D>
+static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+  switch (mod) {
+    case MOD_ALIBI: return launch_bwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, st);
+    case MOD_CHECKERBOARD: return launch_bwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, st);
+    default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, st);
+  }
+}
+
+int bwd16_block_kv() { return 128; }
+int bwd16_block_q() { return 128; }
+
+hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st) {
+  if (bf16) return D == 64 ? launch_bwd16_d<BF16, 64>(a, mod, causal, mask, st) : launch_bwd16_d<BF16, 128>(a, mod, causal, mask, st);
+  return D == 64 ? launch_bwd16_d<F16, 64>(a, mod, causal, mask, st) : launch_bwd16_d<F16, 128>(a, mod, causal, mask, st);
+}
+
+}  // namespace fa

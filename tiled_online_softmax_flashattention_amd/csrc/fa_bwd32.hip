@@ -1,0 +1,393 @@
+// Backward attention for fp32 inputs, head_dim 64, 128 or 512.
+//
+// Same gradients as the 16-bit backward (P recomputed from the saved
+// log-sum-exp; dV = P^T dO, dS = P (dP - delta), dK = scale dS^T Q,
+// dQ = scale dS K) on the fp32 matrix cores.  With one operand value per lane
+// no transposed LDS copy is needed.  Heads of 512 dims are split over the 4
+// waves of a workgroup: each wave owns 128 dims of the register-resident rows
+// and accumulators, and the partial S and dP products are summed through LDS.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D>
+struct B32Cfg {
+  static constexpr int DS = D >= 512 ? 4 : 1;   // dim slices
+  static constexpr int NG = 4 / DS;             // 32-row groups per workgroup
+  static constexpr int P = D + 4;               // LDS pitch (floats)
+  // two 32-row tiles + partial-sum exchange + two 32-float row vectors / mask
+  static constexpr size_t lds = (size_t)2 * 32 * P * 4 + (DS > 1 ? 4 * 16 * 64 * 4 : 0) + 2 * 32 * 4 + 64;
+};
+
+// Sum the DS partial accumulators of a row group through LDS (every wave calls it).
+template <int DS>
+__device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g, int lane) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = x[r];
+  __syncthreads();
+  f32x16 s = zero16();
+#pragma unroll
+  for (int e2 = 0; e2 < DS; ++e2) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
+  }
+  __syncthreads();
+  return s;
+}
+
+// Stage a 32-row fp32 tile (rows row0.., natural layout, pitch D + 4).
+template <int D>
+__device__ __forceinline__ void stage32(float* dst, const float* g, int row0, int nrows, int tid) {
+  constexpr int N = 32 * D / 4 / 256;
+#pragma unroll 4
+  for (int i = 0; i < N; ++i) {
+    const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4);
+    const f32x4 x = (row0 + row < nrows) ? *(const f32x4*)(g + (size_t)(row0 + row) * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *(f32x4*)&dst[row * (D + 4) + 4 * ch] = x;
+  }
+}
+
+// ------------------------------------------------------------- dK / dV pass
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
+  using C = B32Cfg<D>;
+  constexpr int DS = C::DS, NG = C::NG, P = C::P;
+  constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
+  constexpr int BKV = 32 * NG, BQ = 32;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sQ = smem;
+  float* sO = sQ + 32 * P;
+  float* sS = sO + 32 * P;
+  float* sL = sS + (DS > 1 ? 4 * 16 * 64 : 0);
+  float* sDl = sL + 32;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = wave / DS, e = wave % DS;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int kb = blockIdx.x / BH;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int k0 = kb * BKV;
+  const int kw = k0 + 32 * g;
+  const int kj = kw + l32;
+
+  const float* Qg = (const float*)a.q + (size_t)bh * Sq * D;
+  const float* dOg = (const float*)a.dout + (size_t)bh * Sq * D;
+  const float* Kg = (const float*)a.k + (size_t)bh * Skv * D;
+  const float* Vg = (const float*)a.v + (size_t)bh * Skv * D;
+
+  float kf[HS], vf[HS];
+  {
+    const bool ok = kj < Skv;
+    const size_t off = (size_t)(ok ? kj : 0) * D + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 x = *(const f32x4*)(Kg + off + kk);
+      const f32x4 y = *(const f32x4*)(Vg + off + kk);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        kf[kk + c] = ok ? x[c] : 0.f;
+        vf[kk + c] = ok ? y[c] : 0.f;
+      }
+    }
+  }
+  bool key_ok = kj < Skv;
+  if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + (key_ok ? kj : 0)] != 0;
+
+  float slope2 = 0.f, cbe = 0.f, cbo = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MOD == MOD_CHECKERBOARD) {
+    const bool keven = (kj & 1) == 0;
+    cbe = keven ? a.even_log2 : a.odd_log2;
+    cbo = keven ? a.odd_log2 : a.even_log2;
+  }
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  const int nqt = (Sq + BQ - 1) / BQ;
+  for (int it = qt0; it < nqt; ++it) {
+    const int q0 = it * BQ;
+    __syncthreads();
+    stage32<D>(sQ, Qg, q0, Sq, tid);
+    stage32<D>(sO, dOg, q0, Sq, tid);
+    if (tid < 32) {
+      const bool ok = q0 + tid < Sq;
+      sL[tid] = ok ? a.lse2[(size_t)bh * Sq + q0 + tid] : __builtin_inff();
+      sDl[tid] = ok ? a.delta[(size_t)bh * Sq + q0 + tid] : 0.f;
+    }
+    __syncthreads();
+    if (DS == 1 && CAUSAL && q0 + BQ - 1 < kw) continue;
+
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+    const float* qrow = sQ + l32 * P + e * DSL + hi * HS;
+    const float* orow = sO + l32 * P + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 x = *(const f32x4*)(qrow + kk);
+      const f32x4 y = *(const f32x4*)(orow + kk);
+      s0 = mma_f32(x[0], kf[kk + 0], s0);
+      s1 = mma_f32(x[1], kf[kk + 1], s1);
+      p0 = mma_f32(y[0], vf[kk + 0], p0);
+      p1 = mma_f32(y[1], vf[kk + 1], p1);
+      s0 = mma_f32(x[2], kf[kk + 2], s0);
+      s1 = mma_f32(x[3], kf[kk + 3], s1);
+      p0 = mma_f32(y[2], vf[kk + 2], p0);
+      p1 = mma_f32(y[3], vf[kk + 3], p1);
+    }
+    f32x16 s = s0 + s1, dp = p0 + p1;
+    if constexpr (DS > 1) {
+      s = slice_sum<DS>(s, sS, wave, g, lane);
+      dp = slice_sum<DS>(dp, sS, wave, g, lane);
+    }
+
+    const bool diag = CAUSAL && (q0 < kw + 31);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *(const f32x4*)&sL[8 * u + 4 * hi];
+      const f32x4 d4 = *(const f32x4*)&sDl[8 * u + 4 * hi];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * u + c;
+        const int qi = q0 + acc_row(r, hi);
+        float x = s[r] * a.scale_log2;
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi);
+        if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cbo : cbe;
+        float p = exp2_hw(x - l4[c]);
+        if (!key_ok) p = 0.f;
+        if (diag && kj > qi) p = 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - d4[c]);
+      }
+    }
+
+    // dV^T += dO^T P, dK^T += Q^T dS: step t pairs register t (query acc_row(t, hi)).
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int qr = acc_row(t, hi);
+      const float* orw = sO + qr * P + e * DSL + l32;
+      const float* qrw = sQ + qr * P + e * DSL + l32;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = mma_f32(orw[32 * dt], s[t], dv[dt]);
+        dk[dt] = mma_f32(qrw[32 * dt], dp[t], dk[dt]);
+      }
+    }
+  }
+
+  if (kj < Skv) {
+    float* dKg = (float*)a.dk + ((size_t)bh * Skv + kj) * D + e * DSL;
+    float* dVg = (float*)a.dv + ((size_t)bh * Skv + kj) * D + e * DSL;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int col = 32 * dt + 8 * u + 4 * hi;
+        *(f32x4*)(dKg + col) = f32x4{dk[dt][4 * u] * sc, dk[dt][4 * u + 1] * sc, dk[dt][4 * u + 2] * sc, dk[dt][4 * u + 3] * sc};
+        *(f32x4*)(dVg + col) = f32x4{dv[dt][4 * u], dv[dt][4 * u + 1], dv[dt][4 * u + 2], dv[dt][4 * u + 3]};
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- dQ pass
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
+  using C = B32Cfg<D>;
+  constexpr int DS = C::DS, NG = C::NG, P = C::P;
+  constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
+  constexpr int BM = 32 * NG, BN = 32;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sK = smem;
+  float* sV = sK + 32 * P;
+  float* sS = sV + 32 * P;
+  uint8_t* sM = (uint8_t*)(sS + (DS > 1 ? 4 * 16 * 64 : 0) + 64);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = wave / DS, e = wave % DS;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int q0 = qb * BM;
+  const int qw = q0 + 32 * g;
+  const int qi = qw + l32;
+
+  const float* Qg = (const float*)a.q + (size_t)bh * Sq * D;
+  const float* dOg = (const float*)a.dout + (size_t)bh * Sq * D;
+  const float* Kg = (const float*)a.k + (size_t)bh * Skv * D;
+  const float* Vg = (const float*)a.v + (size_t)bh * Skv * D;
+
+  float qf[HS], of[HS];
+  float lse2 = __builtin_inff(), delta = 0.f;
+  {
+    const bool ok = qi < Sq;
+    const size_t off = (size_t)(ok ? qi : 0) * D + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 x = *(const f32x4*)(Qg + off + kk);
+      const f32x4 y = *(const f32x4*)(dOg + off + kk);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qf[kk + c] = ok ? x[c] : 0.f;
+        of[kk + c] = ok ? y[c] : 0.f;
+      }
+    }
+    if (ok) {
+      lse2 = a.lse2[(size_t)bh * Sq + qi];
+      delta = a.delta[(size_t)bh * Sq + qi];
+    }
+  }
+
+  float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MOD == MOD_CHECKERBOARD) {
+    const bool qeven = (qi & 1) == 0;
+    cb0 = qeven ? a.even_log2 : a.odd_log2;
+    cb1 = qeven ? a.odd_log2 : a.even_log2;
+  }
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
+
+  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * BN;
+    __syncthreads();
+    stage32<D>(sK, Kg, kv0, Skv, tid);
+    stage32<D>(sV, Vg, kv0, Skv, tid);
+    if constexpr (MASK) {
+      if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+    }
+    __syncthreads();
+    if (DS == 1 && CAUSAL && kv0 > qw + 31) continue;
+
+    f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
+    const float* krow = sK + l32 * P + e * DSL + hi * HS;
+    const float* vrow = sV + l32 * P + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 x = *(const f32x4*)(krow + kk);
+      const f32x4 y = *(const f32x4*)(vrow + kk);
+      s0 = mma_f32(x[0], qf[kk + 0], s0);
+      s1 = mma_f32(x[1], qf[kk + 1], s1);
+      p0 = mma_f32(y[0], of[kk + 0], p0);
+      p1 = mma_f32(y[1], of[kk + 1], p1);
+      s0 = mma_f32(x[2], qf[kk + 2], s0);
+      s1 = mma_f32(x[3], qf[kk + 3], s1);
+      p0 = mma_f32(y[2], of[kk + 2], p0);
+      p1 = mma_f32(y[3], of[kk + 3], p1);
+    }
+    f32x16 s = s0 + s1, dp = p0 + p1;
+    if constexpr (DS > 1) {
+      s = slice_sum<DS>(s, sS, wave, g, lane);
+      dp = slice_sum<DS>(dp, sS, wave, g, lane);
+    }
+
+    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
+    const bool tail = kv0 + BN > Skv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t mw = 0xffffffffu;
+      if constexpr (MASK) mw = *(const uint32_t*)&sM[8 * u + 4 * hi];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * u + c;
+        const int kv = kv0 + acc_row(r, hi);
+        float x = s[r] * a.scale_log2;
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
+        if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
+        float p = exp2_hw(x - lse2);
+        if constexpr (MASK) {
+          if (((mw >> (8 * c)) & 0xffu) == 0u) p = 0.f;
+        } else {
+          if (tail && kv >= Skv) p = 0.f;
+        }
+        if (diag && kv > qi) p = 0.f;
+        dp[r] = p * (dp[r] - delta);
+      }
+    }
+
+    // dQ^T += K^T dS^T: step t pairs register t (key acc_row(t, hi)) with that key's K row.
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float* krw = sK + acc_row(t, hi) * P + e * DSL + l32;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_f32(krw[32 * dt], dp[t], dq[dt]);
+    }
+  }
+
+  if (qi < Sq) {
+    float* dQg = (float*)a.dq + ((size_t)bh * Sq + qi) * D + e * DSL;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *(f32x4*)(dQg + 32 * dt + 8 * u + 4 * hi) =
+            f32x4{dq[dt][4 * u] * sc, dq[dt][4 * u + 1] * sc, dq[dt][4 * u + 2] * sc, dq[dt][4 * u + 3] * sc};
+    }
+  }
+}
+
+template <class K>
+static hipError_t launch_dyn32(K kern, unsigned grid, size_t lds, hipStream_t st, const AttnArgs& a) {
+  if (lds > 65536) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_bwd32_inst(const AttnArgs& a, hipStream_t st) {
+  using C = B32Cfg<D>;
+  const int BH = a.B * a.H;
+  const unsigned nkb = (unsigned)((a.Skv + 32 * C::NG - 1) / (32 * C::NG));
+  hipError_t err = launch_dyn32(dkdv32_kernel<D, MOD, CAUSAL, MASK>, nkb * BH, C::lds, st, a);
+  if (err != hipSuccess) return err;
+  return launch_dyn32(dq32_kernel<D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, C::lds, st, a);
+}
+
+template <int D, int MOD>
+static hipError_t launch_bwd32_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
+  if (causal) return mask ? launch_bwd32_inst<D, MOD, true, true>(a, st) : launch_bwd32_inst<D, MOD, true, false>(a, st);
+  return mask ? launch_bwd32_inst<D, MOD, false, true>(a, st) : launch_bwd32_inst<D, MOD, false, false>(a, st);
+}
+
+template <int D>
+static hipError_t launch_bwd32_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+  switch (mod) {
+    case MOD_ALIBI: return launch_bwd32_mod<D, MOD_ALIBI>(a, causal, mask, st);
+    case MOD_CHECKERBOARD: return launch_bwd32_mod<D, MOD_CHECKERBOARD>(a, causal, mask, st);
+    default: return launch_bwd32_mod<D, MOD_NONE>(a, causal, mask, st);
+  }
+}
+
+int bwd32_block_kv(int D) { return D >= 512 ? 32 : 128; }
+int bwd32_block_q(int D) { return D >= 512 ? 32 : 128; }
+
+hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st) {
+  if (D == 64) return launch_bwd32_d<64>(a, mod, causal, mask, st);
+  if (D == 128) return launch_bwd32_d<128>(a, mod, causal, mask, st);
+  return launch_bwd32_d<512>(a, mod, causal, mask, st);
+}
+
+}  // namespace fa

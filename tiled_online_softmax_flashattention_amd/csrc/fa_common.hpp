@@ -1,0 +1,136 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Orientation used throughout: a wave computes S^T = K Q^T with one 32x32
+// MFMA tile per 32 keys x 32 queries.  In the 32x32 accumulator layout lane l
+// owns column n = l % 32 and rows m = 8*(r/4) + 4*(l/32) + (r%4) of register
+// r, so every lane holds a single query (or, in the key-stationary backward
+// pass, a single key) and the softmax row statistics stay inside one lane
+// plus its partner lane l ^ 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+enum Mod { MOD_NONE = 0, MOD_ALIBI = 1, MOD_CHECKERBOARD = 2 };
+
+// Element tags for the 16-bit storage types.
+struct F16 {};
+struct BF16 {};
+
+// v_mfma_f32_32x32x16_{f16,bf16}: 8 operand values per lane, fp32 accumulate.
+template <class T>
+__device__ __forceinline__ f32x16 mma16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (__is_same(T, F16)) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
+// v_mfma_f32_32x32x2_f32: one operand value per lane.
+__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Round two floats to the 16-bit type (round to nearest even) and pack them,
+// the first value in the low half.
+template <class T>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  if constexpr (__is_same(T, F16)) {
+    f16x2 v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+template <class T>
+__device__ __forceinline__ float to_f32(uint16_t bits) {
+  if constexpr (__is_same(T, F16)) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  } else {
+    return __builtin_bit_cast(float, (uint32_t)bits << 16);
+  }
+}
+
+// Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row of the 32x32 accumulator held in register r by lane group hi.
+__device__ __forceinline__ constexpr int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Column order of the transposed (key- or query-major) LDS tiles.  A 16-wide
+// MFMA step over keys takes, in lane group hi, the eight accumulator rows
+// {8u + 4hi + c} (u = 0,1; c = 0..3) of one 32x32 tile; swapping bits 2 and 3
+// of the position puts exactly those eight positions in one contiguous
+// 16-byte run, so each operand fragment is a single ds_read_b128.
+__device__ __forceinline__ constexpr int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// ALiBi slope for head h of H: slope_h = 2^(-8 (h+1) / H), or the caller's.
+__device__ __forceinline__ float alibi_slope(const float* slopes, int h, int H) {
+  return slopes ? slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)H);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
+
+// Launch arguments of every attention kernel (tensors contiguous BHSD).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;     // backward workspace: rowsum(dO * O), (B, H, Sq)
+  float* lse2;      // backward workspace: lse * log2(e), +inf for empty rows
+  const uint8_t* key_mask;
+  const float* alibi_slopes;
+  float* partial;   // decode workspace
+  int B, H, Sq, Skv;
+  float scale;         // natural-log scale applied to q.k
+  float scale_log2;    // scale * log2(e)
+  float even_log2;     // checkerboard bias * log2(e) for even (i + j)
+  float odd_log2;      // ... for odd (i + j)
+  float even_nat;      // checkerboard bias, natural units
+  float odd_nat;
+  int causal;
+  int n_qblocks;
+  int n_split;         // decode: number of key chunks
+  int chunk;           // decode: keys per chunk
+};
+
+}  // namespace fa

@@ -1,0 +1,256 @@
+// Split-KV decode: one query per (batch, head) against seq_kv keys.
+//
+// The flaxattention page times single-query decoding separately and lists
+// faster decoding as open work; with one query the problem is a pair of
+// matrix-vector products bound by streaming K and V from HBM, so it gets its
+// own kernels instead of the 128-query tiles of the forward.
+//
+// decode_split_kernel: workgroup (b, h, chunk) streams its chunk of keys.
+// Each key is handled by a group of lanes that each own 16 bytes of the head
+// (8 halves or 4 floats), so a wave reads whole rows with fully coalesced
+// 16-byte loads; the group reduces the dot product with lane shuffles and
+// keeps its own online-softmax state (max, sum, accumulator slice).  Groups,
+// then waves, are merged exactly, and the chunk's (max, sum, accumulator) go
+// to the workspace.
+// decode_merge_kernel: combines the chunks of each (b, h):
+//   M = max_s m_s, w_s = 2^(m_s - M), O = sum w_s acc_s / sum w_s l_s,
+//   lse = (M + log2 sum w_s l_s) ln 2.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+struct F32 {};
+
+template <class T>
+struct Elem {
+  static constexpr int size = 2;
+};
+template <>
+struct Elem<F32> {
+  static constexpr int size = 4;
+};
+
+template <class T>
+__device__ __forceinline__ void unpack16(const u32x4 x, float* out) {
+  if constexpr (__is_same(T, F32)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = __builtin_bit_cast(float, x[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      out[2 * c] = to_f32<T>((uint16_t)(x[c] & 0xffffu));
+      out[2 * c + 1] = to_f32<T>((uint16_t)(x[c] >> 16));
+    }
+  }
+}
+
+// Online-softmax state of a group; all values in log2 units.
+template <int EPL>
+struct State {
+  float m, l, acc[EPL];
+};
+
+template <int EPL>
+__device__ __forceinline__ void merge_into(State<EPL>& s, float m2, float l2, const float* acc2) {
+  const float M = fmaxf(s.m, m2);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  const float w1 = exp2_hw(s.m - Mu), w2 = exp2_hw(m2 - Mu);
+  s.l = s.l * w1 + l2 * w2;
+#pragma unroll
+  for (int c = 0; c < EPL; ++c) s.acc[c] = s.acc[c] * w1 + acc2[c] * w2;
+  s.m = M;
+}
+
+constexpr int kDecodeUnroll = 4;
+
+template <class T, int D, int MOD, bool MASK>
+__global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
+  constexpr int ES = Elem<T>::size;
+  constexpr int EPL = 16 / ES;           // elements per lane
+  constexpr int LPK = D / EPL;           // lanes per key
+  constexpr int KPW = 64 / LPK;          // keys per wave per step
+  constexpr int KPB = 4 * KPW;           // keys per workgroup per step
+  constexpr int U = kDecodeUnroll;
+  __shared__ float sPart[4][D + 2];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int grp = lane / LPK, sub = lane % LPK;
+  const int split = blockIdx.x % a.n_split;
+  const int bh = blockIdx.x / a.n_split;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Skv = a.Skv;
+  const int c0 = split * a.chunk;
+  const int c1 = min(Skv, c0 + a.chunk);
+
+  const char* Kg = (const char*)a.k + ((size_t)bh * Skv * D) * ES + sub * 16;
+  const char* Vg = (const char*)a.v + ((size_t)bh * Skv * D) * ES + sub * 16;
+  float qv[EPL];
+  unpack16<T>(*(const u32x4*)((const char*)a.q + (size_t)bh * D * ES + sub * 16), qv);
+#pragma unroll
+  for (int c = 0; c < EPL; ++c) qv[c] *= a.scale_log2;
+
+  float slope2 = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  const uint8_t* mrow = MASK ? a.key_mask + (size_t)b * Skv : nullptr;
+
+  State<EPL> st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int c = 0; c < EPL; ++c) st.acc[c] = 0.f;
+
+  for (int base = c0 + wave * KPW + grp; base < c1; base += U * KPB) {
+    u32x4 kx[U], vx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kv = base + u * KPB;
+      const bool ok = kv < c1;
+      kx[u] = ok ? *(const u32x4*)(Kg + (size_t)kv * D * ES) : u32x4{0u, 0u, 0u, 0u};
+      vx[u] = ok ? *(const u32x4*)(Vg + (size_t)kv * D * ES) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      unpack16<T>(kx[u], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int c = 0; c < EPL; ++c) d += qv[c] * kf[c];
+#pragma unroll
+      for (int w = 1; w < LPK; w <<= 1) d += __shfl_xor(d, w);
+      const int kv = base + u * KPB;
+      if constexpr (MOD == MOD_ALIBI) d += slope2 * (float)kv;  // -slope * (0 - kv)
+      if constexpr (MOD == MOD_CHECKERBOARD) d += (kv & 1) ? a.odd_log2 : a.even_log2;
+      bool ok = kv < c1;
+      if constexpr (MASK) ok = ok && mrow[ok ? kv : 0] != 0;
+      t[u] = ok ? d : kNegInf;
+    }
+    float mx = st.m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, t[u]);
+    const float mu = (mx == kNegInf) ? 0.f : mx;
+    const float alpha = exp2_hw(st.m - mu);
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < EPL; ++c) st.acc[c] *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = exp2_hw(t[u] - mu);
+      float vf[EPL];
+      unpack16<T>(vx[u], vf);
+      st.l += p;
+#pragma unroll
+      for (int c = 0; c < EPL; ++c) st.acc[c] += p * vf[c];
+    }
+    st.m = mx;
+  }
+
+  // merge the groups of the wave (lanes with equal sub)
+#pragma unroll
+  for (int w = LPK; w < 64; w <<= 1) {
+    float acc2[EPL];
+#pragma unroll
+    for (int c = 0; c < EPL; ++c) acc2[c] = __shfl_xor(st.acc[c], w);
+    const float m2 = __shfl_xor(st.m, w), l2 = __shfl_xor(st.l, w);
+    merge_into<EPL>(st, m2, l2, acc2);
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int c = 0; c < EPL; ++c) sPart[wave][sub * EPL + c] = st.acc[c];
+    if (sub == 0) {
+      sPart[wave][D] = st.m;
+      sPart[wave][D + 1] = st.l;
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && grp == 0) {
+    for (int w2 = 1; w2 < 4; ++w2) {
+      float acc2[EPL];
+#pragma unroll
+      for (int c = 0; c < EPL; ++c) acc2[c] = sPart[w2][sub * EPL + c];
+      merge_into<EPL>(st, sPart[w2][D], sPart[w2][D + 1], acc2);
+    }
+    float* out = a.partial + ((size_t)bh * a.n_split + split) * (D + 2);
+#pragma unroll
+    for (int c = 0; c < EPL; ++c) out[sub * EPL + c] = st.acc[c];
+    if (sub == 0) {
+      out[D] = st.m;
+      out[D + 1] = st.l;
+    }
+  }
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(128) void decode_merge_kernel(const AttnArgs a) {
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* part = a.partial + (size_t)bh * a.n_split * (D + 2);
+  float M = kNegInf;
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, part[(size_t)s * (D + 2) + D]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float* ps = part + (size_t)s * (D + 2);
+    const float w = exp2_hw(ps[D] - Mu);
+    L += w * ps[D + 1];
+    if (d < D) acc += w * ps[d];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (d < D) {
+    const float o = acc * inv;
+    if constexpr (__is_same(T, F32)) {
+      ((float*)a.o)[(size_t)bh * D + d] = o;
+    } else if constexpr (__is_same(T, F16)) {
+      ((_Float16*)a.o)[(size_t)bh * D + d] = (_Float16)o;
+    } else {
+      ((__bf16*)a.o)[(size_t)bh * D + d] = (__bf16)o;
+    }
+  }
+  if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+int decode_choose_split(int BH, int Skv, int* chunk) {
+  // Aim for about 1024 workgroups in total, with chunks of 256 .. 4096 keys
+  // (a multiple of 64 keys).
+  long long c = ((long long)Skv * BH + 1023) / 1024;
+  c = (c + 63) / 64 * 64;
+  if (c < 256) c = 256;
+  if (c > 4096) c = 4096;
+  if (c > Skv) c = (Skv + 63) / 64 * 64;
+  *chunk = (int)c;
+  return (int)((Skv + c - 1) / c);
+}
+
+template <class T, int D, int MOD, bool MASK>
+static hipError_t launch_decode_inst(const AttnArgs& a, hipStream_t st) {
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0, st, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_decode_d(const AttnArgs& a, int mod, bool mask, hipStream_t st) {
+  switch (mod) {
+    case MOD_ALIBI: return mask ? launch_decode_inst<T, D, MOD_ALIBI, true>(a, st) : launch_decode_inst<T, D, MOD_ALIBI, false>(a, st);
+    case MOD_CHECKERBOARD:
+      return mask ? launch_decode_inst<T, D, MOD_CHECKERBOARD, true>(a, st) : launch_decode_inst<T, D, MOD_CHECKERBOARD, false>(a, st);
+    default: return mask ? launch_decode_inst<T, D, MOD_NONE, true>(a, st) : launch_decode_inst<T, D, MOD_NONE, false>(a, st);
+  }
+}
+
+template <class T>
+static hipError_t launch_decode_t(const AttnArgs& a, int D, int mod, bool mask, hipStream_t st) {
+  return D == 64 ? launch_decode_d<T, 64>(a, mod, mask, st) : launch_decode_d<T, 128>(a, mod, mask, st);
+}
+
+hipError_t launch_decode(const AttnArgs& a, int dtype, int D, int mod, bool mask, hipStream_t st) {
+  if (dtype == 0) return launch_decode_t<F32>(a, D, mod, mask, st);
+  if (dtype == 2) return launch_decode_t<BF16>(a, D, mod, mask, st);
+  return launch_decode_t<F16>(a, D, mod, mask, st);
+}
+
+}  // namespace fa

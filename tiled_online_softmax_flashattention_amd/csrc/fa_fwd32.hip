@@ -1,0 +1,238 @@
+// Forward attention for fp32 inputs, head_dim 64, 128 or 512.
+//
+// Same online-softmax recurrence as the 16-bit kernel (attnax
+// pallas_flash_attention page, kernel body; base-2 exponentials), on the fp32
+// matrix cores (v_mfma_f32_32x32x2_f32: one operand value per lane, so V is
+// read in its natural layout and no transposed copy is needed).
+//
+// Large heads are split over waves: with DS slices, each of the DS waves of a
+// 32-query group holds Q and the O accumulator for D/DS dims only, computes a
+// partial S^T over those dims, and the DS partials are summed through LDS
+// before the (redundant, bit-identical) softmax in each wave.  At D = 512 this
+// keeps Q (64 values) and the accumulator (64 values) per lane in registers
+// while a 32-key K tile and V tile (128 KiB together) sit in LDS.
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+template <int D>
+struct F32Cfg {
+  static constexpr int DS = D >= 512 ? 4 : 1;   // dim slices per query group
+  static constexpr int NQ = 4 / DS;             // 32-query groups per workgroup
+  static constexpr int BM = 32 * NQ;
+  static constexpr int BN = 32;
+  static constexpr int P = D + 4;               // LDS pitch of the K and V tiles (floats)
+  static constexpr size_t lds = (size_t)2 * BN * P * 4 + (DS > 1 ? 4 * 16 * 64 * 4 : 0) + 64;
+};
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
+  using C = F32Cfg<D>;
+  constexpr int DS = C::DS, BM = C::BM, BN = C::BN, P = C::P;
+  constexpr int DSL = D / DS;          // dims per slice
+  constexpr int HS = DSL / 2;          // operand values per lane per product
+  constexpr int DT = DSL / 32;         // 32-row tiles of the O^T slice
+  constexpr int NCH = BN * D / 4 / 256;
+
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* sK = smem;
+  float* sV = sK + BN * P;
+  float* sS = sV + BN * P;
+  uint8_t* sM = (uint8_t*)(sS + (DS > 1 ? 4 * 16 * 64 : 0));
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = wave / DS, e = wave % DS;
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int Sq = a.Sq, Skv = a.Skv;
+  const int q0 = qb * BM;
+  const int qw = q0 + 32 * g;
+  const int qi = qw + l32;
+
+  const float* Qg = (const float*)a.q + (size_t)bh * Sq * D;
+  const float* Kg = (const float*)a.k + (size_t)bh * Skv * D;
+  const float* Vg = (const float*)a.v + (size_t)bh * Skv * D;
+
+  // Q as the B operand: lane (query l32, group hi) holds dims e*DSL + hi*HS + kk.
+  float qf[HS];
+  {
+    const bool ok = qi < Sq;
+    const float* src = Qg + (size_t)(ok ? qi : 0) * D + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 v = *(const f32x4*)(src + kk);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[kk + c] = ok ? v[c] : 0.f;
+    }
+  }
+
+  float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MOD == MOD_CHECKERBOARD) {
+    const bool qeven = (qi & 1) == 0;
+    cb0 = qeven ? a.even_log2 : a.odd_log2;
+    cb1 = qeven ? a.odd_log2 : a.even_log2;
+  }
+
+  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int ntiles = (kv_end + BN - 1) / BN;
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv0 = j * BN;
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4), kv = kv0 + row;
+      const bool ok = kv < Skv;
+      const f32x4 kx = ok ? *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 vx = ok ? *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)&sK[row * P + 4 * ch] = kx;
+      *(f32x4*)&sV[row * P + 4 * ch] = vx;
+    }
+    if constexpr (MASK) {
+      if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+    }
+    __syncthreads();
+    if (DS == 1 && CAUSAL && kv0 > qw + 31) continue;
+
+    f32x16 s0 = zero16(), s1 = zero16();
+    const float* krow = sK + l32 * P + e * DSL + hi * HS;
+#pragma unroll
+    for (int kk = 0; kk < HS; kk += 4) {
+      const f32x4 kx = *(const f32x4*)(krow + kk);
+      s0 = mma_f32(kx[0], qf[kk + 0], s0);
+      s1 = mma_f32(kx[1], qf[kk + 1], s1);
+      s0 = mma_f32(kx[2], qf[kk + 2], s0);
+      s1 = mma_f32(kx[3], qf[kk + 3], s1);
+    }
+    f32x16 s = s0 + s1;
+    if constexpr (DS > 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = s[r];
+      __syncthreads();
+      s = zero16();
+#pragma unroll
+      for (int e2 = 0; e2 < DS; ++e2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
+      }
+    }
+
+    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
+    const bool tail = kv0 + BN > Skv;
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t mw = 0xffffffffu;
+      if constexpr (MASK) mw = *(const uint32_t*)&sM[8 * u + 4 * hi];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * u + c;
+        const int kv = kv0 + acc_row(r, hi);
+        float x = s[r] * a.scale_log2;
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
+        if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
+        if constexpr (MASK) {
+          if (((mw >> (8 * c)) & 0xffu) == 0u) x = kNegInf;
+        } else {
+          if (tail && kv >= Skv) x = kNegInf;
+        }
+        if (diag && kv > qi) x = kNegInf;
+        s[r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2_hw(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_hw(s[r] - m_use);
+      s[r] = p;
+      ls += p;
+    }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+
+    // O^T += V^T P^T: step t pairs register t of the probabilities (key
+    // acc_row(t, hi)) with that key's V row, one key per lane group.
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float* vrow = sV + acc_row(t, hi) * P + e * DSL + l32;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma_f32(vrow[32 * dt], s[t], o[dt]);
+    }
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < Sq) {
+    float* Og = (float*)a.o + ((size_t)bh * Sq + qi) * D + e * DSL;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 w = {o[dt][4 * u] * inv, o[dt][4 * u + 1] * inv, o[dt][4 * u + 2] * inv, o[dt][4 * u + 3] * inv};
+        *(f32x4*)(Og + 32 * dt + 8 * u + 4 * hi) = w;
+      }
+    }
+    if (e == 0 && hi == 0 && a.lse) a.lse[(size_t)bh * Sq + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
+  auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK>;
+  const size_t lds = F32Cfg<D>::lds;
+  if (lds > 65536) {
+    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_qblocks * a.B * a.H)), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int MOD>
+static hipError_t launch_fwd32_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
+  if (causal) return mask ? launch_one<D, MOD, true, true>(a, st) : launch_one<D, MOD, true, false>(a, st);
+  return mask ? launch_one<D, MOD, false, true>(a, st) : launch_one<D, MOD, false, false>(a, st);
+}
+
+template <int D>
+static hipError_t launch_fwd32_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+  switch (mod) {
+    case MOD_ALIBI: return launch_fwd32_mod<D, MOD_ALIBI>(a, causal, mask, st);
+    case MOD_CHECKERBOARD: return launch_fwd32_mod<D, MOD_CHECKERBOARD>(a, causal, mask, st);
+    default: return launch_fwd32_mod<D, MOD_NONE>(a, causal, mask, st);
+  }
+}
+
+int fwd32_block_q(int D) {
+  return D == 512 ? F32Cfg<512>::BM : D == 128 ? F32Cfg<128>::BM : F32Cfg<64>::BM;
+}
+
+size_t fwd32_lds_bytes(int D) {
+  return D == 512 ? F32Cfg<512>::lds : D == 128 ? F32Cfg<128>::lds : F32Cfg<64>::lds;
+}
+
+hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st) {
+  if (D == 64) return launch_fwd32_d<64>(a, mod, causal, mask, st);
+  if (D == 128) return launch_fwd32_d<128>(a, mod, causal, mask, st);
+  return launch_fwd32_d<512>(a, mod, causal, mask, st);
+}
+
+}  // namespace fa

@@ -1,0 +1,35 @@
+// Host-side launchers of the attention kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+// 16-bit forward (f16 / bf16, head_dim 64 or 128).
+int fwd16_block_q();
+hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
+                        hipStream_t st);
+
+// fp32 forward (head_dim 64, 128 or 512).
+int fwd32_block_q(int D);
+size_t fwd32_lds_bytes(int D);
+hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st);
+
+// Backward: preprocess (delta = rowsum(dO * O), lse in base 2), then the
+// key-stationary dK/dV pass and the query-stationary dQ pass.
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st);
+int bwd16_block_kv();
+int bwd16_block_q();
+hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
+                        hipStream_t st);
+int bwd32_block_kv(int D);
+int bwd32_block_q(int D);
+hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st);
+
+// Split-KV decode and the merge of the partial (max, sum, accumulator).
+int decode_choose_split(int BH, int Skv, int* chunk);
+hipError_t launch_decode(const AttnArgs& a, int dtype, int D, int mod, bool mask, hipStream_t st);
+
+}  // namespace fa
