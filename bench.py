@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+A step is one forward plus one full backward (dQ, dK, dV) of the prefill
+workload: fp16 q, k, v ~ N(0, 1) of shape (8, 8, 2048, 64), causal, ALiBi
+score_mod, dO ~ N(0, 1).  The headline value is forward+backward TFLOP/s on
+the algorithmic flop count (causal pairs S(S+1)/2 per head; 4*D flop per pair
+forward, 10*D backward).  The same JSON line also carries the forward alone,
+the split-KV decode (fp16, (8, 8, 1, 64) against 2048 and 32768 keys, GB/s
+of K + V + q + O + lse with K/V copies rotated so reads come from HBM), the
+roofline of the dominant kernel, and the fp64 oracle timed on a bounded
+sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, reps: int, torch) -> float:
+    """Average milliseconds per call of fn() from HIP events on the current
+    stream (the stream the library launches on)."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(reps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(w, heads: int) -> dict:
+    """The fp64 oracle (as it is) on a bounded sample: the first `heads`
+    (batch, head) slices of the workload, forward + backward."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl is optional
+        threads = 1
+    x = w.make()
+    B = max(1, heads // w.heads)
+    hs = min(heads, w.heads)
+    sl = lambda t: t[:B, :hs].contiguous()
+    kw = dict(scale=w.scale, causal=w.causal, mod=w.mod)
+    # ALiBi slopes depend on the head count: pass the workload's slopes for the kept heads
+    slopes = oracle.default_alibi_slopes(w.heads)[:hs] if w.mod == W.MOD_ALIBI else None
+    t0 = time.perf_counter()
+    oracle.forward(sl(x["q"]), sl(x["k"]), sl(x["v"]), alibi_slopes=slopes, **kw)
+    oracle.backward(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["dout"]), alibi_slopes=slopes, **kw)
+    dt = time.perf_counter() - t0
+    frac = (B * hs) / (w.batch * w.heads)
+    flops = (w.fwd_flops() + w.bwd_flops()) * frac
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle forward+backward on {B * hs} of {w.batch * w.heads} (batch, head) slices "
+                      f"of the prefill workload, full sequence; {dt:.1f} s wall",
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="calls per per-kernel timing loop")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) slices in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import tiled_online_softmax_flashattention_amd as fa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    w = W.PREFILL_F16
+    log(f"[bench] inputs for {w.name}")
+    x = w.make()
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "dout"))
+    kw = dict(causal=w.causal, score_mod="alibi", scale=w.scale)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device=dev)
+
+    run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
+    run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
+    run_kv = fa.plan_backward(q, k, v, out, lse, do, None, grads[1], grads[2], ws, **kw)
+    run_q = fa.plan_backward(q, k, v, out, lse, do, grads[0], None, None, ws, **kw)
+
+    def step(_i=0):
+        run_fwd()
+        run_bwd()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    fb_flops = w.fwd_flops() + w.bwd_flops()
+    tflops = fb_flops / (ms_step * 1e-3) / 1e12
+
+    log("[bench] per-pass timing")
+    ms_fwd = time_calls(lambda i: run_fwd(), args.reps, torch)
+    ms_kv = time_calls(lambda i: run_kv(), args.reps, torch)
+    ms_q = time_calls(lambda i: run_q(), args.reps, torch)
+    pairs = w.pairs()
+    D = w.head_dim
+    # algorithmic flop per launch of each kernel (the key/value and query
+    # timings include the small delta/lse preprocess kernel)
+    kernels = {
+        "fwd16_kernel": (4.0 * D * pairs, ms_fwd),
+        "dkdv16_kernel": (8.0 * D * pairs, ms_kv),
+        "dq16_kernel": (2.0 * D * pairs, ms_q),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][1])
+    dom_flops, dom_ms = kernels[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "avg_ms": round(dom_ms, 4)}
+
+    log("[bench] decode")
+    decode = {}
+    for wd in (W.DECODE_F16_2K, W.DECODE_F16_32K):
+        per = 2 * wd.batch * wd.heads * wd.seq_kv * wd.head_dim * 2
+        n_sets = max(2, -(-(1 << 30) // per))
+        xd = wd.make()
+        qd = xd["q"].to(dev)
+        ks = [xd["k"].to(dev) for _ in range(n_sets)]
+        vs = [xd["v"].to(dev) for _ in range(n_sets)]
+        od = torch.empty_like(qd)
+        ld = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+        wsd = torch.empty(fa.decode_workspace_bytes(fa.problem(qd, ks[0], scale=wd.scale)), dtype=torch.uint8,
+                          device=dev)
+        plans = [fa.plan_decode(qd, ks[j], vs[j], od, ld, wsd, scale=wd.scale) for j in range(n_sets)]
+        call = lambda i: plans[i % n_sets]()
+        for i in range(3):
+            call(i)
+        ms = time_calls(call, max(args.reps, 2 * n_sets), torch)
+        nbytes = per + wd.batch * wd.heads * wd.head_dim * 2 * 2 + wd.batch * wd.heads * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        decode[str(wd.seq_kv)] = {"GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                                  "us": round(ms * 1e3, 2), "bytes": nbytes, "kv_copies_rotated": n_sets}
+        del ks, vs, plans
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd (% MFMA peak); decode GB/s (% HBM peak)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "prefill forward+backward, fp16, causal, ALiBi", "batch": w.batch,
+                   "heads": w.heads, "seq": w.seq_q, "head_dim": w.head_dim, "scale": "1/sqrt(64)"},
+        "fwd_bwd": {"TFLOP/s": round(tflops, 2), "frac_mfma_peak": round(tflops / PEAK_F16_TFLOPS, 4),
+                    "ms": round(ms_step, 4), "flop": fb_flops, "wall_s": round(wall, 3)},
+        "forward": {"TFLOP/s": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12, 2),
+                    "frac_mfma_peak": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+                    "ms": round(ms_fwd, 4)},
+        "backward_passes_ms": {"dkdv_with_preprocess": round(ms_kv, 4), "dq_with_preprocess": round(ms_q, 4)},
+        "decode": decode,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_heads} slices")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -109,6 +109,11 @@ fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes);
 /* Backward: gradients of sum(dout * out) with respect to q, k and v, with the
  * probabilities recomputed from the saved lse (no score matrix is stored).
  * out and lse must be the values fa_forward produced for the same inputs.
+ * Two passes: a key/value pass writing dk and dv, and a query pass writing
+ * dq.  dq == NULL skips the query pass; dk == dv == NULL skips the key/value
+ * pass (the flaxattention autograd example asks for the query gradient only);
+ * at least one pass must be requested, and dk, dv are NULL together or not
+ * at all.
  * The workspace (>= fa_backward_workspace_size bytes, 256-byte aligned) is
  * scratch: its contents on entry are ignored and on exit undefined.  Every
  * kernel is deterministic: repeated calls give bitwise-equal results. */

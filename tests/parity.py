@@ -23,18 +23,28 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def err(gpu: torch.Tensor, ref: np.ndarray, dtype: str) -> float:
+def err(gpu: torch.Tensor, ref: np.ndarray, dtype: str, strict: bool = True) -> float:
+    """fp32: max-abs-err.  16-bit: max-abs-err / max|ref|.
+
+    With strict=False (edge-case shapes only) two degenerate situations are
+    handled: a reference that is identically zero up to rounding
+    (max|ref| < 1e-3, e.g. dQ and dK with a single key) is compared in absolute
+    terms, and for fp32 a reference larger than 1 in magnitude scales the
+    bound (a sum of hundreds of O(1) terms has an fp32 resolution above 1e-5).
+    The five workloads are always checked with strict=True."""
     g = gpu.detach().double().cpu().numpy()
-    d = np.abs(g - ref).max() if ref.size else 0.0
+    d = float(np.abs(g - ref).max()) if ref.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
     if dtype == "f32":
-        return float(d)
-    scale = np.abs(ref).max() if ref.size else 1.0
-    return float(d / max(scale, 1e-30))
+        return d if strict else d / max(1.0, scale)
+    if not strict and scale < 1e-3:
+        return d
+    return d / max(scale, 1e-30)
 
 
-def check(name: str, gpu: torch.Tensor, ref: np.ndarray, dtype: str, kind: str) -> float:
+def check(name: str, gpu: torch.Tensor, ref: np.ndarray, dtype: str, kind: str, strict: bool = True) -> float:
     tol = (TOL_F32 if dtype == "f32" else TOL_16)[kind]
-    e = err(gpu, ref, dtype)
+    e = err(gpu, ref, dtype, strict)
     assert np.isfinite(gpu.detach().double().cpu().numpy()).all(), f"{name}: non-finite values"
     assert e <= tol, f"{name}: error {e:.3e} > {tol:.1e}"
     return e
@@ -75,7 +85,7 @@ def run_backward(w: W.Workload, dev: dict, out, lse, dout):
     return g
 
 
-def full_parity(w: W.Workload, backward: bool = True, inputs=None) -> dict:
+def full_parity(w: W.Workload, backward: bool = True, inputs=None, strict: bool = True) -> dict:
     """Every output element against the oracle (sizes the oracle finishes quickly)."""
     say(f"[parity] {w.name} B{w.batch} H{w.heads} Sq{w.seq_q} Skv{w.seq_kv} D{w.head_dim} {w.dtype} "
         f"causal={w.causal} mod={w.mod} mask={w.key_mask}")
@@ -84,14 +94,14 @@ def full_parity(w: W.Workload, backward: bool = True, inputs=None) -> dict:
     out, lse = run_forward(w, dev)
     okw = oracle_kw(w, inputs)
     o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
-    res = {"o": check("o", out, o_ref, w.dtype, "o")}
+    res = {"o": check("o", out, o_ref, w.dtype, "o", strict)}
     check_lse(lse, lse_ref)
     if backward:
         dq, dk, dv = run_backward(w, dev, out, lse, dev["dout"])
         dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
-        res["dq"] = check("dq", dq, dq_r, w.dtype, "grad")
-        res["dk"] = check("dk", dk, dk_r, w.dtype, "grad")
-        res["dv"] = check("dv", dv, dv_r, w.dtype, "grad")
+        res["dq"] = check("dq", dq, dq_r, w.dtype, "grad", strict)
+        res["dk"] = check("dk", dk, dk_r, w.dtype, "grad", strict)
+        res["dv"] = check("dv", dv, dv_r, w.dtype, "grad", strict)
     say(f"[parity] ok {res}")
     return res
 

@@ -119,7 +119,8 @@ def test_backward_workspace_rules():
     assert bwd(p, ws=None) == INVALID
     assert bwd(p, ws=ctypes.c_void_p(0x10010)) == INVALID            # workspace must be 256-byte aligned
     assert bwd(p, lse=None) == INVALID
-    assert bwd(p, dk=None) == INVALID
+    assert bwd(p, dk=None) == INVALID                               # dk and dv go together
+    assert bwd(p, dq=None, dk=None, dv=None) == INVALID              # nothing requested
     assert lib.fa_backward_workspace_size(ctypes.byref(p), None) == INVALID
 
 

@@ -25,7 +25,7 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["forward", "backward", "decode", "backward_workspace_bytes", "decode_workspace_bytes",
-           "FaError", "problem"]
+           "FaError", "problem", "plan_forward", "plan_backward", "plan_decode"]
 
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 _MOD = {None: _lib.FA_MOD_NONE, "none": _lib.FA_MOD_NONE, "alibi": _lib.FA_MOD_ALIBI,
@@ -103,8 +103,13 @@ def backward_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
-             alibi_slopes=None, checker=(0.5, -0.5), workspace=None, grads=None):
-    """Gradients (dq, dk, dv) of sum(dout * out)."""
+             alibi_slopes=None, checker=(0.5, -0.5), workspace=None, grads=None, which="all"):
+    """Gradients (dq, dk, dv) of sum(dout * out).
+
+    which="dq" runs only the query pass (dk, dv come back as None), "dkdv"
+    only the key/value pass (dq is None), "all" both."""
+    if which not in ("all", "dq", "dkdv"):
+        raise ValueError(f"which must be 'all', 'dq' or 'dkdv', not {which!r}")
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
@@ -113,6 +118,10 @@ def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    if which == "dq":
+        dk = dv = None
+    elif which == "dkdv":
+        dq = None
     lib = _lib.load()
     _lib.check(lib.fa_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)),
@@ -142,3 +151,54 @@ def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=N
     _lib.check(lib.fa_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                              workspace.numel(), _stream(q)), "fa_decode")
     return out, lse
+
+
+# ---------------------------------------------------------------- prepared calls
+#
+# A plan marshals every argument once and returns a zero-argument callable
+# that only enqueues the library call on the stream that was current when the
+# plan was made.  The tensors are kept alive by the plan.
+
+
+def _plan(fn, name, args, keep):
+    def run():
+        _lib.check(fn(*args), name)
+    run.keep = keep
+    return run
+
+
+def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
+                 alibi_slopes=None, checker=(0.5, -0.5)):
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    lib = _lib.load()
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
+    return _plan(lib.fa_forward, "fa_forward", args, (p, q, k, v, out, lse, key_mask, alibi_slopes))
+
+
+def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,
+                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5)):
+    """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    lib = _lib.load()
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
+    return _plan(lib.fa_backward, "fa_backward", args,
+                 (p, q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes))
+
+
+def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
+                checker=(0.5, -0.5)):
+    key_mask = _mask_u8(key_mask)
+    _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes)
+    p = problem(q, k, causal=False, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker)
+    lib = _lib.load()
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+            _stream(q))
+    return _plan(lib.fa_decode, "fa_decode", args, (p, q, k, v, out, lse, workspace, key_mask, alibi_slopes))

@@ -136,7 +136,12 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
                       size_t workspace_bytes, void* stream) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
-  if (!tensors_ok({q, k, v, out, dout, dq, dk, dv})) return FA_ERR_INVALID_ARGUMENT;
+  if (!tensors_ok({q, k, v, out, dout})) return FA_ERR_INVALID_ARGUMENT;
+  // dq == NULL skips the query pass; dk and dv both NULL skip the key/value pass
+  const bool want_q = dq != nullptr, want_kv = dk != nullptr || dv != nullptr;
+  if (!want_q && !want_kv) return FA_ERR_INVALID_ARGUMENT;
+  if (want_q && !tensors_ok({dq})) return FA_ERR_INVALID_ARGUMENT;
+  if (want_kv && !tensors_ok({dk, dv})) return FA_ERR_INVALID_ARGUMENT;
   if (!lse || ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
   const BwdLayout lay = bwd_layout(p);
@@ -164,9 +169,10 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   hipError_t err = fa::launch_bwd_pre(a, p->dtype, D, st);
   if (err != hipSuccess) return FA_ERR_HIP;
   if (f32)
-    err = fa::launch_bwd32(a, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
+    err = fa::launch_bwd32(a, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, want_kv, want_q, st);
   else
-    err = fa::launch_bwd16(a, p->dtype == FA_BF16, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
+    err = fa::launch_bwd16(a, p->dtype == FA_BF16, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr,
+                           want_kv, want_q, st);
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -47,9 +47,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtyp
       const int off = (it * LPR + sub) * 16;
       const u32x4 x = *(const u32x4*)(O + off);
       const u32x4 y = *(const u32x4*)(dO + off);
-      if (ES == 4) {
+      if constexpr (ES == 4) {
+        // bit-cast whole vectors: a bit_cast of a single vector element is
+        // miscompiled (every element reads as element 0)
+        const f32x4 xf = __builtin_bit_cast(f32x4, x), yf = __builtin_bit_cast(f32x4, y);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc += __builtin_bit_cast(float, x[c]) * __builtin_bit_cast(float, y[c]);
+        for (int c = 0; c < 4; ++c) acc += xf[c] * yf[c];
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -499,35 +502,40 @@ static hipError_t launch_dyn(K kern, unsigned grid, size_t lds, hipStream_t st, 
 }
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-static hipError_t launch_bwd16_inst(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
-  hipError_t err = launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
-  if (err != hipSuccess) return err;
+  if (want_kv) {
+    hipError_t err = launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
+    if (err != hipSuccess) return err;
+  }
+  if (!want_q) return hipSuccess;
   return launch_dyn(dq16_kernel<T, D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, Dq16Cfg<D>::lds, st, a);
 }
 
 template <class T, int D, int MOD>
-static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
-  if (causal) return mask ? launch_bwd16_inst<T, D, MOD, true, true>(a, st) : launch_bwd16_inst<T, D, MOD, true, false>(a, st);
-  return mask ? launch_bwd16_inst<T, D, MOD, false, true>(a, st) : launch_bwd16_inst<T, D, MOD, false, false>(a, st);
+static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
+  if (causal) return mask ? launch_bwd16_inst<T, D, MOD, true, true>(a, kv, qq, st) : launch_bwd16_inst<T, D, MOD, true, false>(a, kv, qq, st);
+  return mask ? launch_bwd16_inst<T, D, MOD, false, true>(a, kv, qq, st) : launch_bwd16_inst<T, D, MOD, false, false>(a, kv, qq, st);
 }
 
 template <class T, int D>
-static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return launch_bwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, st);
-    case MOD_CHECKERBOARD: return launch_bwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, st);
-    default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, st);
+    case MOD_ALIBI: return launch_bwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, kv, qq, st);
+    case MOD_CHECKERBOARD: return launch_bwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, kv, qq, st);
+    default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, kv, qq, st);
   }
 }
 
 int bwd16_block_kv() { return 128; }
 int bwd16_block_q() { return 128; }
 
-hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st) {
-  if (bf16) return D == 64 ? launch_bwd16_d<BF16, 64>(a, mod, causal, mask, st) : launch_bwd16_d<BF16, 128>(a, mod, causal, mask, st);
-  return D == 64 ? launch_bwd16_d<F16, 64>(a, mod, causal, mask, st) : launch_bwd16_d<F16, 128>(a, mod, causal, mask, st);
+hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, bool kv, bool qq,
+                        hipStream_t st) {
+  if (bf16)
+    return D == 64 ? launch_bwd16_d<BF16, 64>(a, mod, causal, mask, kv, qq, st) : launch_bwd16_d<BF16, 128>(a, mod, causal, mask, kv, qq, st);
+  return D == 64 ? launch_bwd16_d<F16, 64>(a, mod, causal, mask, kv, qq, st) : launch_bwd16_d<F16, 128>(a, mod, causal, mask, kv, qq, st);
 }
 
 }  // namespace fa

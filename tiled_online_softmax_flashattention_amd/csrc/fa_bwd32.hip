@@ -357,37 +357,40 @@ static hipError_t launch_dyn32(K kern, unsigned grid, size_t lds, hipStream_t st
 }
 
 template <int D, int MOD, bool CAUSAL, bool MASK>
-static hipError_t launch_bwd32_inst(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bwd32_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   using C = B32Cfg<D>;
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + 32 * C::NG - 1) / (32 * C::NG));
-  hipError_t err = launch_dyn32(dkdv32_kernel<D, MOD, CAUSAL, MASK>, nkb * BH, C::lds, st, a);
-  if (err != hipSuccess) return err;
+  if (want_kv) {
+    hipError_t err = launch_dyn32(dkdv32_kernel<D, MOD, CAUSAL, MASK>, nkb * BH, C::lds, st, a);
+    if (err != hipSuccess) return err;
+  }
+  if (!want_q) return hipSuccess;
   return launch_dyn32(dq32_kernel<D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, C::lds, st, a);
 }
 
 template <int D, int MOD>
-static hipError_t launch_bwd32_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
-  if (causal) return mask ? launch_bwd32_inst<D, MOD, true, true>(a, st) : launch_bwd32_inst<D, MOD, true, false>(a, st);
-  return mask ? launch_bwd32_inst<D, MOD, false, true>(a, st) : launch_bwd32_inst<D, MOD, false, false>(a, st);
+static hipError_t launch_bwd32_mod(const AttnArgs& a, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
+  if (causal) return mask ? launch_bwd32_inst<D, MOD, true, true>(a, kv, qq, st) : launch_bwd32_inst<D, MOD, true, false>(a, kv, qq, st);
+  return mask ? launch_bwd32_inst<D, MOD, false, true>(a, kv, qq, st) : launch_bwd32_inst<D, MOD, false, false>(a, kv, qq, st);
 }
 
 template <int D>
-static hipError_t launch_bwd32_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+static hipError_t launch_bwd32_d(const AttnArgs& a, int mod, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return launch_bwd32_mod<D, MOD_ALIBI>(a, causal, mask, st);
-    case MOD_CHECKERBOARD: return launch_bwd32_mod<D, MOD_CHECKERBOARD>(a, causal, mask, st);
-    default: return launch_bwd32_mod<D, MOD_NONE>(a, causal, mask, st);
+    case MOD_ALIBI: return launch_bwd32_mod<D, MOD_ALIBI>(a, causal, mask, kv, qq, st);
+    case MOD_CHECKERBOARD: return launch_bwd32_mod<D, MOD_CHECKERBOARD>(a, causal, mask, kv, qq, st);
+    default: return launch_bwd32_mod<D, MOD_NONE>(a, causal, mask, kv, qq, st);
   }
 }
 
 int bwd32_block_kv(int D) { return D >= 512 ? 32 : 128; }
 int bwd32_block_q(int D) { return D >= 512 ? 32 : 128; }
 
-hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st) {
-  if (D == 64) return launch_bwd32_d<64>(a, mod, causal, mask, st);
-  if (D == 128) return launch_bwd32_d<128>(a, mod, causal, mask, st);
-  return launch_bwd32_d<512>(a, mod, causal, mask, st);
+hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
+  if (D == 64) return launch_bwd32_d<64>(a, mod, causal, mask, kv, qq, st);
+  if (D == 128) return launch_bwd32_d<128>(a, mod, causal, mask, kv, qq, st);
+  return launch_bwd32_d<512>(a, mod, causal, mask, kv, qq, st);
 }
 
 }  // namespace fa

@@ -34,8 +34,9 @@ struct Elem<F32> {
 template <class T>
 __device__ __forceinline__ void unpack16(const u32x4 x, float* out) {
   if constexpr (__is_same(T, F32)) {
+    const f32x4 xf = __builtin_bit_cast(f32x4, x);  // whole-vector cast (see bwd_pre_kernel)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) out[c] = __builtin_bit_cast(float, x[c]);
+    for (int c = 0; c < 4; ++c) out[c] = xf[c];
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

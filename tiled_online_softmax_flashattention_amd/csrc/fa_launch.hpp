@@ -23,10 +23,11 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st);
 int bwd16_block_kv();
 int bwd16_block_q();
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
-                        hipStream_t st);
+                        bool want_kv, bool want_q, hipStream_t st);
 int bwd32_block_kv(int D);
 int bwd32_block_q(int D);
-hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st);
+hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, bool want_kv, bool want_q,
+                        hipStream_t st);
 
 // Split-KV decode and the merge of the partial (max, sum, accumulator).
 int decode_choose_split(int BH, int Skv, int* chunk);
