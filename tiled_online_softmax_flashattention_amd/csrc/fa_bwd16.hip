@@ -121,7 +121,7 @@ struct Stage2 {
       const int d = 8 * ch + c, word = c >> 1, sh = (c & 1) * 16;
       const uint32_t e0 = (r[0][word] >> sh) & 0xffffu, e1 = (r[1][word] >> sh) & 0xffffu;
       const uint32_t e2 = (r[2][word] >> sh) & 0xffffu, e3 = (r[3][word] >> sh) & 0xffffu;
-      const int phys = (((col >> 3) ^ (d & 7)) << 3) + (col & 7);
+      const int phys = (((col >> 3) ^ tr_swz(d)) << 3) + (col & 7);
       lds_write8(&tr[d * 64 + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
     }
   }
@@ -150,7 +150,7 @@ struct Stage1 {
 
 // Read the A fragment of a transposed tile: lane (row d, group hi), 16-wide step st.
 __device__ __forceinline__ u32x4 read_tr(const uint16_t* tr, int d, int st, int hi) {
-  return lds_read16(&tr[d * 64 + (((2 * st + hi) ^ (d & 7)) << 3)]);
+  return lds_read16(&tr[d * 64 + (((2 * st + hi) ^ tr_swz(d)) << 3)]);
 }
 
 template <class T>
@@ -170,7 +170,7 @@ struct DkdvCfg {
 };
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 1) void dkdv16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
   using C = DkdvCfg<D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, QP = C::QP;
   constexpr int KS = D / 16, DT = D / 32;
@@ -341,7 +341,7 @@ struct Dq16Cfg {
 };
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 1) void dq16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
   using C = Dq16Cfg<D>;
   constexpr int BM = C::BM, BN = C::BN, KP = C::KP;
   constexpr int KS = D / 16, DT = D / 32;

@@ -95,6 +95,12 @@ __device__ __forceinline__ constexpr int swap23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// Row swizzle of the 16-byte chunks of a transposed (dim-major) LDS tile.
+// Readers take 8 consecutive rows at once (conflict-free when the 8 rows map
+// to 8 distinct chunks); writers take rows 8 apart (Stage2) or 4 apart (the
+// forward's V tile), which the d >> 3 term spreads over distinct chunks too.
+__device__ __forceinline__ constexpr int tr_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
 // ALiBi slope for head h of H: slope_h = 2^(-8 (h+1) / H), or the caller's.
 __device__ __forceinline__ float alibi_slope(const float* slopes, int h, int H) {
   return slopes ? slopes[h] : exp2f(-8.0f * (float)(h + 1) / (float)H);

@@ -10,22 +10,35 @@
 // Work decomposition: one workgroup of 4 waves per 128-query block; each wave
 // owns 32 queries.  Key/value tiles of 64 keys are staged through LDS: K in
 // its natural (key, dim) layout, V transposed to (dim, key) so both products
-// read operand fragments with single 16-byte LDS reads.  The next tile is
-// fetched from HBM into registers while the current one is being used.
+// read operand fragments with single 16-byte LDS reads.  The loop is software
+// pipelined: while tile n is reduced on the VALU, the scores of tile n+1 are
+// already on the matrix cores, K of tile n+2 and V of tile n+1 are written to
+// the other LDS buffers, and K of tile n+3 and V of tile n+2 are in flight
+// from HBM into registers.
 //
-// Per tile and wave: S^T = K Q^T (MFMA 32x32x16, Q resident in registers as
-// the B operand), then scale / bias / mask in fp32, row max and sum (inside
-// the lane plus one exchange with lane ^ 32), then O^T += V^T P^T with P
-// rounded to the input type.  Causal: key tiles past the block's last query
-// are never visited, waves skip tiles entirely past their own queries, and
-// per-element masking happens only on diagonal tiles.
+// Per tile and wave: S'^T = K Q^T + C (MFMA 32x32x16, Q resident in registers
+// as the B operand).  The accumulator starts from C = bias / scale, so the
+// score_mod costs no per-score instruction: for ALiBi C holds the bias of the
+// key's offset inside the tile (the tile's own offset is a per-lane scalar
+// folded into the exponent), for the checkerboard the two parity values, and
+// with a key mask C is read from an LDS row that holds 0 or -inf per key.
+// Then one FMA and one v_exp_f32 per score give P = 2^(S' c + b - m).  The
+// running max is updated lazily: only when some query's maximum grows by more
+// than 2^8 does the wave rescale its accumulator, otherwise P stays below 2^8
+// (exact in fp16/bf16 range; the final division by l cancels the scale).
+// Causal: key tiles past the block's last query are never visited, tiles are
+// visited diagonal first (so the largest ALiBi scores set the maximum early),
+// waves skip tiles entirely past their own queries, and the per-score
+// comparison happens only on diagonal and ragged-tail tiles.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
 namespace fa {
 
+constexpr float kLazyRescale = 8.0f;   // log2 units: P is kept below 2^8
+
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnArgs a) {
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
   constexpr int KP = D + 8;        // K tile pitch in elements (16-byte pad)
@@ -34,9 +47,11 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * BN];  // V^T, 16-byte chunks XOR-swizzled by row
-  __shared__ __attribute__((aligned(16))) uint8_t sM[BN];
+  // Double buffers: K (with its mask row) runs two tiles ahead of the tile
+  // being reduced, V one tile ahead, so a single barrier per tile suffices.
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * BN];       // V^T, chunks swizzled by tr_swz(row)
+  __shared__ __attribute__((aligned(16))) float sB[2][MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -49,6 +64,8 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
+  const float c = a.scale_log2;
+  const float inv_scale = 1.0f / a.scale;
 
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)bh * Skv * D;
@@ -66,28 +83,54 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
     }
   }
 
-  float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
-  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
-  if constexpr (MOD == MOD_CHECKERBOARD) {
+  // Accumulator initial value, in units of q.k (bias / scale), per register.
+  float slope2 = 0.f;
+  f32x16 cinit = zero16();
+  if constexpr (MOD == MOD_ALIBI) {
+    const float slope = alibi_slope(a.alibi_slopes, h, a.H);
+    slope2 = slope * kLog2e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = slope * inv_scale * (float)acc_row(r, hi);
+  }
+  if constexpr (MOD == MOD_CHECKERBOARD && !MASK) {
     // register r holds a key of parity (r & 1); (qi + kv) is even when the parities agree
-    const bool qeven = (qi & 1) == 0;
-    cb0 = qeven ? a.even_log2 : a.odd_log2;
-    cb1 = qeven ? a.odd_log2 : a.even_log2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = (((qi + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
   const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
+  // causal: the diagonal tile first, then towards key 0
+  auto kv_of = [&](int n) { return (CAUSAL ? ntiles - 1 - n : n) * BN; };
+  // every key of the tile follows every query of this wave
+  auto skipped = [&](int n) { return CAUSAL && kv_of(n) > qw + 31; };
 
   u32x4 kreg[NK];
   u32x2 vreg[NV][4];
-  uint8_t mreg = 0;
+  float breg0 = 0.f, breg1 = 0.f;
 
-  auto load_tile = [&](int kv0) {
+  auto load_k = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8), kv = kv0 + row;
+      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8), kv = kv0 + row;
       kreg[i] = kv < Skv ? *(const u32x4*)(Kg + (size_t)kv * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
     }
+    if constexpr (MASK) {
+      if (tid < BN) {
+        const int kv = kv0 + tid;
+        const bool keep = kv < Skv && a.key_mask[(size_t)b * Skv + kv] != 0;
+        float e0 = 0.f, e1 = 0.f;   // additive bias for queries of parity 0 / 1
+        if constexpr (MOD == MOD_CHECKERBOARD) {
+          const bool kev = (kv & 1) == 0;
+          e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
+          e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
+        }
+        breg0 = keep ? e0 : kNegInf;
+        breg1 = keep ? e1 : kNegInf;
+      }
+    }
+  };
+  auto load_v = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = tid + 256 * i, db = e % (D / 4), kvb = e / (D / 4);
@@ -97,17 +140,21 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
         vreg[i][r] = kv < Skv ? *(const u32x2*)(Vg + (size_t)kv * D + 4 * db) : u32x2{0u, 0u};
       }
     }
-    if constexpr (MASK) {
-      if (tid < BN) mreg = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
-    }
   };
-
-  auto store_tile = [&]() {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
-      lds_write16(&sK[row * KP + 8 * ch], kreg[i]);
+      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
+      lds_write16(&sK[buf][row * KP + 8 * ch], kreg[i]);
     }
+    if constexpr (MASK) {
+      if (tid < BN) {
+        sB[buf][tid] = breg0;
+        sB[buf][BN + tid] = breg1;
+      }
+    }
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = tid + 256 * i, db = e % (D / 4), kvb = e / (D / 4);
@@ -117,12 +164,29 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
         const int d = 4 * db + c4, word = c4 >> 1, sh = (c4 & 1) * 16;
         const uint32_t e0 = (vreg[i][0][word] >> sh) & 0xffffu, e1 = (vreg[i][1][word] >> sh) & 0xffffu;
         const uint32_t e2 = (vreg[i][2][word] >> sh) & 0xffffu, e3 = (vreg[i][3][word] >> sh) & 0xffffu;
-        const int phys = (((col >> 3) ^ (d & 7)) << 3) + (col & 7);
-        lds_write8(&sV[d * BN + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
+        const int phys = (((col >> 3) ^ tr_swz(d)) << 3) + (col & 7);
+        lds_write8(&sV[buf][d * BN + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
       }
     }
-    if constexpr (MASK) {
-      if (tid < BN) sM[tid] = mreg;
+  };
+  // S'^T = K Q^T + C for the tile held in K buffer `buf`
+  auto scores = [&](int buf, f32x16* s) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 acc = cinit;
+      if constexpr (MASK) {
+        const float* row = sB[buf] + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 m4 = *(const f32x4*)(row + 8 * u);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) acc[4 * u + cc] += m4[cc];
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < QS; ++kk)
+        acc = mma16<T>(lds_read16(&sK[buf][(32 * t + l32) * KP + 16 * kk + 8 * hi]), qf[kk], acc);
+      s[t] = acc;
     }
   };
 
@@ -131,70 +195,88 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
-  load_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BN;
-    if (j > 0) __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (j + 1 < ntiles) load_tile(kv0 + BN);
-    if (CAUSAL && kv0 > qw + 31) continue;  // every key of the tile follows every query of this wave
+  // prologue: K of tiles 0 and 1, V of tile 0 in LDS; scores of tile 0
+  load_k(kv_of(0));
+  load_v(kv_of(0));
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) {
+    load_k(kv_of(1));
+    store_k(1);
+  }
+  __syncthreads();
+  if (ntiles > 2) load_k(kv_of(2));
+  if (ntiles > 1) load_v(kv_of(1));
+  f32x16 sa[2], sb[2];
+  if (!skipped(0)) scores(0, sa);
 
-    f32x16 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < QS; ++kk)
-        s[t] = mma16<T>(lds_read16(&sK[(32 * t + l32) * KP + 16 * kk + 8 * hi]), qf[kk], s[t]);
-    }
+  // one tile: reduce the scores in `s`, while the next tile's scores go to `s_next`
+  auto tile = [&](int n, f32x16* s, f32x16* s_next) {
+    const int kv0 = kv_of(n);
+    __syncthreads();   // everyone is past tile n-1: K buffer n&1 and V buffer (n+1)&1 are free
+    if (n + 2 < ntiles) store_k(n & 1);
+    if (n + 1 < ntiles) store_v((n + 1) & 1);
+    if (n + 3 < ntiles) load_k(kv_of(n + 3));
+    if (n + 2 < ntiles) load_v(kv_of(n + 2));
+    // scores of the next tile go to the matrix cores while this tile's softmax runs
+    if (n + 1 < ntiles && !skipped(n + 1)) scores((n + 1) & 1, s_next);
+    if (skipped(n)) return;
 
-    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
-    const bool tail = kv0 + BN > Skv;
-    float mx = kNegInf;
+    // scores past the diagonal or past seq_kv: -inf (only on such tiles)
+    {
+      int lim = 1 << 30;   // last allowed key position inside the tile, for this lane
+      if (CAUSAL && kv0 + BN - 1 > qw) lim = qi - kv0;
+      if (!MASK && kv0 + BN > Skv) lim = min(lim, Skv - 1 - kv0);
+      if (__builtin_amdgcn_ballot_w64(lim < BN - 1) != 0) {
+        const int lim_l = lim - 4 * hi;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t mw = 0xffffffffu;
-        if constexpr (MASK) mw = *(const uint32_t*)&sM[32 * t + 8 * u + 4 * hi];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * u + c;
-          const int kv = kv0 + 32 * t + acc_row(r, hi);
-          float x = s[t][r] * a.scale_log2;
-          if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
-          if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
-          if constexpr (MASK) {
-            if (((mw >> (8 * c)) & 0xffu) == 0u) x = kNegInf;
-          } else {
-            if (tail && kv >= Skv) x = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            const int pos = 32 * t + 8 * (r >> 2) + (r & 3);   // acc_row(r, hi) - 4 hi
+            if (pos > lim_l) s[t][r] = kNegInf;
           }
-          if (diag && kv > qi) x = kNegInf;
-          s[t][r] = x;
-          mx = fmaxf(mx, x);
         }
       }
     }
+
+    // per-lane exponent offsets of the two 32-key halves (ALiBi: bias of the half's first key)
+    float add0 = 0.f, add1 = 0.f;
+    if constexpr (MOD == MOD_ALIBI) {
+      add0 = slope2 * (float)(kv0 - qi);
+      add1 = add0 + slope2 * 32.0f;
+    }
+    float mx0 = s[0][0], mx1 = s[1][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      mx0 = fmaxf(mx0, s[0][r]);
+      mx1 = fmaxf(mx1, s[1][r]);
+    }
+    float mx = fmaxf(fmaf(mx0, c, add0), fmaf(mx1, c, add1));
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_hw(m_run - ((m_new == kNegInf) ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    const float nb0 = add0 - m_use, nb1 = add1 - m_use;
     float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(s[t][r] - m_use);
-        s[t][r] = p;
-        ls += p;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = exp2_hw(fmaf(s[0][r], c, nb0));
+      const float p1 = exp2_hw(fmaf(s[1][r], c, nb1));
+      s[0][r] = p0;
+      s[1][r] = p1;
+      ls += p0 + p1;
     }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    l_run += ls;
 
+    // O^T += V^T P^T
+    const uint16_t* vb = sV[n & 1];
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {
       const int t = st >> 1, u = st & 1;
@@ -203,10 +285,16 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(const AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + l32;
-        const int phys = ((2 * st + hi) ^ (d & 7)) << 3;
-        o[dt] = mma16<T>(lds_read16(&sV[d * BN + phys]), pb, o[dt]);
+        const int phys = ((2 * st + hi) ^ tr_swz(d)) << 3;
+        o[dt] = mma16<T>(lds_read16(&vb[d * BN + phys]), pb, o[dt]);
       }
     }
+  };
+
+  // unrolled by two so the score registers alternate without copies
+  for (int n = 0; n < ntiles; n += 2) {
+    tile(n, sa, sb);
+    if (n + 1 < ntiles) tile(n + 1, sb, sa);
   }
 
   const float l_tot = l_run + xor32(l_run);
