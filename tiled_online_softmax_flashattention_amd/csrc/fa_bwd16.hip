@@ -101,14 +101,13 @@ struct Stage2 {
   static constexpr int NG = 16 * (D / 8);   // (4-row group, 8-dim chunk) pairs
   u32x4 r[4];
   bool active;
+  // Rows past nrows are clamped to the last row (finite values that the
+  // kernels mask out), so the loads carry no branch.
   __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
     active = tid < NG;
-    const int rg = tid / (D / 8), ch = tid % (D / 8);
+    const int rg = (tid % NG) / (D / 8), ch = tid % (D / 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + 4 * rg + i;
-      r[i] = (active && row < nrows) ? *(const u32x4*)(g + (size_t)row * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 4; ++i) r[i] = *(const u32x4*)(g + (size_t)min(row0 + 4 * rg + i, nrows - 1) * D + 8 * ch);
   }
   __device__ __forceinline__ void store(uint16_t* nat, uint16_t* tr, int tid) const {
     if (!active) return;
@@ -136,7 +135,7 @@ struct Stage1 {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
-      r[i] = (row0 + row < nrows) ? *(const u32x4*)(g + (size_t)(row0 + row) * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      r[i] = *(const u32x4*)(g + (size_t)min(row0 + row, nrows - 1) * D + 8 * ch);
     }
   }
   __device__ __forceinline__ void store(uint16_t* nat, int tid) const {
@@ -236,14 +235,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int nqt = (Sq + BQ - 1) / BQ;
   Stage2<D> stq, sto;
   float lreg = 0.f, dreg = 0.f;
+  int lq = 0;
   auto load_tile = [&](int q0) {
     stq.load(Qg, q0, Sq, tid);
     sto.load(dOg, q0, Sq, tid);
-    if (tid < BQ) {
-      const bool ok = q0 + tid < Sq;
-      lreg = ok ? lse2g[q0 + tid] : __builtin_inff();
-      dreg = ok ? deltag[q0 + tid] : 0.f;
-    }
+    lq = q0 + (tid & (BQ - 1));
+    lreg = lse2g[min(lq, Sq - 1)];
+    dreg = deltag[min(lq, Sq - 1)];
   };
 
   if (qt0 < nqt) load_tile(qt0 * BQ);
@@ -252,12 +250,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     if (it > qt0) __syncthreads();
     stq.store(sQ, sQt, tid);
     sto.store(sO, sOt, tid);
-    if (tid < BQ) {
-      sL[tid] = lreg;
-      sDl[tid] = dreg;
+    if (tid < BQ) {   // rows past seq_q: P = 0 (lse2 = +inf) and delta = 0
+      sL[tid] = lq < Sq ? lreg : __builtin_inff();
+      sDl[tid] = lq < Sq ? dreg : 0.f;
     }
     __syncthreads();
-    if (it + 1 < nqt) load_tile(q0 + BQ);
+    load_tile(min(it + 1, nqt - 1) * BQ);   // unconditional (clamped): no branch next to the loads
     if (CAUSAL && q0 + BQ - 1 < kw) continue;  // every query of the tile precedes every key of this wave
 
     // S = Q K^T and dP = dO V^T, queries as rows.
@@ -402,12 +400,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int ntiles = (kv_end + BN - 1) / BN;
   Stage2<D> stk;
   Stage1<D> stv;
-  uint8_t mreg = 0;
+  uint32_t mreg = 0;
+  int mkv = 0;
   auto load_tile = [&](int kv0) {
     stk.load(Kg, kv0, Skv, tid);
     stv.load(Vg, kv0, Skv, tid);
     if constexpr (MASK) {
-      if (tid < BN) mreg = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+      mkv = kv0 + (tid & (BN - 1));
+      mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
 
@@ -418,10 +418,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     stk.store(sK, sKt, tid);
     stv.store(sV, tid);
     if constexpr (MASK) {
-      if (tid < BN) sM[tid] = mreg;
+      if (tid < BN) sM[tid] = (mkv < Skv && mreg != 0) ? 1 : 0;
     }
     __syncthreads();
-    if (j + 1 < ntiles) load_tile(kv0 + BN);
+    load_tile(min(j + 1, ntiles - 1) * BN);   // unconditional (clamped): no branch next to the loads
     if (CAUSAL && kv0 > qw + 31) continue;
 
     // S^T = K Q^T and dP^T = V dO^T, keys as rows.

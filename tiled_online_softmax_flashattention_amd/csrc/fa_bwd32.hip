@@ -43,7 +43,8 @@ __device__ __forceinline__ void stage32(float* dst, const float* g, int row0, in
 #pragma unroll 4
   for (int i = 0; i < N; ++i) {
     const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4);
-    const f32x4 x = (row0 + row < nrows) ? *(const f32x4*)(g + (size_t)(row0 + row) * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // rows past nrows: the last row (finite; the kernels mask it out)
+    const f32x4 x = *(const f32x4*)(g + (size_t)min(row0 + row, nrows - 1) * D + 4 * ch);
     *(f32x4*)&dst[row * (D + 4) + 4 * ch] = x;
   }
 }

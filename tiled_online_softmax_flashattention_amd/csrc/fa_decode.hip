@@ -105,10 +105,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
     u32x4 kx[U], vx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kv = base + u * KPB;
-      const bool ok = kv < c1;
-      kx[u] = ok ? *(const u32x4*)(Kg + (size_t)kv * D * ES) : u32x4{0u, 0u, 0u, 0u};
-      vx[u] = ok ? *(const u32x4*)(Vg + (size_t)kv * D * ES) : u32x4{0u, 0u, 0u, 0u};
+      // keys past the chunk: the chunk's last key (finite; its score is -inf below)
+      const int kv = min(base + u * KPB, c1 - 1);
+      kx[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
+      vx[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
     }
     float t[U];
 #pragma unroll

@@ -10,11 +10,12 @@
 // Work decomposition: one workgroup of 4 waves per 128-query block; each wave
 // owns 32 queries.  Key/value tiles of 64 keys are staged through LDS: K in
 // its natural (key, dim) layout, V transposed to (dim, key) so both products
-// read operand fragments with single 16-byte LDS reads.  The loop is software
-// pipelined: while tile n is reduced on the VALU, the scores of tile n+1 are
-// already on the matrix cores, K of tile n+2 and V of tile n+1 are written to
-// the other LDS buffers, and K of tile n+3 and V of tile n+2 are in flight
-// from HBM into registers.
+// read operand fragments with single 16-byte LDS reads.  K and V are double
+// buffered: while tile n is used, tile n+1 is written to the other buffers
+// and tile n+2 is in flight from HBM into registers, so one barrier per tile
+// suffices.  At head_dim 64 the kernel fits 3 waves per SIMD; issuing the
+// next tile's scores before the current softmax was measured slower here
+// because its extra registers cost a wave of occupancy.
 //
 // Per tile and wave: S'^T = K Q^T + C (MFMA 32x32x16, Q resident in registers
 // as the B operand).  The accumulator starts from C = bias / scale, so the
@@ -38,7 +39,7 @@ namespace fa {
 constexpr float kLazyRescale = 8.0f;   // log2 units: P is kept below 2^8
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnArgs a) {
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
   constexpr int KP = D + 8;        // K tile pitch in elements (16-byte pad)
@@ -47,8 +48,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
 
-  // Double buffers: K (with its mask row) runs two tiles ahead of the tile
-  // being reduced, V one tile ahead, so a single barrier per tile suffices.
+  // Double buffers: tile n+1 is written while tile n is read.
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * BN];       // V^T, chunks swizzled by tr_swz(row)
   __shared__ __attribute__((aligned(16))) float sB[2][MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
@@ -105,29 +105,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
   // every key of the tile follows every query of this wave
   auto skipped = [&](int n) { return CAUSAL && kv_of(n) > qw + 31; };
 
+  // Staging loads are unconditional: rows past seq_kv are clamped to the last
+  // row (finite values whose scores are masked to -inf), so no branch (and no
+  // wait for outstanding loads at a branch merge) sits next to a load.
   u32x4 kreg[NK];
   u32x2 vreg[NV][4];
-  float breg0 = 0.f, breg1 = 0.f;
+  uint32_t mreg = 0;
+  int mkv = 0;
 
   auto load_k = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8), kv = kv0 + row;
-      kreg[i] = kv < Skv ? *(const u32x4*)(Kg + (size_t)kv * D + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
+      kreg[i] = *(const u32x4*)(Kg + (size_t)min(kv0 + row, Skv - 1) * D + 8 * ch);
     }
     if constexpr (MASK) {
-      if (tid < BN) {
-        const int kv = kv0 + tid;
-        const bool keep = kv < Skv && a.key_mask[(size_t)b * Skv + kv] != 0;
-        float e0 = 0.f, e1 = 0.f;   // additive bias for queries of parity 0 / 1
-        if constexpr (MOD == MOD_CHECKERBOARD) {
-          const bool kev = (kv & 1) == 0;
-          e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
-          e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
-        }
-        breg0 = keep ? e0 : kNegInf;
-        breg1 = keep ? e1 : kNegInf;
-      }
+      mkv = kv0 + (tid & (BN - 1));
+      mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
   auto load_v = [&](int kv0) {
@@ -135,10 +129,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
     for (int i = 0; i < NV; ++i) {
       const int e = tid + 256 * i, db = e % (D / 4), kvb = e / (D / 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kv = kv0 + 4 * kvb + r;
-        vreg[i][r] = kv < Skv ? *(const u32x2*)(Vg + (size_t)kv * D + 4 * db) : u32x2{0u, 0u};
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[i][r] = *(const u32x2*)(Vg + (size_t)min(kv0 + 4 * kvb + r, Skv - 1) * D + 4 * db);
     }
   };
   auto store_k = [&](int buf) {
@@ -149,8 +141,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
     }
     if constexpr (MASK) {
       if (tid < BN) {
-        sB[buf][tid] = breg0;
-        sB[buf][BN + tid] = breg1;
+        const bool keep = mkv < Skv && mreg != 0;
+        float e0 = 0.f, e1 = 0.f;   // additive bias for queries of parity 0 / 1
+        if constexpr (MOD == MOD_CHECKERBOARD) {
+          const bool kev = (mkv & 1) == 0;
+          e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
+          e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
+        }
+        sB[buf][tid] = keep ? e0 : kNegInf;
+        sB[buf][BN + tid] = keep ? e1 : kNegInf;
       }
     }
   };
@@ -195,32 +194,30 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
-  // prologue: K of tiles 0 and 1, V of tile 0 in LDS; scores of tile 0
-  load_k(kv_of(0));
-  load_v(kv_of(0));
+  // Staging is unconditional (tile indices past the end are clamped to the
+  // last tile): the buffers written near the end are never read again, and
+  // straight-line staging keeps the load waits exact.
+  auto kv_c = [&](int n) { return kv_of(min(n, ntiles - 1)); };
+
+  load_k(kv_c(0));
+  load_v(kv_c(0));
   store_k(0);
   store_v(0);
-  if (ntiles > 1) {
-    load_k(kv_of(1));
-    store_k(1);
-  }
   __syncthreads();
-  if (ntiles > 2) load_k(kv_of(2));
-  if (ntiles > 1) load_v(kv_of(1));
+  load_k(kv_c(1));
+  load_v(kv_c(1));
   f32x16 sa[2], sb[2];
-  if (!skipped(0)) scores(0, sa);
 
-  // one tile: reduce the scores in `s`, while the next tile's scores go to `s_next`
-  auto tile = [&](int n, f32x16* s, f32x16* s_next) {
+  // one tile (n): stage tile n+1, then scores, softmax and P V of tile n
+  auto tile = [&](int n, f32x16* s) {
     const int kv0 = kv_of(n);
-    __syncthreads();   // everyone is past tile n-1: K buffer n&1 and V buffer (n+1)&1 are free
-    if (n + 2 < ntiles) store_k(n & 1);
-    if (n + 1 < ntiles) store_v((n + 1) & 1);
-    if (n + 3 < ntiles) load_k(kv_of(n + 3));
-    if (n + 2 < ntiles) load_v(kv_of(n + 2));
-    // scores of the next tile go to the matrix cores while this tile's softmax runs
-    if (n + 1 < ntiles && !skipped(n + 1)) scores((n + 1) & 1, s_next);
+    __syncthreads();   // everyone is past tile n-1, whose buffers ((n+1)&1) are now free
+    store_k((n + 1) & 1);    // K of tile n+1
+    store_v((n + 1) & 1);    // V of tile n+1
+    load_k(kv_c(n + 2));
+    load_v(kv_c(n + 2));
     if (skipped(n)) return;
+    scores(n & 1, s);
 
     // scores past the diagonal or past seq_kv: -inf (only on such tiles)
     {
@@ -291,10 +288,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void fwd16_kernel(const AttnA
     }
   };
 
-  // unrolled by two so the score registers alternate without copies
   for (int n = 0; n < ntiles; n += 2) {
-    tile(n, sa, sb);
-    if (n + 1 < ntiles) tile(n + 1, sb, sa);
+    tile(n, sa);
+    if (n + 1 < ntiles) tile(n + 1, sb);
   }
 
   const float l_tot = l_run + xor32(l_run);

@@ -92,10 +92,10 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     __syncthreads();
 #pragma unroll 4
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4), kv = kv0 + row;
-      const bool ok = kv < Skv;
-      const f32x4 kx = ok ? *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 vx = ok ? *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+      // rows past seq_kv: the last row (finite; its scores are masked to -inf)
+      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4), kv = min(kv0 + row, Skv - 1);
+      const f32x4 kx = *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch);
+      const f32x4 vx = *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch);
       *(f32x4*)&sK[row * P + 4 * ch] = kx;
       *(f32x4*)&sV[row * P + 4 * ch] = vx;
     }
