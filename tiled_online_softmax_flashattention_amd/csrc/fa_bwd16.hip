@@ -165,21 +165,28 @@ struct DkdvCfg {
   static constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 64;     // queries per tile
   static constexpr int QP = D + 8;
-  static constexpr size_t lds = (size_t)2 * (BQ * QP + D * BQ) * 2 + 2 * BQ * 4;
+  // one buffer: Q and dO, each natural and transposed (16-bit), then lse2 and delta rows
+  static constexpr size_t buf_elems = (size_t)2 * (BQ * QP + D * BQ) + 2 * BQ * 2;
+  static constexpr size_t lds = 2 * buf_elems * 2;
 };
 
+// Key-stationary dK/dV pass.  The ALiBi and checkerboard bias start the S
+// accumulator (the per-query part, per register) with the per-key part and
+// the key mask (-inf) folded into one per-lane exponent term, so per score
+// the work is one subtraction of the row's lse, one FMA and one exp for P
+// and a subtraction and a multiply for dS.  Query tiles are double buffered.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
   using C = DkdvCfg<D>;
   constexpr int BKV = C::BKV, BQ = C::BQ, QP = C::QP;
   constexpr int KS = D / 16, DT = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
-  uint16_t* sQ = smem16;
-  uint16_t* sQt = sQ + BQ * QP;
-  uint16_t* sO = sQt + D * BQ;
-  uint16_t* sOt = sO + BQ * QP;
-  float* sL = (float*)(sOt + D * BQ);
-  float* sDl = sL + BQ;
+  auto sQ = [&](int buf) { return smem16 + buf * C::buf_elems; };
+  auto sQt = [&](int buf) { return sQ(buf) + BQ * QP; };
+  auto sO = [&](int buf) { return sQt(buf) + D * BQ; };
+  auto sOt = [&](int buf) { return sO(buf) + BQ * QP; };
+  auto sL = [&](int buf) { return (float*)(sOt(buf) + D * BQ); };
+  auto sDl = [&](int buf) { return sL(buf) + BQ; };
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -191,6 +198,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int k0 = kb * BKV;
   const int kw = k0 + 32 * wave;
   const int kj = kw + l32;            // this lane's key
+  const float c = a.scale_log2;
+  const float inv_scale = 1.0f / a.scale;
 
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
   const uint16_t* dOg = (const uint16_t*)a.dout + (size_t)bh * Sq * D;
@@ -202,26 +211,30 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   // K and V rows of this lane's key as B operands (dims 16kk + 8hi .. +7).
   u32x4 kf[KS], vf[KS];
   {
-    const bool ok = kj < Skv;
-    const size_t off = (size_t)(ok ? kj : 0) * D + 8 * hi;
+    const size_t off = (size_t)min(kj, Skv - 1) * D + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const u32x4 x = *(const u32x4*)(Kg + off + 16 * kk);
-      const u32x4 y = *(const u32x4*)(Vg + off + 16 * kk);
-      kf[kk] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-      vf[kk] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+      kf[kk] = *(const u32x4*)(Kg + off + 16 * kk);
+      vf[kk] = *(const u32x4*)(Vg + off + 16 * kk);
     }
   }
+  // per-lane exponent term: the key's share of the bias, or -inf for a
+  // masked key or a key past seq_kv (its dK, dV rows are not stored)
   bool key_ok = kj < Skv;
-  if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + (key_ok ? kj : 0)] != 0;
-
-  float slope2 = 0.f, cbe = 0.f, cbo = 0.f;
-  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
+  if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + min(kj, Skv - 1)] != 0;
+  float slope2 = 0.f;
+  f32x16 cinit = zero16();
+  if constexpr (MOD == MOD_ALIBI) {
+    // bias = slope (kj - q); per register: -slope * acc_row / scale
+    const float slope = alibi_slope(a.alibi_slopes, h, a.H);
+    slope2 = slope * kLog2e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = -slope * inv_scale * (float)acc_row(r, hi);
+  }
   if constexpr (MOD == MOD_CHECKERBOARD) {
     // query tiles start at even positions, so register r holds a query of parity (r & 1)
-    const bool keven = (kj & 1) == 0;
-    cbe = keven ? a.even_log2 : a.odd_log2;   // even query
-    cbo = keven ? a.odd_log2 : a.even_log2;   // odd query
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = (((kj + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
   f32x16 dk[DT], dv[DT];
@@ -236,76 +249,89 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   Stage2<D> stq, sto;
   float lreg = 0.f, dreg = 0.f;
   int lq = 0;
-  auto load_tile = [&](int q0) {
+  auto load_tile = [&](int it) {
+    const int q0 = min(it, nqt - 1) * BQ;   // clamped: no branch next to the loads
     stq.load(Qg, q0, Sq, tid);
     sto.load(dOg, q0, Sq, tid);
     lq = q0 + (tid & (BQ - 1));
     lreg = lse2g[min(lq, Sq - 1)];
     dreg = deltag[min(lq, Sq - 1)];
   };
+  auto store_tile = [&](int buf) {
+    stq.store(sQ(buf), sQt(buf), tid);
+    sto.store(sO(buf), sOt(buf), tid);
+    if (tid < BQ) {   // rows past seq_q: P = 0 (lse2 = +inf) and delta = 0
+      sL(buf)[tid] = lq < Sq ? lreg : __builtin_inff();
+      sDl(buf)[tid] = lq < Sq ? dreg : 0.f;
+    }
+  };
 
-  if (qt0 < nqt) load_tile(qt0 * BQ);
+  if (qt0 < nqt) {
+    load_tile(qt0);
+    store_tile(qt0 & 1);
+    __syncthreads();
+    load_tile(qt0 + 1);
+  }
   for (int it = qt0; it < nqt; ++it) {
     const int q0 = it * BQ;
-    if (it > qt0) __syncthreads();
-    stq.store(sQ, sQt, tid);
-    sto.store(sO, sOt, tid);
-    if (tid < BQ) {   // rows past seq_q: P = 0 (lse2 = +inf) and delta = 0
-      sL[tid] = lq < Sq ? lreg : __builtin_inff();
-      sDl[tid] = lq < Sq ? dreg : 0.f;
-    }
-    __syncthreads();
-    load_tile(min(it + 1, nqt - 1) * BQ);   // unconditional (clamped): no branch next to the loads
+    __syncthreads();   // everyone is past tile it-1, whose buffer ((it+1)&1) is free
+    store_tile((it + 1) & 1);
+    load_tile(it + 2);
     if (CAUSAL && q0 + BQ - 1 < kw) continue;  // every query of the tile precedes every key of this wave
+    const int buf = it & 1;
+    const uint16_t* qb = sQ(buf);
+    const uint16_t* ob = sO(buf);
 
-    // S = Q K^T and dP = dO V^T, queries as rows.
-    f32x16 s[2], dp[2];
+    const uint16_t* otb = sOt(buf);
+    const uint16_t* qtb = sQt(buf);
+    // one 32-query half at a time keeps S and dP to 32 registers
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = zero16();
-      dp[mt] = zero16();
+      // S' = Q K^T + C and dP = dO V^T, queries as rows
+      f32x16 sv = cinit, dpv = zero16();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int off = (32 * mt + l32) * QP + 16 * kk + 8 * hi;
-        s[mt] = mma16<T>(lds_read16(&sQ[off]), kf[kk], s[mt]);
-        dp[mt] = mma16<T>(lds_read16(&sO[off]), vf[kk], dp[mt]);
+        sv = mma16<T>(lds_read16(&qb[off]), kf[kk], sv);
+        dpv = mma16<T>(lds_read16(&ob[off]), vf[kk], dpv);
       }
-    }
-
-    const bool diag = CAUSAL && (q0 < kw + 31);
+      // queries before the key (causal): P = 0, only on diagonal tiles
+      if (CAUSAL && __builtin_amdgcn_ballot_w64(q0 + 32 * mt < kj) != 0) {
+        const int lim_l = kj - q0 - 32 * mt - 4 * hi;   // rows with acc_row < kj - q0 - 32 mt are masked
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x4 l4 = *(const f32x4*)&sL[32 * mt + 8 * u + 4 * hi];
-        const f32x4 d4 = *(const f32x4*)&sDl[32 * mt + 8 * u + 4 * hi];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * u + c;
-          const int qi = q0 + 32 * mt + acc_row(r, hi);
-          float x = s[mt][r] * a.scale_log2;
-          if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi);
-          if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cbo : cbe;
-          float p = exp2_hw(x - l4[c]);
-          if (!key_ok) p = 0.f;
-          if (diag && kj > qi) p = 0.f;
-          s[mt][r] = p;
-          dp[mt][r] = p * (dp[mt][r] - d4[c]);
+        for (int r = 0; r < 16; ++r) {
+          const int pos = 8 * (r >> 2) + (r & 3);
+          if (pos < lim_l) sv[r] = kNegInf;
         }
       }
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries.
+      float lb = key_ok ? 0.f : kNegInf;
+      if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - q0 - 32 * mt) : kNegInf;
+      const float* lrow = sL(buf) + 32 * mt + 4 * hi;
+      const float* drow = sDl(buf) + 32 * mt + 4 * hi;
 #pragma unroll
-    for (int st = 0; st < BQ / 16; ++st) {
-      const int mt = st >> 1, u = st & 1;
-      const u32x4 pb = pack8<T>(s[mt], u);
-      const u32x4 db = pack8<T>(dp[mt], u);
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
+        const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + l32;
-        dv[dt] = mma16<T>(read_tr(sOt, d, st, hi), pb, dv[dt]);
-        dk[dt] = mma16<T>(read_tr(sQt, d, st, hi), db, dk[dt]);
+        for (int cc = 0; cc < 4; ++cc) {
+          const int r = 4 * u + cc;
+          const float p = exp2_hw(fmaf(sv[r], c, lb - l4[cc]));
+          sv[r] = p;
+          dpv[r] = p * (dpv[r] - d4[cc]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int st = 2 * mt + u;
+        const u32x4 pb = pack8<T>(sv, u);
+        const u32x4 db = pack8<T>(dpv, u);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 32 * dt + l32;
+          dv[dt] = mma16<T>(read_tr(otb, d, st, hi), pb, dv[dt]);
+          dk[dt] = mma16<T>(read_tr(qtb, d, st, hi), db, dk[dt]);
+        }
       }
     }
   }
@@ -335,19 +361,25 @@ struct Dq16Cfg {
   static constexpr int BM = 128;   // queries per workgroup
   static constexpr int BN = 64;    // keys per tile
   static constexpr int KP = D + 8;
-  static constexpr size_t lds = (size_t)(2 * BN * KP + D * BN) * 2 + 64;
+  // one buffer: K natural, K transposed, V natural (16-bit) and the key row
+  static constexpr size_t buf_elems = (size_t)2 * BN * KP + D * BN + 2 * BN * 2;
+  static constexpr size_t lds = 2 * buf_elems * 2;
 };
 
+// Query-stationary dQ pass, structured like the forward kernel: the score_mod
+// bias (and the key mask row) start the S^T accumulator, masking runs only on
+// diagonal and tail tiles, tiles are double buffered with branch-free staging,
+// and per score one FMA and one exp give P = 2^(S' c + b - lse2).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
   using C = Dq16Cfg<D>;
   constexpr int BM = C::BM, BN = C::BN, KP = C::KP;
   constexpr int KS = D / 16, DT = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
-  uint16_t* sK = smem16;
-  uint16_t* sKt = sK + BN * KP;
-  uint16_t* sV = sKt + D * BN;
-  uint8_t* sM = (uint8_t*)(sV + BN * KP);
+  auto sK = [&](int buf) { return smem16 + buf * C::buf_elems; };
+  auto sKt = [&](int buf) { return sK(buf) + BN * KP; };
+  auto sV = [&](int buf) { return sKt(buf) + D * BN; };
+  auto sB = [&](int buf) { return (float*)(sV(buf) + BN * KP); };   // 2 x BN floats: q parity 0 / 1
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -360,6 +392,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int q0 = qb * BM;
   const int qw = q0 + 32 * wave;
   const int qi = qw + l32;
+  const float c = a.scale_log2;
+  const float inv_scale = 1.0f / a.scale;
 
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
   const uint16_t* dOg = (const uint16_t*)a.dout + (size_t)bh * Sq * D;
@@ -367,10 +401,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)bh * Skv * D;
 
   u32x4 qf[KS], of[KS];
-  float lse2 = __builtin_inff(), delta = 0.f;
+  float lse2, delta;
   {
     const bool ok = qi < Sq;
-    const size_t off = (size_t)(ok ? qi : 0) * D + 8 * hi;
+    const size_t off = (size_t)min(qi, Sq - 1) * D + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const u32x4 x = *(const u32x4*)(Qg + off + 16 * kk);
@@ -378,18 +412,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       qf[kk] = ok ? x : u32x4{0u, 0u, 0u, 0u};
       of[kk] = ok ? y : u32x4{0u, 0u, 0u, 0u};
     }
-    if (ok) {
-      lse2 = a.lse2[(size_t)bh * Sq + qi];
-      delta = a.delta[(size_t)bh * Sq + qi];
-    }
+    const float l2 = a.lse2[(size_t)bh * Sq + min(qi, Sq - 1)];
+    const float dl = a.delta[(size_t)bh * Sq + min(qi, Sq - 1)];
+    lse2 = ok ? l2 : __builtin_inff();   // rows past seq_q: P = 0
+    delta = ok ? dl : 0.f;
   }
 
-  float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
-  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
-  if constexpr (MOD == MOD_CHECKERBOARD) {
-    const bool qeven = (qi & 1) == 0;
-    cb0 = qeven ? a.even_log2 : a.odd_log2;
-    cb1 = qeven ? a.odd_log2 : a.even_log2;
+  float slope2 = 0.f;
+  f32x16 cinit = zero16();
+  if constexpr (MOD == MOD_ALIBI) {
+    const float slope = alibi_slope(a.alibi_slopes, h, a.H);
+    slope2 = slope * kLog2e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = slope * inv_scale * (float)acc_row(r, hi);
+  }
+  if constexpr (MOD == MOD_CHECKERBOARD && !MASK) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = (((qi + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
   f32x16 dq[DT];
@@ -402,7 +441,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   Stage1<D> stv;
   uint32_t mreg = 0;
   int mkv = 0;
-  auto load_tile = [&](int kv0) {
+  auto load_tile = [&](int n) {
+    const int kv0 = min(n, ntiles - 1) * BN;   // clamped: no branch next to the loads
     stk.load(Kg, kv0, Skv, tid);
     stv.load(Vg, kv0, Skv, tid);
     if constexpr (MASK) {
@@ -410,68 +450,102 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
+  auto store_tile = [&](int buf) {
+    stk.store(sK(buf), sKt(buf), tid);
+    stv.store(sV(buf), tid);
+    if constexpr (MASK) {
+      if (tid < BN) {
+        const bool keep = mkv < Skv && mreg != 0;
+        float e0 = 0.f, e1 = 0.f;
+        if constexpr (MOD == MOD_CHECKERBOARD) {
+          const bool kev = (mkv & 1) == 0;
+          e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
+          e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
+        }
+        sB(buf)[tid] = keep ? e0 : kNegInf;
+        sB(buf)[BN + tid] = keep ? e1 : kNegInf;
+      }
+    }
+  };
 
   load_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BN;
-    if (j > 0) __syncthreads();
-    stk.store(sK, sKt, tid);
-    stv.store(sV, tid);
-    if constexpr (MASK) {
-      if (tid < BN) sM[tid] = (mkv < Skv && mreg != 0) ? 1 : 0;
-    }
-    __syncthreads();
-    load_tile(min(j + 1, ntiles - 1) * BN);   // unconditional (clamped): no branch next to the loads
+  store_tile(0);
+  __syncthreads();
+  load_tile(1);
+  for (int n = 0; n < ntiles; ++n) {
+    const int kv0 = n * BN;
+    __syncthreads();   // everyone is past tile n-1, whose buffer ((n+1)&1) is free
+    store_tile((n + 1) & 1);
+    load_tile(n + 2);
     if (CAUSAL && kv0 > qw + 31) continue;
+    const uint16_t* kb = sK(n & 1);
+    const uint16_t* vb = sV(n & 1);
 
-    // S^T = K Q^T and dP^T = V dO^T, keys as rows.
+    // S'^T = K Q^T + C and dP^T = V dO^T, keys as rows
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      s[t] = zero16();
-      dp[t] = zero16();
+      f32x16 acc = cinit;
+      if constexpr (MASK) {
+        const float* row = sB(n & 1) + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 m4 = *(const f32x4*)(row + 8 * u);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) acc[4 * u + cc] += m4[cc];
+        }
+      }
+      f32x16 pacc = zero16();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int off = (32 * t + l32) * KP + 16 * kk + 8 * hi;
-        s[t] = mma16<T>(lds_read16(&sK[off]), qf[kk], s[t]);
-        dp[t] = mma16<T>(lds_read16(&sV[off]), of[kk], dp[t]);
+        acc = mma16<T>(lds_read16(&kb[off]), qf[kk], acc);
+        pacc = mma16<T>(lds_read16(&vb[off]), of[kk], pacc);
       }
+      s[t] = acc;
+      dp[t] = pacc;
     }
 
-    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
-    const bool tail = kv0 + BN > Skv;
+    // scores past the diagonal or past seq_kv: -inf (only on such tiles)
+    {
+      int lim = 1 << 30;
+      if (CAUSAL && kv0 + BN - 1 > qw) lim = qi - kv0;
+      if (!MASK && kv0 + BN > Skv) lim = min(lim, Skv - 1 - kv0);
+      if (__builtin_amdgcn_ballot_w64(lim < BN - 1) != 0) {
+        const int lim_l = lim - 4 * hi;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t mw = 0xffffffffu;
-        if constexpr (MASK) mw = *(const uint32_t*)&sM[32 * t + 8 * u + 4 * hi];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * u + c;
-          const int kv = kv0 + 32 * t + acc_row(r, hi);
-          float x = s[t][r] * a.scale_log2;
-          if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
-          if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
-          float p = exp2_hw(x - lse2);
-          if constexpr (MASK) {
-            if (((mw >> (8 * c)) & 0xffu) == 0u) p = 0.f;
-          } else {
-            if (tail && kv >= Skv) p = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int pos = 32 * t + 8 * (r >> 2) + (r & 3);
+            if (pos > lim_l) s[t][r] = kNegInf;
           }
-          if (diag && kv > qi) p = 0.f;
-          dp[t][r] = p * (dp[t][r] - delta);
         }
       }
     }
 
-    // dQ^T += K^T dS^T over the tile's 64 keys.
+    float nb0 = -lse2, nb1 = -lse2;
+    if constexpr (MOD == MOD_ALIBI) {
+      const float add0 = slope2 * (float)(kv0 - qi);
+      nb0 = add0 - lse2;
+      nb1 = add0 + slope2 * 32.0f - lse2;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = exp2_hw(fmaf(s[0][r], c, nb0));
+      const float p1 = exp2_hw(fmaf(s[1][r], c, nb1));
+      dp[0][r] = p0 * (dp[0][r] - delta);
+      dp[1][r] = p1 * (dp[1][r] - delta);
+    }
+
+    // dQ^T += K^T dS^T over the tile's 64 keys
+    const uint16_t* ktb = sKt(n & 1);
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {
       const int t = st >> 1, u = st & 1;
       const u32x4 db = pack8<T>(dp[t], u);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_tr(sKt, 32 * dt + l32, st, hi), db, dq[dt]);
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_tr(ktb, 32 * dt + l32, st, hi), db, dq[dt]);
     }
   }
 
