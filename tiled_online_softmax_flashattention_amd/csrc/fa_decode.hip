@@ -101,15 +101,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < EPL; ++c) st.acc[c] = 0.f;
 
-  for (int base = c0 + wave * KPW + grp; base < c1; base += U * KPB) {
-    u32x4 kx[U], vx[U];
+  // Software prefetch: the next batch of U keys per group is requested before
+  // the current one is used (rows past the chunk are clamped to its last key
+  // and masked), so two batches are in flight per lane.
+  u32x4 kx[U], vx[U], kn[U], vn[U];
+  auto load_batch = [&](int base, u32x4* kk, u32x4* vv) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // keys past the chunk: the chunk's last key (finite; its score is -inf below)
       const int kv = min(base + u * KPB, c1 - 1);
-      kx[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
-      vx[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
+      kk[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
+      vv[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
     }
+  };
+  const int base0 = c0 + wave * KPW + grp;
+  load_batch(base0, kx, vx);
+  for (int base = base0; base < c1; base += U * KPB) {
+    load_batch(base + U * KPB, kn, vn);
     float t[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -124,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
       if constexpr (MOD == MOD_ALIBI) d += slope2 * (float)kv;  // -slope * (0 - kv)
       if constexpr (MOD == MOD_CHECKERBOARD) d += (kv & 1) ? a.odd_log2 : a.even_log2;
       bool ok = kv < c1;
-      if constexpr (MASK) ok = ok && mrow[ok ? kv : 0] != 0;
+      if constexpr (MASK) ok = ok && mrow[min(kv, c1 - 1)] != 0;
       t[u] = ok ? d : kNegInf;
     }
     float mx = st.m;
@@ -145,6 +152,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
       for (int c = 0; c < EPL; ++c) st.acc[c] += p * vf[c];
     }
     st.m = mx;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kx[u] = kn[u];
+      vx[u] = vn[u];
+    }
   }
 
   // merge the groups of the wave (lanes with equal sub)
@@ -182,24 +194,51 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
   }
 }
 
+constexpr int kMaxSplit = 256;
+
+// One workgroup per (b, h).  The chunks' (max, sum) are read in parallel into
+// LDS, the weights 2^(m_s - M) computed once, and every thread then issues
+// its accumulator loads for all chunks back to back (no serial chain of
+// dependent loads).
 template <class T, int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(const AttnArgs a) {
+  __shared__ float sw[kMaxSplit];
+  __shared__ float sl[kMaxSplit];
+  __shared__ float sM;
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* part = a.partial + (size_t)bh * a.n_split * (D + 2);
-  float M = kNegInf;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, part[(size_t)s * (D + 2) + D]);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const float* ps = part + (size_t)s * (D + 2);
-    const float w = exp2_hw(ps[D] - Mu);
-    L += w * ps[D + 1];
-    if (d < D) acc += w * ps[d];
+  const int tid = threadIdx.x;
+  const int ns = a.n_split;
+  const float* part = a.partial + (size_t)bh * ns * (D + 2);
+  for (int sp = tid; sp < ns; sp += 256) {
+    sw[sp] = part[(size_t)sp * (D + 2) + D];
+    sl[sp] = part[(size_t)sp * (D + 2) + D + 1];
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  __syncthreads();
+  if (tid < 64) {
+    float m = kNegInf;
+    for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, sw[sp]);
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) m = fmaxf(m, __shfl_xor(m, w));
+    if (tid == 0) sM = m;
+  }
+  __syncthreads();
+  const float M = sM;
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  for (int sp = tid; sp < ns; sp += 256) sw[sp] = exp2_hw(sw[sp] - Mu);
+  __syncthreads();
+  float L = 0.f;
+  for (int sp = 0; sp < ns; ++sp) L += sw[sp] * sl[sp];
+  const int d = tid;
   if (d < D) {
-    const float o = acc * inv;
+    float acc = 0.f;
+    int sp = 0;
+    for (; sp + 4 <= ns; sp += 4) {
+      const float x0 = part[(size_t)(sp + 0) * (D + 2) + d], x1 = part[(size_t)(sp + 1) * (D + 2) + d];
+      const float x2 = part[(size_t)(sp + 2) * (D + 2) + d], x3 = part[(size_t)(sp + 3) * (D + 2) + d];
+      acc += sw[sp] * x0 + sw[sp + 1] * x1 + sw[sp + 2] * x2 + sw[sp + 3] * x3;
+    }
+    for (; sp < ns; ++sp) acc += sw[sp] * part[(size_t)sp * (D + 2) + d];
+    const float o = L > 0.f ? acc / L : 0.f;
     if constexpr (__is_same(T, F32)) {
       ((float*)a.o)[(size_t)bh * D + d] = o;
     } else if constexpr (__is_same(T, F16)) {
@@ -208,17 +247,19 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const AttnArgs a) {
       ((__bf16*)a.o)[(size_t)bh * D + d] = (__bf16)o;
     }
   }
-  if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+  if (tid == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 int decode_choose_split(int BH, int Skv, int* chunk) {
-  // Aim for about 1024 workgroups in total, with chunks of 256 .. 4096 keys
-  // (a multiple of 64 keys).
-  long long c = ((long long)Skv * BH + 1023) / 1024;
+  // Aim for about 512 workgroups in total (two per CU; longer streams per
+  // workgroup measured faster than more, shorter chunks), with chunks of
+  // 256 .. 4096 keys (a multiple of 64 keys).
+  long long c = ((long long)Skv * BH + 511) / 512;
   c = (c + 63) / 64 * 64;
   if (c < 256) c = 256;
   if (c > 4096) c = 4096;
   if (c > Skv) c = (Skv + 63) / 64 * 64;
+  if ((Skv + c - 1) / c > kMaxSplit) c = (Skv + kMaxSplit - 1) / kMaxSplit;  // the merge holds at most kMaxSplit chunks
   *chunk = (int)c;
   return (int)((Skv + c - 1) / c);
 }
@@ -229,7 +270,7 @@ static hipError_t launch_decode_inst(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0, st, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(128), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
