@@ -11,14 +11,16 @@
 // Two deterministic passes, no atomics:
 //  * dkdv16_kernel: key-stationary.  Each wave keeps 32 keys' K and V rows in
 //    registers and their dK^T, dV^T accumulators, and loops over 64-query
-//    tiles whose Q and dO are staged through LDS in both the natural and the
-//    transposed layout.  S and dP are formed with queries as rows, so the
-//    lane holds one key and the probabilities feed dV^T = dO^T P and
-//    dK^T = Q^T dS directly as MFMA B operands.
+//    tiles whose Q and dO are staged through LDS.  S and dP are formed with
+//    queries as rows, so the lane holds one key and the probabilities feed
+//    dV^T = dO^T P and dK^T = Q^T dS directly as MFMA B operands; the dO^T
+//    and Q^T fragments come from the natural tiles through the transposing
+//    LDS read.
 //  * dq16_kernel: query-stationary, like the forward.  Each wave keeps 32
-//    queries' Q and dO rows in registers; K tiles are staged natural and
-//    transposed, V natural; S^T and dP^T are formed with keys as rows so the
-//    lane holds one query, and dQ^T = K^T dS^T accumulates in registers.
+//    queries' Q and dO rows in registers; K and V tiles are staged natural;
+//    S^T and dP^T are formed with keys as rows so the lane holds one query,
+//    and dQ^T = K^T dS^T accumulates in registers (K^T fragments through the
+//    transposing LDS read).
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -92,44 +94,12 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st) {
 
 // ------------------------------------------------------------ shared helpers
 
-// Stage a 64-row tile of a (rows, D) 16-bit tensor into LDS twice: natural
-// rows with pitch D + 8, and transposed (D rows of 64 positions) with the
-// swap23 column order and 16-byte chunks XOR-swizzled by row.  Each thread
-// owns 4 consecutive rows x 8 dims.
-template <int D>
-struct Stage2 {
-  static constexpr int NG = 16 * (D / 8);   // (4-row group, 8-dim chunk) pairs
-  u32x4 r[4];
-  bool active;
-  // Rows past nrows are clamped to the last row (finite values that the
-  // kernels mask out), so the loads carry no branch.
-  __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
-    active = tid < NG;
-    const int rg = (tid % NG) / (D / 8), ch = tid % (D / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = *(const u32x4*)(g + (size_t)min(row0 + 4 * rg + i, nrows - 1) * D + 8 * ch);
-  }
-  __device__ __forceinline__ void store(uint16_t* nat, uint16_t* tr, int tid) const {
-    if (!active) return;
-    const int rg = tid / (D / 8), ch = tid % (D / 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_write16(&nat[(4 * rg + i) * (D + 8) + 8 * ch], r[i]);
-    const int col = swap23(4 * rg);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d = 8 * ch + c, word = c >> 1, sh = (c & 1) * 16;
-      const uint32_t e0 = (r[0][word] >> sh) & 0xffffu, e1 = (r[1][word] >> sh) & 0xffffu;
-      const uint32_t e2 = (r[2][word] >> sh) & 0xffffu, e3 = (r[3][word] >> sh) & 0xffffu;
-      const int phys = (((col >> 3) ^ tr_swz(d)) << 3) + (col & 7);
-      lds_write8(&tr[d * 64 + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
-    }
-  }
-};
-
-// Natural-layout staging of a 64-row tile (pitch D + 8).
-template <int D>
+// Natural-layout staging of a ROWS-row tile of a (rows, D) 16-bit tensor
+// (pitch D + 8).  Rows past nrows are clamped to the last row (finite values
+// that the kernels mask out), so the loads carry no branch.
+template <int D, int ROWS>
 struct Stage1 {
-  static constexpr int N = 64 * D / 8 / 256;   // 16-byte chunks per thread
+  static constexpr int N = ROWS * D / 8 / 256;   // 16-byte chunks per thread
   u32x4 r[N];
   __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
 #pragma unroll
@@ -147,11 +117,6 @@ struct Stage1 {
   }
 };
 
-// Read the A fragment of a transposed tile: lane (row d, group hi), 16-wide step st.
-__device__ __forceinline__ u32x4 read_tr(const uint16_t* tr, int d, int st, int hi) {
-  return lds_read16(&tr[d * 64 + (((2 * st + hi) ^ tr_swz(d)) << 3)]);
-}
-
 template <class T>
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
   return u32x4{pack2<T>(x[8 * u + 0], x[8 * u + 1]), pack2<T>(x[8 * u + 2], x[8 * u + 3]),
@@ -165,8 +130,8 @@ struct DkdvCfg {
   static constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 64;     // queries per tile
   static constexpr int QP = D + 8;
-  // one buffer: Q and dO, each natural and transposed (16-bit), then lse2 and delta rows
-  static constexpr size_t buf_elems = (size_t)2 * (BQ * QP + D * BQ) + 2 * BQ * 2;
+  // one buffer: Q and dO (natural, 16-bit), then the lse2 and delta rows
+  static constexpr size_t buf_elems = (size_t)2 * BQ * QP + 2 * BQ * 2;
   static constexpr size_t lds = 2 * buf_elems * 2;
 };
 
@@ -182,10 +147,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   constexpr int KS = D / 16, DT = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
   auto sQ = [&](int buf) { return smem16 + buf * C::buf_elems; };
-  auto sQt = [&](int buf) { return sQ(buf) + BQ * QP; };
-  auto sO = [&](int buf) { return sQt(buf) + D * BQ; };
-  auto sOt = [&](int buf) { return sO(buf) + BQ * QP; };
-  auto sL = [&](int buf) { return (float*)(sOt(buf) + D * BQ); };
+  auto sO = [&](int buf) { return sQ(buf) + BQ * QP; };
+  auto sL = [&](int buf) { return (float*)(sO(buf) + BQ * QP); };
   auto sDl = [&](int buf) { return sL(buf) + BQ; };
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -246,7 +209,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
 
   const int qt0 = CAUSAL ? k0 / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
-  Stage2<D> stq, sto;
+  Stage1<D, BQ> stq, sto;
   float lreg = 0.f, dreg = 0.f;
   int lq = 0;
   auto load_tile = [&](int it) {
@@ -258,8 +221,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     dreg = deltag[min(lq, Sq - 1)];
   };
   auto store_tile = [&](int buf) {
-    stq.store(sQ(buf), sQt(buf), tid);
-    sto.store(sO(buf), sOt(buf), tid);
+    stq.store(sQ(buf), tid);
+    sto.store(sO(buf), tid);
     if (tid < BQ) {   // rows past seq_q: P = 0 (lse2 = +inf) and delta = 0
       sL(buf)[tid] = lq < Sq ? lreg : __builtin_inff();
       sDl(buf)[tid] = lq < Sq ? dreg : 0.f;
@@ -282,8 +245,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     const uint16_t* qb = sQ(buf);
     const uint16_t* ob = sO(buf);
 
-    const uint16_t* otb = sOt(buf);
-    const uint16_t* qtb = sQt(buf);
     // one 32-query half at a time keeps S and dP to 32 registers
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -328,9 +289,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
         const u32x4 db = pack8<T>(dpv, u);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int d = 32 * dt + l32;
-          dv[dt] = mma16<T>(read_tr(otb, d, st, hi), pb, dv[dt]);
-          dk[dt] = mma16<T>(read_tr(qtb, d, st, hi), db, dk[dt]);
+          dv[dt] = mma16<T>(read_a_tr(ob, QP, 16 * st, 32 * dt, lane), pb, dv[dt]);
+          dk[dt] = mma16<T>(read_a_tr(qb, QP, 16 * st, 32 * dt, lane), db, dk[dt]);
         }
       }
     }
@@ -361,8 +321,8 @@ struct Dq16Cfg {
   static constexpr int BM = 128;   // queries per workgroup
   static constexpr int BN = 64;    // keys per tile
   static constexpr int KP = D + 8;
-  // one buffer: K natural, K transposed, V natural (16-bit) and the key row
-  static constexpr size_t buf_elems = (size_t)2 * BN * KP + D * BN + 2 * BN * 2;
+  // one buffer: K and V natural (16-bit) and the key row
+  static constexpr size_t buf_elems = (size_t)2 * BN * KP + 2 * BN * 2;
   static constexpr size_t lds = 2 * buf_elems * 2;
 };
 
@@ -377,8 +337,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   constexpr int KS = D / 16, DT = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
   auto sK = [&](int buf) { return smem16 + buf * C::buf_elems; };
-  auto sKt = [&](int buf) { return sK(buf) + BN * KP; };
-  auto sV = [&](int buf) { return sKt(buf) + D * BN; };
+  auto sV = [&](int buf) { return sK(buf) + BN * KP; };
   auto sB = [&](int buf) { return (float*)(sV(buf) + BN * KP); };   // 2 x BN floats: q parity 0 / 1
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -437,8 +396,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
   const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
-  Stage2<D> stk;
-  Stage1<D> stv;
+  Stage1<D, BN> stk, stv;
   uint32_t mreg = 0;
   int mkv = 0;
   auto load_tile = [&](int n) {
@@ -451,7 +409,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     }
   };
   auto store_tile = [&](int buf) {
-    stk.store(sK(buf), sKt(buf), tid);
+    stk.store(sK(buf), tid);
     stv.store(sV(buf), tid);
     if constexpr (MASK) {
       if (tid < BN) {
@@ -539,13 +497,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     }
 
     // dQ^T += K^T dS^T over the tile's 64 keys
-    const uint16_t* ktb = sKt(n & 1);
 #pragma unroll
     for (int st = 0; st < BN / 16; ++st) {
       const int t = st >> 1, u = st & 1;
       const u32x4 db = pack8<T>(dp[t], u);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_tr(ktb, 32 * dt + l32, st, hi), db, dq[dt]);
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_a_tr(kb, KP, 16 * st, 32 * dt, lane), db, dq[dt]);
     }
   }
 

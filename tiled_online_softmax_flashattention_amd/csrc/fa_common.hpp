@@ -107,6 +107,31 @@ __device__ __forceinline__ float alibi_slope(const float* slopes, int h, int H) 
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const void* p) { return *(const u32x4*)p; }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i receives,
+// as element j, element (i & 3) of the four 16-bit values that lane
+// 4j + (i >> 2) of the group addressed (measured on gfx950).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_ptr;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// A operand (M = 32 rows of dim d, K = 16 positions) of a product whose
+// 16-bit tile is stored natural, position-major: tile[pos * pitch + d].
+// Lane L gets dim d0 + (L & 31) and, in slots 0..3 / 4..7, positions
+// p0 + 4 hi + 0..3 / p0 + 8 + 4 hi + 0..3 (hi = L >> 5): the positions an
+// accumulator-layout B operand holds in its registers 8u .. 8u+7.  Each
+// group of 16 lanes addresses 4 positions x 16 dims (8 bytes per lane).
+__device__ __forceinline__ u32x4 read_a_tr(const uint16_t* tile, int pitch, int p0, int d0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int row = p0 + 4 * (g >> 1) + (s >> 2);
+  const int col = d0 + 16 * (g & 1) + 4 * (s & 3);
+  const u32x2 lo = lds_read_tr(tile + row * pitch + col);
+  const u32x2 hi = lds_read_tr(tile + (row + 8) * pitch + col);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
 __device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
 

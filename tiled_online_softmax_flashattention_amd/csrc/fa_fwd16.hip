@@ -8,9 +8,10 @@
 // a native v_exp_f32).
 //
 // Work decomposition: one workgroup of 4 waves per 128-query block; each wave
-// owns 32 queries.  Key/value tiles of 64 keys are staged through LDS: K in
-// its natural (key, dim) layout, V transposed to (dim, key) so both products
-// read operand fragments with single 16-byte LDS reads.  K and V are double
+// owns 32 queries.  Key/value tiles of 64 keys are staged through LDS in their
+// natural (key, dim) layout; the P V product reads its V fragments with the
+// transposing LDS read (ds_read_b64_tr_b16), so no transpose is done in
+// registers.  K and V are double
 // buffered: while tile n is used, tile n+1 is written to the other buffers
 // and tile n+2 is in flight from HBM into registers, so one barrier per tile
 // suffices.  At head_dim 64 the kernel fits 3 waves per SIMD; issuing the
@@ -43,14 +44,13 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
   constexpr int KP = D + 8;        // K tile pitch in elements (16-byte pad)
-  constexpr int NK = D / 32;       // 16-byte K chunks per thread per tile
-  constexpr int NV = D / 64;       // 4x4 V blocks per thread per tile
+  constexpr int NK = D / 32;       // 16-byte K (and V) chunks per thread per tile
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
 
   // Double buffers: tile n+1 is written while tile n is read.
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * BN];       // V^T, chunks swizzled by tr_swz(row)
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * KP];      // V natural, read transposed
   __shared__ __attribute__((aligned(16))) float sB[2][MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -108,8 +108,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
   // Staging loads are unconditional: rows past seq_kv are clamped to the last
   // row (finite values whose scores are masked to -inf), so no branch (and no
   // wait for outstanding loads at a branch merge) sits next to a load.
-  u32x4 kreg[NK];
-  u32x2 vreg[NV][4];
+  u32x4 kreg[NK], vreg[NK];
   uint32_t mreg = 0;
   int mkv = 0;
 
@@ -126,11 +125,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
   };
   auto load_v = [&](int kv0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + 256 * i, db = e % (D / 4), kvb = e / (D / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[i][r] = *(const u32x2*)(Vg + (size_t)min(kv0 + 4 * kvb + r, Skv - 1) * D + 4 * db);
+    for (int i = 0; i < NK; ++i) {
+      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
+      vreg[i] = *(const u32x4*)(Vg + (size_t)min(kv0 + row, Skv - 1) * D + 8 * ch);
     }
   };
   auto store_k = [&](int buf) {
@@ -155,17 +152,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
   };
   auto store_v = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + 256 * i, db = e % (D / 4), kvb = e / (D / 4);
-      const int col = swap23(4 * kvb);  // logical column of keys 4kvb .. 4kvb+3
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const int d = 4 * db + c4, word = c4 >> 1, sh = (c4 & 1) * 16;
-        const uint32_t e0 = (vreg[i][0][word] >> sh) & 0xffffu, e1 = (vreg[i][1][word] >> sh) & 0xffffu;
-        const uint32_t e2 = (vreg[i][2][word] >> sh) & 0xffffu, e3 = (vreg[i][3][word] >> sh) & 0xffffu;
-        const int phys = (((col >> 3) ^ tr_swz(d)) << 3) + (col & 7);
-        lds_write8(&sV[buf][d * BN + phys], u32x2{e0 | (e1 << 16), e2 | (e3 << 16)});
-      }
+    for (int i = 0; i < NK; ++i) {
+      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
+      lds_write16(&sV[buf][row * KP + 8 * ch], vreg[i]);
     }
   };
   // S'^T = K Q^T + C for the tile held in K buffer `buf`
@@ -280,11 +269,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
       const u32x4 pb = {pack2<T>(s[t][8 * u + 0], s[t][8 * u + 1]), pack2<T>(s[t][8 * u + 2], s[t][8 * u + 3]),
                         pack2<T>(s[t][8 * u + 4], s[t][8 * u + 5]), pack2<T>(s[t][8 * u + 6], s[t][8 * u + 7])};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + l32;
-        const int phys = ((2 * st + hi) ^ tr_swz(d)) << 3;
-        o[dt] = mma16<T>(lds_read16(&vb[d * BN + phys]), pb, o[dt]);
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(read_a_tr(vb, KP, 16 * st, 32 * dt, lane), pb, o[dt]);
     }
   };
 
