@@ -110,7 +110,15 @@ def test_backward_single_pass_matches_full(gpu_lib, dtype, D):
     n3, dk1, dv1 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], which="dkdv", **kw)
     torch.cuda.synchronize()
     assert n1 is None and n2 is None and n3 is None
-    assert torch.equal(dq, dq1) and torch.equal(dk, dk1) and torch.equal(dv, dv1)
+    assert torch.equal(dq, dq1)
+    if dtype == "f32":
+        assert torch.equal(dk, dk1) and torch.equal(dv, dv1)
+    else:
+        # 16-bit: the full call takes delta = <dO, O> from the query pass, the
+        # key/value-only call from the preprocess kernel (another fp32
+        # summation order), so dK and dV may differ in the last bit
+        for x, y in ((dk, dk1), (dv, dv1)):
+            assert (x.float() - y.float()).abs().max().item() <= 1e-2 * x.float().abs().max().item()
 
 
 def test_uniform_scores_full_shape_invariants(gpu_lib):

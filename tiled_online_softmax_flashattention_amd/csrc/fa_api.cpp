@@ -166,13 +166,15 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   a.lse2 = (float*)((char*)workspace + lay.lse2_off);
   a.n_qblocks = (int)nqb;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t err = fa::launch_bwd_pre(a, p->dtype, D, st);
-  if (err != hipSuccess) return FA_ERR_HIP;
-  if (f32)
+  hipError_t err;
+  if (f32) {   // fp32: preprocess kernel, then the passes
+    err = fa::launch_bwd_pre(a, p->dtype, D, st);
+    if (err != hipSuccess) return FA_ERR_HIP;
     err = fa::launch_bwd32(a, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, want_kv, want_q, st);
-  else
+  } else {     // 16-bit: the query pass computes the preprocess itself
     err = fa::launch_bwd16(a, p->dtype == FA_BF16, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr,
                            want_kv, want_q, st);
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

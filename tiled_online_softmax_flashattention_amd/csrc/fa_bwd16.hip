@@ -359,22 +359,37 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)bh * Skv * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)bh * Skv * D;
 
+  // This lane's query: Q and dO rows as B operands, and the row's delta =
+  // <dO, O> and lse * log2(e), which this pass also writes to the workspace
+  // for the key/value pass that runs after it.
+  const uint16_t* Og = (const uint16_t*)a.o + (size_t)bh * Sq * D;
   u32x4 qf[KS], of[KS];
   float lse2, delta;
   {
     const bool ok = qi < Sq;
     const size_t off = (size_t)min(qi, Sq - 1) * D + 8 * hi;
+    float dsum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const u32x4 x = *(const u32x4*)(Qg + off + 16 * kk);
       const u32x4 y = *(const u32x4*)(dOg + off + 16 * kk);
+      const u32x4 z = *(const u32x4*)(Og + off + 16 * kk);
       qf[kk] = ok ? x : u32x4{0u, 0u, 0u, 0u};
       of[kk] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        dsum += to_f32<T>((uint16_t)(y[cc] & 0xffffu)) * to_f32<T>((uint16_t)(z[cc] & 0xffffu));
+        dsum += to_f32<T>((uint16_t)(y[cc] >> 16)) * to_f32<T>((uint16_t)(z[cc] >> 16));
+      }
     }
-    const float l2 = a.lse2[(size_t)bh * Sq + min(qi, Sq - 1)];
-    const float dl = a.delta[(size_t)bh * Sq + min(qi, Sq - 1)];
-    lse2 = ok ? l2 : __builtin_inff();   // rows past seq_q: P = 0
-    delta = ok ? dl : 0.f;
+    dsum += xor32(dsum);   // the partner lane holds the other half of the dims
+    const float lse = a.lse[(size_t)bh * Sq + min(qi, Sq - 1)];
+    lse2 = (ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();   // empty rows and rows past seq_q: P = 0
+    delta = ok ? dsum : 0.f;
+    if (ok && hi == 0) {
+      a.delta[(size_t)bh * Sq + qi] = delta;
+      a.lse2[(size_t)bh * Sq + qi] = lse2;
+    }
   }
 
   float slope2 = 0.f;
@@ -532,16 +547,20 @@ static hipError_t launch_dyn(K kern, unsigned grid, size_t lds, hipStream_t st, 
   return hipGetLastError();
 }
 
+// The query pass runs first and writes delta and lse2 for the key/value
+// pass; without it, the preprocess kernel provides them.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
-  if (want_kv) {
-    hipError_t err = launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
-    if (err != hipSuccess) return err;
+  hipError_t err;
+  if (want_q) {
+    err = launch_dyn(dq16_kernel<T, D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, Dq16Cfg<D>::lds, st, a);
+  } else {
+    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st);
   }
-  if (!want_q) return hipSuccess;
-  return launch_dyn(dq16_kernel<T, D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, Dq16Cfg<D>::lds, st, a);
+  if (err != hipSuccess || !want_kv) return err;
+  return launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
 }
 
 template <class T, int D, int MOD>
