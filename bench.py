@@ -46,6 +46,49 @@ def time_calls(fn, reps: int, torch) -> float:
     return start.elapsed_time(end) / reps
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel's source has changed since then."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_prefill_f16_causal_alibi.json")
+    try:
+        rec = json.load(open(path))["kernels"][kernel]
+        sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["hbm_bytes"] if sha == rec["source_sha256"] else None
+
+
+def extra_workloads(fa, W, torch, reps: int) -> dict:
+    """Forward and forward+backward times of the key-padding (bf16) and the
+    long-context (fp32, head_dim 512) workloads."""
+    res = {}
+    for w, kw, peak in ((W.KEYPAD_BF16, dict(score_mod="checkerboard"), PEAK_F16_TFLOPS),
+                        (W.LONG_F32, dict(causal=True), PEAK_F32_TFLOPS)):
+        log(f"[bench] extra: {w.name}")
+        x = w.make()
+        dev = {k2: (None if t is None else t.cuda()) for k2, t in x.items()}
+        kw = dict(kw, key_mask=dev["key_mask"], scale=w.scale)
+        q, k, v, do = dev["q"], dev["k"], dev["v"], dev["dout"]
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device=q.device)
+        run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
+        run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
+        run_fwd(); run_bwd()
+        n = reps if w.head_dim < 512 else 2
+        ms_f = time_calls(lambda i: run_fwd(), n, torch)
+        ms_fb = time_calls(lambda i: (run_fwd(), run_bwd()), n, torch)
+        res[w.name] = {"forward_ms": round(ms_f, 3), "fwd_bwd_ms": round(ms_fb, 3),
+                       "forward_TFLOP/s": round(w.fwd_flops() / ms_f / 1e9, 1),
+                       "fwd_bwd_TFLOP/s": round((w.fwd_flops() + w.bwd_flops()) / ms_fb / 1e9, 1),
+                       "peak_TFLOP/s": peak, "flop_convention": "causal pairs" if w.causal else "all pairs"}
+        del dev, q, k, v, do, out, grads, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, heads: int) -> dict:
     """The fp64 oracle (as it is) on a bounded sample: the first `heads`
     (batch, head) slices of the workload, forward + backward."""
@@ -84,6 +127,7 @@ def main() -> int:
     ap.add_argument("--reps", type=int, default=20, help="calls per per-kernel timing loop")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) slices in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true", help="also time the key-padding and long-context workloads")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -112,7 +156,6 @@ def main() -> int:
 
     run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
     run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
-    run_kv = fa.plan_backward(q, k, v, out, lse, do, None, grads[1], grads[2], ws, **kw)
     run_q = fa.plan_backward(q, k, v, out, lse, do, grads[0], None, None, ws, **kw)
 
     def step(_i=0):
@@ -139,12 +182,15 @@ def main() -> int:
 
     log("[bench] per-pass timing")
     ms_fwd = time_calls(lambda i: run_fwd(), args.reps, torch)
-    ms_kv = time_calls(lambda i: run_kv(), args.reps, torch)
     ms_q = time_calls(lambda i: run_q(), args.reps, torch)
+    ms_bwd = time_calls(lambda i: run_bwd(), args.reps, torch)
+    # A full 16-bit backward launches the query kernel (which also writes the
+    # row statistics) and then the key/value kernel on one stream, so the
+    # key/value kernel's time is the difference of the two timings.
+    ms_kv = ms_bwd - ms_q
     pairs = w.pairs()
     D = w.head_dim
-    # algorithmic flop per launch of each kernel (the key/value and query
-    # timings include the small delta/lse preprocess kernel)
+    # algorithmic flop per launch of each kernel
     kernels = {
         "fwd16_kernel": (4.0 * D * pairs, ms_fwd),
         "dkdv16_kernel": (8.0 * D * pairs, ms_kv),
@@ -154,7 +200,7 @@ def main() -> int:
     dom_flops, dom_ms = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": measured_traffic(dom),
                 "avg_ms": round(dom_ms, 4)}
 
     log("[bench] decode")
@@ -202,10 +248,12 @@ def main() -> int:
         "forward": {"TFLOP/s": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12, 2),
                     "frac_mfma_peak": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
                     "ms": round(ms_fwd, 4)},
-        "backward_passes_ms": {"dkdv_with_preprocess": round(ms_kv, 4), "dq_with_preprocess": round(ms_q, 4)},
+        "backward_ms": {"all": round(ms_bwd, 4), "dq16_kernel": round(ms_q, 4), "dkdv16_kernel": round(ms_kv, 4)},
         "decode": decode,
         "roofline": roofline,
     }
+    if args.extra:
+        result["extra"] = extra_workloads(fa, W, torch, args.reps)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_heads} slices")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
