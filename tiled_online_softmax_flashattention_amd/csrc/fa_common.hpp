@@ -74,7 +74,11 @@ __device__ __forceinline__ float to_f32(uint16_t bits) {
 // Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// Value held by lane (l ^ 32): one ds_bpermute with a loop-invariant address.
+__device__ __forceinline__ float xor32(float x) {
+  const int addr = (int)(((threadIdx.x & 63u) ^ 32u) << 2);
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(addr, __builtin_bit_cast(int, x)));
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;

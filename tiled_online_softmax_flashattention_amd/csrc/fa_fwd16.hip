@@ -8,30 +8,38 @@
 // a native v_exp_f32).
 //
 // Work decomposition: one workgroup of 4 waves per 128-query block; each wave
-// owns 32 queries.  Key/value tiles of 64 keys are staged through LDS in their
-// natural (key, dim) layout; the P V product reads its V fragments with the
-// transposing LDS read (ds_read_b64_tr_b16), so no transpose is done in
-// registers.  K and V are double
-// buffered: while tile n is used, tile n+1 is written to the other buffers
-// and tile n+2 is in flight from HBM into registers, so one barrier per tile
-// suffices.  At head_dim 64 the kernel fits 3 waves per SIMD; issuing the
-// next tile's scores before the current softmax was measured slower here
-// because its extra registers cost a wave of occupancy.
+// owns 32 queries.  Key/value tiles of 64 keys go from HBM straight into LDS
+// (global_load_lds_dwordx4: no staging registers, no LDS write instructions)
+// and are double buffered: while tile n is used, tile n+1 is in flight, so
+// one barrier per tile suffices.  Each tile is processed as two 32-key halves
+// in sequence, which keeps a wave's registers small enough for three waves
+// per SIMD at head_dim 64 (two at 128): the matrix cores of a SIMD are kept
+// busy by the other waves while one wave works through its softmax (a wave's
+// own vector instructions overlap its MFMAs poorly on this chip).
 //
-// Per tile and wave: S'^T = K Q^T + C (MFMA 32x32x16, Q resident in registers
-// as the B operand).  The accumulator starts from C = bias / scale, so the
-// score_mod costs no per-score instruction: for ALiBi C holds the bias of the
-// key's offset inside the tile (the tile's own offset is a per-lane scalar
-// folded into the exponent), for the checkerboard the two parity values, and
-// with a key mask C is read from an LDS row that holds 0 or -inf per key.
-// Then one FMA and one v_exp_f32 per score give P = 2^(S' c + b - m).  The
-// running max is updated lazily: only when some query's maximum grows by more
-// than 2^8 does the wave rescale its accumulator, otherwise P stays below 2^8
-// (exact in fp16/bf16 range; the final division by l cancels the scale).
+// LDS layout: tiles are unpadded (key, dim) rows, because a direct load
+// writes 64 consecutive 16-byte chunks.  The K tile permutes the 16-byte
+// chunks of row r by XOR with kswz(r), so the 32 lanes of a score MFMA, which
+// read one chunk column of 32 consecutive rows, hit distinct banks; each lane
+// of the load fetches the global chunk that belongs at its LDS slot.  The V
+// tile is read with the transposing LDS read (ds_read_b64_tr_b16) for the P V
+// product; at head_dim 128 its chunks are permuted by vswz(r) so the four
+// rows of one such read fall in distinct banks.
+//
+// Per half tile and wave: S'^T = K Q^T + C (MFMA 32x32x16, Q resident in
+// registers as the B operand).  The accumulator starts from C = bias / scale,
+// so the score_mod costs no per-score instruction: for ALiBi C holds the bias
+// of the key's offset inside the half (the half's own offset is a per-lane
+// scalar folded into the exponent), for the checkerboard the two parity
+// values, and with a key mask C is read from an LDS row that holds 0 or -inf
+// per key.  Then one FMA and one v_exp_f32 per score give P = 2^(S' c + b - m).
+// The running max is updated lazily: only when some query's maximum grows by
+// more than 2^8 does the wave rescale its accumulator, otherwise P stays below
+// 2^8 (exact in fp16/bf16 range; the final division by l cancels the scale).
 // Causal: key tiles past the block's last query are never visited, tiles are
 // visited diagonal first (so the largest ALiBi scores set the maximum early),
-// waves skip tiles entirely past their own queries, and the per-score
-// comparison happens only on diagonal and ragged-tail tiles.
+// waves skip halves entirely past their own queries, and the per-score
+// comparison happens only on diagonal and ragged-tail halves.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -39,26 +47,47 @@ namespace fa {
 
 constexpr float kLazyRescale = 8.0f;   // log2 units: P is kept below 2^8
 
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Chunk permutations of the K and V tiles (XOR on the 16-byte chunk index).
+template <int D>
+__device__ __forceinline__ constexpr int kswz(int r) {
+  return D == 64 ? ((r ^ (r >> 3)) & 7) : (r & 15);
+}
+template <int D>
+__device__ __forceinline__ constexpr int vswz(int r) {
+  // even values keep the chunk pair read by one 16-lane group adjacent
+  return D == 64 ? 0 : (0xAC60 >> (4 * (r & 3))) & 15;   // 0, 6, 12, 10
+}
+
+// Element offset of (row, col) in a tile of D-element rows whose 16-byte
+// chunks are permuted by XOR with swz.
+__device__ __forceinline__ int swz_off(int row, int col, int D, int swz) {
+  return row * D + (((col >> 3) ^ swz) << 3) + (col & 7);
+}
+
+// One 128-query block (qb) of one (batch, head) slice (bh).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnArgs a) {
+__device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb) {
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
-  constexpr int KP = D + 8;        // K tile pitch in elements (16-byte pad)
-  constexpr int NK = D / 32;       // 16-byte K (and V) chunks per thread per tile
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
+  constexpr int TILE = BN * D;     // elements per K or V tile
+  constexpr int NJ = TILE * 2 / 1024 / 4;   // 1 KiB direct loads per wave per tile (K, and V)
 
-  // Double buffers: tile n+1 is written while tile n is read.
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * KP];      // V natural, read transposed
-  __shared__ __attribute__((aligned(16))) float sB[2][MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
+  // Separate arrays per buffer: the compiler then sees that a direct load
+  // into one buffer cannot alias reads of the other, and does not wait for it.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
+  __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN : 4];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
-  if (CAUSAL) qb = a.n_qblocks - 1 - qb;  // longest query blocks are dispatched first
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM;
@@ -102,40 +131,32 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
   const int ntiles = (kv_end + BN - 1) / BN;
   // causal: the diagonal tile first, then towards key 0
   auto kv_of = [&](int n) { return (CAUSAL ? ntiles - 1 - n : n) * BN; };
-  // every key of the tile follows every query of this wave
-  auto skipped = [&](int n) { return CAUSAL && kv_of(n) > qw + 31; };
 
-  // Staging loads are unconditional: rows past seq_kv are clamped to the last
-  // row (finite values whose scores are masked to -inf), so no branch (and no
-  // wait for outstanding loads at a branch merge) sits next to a load.
-  u32x4 kreg[NK], vreg[NK];
+  // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
+  // the last row (finite values whose scores are masked to -inf).
+  auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int blk = wave * NJ + j;                 // 1 KiB block of the tile
+      const int e = blk * 512 + lane * 8;            // element offset of this lane's slot
+      const int row = e / D, pch = (e % D) >> 3;     // row and physical chunk
+      const size_t g = (size_t)min(kv0 + row, Skv - 1) * D;
+      __builtin_amdgcn_global_load_lds((const void*)(Kg + g + ((pch ^ kswz<D>(row)) << 3)),
+                                       (lds_void_ptr)(sK + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Vg + g + ((pch ^ vswz<D>(row)) << 3)),
+                                       (lds_void_ptr)(sV + blk * 512), 16, 0, 0);
+    }
+  };
+  // Key-mask row: one byte per key, converted to an additive row in LDS.
   uint32_t mreg = 0;
   int mkv = 0;
-
-  auto load_k = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
-      kreg[i] = *(const u32x4*)(Kg + (size_t)min(kv0 + row, Skv - 1) * D + 8 * ch);
-    }
+  auto load_m = [&](int kv0) {
     if constexpr (MASK) {
       mkv = kv0 + (tid & (BN - 1));
       mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
-  auto load_v = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
-      vreg[i] = *(const u32x4*)(Vg + (size_t)min(kv0 + row, Skv - 1) * D + 8 * ch);
-    }
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
-      lds_write16(&sK[buf][row * KP + 8 * ch], kreg[i]);
-    }
+  auto store_m = [&](float* sB) {
     if constexpr (MASK) {
       if (tid < BN) {
         const bool keep = mkv < Skv && mreg != 0;
@@ -145,36 +166,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
           e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
           e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
         }
-        sB[buf][tid] = keep ? e0 : kNegInf;
-        sB[buf][BN + tid] = keep ? e1 : kNegInf;
+        sB[tid] = keep ? e0 : kNegInf;
+        sB[BN + tid] = keep ? e1 : kNegInf;
       }
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int cc = tid + 256 * i, row = cc / (D / 8), ch = cc % (D / 8);
-      lds_write16(&sV[buf][row * KP + 8 * ch], vreg[i]);
-    }
-  };
-  // S'^T = K Q^T + C for the tile held in K buffer `buf`
-  auto scores = [&](int buf, f32x16* s) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 acc = cinit;
-      if constexpr (MASK) {
-        const float* row = sB[buf] + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 m4 = *(const f32x4*)(row + 8 * u);
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) acc[4 * u + cc] += m4[cc];
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < QS; ++kk)
-        acc = mma16<T>(lds_read16(&sK[buf][(32 * t + l32) * KP + 16 * kk + 8 * hi]), qf[kk], acc);
-      s[t] = acc;
     }
   };
 
@@ -183,62 +177,51 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
-  // Staging is unconditional (tile indices past the end are clamped to the
-  // last tile): the buffers written near the end are never read again, and
-  // straight-line staging keeps the load waits exact.
-  auto kv_c = [&](int n) { return kv_of(min(n, ntiles - 1)); };
+  // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
+  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) {
+    const int k0 = kv_of(n) + 32 * t;   // first key of the half
+    if (CAUSAL && k0 > qw + 31) return;   // every key follows every query of this wave
 
-  load_k(kv_c(0));
-  load_v(kv_c(0));
-  store_k(0);
-  store_v(0);
-  __syncthreads();
-  load_k(kv_c(1));
-  load_v(kv_c(1));
-  f32x16 sa[2], sb[2];
-
-  // one tile (n): stage tile n+1, then scores, softmax and P V of tile n
-  auto tile = [&](int n, f32x16* s) {
-    const int kv0 = kv_of(n);
-    __syncthreads();   // everyone is past tile n-1, whose buffers ((n+1)&1) are now free
-    store_k((n + 1) & 1);    // K of tile n+1
-    store_v((n + 1) & 1);    // V of tile n+1
-    load_k(kv_c(n + 2));
-    load_v(kv_c(n + 2));
-    if (skipped(n)) return;
-    scores(n & 1, s);
-
-    // scores past the diagonal or past seq_kv: -inf (only on such tiles)
+    // S'^T = K Q^T + C
+    f32x16 s = cinit;
+    if constexpr (MASK) {
+      const float* row = sB + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 m4 = *(const f32x4*)(row + 8 * u);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] += m4[cc];
+      }
+    }
     {
-      int lim = 1 << 30;   // last allowed key position inside the tile, for this lane
-      if (CAUSAL && kv0 + BN - 1 > qw) lim = qi - kv0;
-      if (!MASK && kv0 + BN > Skv) lim = min(lim, Skv - 1 - kv0);
-      if (__builtin_amdgcn_ballot_w64(lim < BN - 1) != 0) {
+      const int kr = 32 * t + l32;
+#pragma unroll
+      for (int kk = 0; kk < QS; ++kk)
+        s = mma16<T>(lds_read16(sK + swz_off(kr, 16 * kk + 8 * hi, D, kswz<D>(kr))), qf[kk], s);
+    }
+
+    // scores past the diagonal or past seq_kv: -inf (only on such halves)
+    {
+      int lim = 1 << 30;   // last allowed key position inside the half, for this lane
+      if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
+      if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
+      if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
         const int lim_l = lim - 4 * hi;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int pos = 32 * t + 8 * (r >> 2) + (r & 3);   // acc_row(r, hi) - 4 hi
-            if (pos > lim_l) s[t][r] = kNegInf;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int pos = 8 * (r >> 2) + (r & 3);   // acc_row(r, hi) - 4 hi
+          if (pos > lim_l) s[r] = kNegInf;
         }
       }
     }
 
-    // per-lane exponent offsets of the two 32-key halves (ALiBi: bias of the half's first key)
-    float add0 = 0.f, add1 = 0.f;
-    if constexpr (MOD == MOD_ALIBI) {
-      add0 = slope2 * (float)(kv0 - qi);
-      add1 = add0 + slope2 * 32.0f;
-    }
-    float mx0 = s[0][0], mx1 = s[1][0];
+    // per-lane exponent offset (ALiBi: bias of the half's first key)
+    float add = 0.f;
+    if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qi);
+    float mx = s[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      mx0 = fmaxf(mx0, s[0][r]);
-      mx1 = fmaxf(mx1, s[1][r]);
-    }
-    float mx = fmaxf(fmaf(mx0, c, add0), fmaf(mx1, c, add1));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaf(mx, c, add);
     mx = fmaxf(mx, xor32(mx));
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
       const float m_new = fmaxf(m_run, mx);
@@ -248,35 +231,61 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    const float nb0 = add0 - m_use, nb1 = add1 - m_use;
-    float ls = 0.f;
+    const float nb = add - ((m_run == kNegInf) ? 0.f : m_run);
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = exp2_hw(fmaf(s[0][r], c, nb0));
-      const float p1 = exp2_hw(fmaf(s[1][r], c, nb1));
-      s[0][r] = p0;
-      s[1][r] = p1;
-      ls += p0 + p1;
+      s[r] = exp2_hw(fmaf(s[r], c, nb));
+      ls[r & 3] += s[r];
     }
-    l_run += ls;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // O^T += V^T P^T
-    const uint16_t* vb = sV[n & 1];
+    // O^T += V^T P^T over the two 16-key steps of the half; the V fragments
+    // are transposed reads (see read_a_tr) under this tile's chunk permutation
+    const int sidx = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int st = 0; st < BN / 16; ++st) {
-      const int t = st >> 1, u = st & 1;
-      const u32x4 pb = {pack2<T>(s[t][8 * u + 0], s[t][8 * u + 1]), pack2<T>(s[t][8 * u + 2], s[t][8 * u + 3]),
-                        pack2<T>(s[t][8 * u + 4], s[t][8 * u + 5]), pack2<T>(s[t][8 * u + 6], s[t][8 * u + 7])};
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 pb = {pack2<T>(s[8 * u + 0], s[8 * u + 1]), pack2<T>(s[8 * u + 2], s[8 * u + 3]),
+                        pack2<T>(s[8 * u + 4], s[8 * u + 5]), pack2<T>(s[8 * u + 6], s[8 * u + 7])};
+      const int row = 32 * t + 16 * u + 4 * (g >> 1) + (sidx >> 2);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(read_a_tr(vb, KP, 16 * st, 32 * dt, lane), pb, o[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        const int col = 32 * dt + 16 * (g & 1) + 4 * (sidx & 3);
+        const u32x2 lo = lds_read_tr(sV + swz_off(row, col, D, vswz<D>(row)));
+        const u32x2 up = lds_read_tr(sV + swz_off(row + 8, col, D, vswz<D>(row + 8)));
+        o[dt] = mma16<T>(u32x4{lo[0], lo[1], up[0], up[1]}, pb, o[dt]);
+      }
     }
   };
 
-  for (int n = 0; n < ntiles; n += 2) {
-    tile(n, sa);
-    if (n + 1 < ntiles) tile(n + 1, sb);
+  // Prologue: tile 0 (and its mask row) requested.
+  load_tile(kv_of(0), sK0, sV0);
+  load_m(kv_of(0));
+  store_m(sB0);
+  load_m(kv_of(min(1, ntiles - 1)));
+
+  // Tile n in buffers (n & 1); tile n+1 is requested into the other buffers
+  // right after the barrier that retires tile n-1.
+  auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB,
+                  uint16_t* sKn, uint16_t* sVn, float* sBn) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's loads of tile n are in LDS
+    __syncthreads();                       // ... and every other wave's; tile n-1 is retired
+    if (n + 1 < ntiles) {
+      load_tile(kv_of(n + 1), sKn, sVn);
+      store_m(sBn);
+      load_m(kv_of(min(n + 2, ntiles - 1)));
+    }
+    half(n, 0, sK, sV, sB);
+    __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: their registers are shared
+    half(n, 1, sK, sV, sB);
+  };
+
+  int n = 0;
+  for (; n + 1 < ntiles; n += 2) {
+    tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
+    tile(n + 1, sK1, sV1, sB1, sK0, sV0, sB0);
   }
+  if (n < ntiles) tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
 
   const float l_tot = l_run + xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -293,6 +302,18 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void fwd16_kernel(const AttnA
     }
     if (hi == 0 && a.lse) a.lse[(size_t)bh * Sq + qi] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
   }
+}
+
+// Workgroup blockIdx.x handles slice bh = blockIdx.x mod (batch * heads), so
+// with batch * heads a multiple of 8 all blocks of one slice run on one XCD
+// (workgroups are dealt to the 8 XCDs round robin) and share its L2.  Causal
+// query blocks are dispatched longest first.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_kernel(const AttnArgs a) {
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int p = blockIdx.x / BH;
+  fwd16_block<T, D, MOD, CAUSAL, MASK>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p);
 }
 
 template <class T, int D, int MOD>
