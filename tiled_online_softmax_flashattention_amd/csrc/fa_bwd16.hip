@@ -11,16 +11,19 @@
 // Two deterministic passes, no atomics:
 //  * dkdv16_kernel: key-stationary.  Each wave keeps 32 keys' K and V rows in
 //    registers and their dK^T, dV^T accumulators, and loops over 64-query
-//    tiles whose Q and dO are staged through LDS.  S and dP are formed with
-//    queries as rows, so the lane holds one key and the probabilities feed
-//    dV^T = dO^T P and dK^T = Q^T dS directly as MFMA B operands; the dO^T
-//    and Q^T fragments come from the natural tiles through the transposing
-//    LDS read.
+//    tiles whose Q and dO go straight from HBM into LDS.  S and dP are formed
+//    with queries as rows, so the lane holds one key and the probabilities
+//    feed dV^T = dO^T P and dK^T = Q^T dS directly as MFMA B operands; the
+//    dO^T and Q^T fragments come from the tiles through the transposing LDS
+//    read.
 //  * dq16_kernel: query-stationary, like the forward.  Each wave keeps 32
-//    queries' Q and dO rows in registers; K and V tiles are staged natural;
-//    S^T and dP^T are formed with keys as rows so the lane holds one query,
-//    and dQ^T = K^T dS^T accumulates in registers (K^T fragments through the
-//    transposing LDS read).
+//    queries' Q and dO rows in registers; K and V tiles go straight into
+//    LDS; S^T and dP^T are formed with keys as rows so the lane holds one
+//    query, and dQ^T = K^T dS^T accumulates in registers (K^T fragments
+//    through the transposing LDS read).
+// The LDS tiles are unpadded rows with permuted 16-byte chunks (tswz), which
+// keeps both the row-fragment and the transposing reads free of bank
+// conflicts.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -28,10 +31,16 @@ namespace fa {
 
 // ---------------------------------------------------------------- preprocess
 
+// Query tile of the 16-bit key/value pass; its ALiBi rows are folded into lse2
+// relative to the tile start.
+constexpr int kDkdvBQ = 64;
+
 // delta_i = sum_d dO_id * O_id; lse2_i = lse_i * log2(e), +inf for an empty
-// row (so that exp2(s - lse2) = 0 there).
+// row (so that exp2(s - lse2) = 0 there).  With fold_alibi, lse2_i also
+// carries the query's share of the ALiBi bias relative to its 64-query tile,
+// slope * log2(e) * (i mod 64), as the 16-bit key/value pass expects.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtype) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtype, int fold_alibi) {
   constexpr int EPL = 16 / ES;                        // elements per 16-byte load
   constexpr int LPR = (D * ES / 16) < 64 ? (D * ES / 16) : 64;  // lanes per row
   constexpr int IT = D * ES / 16 / LPR;               // loads per lane
@@ -70,52 +79,35 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtyp
   if (row < rows && sub == 0) {
     a.delta[row] = acc;
     const float l = a.lse[row];
-    a.lse2[row] = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+    float l2 = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
+    if (fold_alibi) {
+      const int64_t bhr = row / a.Sq;
+      const int qrow = (int)(row - bhr * a.Sq);
+      l2 += alibi_slope(a.alibi_slopes, (int)(bhr % a.H), a.H) * kLog2e * (float)(qrow & (kDkdvBQ - 1));
+    }
+    a.lse2[row] = l2;
   }
   (void)EPL;
 }
 
-hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st) {
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, bool fold_alibi) {
   const int64_t rows = (int64_t)a.B * a.H * a.Sq;
   const int es = dtype == 0 ? 4 : 2;
   const int lpr = (D * es / 16) < 64 ? (D * es / 16) : 64;
   const int rpb = 256 / lpr;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (es == 4) {
-    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<4, 64>), grid, block, 0, st, a, dtype);
-    else if (D == 128) hipLaunchKernelGGL((bwd_pre_kernel<4, 128>), grid, block, 0, st, a, dtype);
-    else hipLaunchKernelGGL((bwd_pre_kernel<4, 512>), grid, block, 0, st, a, dtype);
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<4, 64>), grid, block, 0, st, a, dtype, (int)fold_alibi);
+    else if (D == 128) hipLaunchKernelGGL((bwd_pre_kernel<4, 128>), grid, block, 0, st, a, dtype, (int)fold_alibi);
+    else hipLaunchKernelGGL((bwd_pre_kernel<4, 512>), grid, block, 0, st, a, dtype, (int)fold_alibi);
   } else {
-    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<2, 64>), grid, block, 0, st, a, dtype);
-    else hipLaunchKernelGGL((bwd_pre_kernel<2, 128>), grid, block, 0, st, a, dtype);
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<2, 64>), grid, block, 0, st, a, dtype, (int)fold_alibi);
+    else hipLaunchKernelGGL((bwd_pre_kernel<2, 128>), grid, block, 0, st, a, dtype, (int)fold_alibi);
   }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ shared helpers
-
-// Natural-layout staging of a ROWS-row tile of a (rows, D) 16-bit tensor
-// (pitch D + 8).  Rows past nrows are clamped to the last row (finite values
-// that the kernels mask out), so the loads carry no branch.
-template <int D, int ROWS>
-struct Stage1 {
-  static constexpr int N = ROWS * D / 8 / 256;   // 16-byte chunks per thread
-  u32x4 r[N];
-  __device__ __forceinline__ void load(const uint16_t* g, int row0, int nrows, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
-      r[i] = *(const u32x4*)(g + (size_t)min(row0 + row, nrows - 1) * D + 8 * ch);
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* nat, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int c = tid + 256 * i, row = c / (D / 8), ch = c % (D / 8);
-      lds_write16(&nat[row * (D + 8) + 8 * ch], r[i]);
-    }
-  }
-};
 
 template <class T>
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
@@ -125,33 +117,35 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
 
 // ------------------------------------------------------------- dK / dV pass
 
-template <int D>
-struct DkdvCfg {
-  static constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
-  static constexpr int BQ = 64;     // queries per tile
-  static constexpr int QP = D + 8;
-  // one buffer: Q and dO (natural, 16-bit), then the lse2 and delta rows
-  static constexpr size_t buf_elems = (size_t)2 * BQ * QP + 2 * BQ * 2;
-  static constexpr size_t lds = 2 * buf_elems * 2;
-};
-
-// Key-stationary dK/dV pass.  The ALiBi and checkerboard bias start the S
-// accumulator (the per-query part, per register) with the per-key part and
-// the key mask (-inf) folded into one per-lane exponent term, so per score
-// the work is one subtraction of the row's lse, one FMA and one exp for P
-// and a subtraction and a multiply for dS.  Query tiles are double buffered.
+// Key-stationary dK/dV pass.  The ALiBi bias slope (k - q) splits into the
+// query's part relative to its tile start, which arrives folded into the
+// lse2 row, and a per-lane term slope (k - tile start) that joins the key
+// mask (-inf) in one exponent offset; the checkerboard bias starts the S
+// accumulator per register.  Per score the work is one subtraction of the
+// row's lse2, one FMA and one exp for P and a subtraction and a multiply for
+// dS.  Query tiles (Q, dO and their
+// lse2 and delta rows) go from HBM straight into double-buffered LDS; both
+// 16-bit tiles are read as row fragments (S, dP) and transposed (dV, dK), so
+// their chunks carry the permutation that serves both reads.  Each 64-query
+// tile is processed as two 32-query halves to keep registers low enough for
+// three waves per SIMD at head_dim 64.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
-  using C = DkdvCfg<D>;
-  constexpr int BKV = C::BKV, BQ = C::BQ, QP = C::QP;
+  constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
+  constexpr int BQ = kDkdvBQ;   // queries per tile
   constexpr int KS = D / 16, DT = D / 32;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
-  auto sQ = [&](int buf) { return smem16 + buf * C::buf_elems; };
-  auto sO = [&](int buf) { return sQ(buf) + BQ * QP; };
-  auto sL = [&](int buf) { return (float*)(sO(buf) + BQ * QP); };
-  auto sDl = [&](int buf) { return sL(buf) + BQ; };
+  constexpr int TILE = BQ * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sO0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sO1[TILE];
+  __shared__ __attribute__((aligned(16))) float sL0[BQ];
+  __shared__ __attribute__((aligned(16))) float sL1[BQ];
+  __shared__ __attribute__((aligned(16))) float sD0[BQ];
+  __shared__ __attribute__((aligned(16))) float sD1[BQ];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
@@ -186,14 +180,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   bool key_ok = kj < Skv;
   if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + min(kj, Skv - 1)] != 0;
   float slope2 = 0.f;
+  if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
   f32x16 cinit = zero16();
-  if constexpr (MOD == MOD_ALIBI) {
-    // bias = slope (kj - q); per register: -slope * acc_row / scale
-    const float slope = alibi_slope(a.alibi_slopes, h, a.H);
-    slope2 = slope * kLog2e;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = -slope * inv_scale * (float)acc_row(r, hi);
-  }
   if constexpr (MOD == MOD_CHECKERBOARD) {
     // query tiles start at even positions, so register r holds a query of parity (r & 1)
 #pragma unroll
@@ -209,92 +197,93 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
 
   const int qt0 = CAUSAL ? k0 / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
-  Stage1<D, BQ> stq, sto;
-  float lreg = 0.f, dreg = 0.f;
-  int lq = 0;
-  auto load_tile = [&](int it) {
-    const int q0 = min(it, nqt - 1) * BQ;   // clamped: no branch next to the loads
-    stq.load(Qg, q0, Sq, tid);
-    sto.load(dOg, q0, Sq, tid);
-    lq = q0 + (tid & (BQ - 1));
-    lreg = lse2g[min(lq, Sq - 1)];
-    dreg = deltag[min(lq, Sq - 1)];
-  };
-  auto store_tile = [&](int buf) {
-    stq.store(sQ(buf), tid);
-    sto.store(sO(buf), tid);
-    if (tid < BQ) {   // rows past seq_q: P = 0 (lse2 = +inf) and delta = 0
-      sL(buf)[tid] = lq < Sq ? lreg : __builtin_inff();
-      sDl(buf)[tid] = lq < Sq ? dreg : 0.f;
-    }
-  };
 
-  if (qt0 < nqt) {
-    load_tile(qt0);
-    store_tile(qt0 & 1);
-    __syncthreads();
-    load_tile(qt0 + 1);
-  }
-  for (int it = qt0; it < nqt; ++it) {
+  // Direct loads of query tile it.  Rows past seq_q are clamped to the last
+  // row; their scores are masked below.
+  auto load_tile = [&](int it, uint16_t* sQ, uint16_t* sO, float* sL, float* sD) __attribute__((always_inline)) {
     const int q0 = it * BQ;
-    __syncthreads();   // everyone is past tile it-1, whose buffer ((it+1)&1) is free
-    store_tile((it + 1) & 1);
-    load_tile(it + 2);
-    if (CAUSAL && q0 + BQ - 1 < kw) continue;  // every query of the tile precedes every key of this wave
-    const int buf = it & 1;
-    const uint16_t* qb = sQ(buf);
-    const uint16_t* ob = sO(buf);
+    load_tile_lds<D, BQ, SW_BOTH>(Qg, q0, Sq, sQ, wave, lane);
+    load_tile_lds<D, BQ, SW_BOTH>(dOg, q0, Sq, sO, wave, lane);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((const void*)(lse2g + min(q0 + lane, Sq - 1)), (lds_void_ptr)sL, 4, 0, 0);
+    if (wave == 1)
+      __builtin_amdgcn_global_load_lds((const void*)(deltag + min(q0 + lane, Sq - 1)), (lds_void_ptr)sD, 4, 0, 0);
+  };
 
-    // one 32-query half at a time keeps S and dP to 32 registers
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      // S' = Q K^T + C and dP = dO V^T, queries as rows
-      f32x16 sv = cinit, dpv = zero16();
+  // Queries 32mt .. 32mt+31 of tile it.
+  auto half = [&](int it, int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD) __attribute__((always_inline)) {
+    const int qs = it * BQ + 32 * mt;   // first query of the half
+    if (CAUSAL && qs + 31 < kw) return;   // every query precedes every key of this wave
+
+    // S' = Q K^T + C and dP = dO V^T, queries as rows
+    f32x16 sv = cinit, dpv = zero16();
+    {
+      const int qr = 32 * mt + l32;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const int off = (32 * mt + l32) * QP + 16 * kk + 8 * hi;
-        sv = mma16<T>(lds_read16(&qb[off]), kf[kk], sv);
-        dpv = mma16<T>(lds_read16(&ob[off]), vf[kk], dpv);
-      }
-      // queries before the key (causal): P = 0, only on diagonal tiles
-      if (CAUSAL && __builtin_amdgcn_ballot_w64(q0 + 32 * mt < kj) != 0) {
-        const int lim_l = kj - q0 - 32 * mt - 4 * hi;   // rows with acc_row < kj - q0 - 32 mt are masked
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pos = 8 * (r >> 2) + (r & 3);
-          if (pos < lim_l) sv[r] = kNegInf;
-        }
-      }
-      float lb = key_ok ? 0.f : kNegInf;
-      if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - q0 - 32 * mt) : kNegInf;
-      const float* lrow = sL(buf) + 32 * mt + 4 * hi;
-      const float* drow = sDl(buf) + 32 * mt + 4 * hi;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
-        const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const int r = 4 * u + cc;
-          const float p = exp2_hw(fmaf(sv[r], c, lb - l4[cc]));
-          sv[r] = p;
-          dpv[r] = p * (dpv[r] - d4[cc]);
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int st = 2 * mt + u;
-        const u32x4 pb = pack8<T>(sv, u);
-        const u32x4 db = pack8<T>(dpv, u);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dv[dt] = mma16<T>(read_a_tr(ob, QP, 16 * st, 32 * dt, lane), pb, dv[dt]);
-          dk[dt] = mma16<T>(read_a_tr(qb, QP, 16 * st, 32 * dt, lane), db, dk[dt]);
-        }
+        const int off = tile_off<D, SW_BOTH>(qr, 16 * kk + 8 * hi);
+        sv = mma16<T>(lds_read16(sQ + off), kf[kk], sv);
+        dpv = mma16<T>(lds_read16(sO + off), vf[kk], dpv);
       }
     }
+    // P = 0 for queries before the key (causal) and past seq_q, only on such halves
+    if (__builtin_amdgcn_ballot_w64((CAUSAL && qs < kj) || qs + 31 >= Sq) != 0) {
+      const int ql = qs + 4 * hi;   // query of register r: ql + 8 (r / 4) + r % 4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = ql + 8 * (r >> 2) + (r & 3);
+        if ((CAUSAL && q < kj) || q >= Sq) sv[r] = kNegInf;
+      }
+    }
+    float lb = key_ok ? 0.f : kNegInf;
+    if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ) : kNegInf;
+    const float* lrow = sL + 32 * mt + 4 * hi;
+    const float* drow = sD + 32 * mt + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
+      const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int r = 4 * u + cc;
+        const float p = exp2_hw(fmaf(sv[r], c, lb - l4[cc]));
+        sv[r] = p;
+        dpv[r] = p * (dpv[r] - d4[cc]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int p0 = 32 * mt + 16 * u;
+      const u32x4 pb = pack8<T>(sv, u);
+      const u32x4 db = pack8<T>(dpv, u);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sO, p0, 32 * dt, lane), pb, dv[dt]);
+        dk[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sQ, p0, 32 * dt, lane), db, dk[dt]);
+      }
+    }
+  };
+
+  // Tile it in the buffers of its parity; tile it+1 is requested into the
+  // other buffers right after the barrier that retires tile it-1.
+  auto tile = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
+                  uint16_t* sOn, float* sLn, float* sDn) __attribute__((always_inline)) {
+    wait_direct_loads();   // this wave's loads of tile it are in LDS
+    __syncthreads();       // ... and every other wave's; tile it-1 is retired
+    if (it + 1 < nqt) load_tile(it + 1, sQn, sOn, sLn, sDn);
+    half(it, 0, sQ, sO, sL, sD);
+    __builtin_amdgcn_sched_barrier(0);   // the halves share registers
+    half(it, 1, sQ, sO, sL, sD);
+  };
+
+  if (qt0 < nqt) load_tile(qt0, sQ0, sO0, sL0, sD0);
+  int it = qt0;
+  for (; it + 1 < nqt; it += 2) {
+    tile(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+    tile(it + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
   }
+  if (it < nqt) tile(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
 
   if (kj < Skv) {
     uint16_t* dKg = (uint16_t*)a.dk + ((size_t)bh * Skv + kj) * D;
@@ -316,31 +305,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
 
 // ----------------------------------------------------------------- dQ pass
 
-template <int D>
-struct Dq16Cfg {
-  static constexpr int BM = 128;   // queries per workgroup
-  static constexpr int BN = 64;    // keys per tile
-  static constexpr int KP = D + 8;
-  // one buffer: K and V natural (16-bit) and the key row
-  static constexpr size_t buf_elems = (size_t)2 * BN * KP + 2 * BN * 2;
-  static constexpr size_t lds = 2 * buf_elems * 2;
-};
-
 // Query-stationary dQ pass, structured like the forward kernel: the score_mod
 // bias (and the key mask row) start the S^T accumulator, masking runs only on
-// diagonal and tail tiles, tiles are double buffered with branch-free staging,
-// and per score one FMA and one exp give P = 2^(S' c + b - lse2).
+// diagonal and tail halves, K/V tiles go straight into double-buffered LDS
+// (K permuted for both of its reads: row fragments for S^T, transposed for
+// dQ), and per score one FMA and one exp give P = 2^(S' c + b - lse2).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
-  using C = Dq16Cfg<D>;
-  constexpr int BM = C::BM, BN = C::BN, KP = C::KP;
+__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void dq16_kernel(const AttnArgs a) {
+  constexpr int BM = 128;   // queries per workgroup
+  constexpr int BN = 64;    // keys per tile
   constexpr int KS = D / 16, DT = D / 32;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
-  auto sK = [&](int buf) { return smem16 + buf * C::buf_elems; };
-  auto sV = [&](int buf) { return sK(buf) + BN * KP; };
-  auto sB = [&](int buf) { return (float*)(sV(buf) + BN * KP); };   // 2 x BN floats: q parity 0 / 1
+  constexpr int TILE = BN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN : 4];   // q parity 0 / 1
+  __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN : 4];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
@@ -361,7 +345,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
   // This lane's query: Q and dO rows as B operands, and the row's delta =
   // <dO, O> and lse * log2(e), which this pass also writes to the workspace
-  // for the key/value pass that runs after it.
+  // for the key/value pass that runs after it (lse2 with the query's ALiBi
+  // share folded in, as bwd_pre_kernel does).
   const uint16_t* Og = (const uint16_t*)a.o + (size_t)bh * Sq * D;
   u32x4 qf[KS], of[KS];
   float lse2, delta;
@@ -387,8 +372,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     lse2 = (ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();   // empty rows and rows past seq_q: P = 0
     delta = ok ? dsum : 0.f;
     if (ok && hi == 0) {
+      float l2 = lse2;   // for the key/value pass: with the query's ALiBi share (see bwd_pre_kernel)
+      if constexpr (MOD == MOD_ALIBI)
+        l2 += alibi_slope(a.alibi_slopes, h, a.H) * kLog2e * (float)(qi & (kDkdvBQ - 1));
       a.delta[(size_t)bh * Sq + qi] = delta;
-      a.lse2[(size_t)bh * Sq + qi] = lse2;
+      a.lse2[(size_t)bh * Sq + qi] = l2;
     }
   }
 
@@ -411,21 +399,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
   const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
-  Stage1<D, BN> stk, stv;
+
+  // Key-mask row: one byte per key, converted to an additive row in LDS.
   uint32_t mreg = 0;
   int mkv = 0;
-  auto load_tile = [&](int n) {
-    const int kv0 = min(n, ntiles - 1) * BN;   // clamped: no branch next to the loads
-    stk.load(Kg, kv0, Skv, tid);
-    stv.load(Vg, kv0, Skv, tid);
+  auto load_m = [&](int kv0) __attribute__((always_inline)) {
     if constexpr (MASK) {
       mkv = kv0 + (tid & (BN - 1));
       mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
-  auto store_tile = [&](int buf) {
-    stk.store(sK(buf), tid);
-    stv.store(sV(buf), tid);
+  auto store_m = [&](float* sB) __attribute__((always_inline)) {
     if constexpr (MASK) {
       if (tid < BN) {
         const bool keep = mkv < Skv && mreg != 0;
@@ -435,91 +419,97 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
           e0 = (kev ? a.even_nat : a.odd_nat) * inv_scale;
           e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
         }
-        sB(buf)[tid] = keep ? e0 : kNegInf;
-        sB(buf)[BN + tid] = keep ? e1 : kNegInf;
+        sB[tid] = keep ? e0 : kNegInf;
+        sB[BN + tid] = keep ? e1 : kNegInf;
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  load_tile(1);
-  for (int n = 0; n < ntiles; ++n) {
-    const int kv0 = n * BN;
-    __syncthreads();   // everyone is past tile n-1, whose buffer ((n+1)&1) is free
-    store_tile((n + 1) & 1);
-    load_tile(n + 2);
-    if (CAUSAL && kv0 > qw + 31) continue;
-    const uint16_t* kb = sK(n & 1);
-    const uint16_t* vb = sV(n & 1);
+  // Keys 32t .. 32t+31 of tile n.
+  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
+    const int k0 = n * BN + 32 * t;   // first key of the half
+    if (CAUSAL && k0 > qw + 31) return;
 
     // S'^T = K Q^T + C and dP^T = V dO^T, keys as rows
-    f32x16 s[2], dp[2];
+    f32x16 s = cinit, dp = zero16();
+    if constexpr (MASK) {
+      const float* row = sB + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 acc = cinit;
-      if constexpr (MASK) {
-        const float* row = sB(n & 1) + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 m4 = *(const f32x4*)(row + 8 * u);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 m4 = *(const f32x4*)(row + 8 * u);
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) acc[4 * u + cc] += m4[cc];
-        }
+        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] += m4[cc];
       }
-      f32x16 pacc = zero16();
+    }
+    {
+      const int kr = 32 * t + l32;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const int off = (32 * t + l32) * KP + 16 * kk + 8 * hi;
-        acc = mma16<T>(lds_read16(&kb[off]), qf[kk], acc);
-        pacc = mma16<T>(lds_read16(&vb[off]), of[kk], pacc);
+        const int off = tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi);
+        s = mma16<T>(lds_read16(sK + off), qf[kk], s);
+        dp = mma16<T>(lds_read16(sV + off), of[kk], dp);
       }
-      s[t] = acc;
-      dp[t] = pacc;
     }
 
-    // scores past the diagonal or past seq_kv: -inf (only on such tiles)
+    // scores past the diagonal or past seq_kv: -inf (only on such halves)
     {
       int lim = 1 << 30;
-      if (CAUSAL && kv0 + BN - 1 > qw) lim = qi - kv0;
-      if (!MASK && kv0 + BN > Skv) lim = min(lim, Skv - 1 - kv0);
-      if (__builtin_amdgcn_ballot_w64(lim < BN - 1) != 0) {
+      if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
+      if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
+      if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
         const int lim_l = lim - 4 * hi;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int pos = 32 * t + 8 * (r >> 2) + (r & 3);
-            if (pos > lim_l) s[t][r] = kNegInf;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int pos = 8 * (r >> 2) + (r & 3);
+          if (pos > lim_l) s[r] = kNegInf;
         }
       }
     }
 
-    float nb0 = -lse2, nb1 = -lse2;
-    if constexpr (MOD == MOD_ALIBI) {
-      const float add0 = slope2 * (float)(kv0 - qi);
-      nb0 = add0 - lse2;
-      nb1 = add0 + slope2 * 32.0f - lse2;
-    }
+    float nb = -lse2;
+    if constexpr (MOD == MOD_ALIBI) nb = slope2 * (float)(k0 - qi) - lse2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p0 = exp2_hw(fmaf(s[0][r], c, nb0));
-      const float p1 = exp2_hw(fmaf(s[1][r], c, nb1));
-      dp[0][r] = p0 * (dp[0][r] - delta);
-      dp[1][r] = p1 * (dp[1][r] - delta);
+      const float p = exp2_hw(fmaf(s[r], c, nb));
+      dp[r] = p * (dp[r] - delta);
     }
 
-    // dQ^T += K^T dS^T over the tile's 64 keys
+    // dQ^T += K^T dS^T over the half's 32 keys
 #pragma unroll
-    for (int st = 0; st < BN / 16; ++st) {
-      const int t = st >> 1, u = st & 1;
-      const u32x4 db = pack8<T>(dp[t], u);
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 db = pack8<T>(dp, u);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(read_a_tr(kb, KP, 16 * st, 32 * dt, lane), db, dq[dt]);
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sK, 32 * t + 16 * u, 32 * dt, lane), db, dq[dt]);
     }
+  };
+
+  auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB, uint16_t* sKn, uint16_t* sVn,
+                  float* sBn) __attribute__((always_inline)) {
+    wait_direct_loads();   // this wave's loads of tile n are in LDS
+    __syncthreads();       // ... and every other wave's; tile n-1 is retired
+    if (n + 1 < ntiles) {
+      load_tile_lds<D, BN, SW_BOTH>(Kg, (n + 1) * BN, Skv, sKn, wave, lane);
+      load_tile_lds<D, BN, SW_BOTH>(Vg, (n + 1) * BN, Skv, sVn, wave, lane);
+      store_m(sBn);
+      load_m(min(n + 2, ntiles - 1) * BN);
+    }
+    half(n, 0, sK, sV, sB);
+    __builtin_amdgcn_sched_barrier(0);   // the halves share registers
+    half(n, 1, sK, sV, sB);
+  };
+
+  load_tile_lds<D, BN, SW_BOTH>(Kg, 0, Skv, sK0, wave, lane);
+  load_tile_lds<D, BN, SW_BOTH>(Vg, 0, Skv, sV0, wave, lane);
+  load_m(0);
+  store_m(sB0);
+  load_m(min(1, ntiles - 1) * BN);
+  int n = 0;
+  for (; n + 1 < ntiles; n += 2) {
+    tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
+    tile(n + 1, sK1, sV1, sB1, sK0, sV0, sB0);
   }
+  if (n < ntiles) tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
 
   if (qi < Sq) {
     uint16_t* dQg = (uint16_t*)a.dq + ((size_t)bh * Sq + qi) * D;
@@ -537,30 +527,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
 // ----------------------------------------------------------------- launchers
 
-template <class K>
-static hipError_t launch_dyn(K kern, unsigned grid, size_t lds, hipStream_t st, const AttnArgs& a) {
-  if (lds > 65536) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, a);
-  return hipGetLastError();
-}
+int bwd16_block_kv() { return 128; }
+int bwd16_block_q() { return 128; }
 
 // The query pass runs first and writes delta and lse2 for the key/value
 // pass; without it, the preprocess kernel provides them.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   const int BH = a.B * a.H;
-  const unsigned nkb = (unsigned)((a.Skv + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
+  const unsigned nkb = (unsigned)((a.Skv + bwd16_block_kv() - 1) / bwd16_block_kv());
   hipError_t err;
   if (want_q) {
-    err = launch_dyn(dq16_kernel<T, D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, Dq16Cfg<D>::lds, st, a);
+    hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK>), dim3((unsigned)a.n_qblocks * BH), dim3(256), 0, st, a);
+    err = hipGetLastError();
   } else {
-    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st);
+    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI);
   }
   if (err != hipSuccess || !want_kv) return err;
-  return launch_dyn(dkdv16_kernel<T, D, MOD, CAUSAL, MASK>, nkb * BH, DkdvCfg<D>::lds, st, a);
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK>), dim3(nkb * BH), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 template <class T, int D, int MOD>
@@ -577,9 +562,6 @@ static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool m
     default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, kv, qq, st);
   }
 }
-
-int bwd16_block_kv() { return 128; }
-int bwd16_block_q() { return 128; }
 
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, bool kv, bool qq,
                         hipStream_t st) {

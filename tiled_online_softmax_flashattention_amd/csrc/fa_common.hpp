@@ -136,6 +136,74 @@ __device__ __forceinline__ u32x4 read_a_tr(const uint16_t* tile, int pitch, int 
   const u32x2 hi = lds_read_tr(tile + (row + 8) * pitch + col);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
+// Unpadded (position, dim) 16-bit LDS tiles filled by direct loads store the
+// 16-byte chunk c of row r at chunk c ^ tswz(r).  LDS has 64 banks of 4 bytes;
+// a 16-byte read serves 16 lanes per pass and an 8-byte transposing read 32
+// lanes (measured).  The row-fragment read (16 lanes: 16 consecutive rows, one
+// chunk) and the transposing read (32 lanes: 4 consecutive rows, 4 adjacent
+// chunks) are then both conflict-free: at 128-byte rows the two row parities
+// use different bank halves, so bit 2 of the permutation (flipping every two
+// rows) separates rows r and r+2 and bits 0-1 spread 8 rows of one parity; at
+// 256-byte rows bits 2-3 separate the 4 rows of a transposing read and all 16
+// rows of a fragment read get distinct chunks.
+template <int D>
+__device__ __forceinline__ constexpr int tswz(int r) {
+  return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+// Chunk permutation by tile mode: SW_BOTH uses tswz (tiles read both ways);
+// SW_TR, for tiles read only by transposing reads, depends on r mod 4 alone
+// (0, 6, 12, 10 at 256-byte rows: the 4 rows of one read get disjoint 4-chunk
+// blocks), so rows r and r+8 share it and a lane's addresses differ by
+// constant offsets; SW_NONE is plain rows.  Every permutation costs address
+// registers where a lane's offsets stop being constants.
+enum { SW_NONE = 0, SW_BOTH = 1, SW_TR = 2 };
+template <int D, int SW>
+__device__ __forceinline__ constexpr int chunk_perm(int r) {
+  return SW == SW_BOTH ? tswz<D>(r) : SW == SW_TR ? (D == 64 ? 2 * (r & 3) : (0xAC60 >> (4 * (r & 3))) & 15) : 0;
+}
+
+// Element offset of (row, col) in a tile of D-element rows.
+template <int D, int SW>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ chunk_perm<D, SW>(row)) << 3)) + (col & 7);
+}
+
+// A operand read from a tile (see read_a_tr for the lane layout).
+template <int D, int SW>
+__device__ __forceinline__ u32x4 read_a_tr_tile(const uint16_t* tile, int p0, int d0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int row = p0 + 4 * (g >> 1) + (s >> 2);
+  const int col = d0 + 16 * (g & 1) + 4 * (s & 3);
+  const u32x2 lo = lds_read_tr(tile + tile_off<D, SW>(row, col));
+  const u32x2 hi = lds_read_tr(tile + tile_off<D, SW>(row + 8, col));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Direct load (global_load_lds_dwordx4) of a ROWS x D 16-bit tile into an LDS
+// tile by the 256 threads of a workgroup: wave w issues the 1 KiB blocks
+// w*NJ .. w*NJ+NJ-1, each lane fetching the global chunk that belongs at its
+// LDS slot.  Rows past nrows are clamped to the last row.
+template <int D, int ROWS, int SW>
+__device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int nrows, uint16_t* tile, int wave,
+                                              int lane) {
+  constexpr int NJ = ROWS * D * 2 / 1024 / 4;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int blk = wave * NJ + j;
+    const int e = blk * 512 + lane * 8;
+    const int row = e / D, pch = (e % D) >> 3;
+    const int lch = pch ^ chunk_perm<D, SW>(row);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)min(row0 + row, nrows - 1) * D + (lch << 3)),
+                                     (lds_void_ptr)(tile + blk * 512), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's direct loads have landed (vmcnt(0)).
+__device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+
 __device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
 
@@ -151,7 +219,8 @@ struct AttnArgs {
   void* dk;
   void* dv;
   float* delta;     // backward workspace: rowsum(dO * O), (B, H, Sq)
-  float* lse2;      // backward workspace: lse * log2(e), +inf for empty rows
+  float* lse2;      // backward workspace: lse * log2(e), +inf for empty rows (16-bit ALiBi: plus the
+                    // query's bias share within its 64-query tile)
   const uint8_t* key_mask;
   const float* alibi_slopes;
   float* partial;   // decode workspace

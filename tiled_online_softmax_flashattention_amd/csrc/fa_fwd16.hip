@@ -18,13 +18,10 @@
 // own vector instructions overlap its MFMAs poorly on this chip).
 //
 // LDS layout: tiles are unpadded (key, dim) rows, because a direct load
-// writes 64 consecutive 16-byte chunks.  The K tile permutes the 16-byte
-// chunks of row r by XOR with kswz(r), so the 32 lanes of a score MFMA, which
-// read one chunk column of 32 consecutive rows, hit distinct banks; each lane
-// of the load fetches the global chunk that belongs at its LDS slot.  The V
-// tile is read with the transposing LDS read (ds_read_b64_tr_b16) for the P V
-// product; at head_dim 128 its chunks are permuted by vswz(r) so the four
-// rows of one such read fall in distinct banks.
+// writes 64 consecutive 16-byte chunks; the chunks of each K row are permuted
+// (tswz) so the score MFMA's fragment reads are free of bank conflicts, and
+// at head_dim 128 so are V's for the transposing reads (ds_read_b64_tr_b16)
+// of the P V product.
 //
 // Per half tile and wave: S'^T = K Q^T + C (MFMA 32x32x16, Q resident in
 // registers as the B operand).  The accumulator starts from C = bias / scale,
@@ -47,25 +44,6 @@ namespace fa {
 
 constexpr float kLazyRescale = 8.0f;   // log2 units: P is kept below 2^8
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-
-// Chunk permutations of the K and V tiles (XOR on the 16-byte chunk index).
-template <int D>
-__device__ __forceinline__ constexpr int kswz(int r) {
-  return D == 64 ? ((r ^ (r >> 3)) & 7) : (r & 15);
-}
-template <int D>
-__device__ __forceinline__ constexpr int vswz(int r) {
-  // even values keep the chunk pair read by one 16-lane group adjacent
-  return D == 64 ? 0 : (0xAC60 >> (4 * (r & 3))) & 15;   // 0, 6, 12, 10
-}
-
-// Element offset of (row, col) in a tile of D-element rows whose 16-byte
-// chunks are permuted by XOR with swz.
-__device__ __forceinline__ int swz_off(int row, int col, int D, int swz) {
-  return row * D + (((col >> 3) ^ swz) << 3) + (col & 7);
-}
-
 // One 128-query block (qb) of one (batch, head) slice (bh).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb) {
@@ -74,7 +52,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
   constexpr int TILE = BN * D;     // elements per K or V tile
-  constexpr int NJ = TILE * 2 / 1024 / 4;   // 1 KiB direct loads per wave per tile (K, and V)
+  constexpr int VSW = D == 64 ? SW_NONE : SW_TR;   // V is read only transposed
 
   // Separate arrays per buffer: the compiler then sees that a direct load
   // into one buffer cannot alias reads of the other, and does not wait for it.
@@ -134,29 +112,20 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
   // the last row (finite values whose scores are masked to -inf).
-  auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int blk = wave * NJ + j;                 // 1 KiB block of the tile
-      const int e = blk * 512 + lane * 8;            // element offset of this lane's slot
-      const int row = e / D, pch = (e % D) >> 3;     // row and physical chunk
-      const size_t g = (size_t)min(kv0 + row, Skv - 1) * D;
-      __builtin_amdgcn_global_load_lds((const void*)(Kg + g + ((pch ^ kswz<D>(row)) << 3)),
-                                       (lds_void_ptr)(sK + blk * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(Vg + g + ((pch ^ vswz<D>(row)) << 3)),
-                                       (lds_void_ptr)(sV + blk * 512), 16, 0, 0);
-    }
+  auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) __attribute__((always_inline)) {
+    load_tile_lds<D, BN, SW_BOTH>(Kg, kv0, Skv, sK, wave, lane);
+    load_tile_lds<D, BN, VSW>(Vg, kv0, Skv, sV, wave, lane);
   };
   // Key-mask row: one byte per key, converted to an additive row in LDS.
   uint32_t mreg = 0;
   int mkv = 0;
-  auto load_m = [&](int kv0) {
+  auto load_m = [&](int kv0) __attribute__((always_inline)) {
     if constexpr (MASK) {
       mkv = kv0 + (tid & (BN - 1));
       mreg = a.key_mask[(size_t)b * Skv + min(mkv, Skv - 1)];
     }
   };
-  auto store_m = [&](float* sB) {
+  auto store_m = [&](float* sB) __attribute__((always_inline)) {
     if constexpr (MASK) {
       if (tid < BN) {
         const bool keep = mkv < Skv && mreg != 0;
@@ -178,7 +147,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
   // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
-  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) {
+  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
     const int k0 = kv_of(n) + 32 * t;   // first key of the half
     if (CAUSAL && k0 > qw + 31) return;   // every key follows every query of this wave
 
@@ -197,7 +166,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       const int kr = 32 * t + l32;
 #pragma unroll
       for (int kk = 0; kk < QS; ++kk)
-        s = mma16<T>(lds_read16(sK + swz_off(kr, 16 * kk + 8 * hi, D, kswz<D>(kr))), qf[kk], s);
+        s = mma16<T>(lds_read16(sK + tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi)), qf[kk], s);
     }
 
     // scores past the diagonal or past seq_kv: -inf (only on such halves)
@@ -240,21 +209,13 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // O^T += V^T P^T over the two 16-key steps of the half; the V fragments
-    // are transposed reads (see read_a_tr) under this tile's chunk permutation
-    const int sidx = lane & 15, g = lane >> 4;
+    // O^T += V^T P^T over the two 16-key steps of the half
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const u32x4 pb = {pack2<T>(s[8 * u + 0], s[8 * u + 1]), pack2<T>(s[8 * u + 2], s[8 * u + 3]),
                         pack2<T>(s[8 * u + 4], s[8 * u + 5]), pack2<T>(s[8 * u + 6], s[8 * u + 7])};
-      const int row = 32 * t + 16 * u + 4 * (g >> 1) + (sidx >> 2);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int col = 32 * dt + 16 * (g & 1) + 4 * (sidx & 3);
-        const u32x2 lo = lds_read_tr(sV + swz_off(row, col, D, vswz<D>(row)));
-        const u32x2 up = lds_read_tr(sV + swz_off(row + 8, col, D, vswz<D>(row + 8)));
-        o[dt] = mma16<T>(u32x4{lo[0], lo[1], up[0], up[1]}, pb, o[dt]);
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(read_a_tr_tile<D, VSW>(sV, 32 * t + 16 * u, 32 * dt, lane), pb, o[dt]);
     }
   };
 
@@ -267,8 +228,8 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   // Tile n in buffers (n & 1); tile n+1 is requested into the other buffers
   // right after the barrier that retires tile n-1.
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB,
-                  uint16_t* sKn, uint16_t* sVn, float* sBn) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's loads of tile n are in LDS
+                  uint16_t* sKn, uint16_t* sVn, float* sBn) __attribute__((always_inline)) {
+    wait_direct_loads();                   // this wave's loads of tile n are in LDS
     __syncthreads();                       // ... and every other wave's; tile n-1 is retired
     if (n + 1 < ntiles) {
       load_tile(kv_of(n + 1), sKn, sVn);

@@ -19,7 +19,7 @@ hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
 
 // Backward: preprocess (delta = rowsum(dO * O), lse in base 2), then the
 // key-stationary dK/dV pass and the query-stationary dQ pass.
-hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, bool fold_alibi = false);
 int bwd16_block_kv();
 int bwd16_block_q();
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
