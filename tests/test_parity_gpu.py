@@ -14,7 +14,7 @@ import torch
 import oracle
 import tiled_online_softmax_flashattention_amd as fa
 import workloads as W
-from parity import check, check_lse, full_parity, oracle_kw, sampled_parity, say, to_dev
+from parity import check, check_lse, full_parity, oracle_kw, run_backward, run_forward, sampled_parity, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +137,44 @@ def test_uniform_scores_full_shape_invariants(gpu_lib):
     assert (lse.double().cpu() - ref).abs().max().item() < 3e-5
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("causal,mod,mask", [(True, W.MOD_ALIBI, False), (False, W.MOD_CHECKERBOARD, True),
+                                             (False, W.MOD_NONE, False)])
+def test_ones_v_gives_ones(gpu_lib, dtype, causal, mod, mask):
+    """Rows of P sum to 1: with V = 1 every output is 1 (each row here has an
+    allowed key).  The 16-bit bound is the rounding of P to the input type."""
+    w = small(dtype, 64, causal, mod, mask, Sq=300, Skv=517)
+    inputs = w.make(with_dout=False)
+    inputs["v"] = torch.ones_like(inputs["v"])
+    dev = to_dev(inputs)
+    say(f"[ones] {dtype} causal={causal} mod={mod} mask={mask}")
+    out, _ = run_forward(w, dev)
+    tol = {"f32": 1e-5, "f16": 2e-3, "bf16": 8e-3}[dtype]
+    assert (out.float() - 1.0).abs().max().item() <= tol
+
+
+@pytest.mark.parametrize("w", [W.PREFILL_F16, W.KEYPAD_BF16], ids=["prefill", "keypad"])
+def test_full_shape_hull_and_gradient_sums(gpu_lib, w):
+    """At the full workload shape, for every row: the output lies in the box
+    spanned by the head's V rows (per dim), sum_j dV_j = sum_i dO_i (rows of P
+    sum to 1) and sum_j dK_j = 0 (rows of dS sum to 0)."""
+    inputs = w.make()
+    dev = to_dev(inputs)
+    say(f"[invariants] {w.name}")
+    out, lse = run_forward(w, dev)
+    v = dev["v"].float()
+    lo, hi = v.amin(dim=2, keepdim=True), v.amax(dim=2, keepdim=True)
+    slack = 1e-2 * (hi - lo)   # P and O rounded to the 16-bit type
+    o = out.float()
+    assert bool(((o >= lo - slack) & (o <= hi + slack)).all())
+    _, dk, dv = run_backward(w, dev, out, lse, dev["dout"])
+    do = dev["dout"].double()
+    sum_dv, sum_do, abs_do = dv.double().sum(dim=2), do.sum(dim=2), do.abs().sum(dim=2)
+    assert bool(((sum_dv - sum_do).abs() <= 1e-2 * abs_do + 1e-3).all())
+    sum_dk, abs_dk = dk.double().sum(dim=2), dk.double().abs().sum(dim=2)
+    assert bool((sum_dk.abs() <= 2e-2 * abs_dk + 1e-3).all())
+
+
 # ------------------------------------------------------------------ decode
 
 
@@ -169,6 +207,29 @@ def test_decode_matches_forward_at_one_query(gpu_lib, dtype):
     tol = 1e-5 if dtype == "f32" else 1e-2
     assert (out.float() - out2.float()).abs().max().item() <= tol * max(1.0, out2.float().abs().max().item())
     assert (lse - lse2).abs().max().item() < 1e-4
+
+
+def test_decode_independent_of_split(gpu_lib):
+    """The number of key chunks depends on batch * heads: one head decoded
+    alone (many chunks) and as head 0 of a 64-head batch (few chunks) agree,
+    and both match the oracle."""
+    Skv, D = 32768, 64
+    w1 = W.Workload("decode one head", 120, 1, 1, 1, Skv, D, "f16", backward=False)
+    one = w1.make()
+    w64 = W.Workload("decode 64 heads", 121, 8, 8, 1, Skv, D, "f16", backward=False)
+    many = w64.make()
+    for k in ("q", "k", "v"):
+        many[k][0, 0] = one[k][0, 0]
+    d1, d64 = to_dev(one), to_dev(many)
+    say("[decode split] one head vs 64 heads")
+    o1, l1 = fa.decode(d1["q"], d1["k"], d1["v"])
+    o64, l64 = fa.decode(d64["q"], d64["k"], d64["v"])
+    torch.cuda.synchronize()
+    assert (o1[0, 0].float() - o64[0, 0].float()).abs().max().item() <= 2e-3 * o1.float().abs().max().item()
+    assert abs(l1[0, 0, 0].item() - l64[0, 0, 0].item()) < 1e-4
+    o_ref, lse_ref = oracle.decode(one["q"], one["k"], one["v"], scale=w1.scale)
+    check("decode o (one head)", o1, o_ref, "f16", "o")
+    check_lse(l1, lse_ref)
 
 
 # ------------------------------------------------------------- the workloads

@@ -51,7 +51,7 @@ bool tensors_ok(std::initializer_list<const void*> ptrs) {
 }
 
 int block_q_fwd(const fa_problem* p) {
-  return p->dtype == FA_F32 ? fa::fwd32_block_q((int)p->head_dim) : fa::fwd16_block_q();
+  return p->dtype == FA_F32 ? fa::fwd32_block_q((int)p->head_dim) : fa::fwd16_block_q((int)p->head_dim);
 }
 
 fa::AttnArgs make_args(const fa_problem* p) {

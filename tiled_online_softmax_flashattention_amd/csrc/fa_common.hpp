@@ -183,13 +183,14 @@ __device__ __forceinline__ u32x4 read_a_tr_tile(const uint16_t* tile, int p0, in
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Direct load (global_load_lds_dwordx4) of a ROWS x D 16-bit tile into an LDS
-// tile by the 256 threads of a workgroup: wave w issues the 1 KiB blocks
+// tile by the NW waves of a workgroup: wave w issues the 1 KiB blocks
 // w*NJ .. w*NJ+NJ-1, each lane fetching the global chunk that belongs at its
 // LDS slot.  Rows past nrows are clamped to the last row.
-template <int D, int ROWS, int SW>
+template <int D, int ROWS, int SW, int NW = 4>
 __device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int nrows, uint16_t* tile, int wave,
                                               int lane) {
-  constexpr int NJ = ROWS * D * 2 / 1024 / 4;
+  constexpr int NJ = ROWS * D * 2 / 1024 / NW;
+  static_assert(NJ * NW * 1024 == ROWS * D * 2, "tile must split into 1 KiB blocks per wave");
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int blk = wave * NJ + j;

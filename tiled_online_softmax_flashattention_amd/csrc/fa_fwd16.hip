@@ -299,7 +299,7 @@ static hipError_t launch_fwd16_d(const AttnArgs& a, int mod, bool causal, bool m
   }
 }
 
-int fwd16_block_q() { return 128; }
+int fwd16_block_q(int) { return 128; }
 
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st) {
   if (bf16) {

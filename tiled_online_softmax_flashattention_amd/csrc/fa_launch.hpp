@@ -8,7 +8,7 @@
 namespace fa {
 
 // 16-bit forward (f16 / bf16, head_dim 64 or 128).
-int fwd16_block_q();
+int fwd16_block_q(int D);
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
                         hipStream_t st);
 
