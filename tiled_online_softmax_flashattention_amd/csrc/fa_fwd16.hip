@@ -30,9 +30,13 @@
 // scalar folded into the exponent), for the checkerboard the two parity
 // values, and with a key mask C is read from an LDS row that holds 0 or -inf
 // per key.  Then one FMA and one v_exp_f32 per score give P = 2^(S' c + b - m).
-// The running max is updated lazily: only when some query's maximum grows by
-// more than 2^8 does the wave rescale its accumulator, otherwise P stays below
-// 2^8 (exact in fp16/bf16 range; the final division by l cancels the scale).
+// The running max is updated lazily and without a per-half maximum: the
+// exponentials are taken against the max as it stands, and only when some
+// query's sum over the half exceeds 2^15 (or the query has no max yet) does
+// the wave recompute the half's scores, update the max and rescale its
+// accumulator.  P stays below 2^15 (inside fp16 range; the final division by l
+// cancels the scale), and the common path needs no row maximum and no
+// cross-lane exchange.
 // Causal: key tiles past the block's last query are never visited, tiles are
 // visited diagonal first (so the largest ALiBi scores set the maximum early),
 // waves skip halves entirely past their own queries, and the per-score
@@ -42,7 +46,11 @@
 
 namespace fa {
 
-constexpr float kLazyRescale = 8.0f;   // log2 units: P is kept below 2^8
+constexpr float kSumLimit = 32768.0f;   // a half's row sum above this forces a max update
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // One 128-query block (qb) of one (batch, head) slice (bh).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
@@ -146,12 +154,10 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
-  // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
-  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
-    const int k0 = kv_of(n) + 32 * t;   // first key of the half
-    if (CAUSAL && k0 > qw + 31) return;   // every key follows every query of this wave
-
-    // S'^T = K Q^T + C
+  // S'^T = K Q^T + C for keys 32t .. 32t+31 (first key k0) of the tile in
+  // (sK, sB), with scores past the diagonal or past seq_kv set to -inf (the
+  // comparison runs only on such halves).
+  auto scores = [&](int t, int k0, const uint16_t* sK, const float* sB) __attribute__((always_inline)) {
     f32x16 s = cinit;
     if constexpr (MASK) {
       const float* row = sB + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
@@ -163,59 +169,97 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       }
     }
     {
+      // every K fragment is requested (into its own registers) before the
+      // first MFMA, so the LDS latency is paid once per half, not per MFMA
       const int kr = 32 * t + l32;
+      u32x4 kfr[QS];
 #pragma unroll
-      for (int kk = 0; kk < QS; ++kk)
-        s = mma16<T>(lds_read16(sK + tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi)), qf[kk], s);
+      for (int kk = 0; kk < QS; ++kk) kfr[kk] = lds_read16(sK + tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi));
+#pragma unroll
+      for (int kk = 0; kk < QS; ++kk) s = mma16<T>(kfr[kk], qf[kk], s);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QS, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, QS, 0);
     }
-
-    // scores past the diagonal or past seq_kv: -inf (only on such halves)
-    {
-      int lim = 1 << 30;   // last allowed key position inside the half, for this lane
-      if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
-      if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
-      if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
-        const int lim_l = lim - 4 * hi;
+    int lim = 1 << 30;   // last allowed key position inside the half, for this lane
+    if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
+    if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
+    if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
+      const int lim_l = lim - 4 * hi;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int pos = 8 * (r >> 2) + (r & 3);   // acc_row(r, hi) - 4 hi
-          if (pos > lim_l) s[r] = kNegInf;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int pos = 8 * (r >> 2) + (r & 3);   // acc_row(r, hi) - 4 hi
+        if (pos > lim_l) s[r] = kNegInf;
       }
     }
+    return s;
+  };
 
+  // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
+  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
+    const int k0 = kv_of(n) + 32 * t;   // first key of the half
+    if (CAUSAL && k0 > qw + 31) return;   // every key follows every query of this wave
+
+    f32x16 s = scores(t, k0, sK, sB);
     // per-lane exponent offset (ALiBi: bias of the half's first key)
     float add = 0.f;
     if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qi);
-    float mx = s[0];
+
+    // Fast path: exponentials against the running max as it stands, valid
+    // when every lane has one and no lane's sum over the half exceeds 2^15
+    // (so every P fits fp16).  Otherwise (a row's first visible keys, or a max
+    // that grew) the scores are recomputed from LDS, the max updated and the
+    // accumulator rescaled.
+    float ls = 0.f;
+    bool ok = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
+    if (ok) {
+      const float nb = add - m_run;
+      float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaf(mx, c, add);
-    mx = fmaxf(mx, xor32(mx));
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyRescale) != 0) {
+      for (int r = 0; r < 16; ++r) {
+        s[r] = exp2_hw(fmaf(s[r], c, nb));
+        l4[r & 3] += s[r];
+      }
+      ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+      ok = __builtin_amdgcn_ballot_w64(!(ls <= kSumLimit)) == 0;
+    }
+    if (!ok) {
+      s = scores(t, k0, sK, sB);
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaf(mx, c, add);
+      mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_hw(m_run - ((m_new == kNegInf) ? 0.f : m_new));
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_hw(m_run - m_use);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_run = m_new;
-    }
-    const float nb = add - ((m_run == kNegInf) ? 0.f : m_run);
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      const float nb = add - m_use;
+      float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = exp2_hw(fmaf(s[r], c, nb));
-      ls[r & 3] += s[r];
+      for (int r = 0; r < 16; ++r) {
+        s[r] = exp2_hw(fmaf(s[r], c, nb));
+        l4[r & 3] += s[r];
+      }
+      ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
     }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    l_run += ls;
 
-    // O^T += V^T P^T over the two 16-key steps of the half
+    // O^T += V^T P^T over the two 16-key steps of the half (all V fragments
+    // requested before the first MFMA)
+    u32x4 vfr[2][DT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vfr[u][dt] = read_a_tr_tile<D, VSW>(sV, 32 * t + 16 * u, 32 * dt, lane);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const u32x4 pb = {pack2<T>(s[8 * u + 0], s[8 * u + 1]), pack2<T>(s[8 * u + 2], s[8 * u + 3]),
                         pack2<T>(s[8 * u + 4], s[8 * u + 5]), pack2<T>(s[8 * u + 6], s[8 * u + 7])};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(read_a_tr_tile<D, VSW>(sV, 32 * t + 16 * u, 32 * dt, lane), pb, o[dt]);
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(vfr[u][dt], pb, o[dt]);
     }
   };
 
