@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
 // (K permuted for both of its reads: row fragments for S^T, transposed for
 // dQ), and per score one FMA and one exp give P = 2^(S' c + b - lse2).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void dq16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
   constexpr int BM = 128;   // queries per workgroup
   constexpr int BN = 64;    // keys per tile
   constexpr int KS = D / 16, DT = D / 32;
@@ -442,13 +442,22 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void dq16_kernel(const AttnAr
       }
     }
     {
+      // every K and V fragment is requested before the first MFMA
       const int kr = 32 * t + l32;
+      u32x4 kfr[KS], vfr[KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int off = tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi);
-        s = mma16<T>(lds_read16(sK + off), qf[kk], s);
-        dp = mma16<T>(lds_read16(sV + off), of[kk], dp);
+        kfr[kk] = lds_read16(sK + off);
+        vfr[kk] = lds_read16(sV + off);
       }
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s = mma16<T>(kfr[kk], qf[kk], s);
+        dp = mma16<T>(vfr[kk], of[kk], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // MFMAs
     }
 
     // scores past the diagonal or past seq_kv: -inf (only on such halves)
@@ -474,13 +483,17 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void dq16_kernel(const AttnAr
       dp[r] = p * (dp[r] - delta);
     }
 
-    // dQ^T += K^T dS^T over the half's 32 keys
+    // dQ^T += K^T dS^T over the half's 32 keys (K^T fragments requested first)
+    u32x4 kt[2][DT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) kt[u][dt] = read_a_tr_tile<D, SW_BOTH>(sK, 32 * t + 16 * u, 32 * dt, lane);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const u32x4 db = pack8<T>(dp, u);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        dq[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sK, 32 * t + 16 * u, 32 * dt, lane), db, dq[dt]);
+      for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(kt[u][dt], db, dq[dt]);
     }
   };
 
