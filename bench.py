@@ -46,13 +46,99 @@ def time_calls(fn, reps: int, torch) -> float:
     return start.elapsed_time(end) / reps
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_f16_causal_alibi.json")
+KERNEL_SOURCES = {"fwd16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
+                  "dq16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+                  "dkdv16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip"}
+COPY_BYTES = 256 * 1024 * 1024    # the calibration copy of --counters
+
+
+def counters_pass() -> int:
+    """What the rocprofv3 --pmc runs profile: a device copy of COPY_BYTES (the
+    counters' calibration), then two forward + backward steps of the prefill
+    workload."""
+    import torch
+
+    import tiled_online_softmax_flashattention_amd as fa
+    import workloads as W
+
+    x = torch.ones(COPY_BYTES // 4, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    w = W.PREFILL_F16
+    d = w.make()
+    q, k, v, do = (d[t].cuda() for t in ("q", "k", "v", "dout"))
+    kw = dict(causal=True, score_mod="alibi", scale=w.scale)
+    out, lse = fa.forward(q, k, v, **kw)
+    for _ in range(2):
+        fa.forward(q, k, v, out=out, lse=lse, **kw)
+        fa.backward(q, k, v, out, lse, do, **kw)
+    torch.cuda.synchronize()
+    print("counters pass done", flush=True)
+    return 0
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, command: str) -> int:
+    """Writes TRAFFIC_FILE from the counter_collection CSVs of the two
+    rocprofv3 passes over --counters: per-dispatch FETCH_SIZE / WRITE_SIZE
+    (KiB, summed over the device) of each kernel, scaled by what the same
+    counters read for the calibration copy, with the source hash of each
+    kernel."""
+    import csv
+    import hashlib
+    from collections import defaultdict
+
+    def per_kernel(path, counter):
+        vals = defaultdict(list)
+        by_dispatch = defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = r["Dispatch_Id"]
+            by_dispatch[key] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+        for key, v in by_dispatch.items():
+            vals[names[key]].append(v)
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def find(vals, frag):
+        got = [v for n, v in vals.items() if frag in n]
+        return sorted(x for lst in got for x in lst)
+
+    copy_kib = COPY_BYTES / 1024
+    cf = find(fetch, "copyBuffer") or find(fetch, "elementwise") or find(fetch, "copy")
+    cw = find(write, "copyBuffer") or find(write, "elementwise") or find(write, "copy")
+    fetch_factor = copy_kib / max(cf)
+    write_factor = copy_kib / max(cw)
+    out = {"command": command, "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": max(cf), "write_kib": max(cw),
+                                                    "fetch_factor": round(fetch_factor, 4),
+                                                    "write_factor": round(write_factor, 4)},
+           "kernels": {}}
+    for kern, src in KERNEL_SOURCES.items():
+        f, wv = find(fetch, kern), find(write, kern)
+        if not f or not wv:
+            continue
+        fk, wk = f[len(f) // 2], wv[len(wv) // 2]
+        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        out["kernels"][kern] = {"fetch_kib": fk, "write_kib": wk,
+                                "hbm_bytes": int(round((fk * fetch_factor + wk * write_factor) * 1024)),
+                                "source": src, "source_sha256": sha}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary, or None when the kernel's source has changed since then."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_prefill_f16_causal_alibi.json")
     try:
-        rec = json.load(open(path))["kernels"][kernel]
+        rec = json.load(open(TRAFFIC_FILE))["kernels"][kernel]
         sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
     except (OSError, KeyError, ValueError):
         return None
@@ -128,7 +214,15 @@ def main() -> int:
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) slices in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", action="store_true", help="also time the key-padding and long-context workloads")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run the calibration copy and two untimed steps (for rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the HBM traffic summary from two rocprofv3 counter CSVs of --counters")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
+    if args.counters:
+        return counters_pass()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
