@@ -11,7 +11,7 @@ of K + V + q + O + lse with K/V copies rotated so reads come from HBM), the
 roofline of the dominant kernel, and the fp64 oracle timed on a bounded
 sample on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s SECONDS]
 """
 from __future__ import annotations
 
@@ -208,8 +208,10 @@ def cpu_baseline(w, heads: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warmup, so the GPU clock has left its ramp")
     ap.add_argument("--reps", type=int, default=20, help="calls per per-kernel timing loop")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) slices in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -256,7 +258,17 @@ def main() -> int:
         run_fwd()
         run_bwd()
 
-    log(f"[bench] warmup {args.warmup}")
+    # The GPU clock ramps up over the first few tens of milliseconds of load
+    # (the first 100 steps run about a third slower than the rest), so steps
+    # are run untimed for settle_s seconds before the W warmup steps.
+    log(f"[bench] settle {args.settle_s} s, warmup {args.warmup}")
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(50):
+            step()
+        settle_steps += 50
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -329,6 +341,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
