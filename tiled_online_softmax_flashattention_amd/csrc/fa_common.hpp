@@ -202,6 +202,24 @@ __device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int n
   }
 }
 
+// The same load for a tile whose rows all exist (row0 + ROWS <= nrows): a
+// uniform base address plus a per-lane 32-bit byte offset, so the address
+// arithmetic per tile is scalar.
+template <int D, int ROWS, int SW, int NW = 4>
+__device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint16_t* tile, int wave, int lane) {
+  constexpr int NJ = ROWS * D * 2 / 1024 / NW;
+  static_assert(NJ * NW * 1024 == ROWS * D * 2, "tile must split into 1 KiB blocks per wave");
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int blk = wave * NJ + j;
+    const int e = blk * 512 + lane * 8;
+    const int row = e / D, pch = (e % D) >> 3;
+    const uint32_t off = (uint32_t)(row * D + ((pch ^ chunk_perm<D, SW>(row)) << 3)) * 2u;
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)g_row0 + off), (lds_void_ptr)(tile + blk * 512), 16,
+                                     0, 0);
+  }
+}
+
 // Wait until this wave's direct loads have landed (vmcnt(0)).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 

@@ -38,7 +38,8 @@
 // cancels the scale), and the common path needs no row maximum and no
 // cross-lane exchange.
 // Causal: key tiles past the block's last query are never visited, tiles are
-// visited diagonal first (so the largest ALiBi scores set the maximum early),
+// visited diagonal first (so the largest ALiBi scores set the maximum early;
+// non-causal ALiBi also visits the tiles from the last one down),
 // waves skip halves entirely past their own queries, and the per-score
 // comparison happens only on diagonal and ragged-tail halves.
 #include "fa_common.hpp"
@@ -115,14 +116,22 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
 
   const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
-  // causal: the diagonal tile first, then towards key 0
-  auto kv_of = [&](int n) { return (CAUSAL ? ntiles - 1 - n : n) * BN; };
+  // Causal: the diagonal tile first, then towards key 0.  ALiBi grows with the
+  // key index, so its largest scores also come first when the tiles are
+  // visited from the last one down, and the running max rarely moves.
+  constexpr bool REV = CAUSAL || MOD == MOD_ALIBI;
+  auto kv_of = [&](int n) { return (REV ? ntiles - 1 - n : n) * BN; };
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
   // the last row (finite values whose scores are masked to -inf).
   auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) __attribute__((always_inline)) {
-    load_tile_lds<D, BN, SW_BOTH>(Kg, kv0, Skv, sK, wave, lane);
-    load_tile_lds<D, BN, VSW>(Vg, kv0, Skv, sV, wave, lane);
+    if (kv0 + BN <= Skv) {
+      load_full_tile_lds<D, BN, SW_BOTH>(Kg + (size_t)kv0 * D, sK, wave, lane);
+      load_full_tile_lds<D, BN, VSW>(Vg + (size_t)kv0 * D, sV, wave, lane);
+    } else {
+      load_tile_lds<D, BN, SW_BOTH>(Kg, kv0, Skv, sK, wave, lane);
+      load_tile_lds<D, BN, VSW>(Vg, kv0, Skv, sV, wave, lane);
+    }
   };
   // Key-mask row: one byte per key, converted to an additive row in LDS.
   uint32_t mreg = 0;
@@ -150,6 +159,8 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   };
 
   float m_run = kNegInf, l_run = 0.f;
+  float neg_m = 0.f;         // -m_run (read only once have_max holds)
+  bool have_max = false;     // every lane of the wave has a finite m_run
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
@@ -180,10 +191,12 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, QS, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, QS, 0);
     }
-    int lim = 1 << 30;   // last allowed key position inside the half, for this lane
-    if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
-    if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
-    if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
+    // the diagonal and ragged-tail conditions are uniform over the wave
+    const bool diag = CAUSAL && k0 + 31 > qw;
+    const bool tail = !MASK && k0 + 32 > Skv;
+    if (diag || tail) {
+      int lim = diag ? qi - k0 : (1 << 30);   // last allowed key position inside the half
+      if (tail) lim = min(lim, Skv - 1 - k0);
       const int lim_l = lim - 4 * hi;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -205,19 +218,19 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qi);
 
     // Fast path: exponentials against the running max as it stands, valid
-    // when every lane has one and no lane's sum over the half exceeds 2^15
-    // (so every P fits fp16).  Otherwise (a row's first visible keys, or a max
-    // that grew) the scores are recomputed from LDS, the max updated and the
-    // accumulator rescaled.
+    // when every lane has one (have_max, uniform) and no lane's sum over the
+    // half exceeds 2^15 (so every P fits fp16).  Otherwise (a row's first
+    // visible keys, or a max that grew) the scores are recomputed from LDS,
+    // the max updated and the accumulator rescaled.
     float ls = 0.f;
-    bool ok = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
+    bool ok = have_max;
     if (ok) {
-      const float nb = add - m_run;
-      float l4[4] = {0.f, 0.f, 0.f, 0.f};
+      const float nb = MOD == MOD_ALIBI ? add - m_run : neg_m;
+      float l4[4];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = exp2_hw(fmaf(s[r], c, nb));
-        l4[r & 3] += s[r];
+        l4[r & 3] = r < 4 ? s[r] : l4[r & 3] + s[r];
       }
       ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       ok = __builtin_amdgcn_ballot_w64(!(ls <= kSumLimit)) == 0;
@@ -236,12 +249,14 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       m_run = m_new;
+      neg_m = -m_run;
+      have_max = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
       const float nb = add - m_use;
-      float l4[4] = {0.f, 0.f, 0.f, 0.f};
+      float l4[4];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] = exp2_hw(fmaf(s[r], c, nb));
-        l4[r & 3] += s[r];
+        l4[r & 3] = r < 4 ? s[r] : l4[r & 3] + s[r];
       }
       ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
     }
