@@ -261,3 +261,28 @@ def test_workload_decode_f16(gpu_lib, w):
 
 def test_workload_long_f32_d512_causal(gpu_lib):
     sampled_parity(W.LONG_F32, 256)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 64), ("f16", 128)])
+@pytest.mark.parametrize("causal,mod,spike", [(False, W.MOD_NONE, "last"), (False, W.MOD_ALIBI, "first"),
+                                              (True, W.MOD_NONE, "first"), (True, W.MOD_ALIBI, "first")])
+def test_running_max_grows_on_the_last_visited_tile(gpu_lib, dtype, D, causal, mod, spike):
+    """One key scores far above the rest (about 2^23 in P) and sits in the tile
+    the forward visits last (key 0 for causal and for ALiBi, whose tiles are
+    visited last key first; the last key otherwise), so the running max grows
+    at the very end and the accumulator rescale runs on the final tile.
+
+    Forward only: with attention this close to one-hot, dS = P (dP - D) is a
+    difference of two nearly equal numbers (D = rowsum(dO * O) uses the
+    stored 16-bit O), so the exact dQ and dK are near zero and an error
+    relative to their maximum says nothing about the kernel."""
+    S = 260
+    w = small(dtype, D, causal, mod, False, Sq=S, Skv=S, B=1, H=8, wid=106)
+    inputs = w.make()
+    g = torch.Generator().manual_seed(106)
+    q = 1.25 + 0.1 * torch.randn(1, 8, S, D, generator=g, dtype=torch.float64)
+    k = inputs["k"].double().clone()
+    k[:, :, 0 if spike == "first" else S - 1, :] = 2.0
+    tdt = inputs["q"].dtype
+    inputs["q"], inputs["k"] = q.to(tdt), k.to(tdt)
+    full_parity(w, backward=False, inputs=inputs)
