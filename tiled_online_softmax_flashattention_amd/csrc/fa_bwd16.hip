@@ -127,8 +127,9 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
 // lse2 and delta rows) go from HBM straight into double-buffered LDS; both
 // 16-bit tiles are read as row fragments (S, dP) and transposed (dV, dK), so
 // their chunks carry the permutation that serves both reads.  Each 64-query
-// tile is processed as two 32-query halves to keep registers low enough for
-// three waves per SIMD at head_dim 64.
+// tile is processed as two 32-query halves, which keeps the live registers
+// (K, V, dK, dV and two score blocks) within the 256 of two waves per SIMD
+// at head_dim 64.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
   constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
