@@ -41,10 +41,13 @@
  *
  * Semantics
  * ---------
- * s_ij = scale * <q_i, k_j> + bias_h(i, j), where i and j are global 0-based
- * query and key positions and the bias is NOT multiplied by scale.  Key j is
- * allowed for query i when key_mask[b][j] != 0 (or key_mask == NULL) and, if
- * causal, j <= i.  lse_i = log sum_{allowed j} exp(s_ij); out_i =
+ * s_ij = scale * <q_i, k_j> + bias_h(pos_i, j), where pos_i = i + q_offset is
+ * the position of query row i in the key sequence (q_offset = 0 for
+ * self-attention; the number of cached keys before the first query when
+ * decoding or prefilling against a KV cache), j is the 0-based key position,
+ * and the bias is NOT multiplied by scale.  Key j is allowed for query i when
+ * key_mask[b][j] != 0 (or key_mask == NULL) and, if causal, j <= pos_i.
+ * lse_i = log sum_{allowed j} exp(s_ij); out_i =
  * sum_{allowed j} exp(s_ij - lse_i) v_j.  A row with no allowed key gets
  * out_i = 0, lse_i = -inf and zero gradients.  Score, softmax and
  * accumulation arithmetic is float32; probabilities are rounded to ``dtype``
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -73,29 +76,32 @@ typedef enum {
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
 /* score_mod kinds (flaxattention page: example and benchmark).
- *  FA_MOD_ALIBI:        bias = -slope_h * (i - j).  slope_h comes from
+ *  FA_MOD_ALIBI:        bias = -slope_h * (pos_i - j).  slope_h comes from
  *                       alibi_slopes[h] (device float[heads]) or, when that is
  *                       NULL, slope_h = 2^(-8 (h + 1) / heads).
- *  FA_MOD_CHECKERBOARD: bias = checker_even when (i + j) is even, otherwise
+ *  FA_MOD_CHECKERBOARD: bias = checker_even when (pos_i + j) is even, otherwise
  *                       checker_odd (the workloads use +0.5 / -0.5). */
 typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2 } fa_mod_kind;
 
 typedef struct {
   int64_t batch, heads, seq_q, seq_kv, head_dim;
   int32_t dtype;             /* fa_dtype */
-  int32_t causal;            /* 0 or 1; 1 requires seq_q == seq_kv (key j <= query i) */
+  int32_t causal;            /* 0 or 1: key j allowed only when j <= i + q_offset */
   float scale;               /* multiplies q.k; pass 1/sqrt(head_dim) for the usual scaling */
   int32_t mod_kind;          /* fa_mod_kind */
   const float* alibi_slopes; /* device float[heads] or NULL (FA_MOD_ALIBI only) */
   float checker_even;        /* FA_MOD_CHECKERBOARD only */
   float checker_odd;
   const uint8_t* key_mask;   /* device uint8 (batch, seq_kv), nonzero = keep; NULL = keep all */
+  int64_t q_offset;          /* >= 0: position of query row 0 among the keys (0 = self-attention) */
 } fa_problem;
 
 /* Supported: dtype f16 or bf16 with head_dim 64 or 128; dtype f32 with
  * head_dim 64, 128 or 512.  Any seq_q, seq_kv >= 1 (ragged tails are masked
  * inside the kernels).  Sizes must keep every tensor under 2^31 elements per
- * (batch, head) slice and batch * heads under 2^31. */
+ * (batch, head) slice, batch * heads under 2^31 and q_offset + seq_q under
+ * 2^31.  A query whose position is past the last key (causal or not) sees
+ * every key. */
 
 /* Forward (attnax kernel body: online-softmax loop, final acc / l).
  * Writes out (dtype) and, when lse != NULL, lse (float32, natural log).  The
@@ -125,8 +131,9 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
 /* Bytes of device workspace fa_decode needs for problem p (seq_q must be 1). */
 fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
 
-/* Decode: one query per (batch, head) (seq_q == 1, query position 0,
- * causal == 0) against seq_kv keys, split over the key axis into chunks whose
+/* Decode: one query per (batch, head) (seq_q == 1, at position q_offset; with
+ * causal only keys 0 .. q_offset count) against seq_kv keys, split over the
+ * key axis into chunks whose
  * partial (max, sum, accumulator) are merged exactly.  The flaxattention page
  * (decoding benchmark and TODO list) singles this case out.  f16, bf16 and
  * f32 with head_dim 64 or 128.  Same outputs as fa_forward at seq_q = 1. */

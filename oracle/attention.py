@@ -20,6 +20,10 @@ What it computes (the definition the flash kernels reach up to rounding order):
   pairs and 0 elsewhere, O_i = sum_j P_ij v_j.  This is the exact result the
   online softmax of the attnax kernel body (running max, running sum, rescaled
   accumulator, final division by the sum) arrives at.
+* positions: query row i sits at position i + q_offset (q_offset = 0 by
+  default; a KV cache of q_offset earlier keys otherwise: the flaxattention
+  page's TODO list names decoding with a cache), and both the causal rule and
+  the score_mod use that position.
 * a query row with no allowed key is an empty sum: O_i = 0, lse_i = -inf, and
   its gradients are zero.  (The pages leave this open; the attnax kernel's
   finite ``min`` fill would instead average V.)
@@ -127,11 +131,14 @@ def _setup(q, k, v, rows, key_mask):
 
 def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
             mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-            rows: Optional[Sequence[int]] = None):
+            rows: Optional[Sequence[int]] = None, q_offset: int = 0):
     """Exact attention output and log-sum-exp.
 
     Returns ``(o, lse)``: o (B, H, R, D), lse (B, H, R) in fp64, where R are the
-    requested query rows (all rows by default).
+    requested query rows (all rows by default).  Query row i sits at position
+    i + q_offset of the key sequence (a KV cache holding q_offset earlier
+    keys): the causal mask keeps keys j <= i + q_offset and the score_mod sees
+    that position.
     """
     q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
     B, H = q.shape[:2]
@@ -139,10 +146,11 @@ def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
     o = np.zeros((B, H, len(rows), v.shape[3]))
     lse = np.zeros((B, H, len(rows)))
     kv_idx = np.arange(seq_kv)
+    pos = rows + int(q_offset)
     for b in range(B):
-        ok = allowed_pairs(rows, seq_kv, causal, None if km is None else km[b])
+        ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
         for h in range(H):
-            bias = score_bias(mod, h, rows, kv_idx, H, alibi_slopes, checker)
+            bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
             _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, ok)
             o[b, h] = p @ v[b, h]
     return o, lse
@@ -150,12 +158,12 @@ def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
 
 def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None,
              mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-             rows: Optional[Sequence[int]] = None):
+             rows: Optional[Sequence[int]] = None, q_offset: int = 0):
     """Analytic gradients of sum(dout * O) with respect to q, k and v.
 
     Returns ``(dq, dk, dv)``: dq (B, H, R, D) for the requested rows; dk and dv
     (B, H, Skv, D) are the gradients for a dout that is zero outside those rows
-    (with all rows, the ordinary full gradient).
+    (with all rows, the ordinary full gradient).  q_offset as in forward.
     """
     q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
     do = as_f64(dout)
@@ -167,10 +175,11 @@ def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     kv_idx = np.arange(seq_kv)
+    pos = rows + int(q_offset)
     for b in range(B):
-        ok = allowed_pairs(rows, seq_kv, causal, None if km is None else km[b])
+        ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
         for h in range(H):
-            bias = score_bias(mod, h, rows, kv_idx, H, alibi_slopes, checker)
+            bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
             qb, dob = q[b, h, rows], do[b, h, rows]
             _, _, p = _probabilities(qb, k[b, h], scale, bias, ok)
             dp = dob @ v[b, h].T
@@ -183,10 +192,11 @@ def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None
 
 
 def decode(q, k, v, *, scale: float, key_mask=None, mod: int = MOD_NONE, alibi_slopes=None,
-           checker=(0.5, -0.5)):
-    """Single-query attention (seq_q = 1, query index 0): the forward at Sq = 1."""
+           checker=(0.5, -0.5), q_offset: int = 0, causal: bool = False):
+    """Single-query attention (seq_q = 1, query at position q_offset): the
+    forward at Sq = 1."""
     q = as_f64(q)
     if q.shape[2] != 1:
         raise ValueError("decode takes seq_q = 1")
-    return forward(q, k, v, scale=scale, causal=False, key_mask=key_mask, mod=mod,
-                   alibi_slopes=alibi_slopes, checker=checker)
+    return forward(q, k, v, scale=scale, causal=causal, key_mask=key_mask, mod=mod,
+                   alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     for s in range(5):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"
@@ -90,8 +90,20 @@ def test_null_problem_and_pointers():
     assert fwd(prob(), lse=ctypes.c_void_p(0x10002)) == INVALID
 
 
-def test_causal_needs_square():
-    assert fwd(prob(causal=1, seq_kv=101)) == INVALID
+def test_query_offset_rules():
+    """Causal needs no square shape (query row i sits at key position i +
+    q_offset); q_offset must be >= 0 and keep positions below 2^31."""
+    assert fwd(prob(q_offset=-1)) == INVALID
+    assert fwd(prob(causal=1, q_offset=-5)) == INVALID
+    assert fwd(prob(seq_q=100, q_offset=(1 << 31) - 100)) == UNSUP
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    assert lib.fa_backward_workspace_size(ctypes.byref(prob(causal=1, seq_q=7, seq_kv=101, q_offset=94)),
+                                          ctypes.byref(n)) == _lib.FA_OK
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(causal=1, seq_q=1, seq_kv=4096, q_offset=100)),
+                                        ctypes.byref(n)) == _lib.FA_OK
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(causal=1, seq_q=1, seq_kv=4096, q_offset=-1)),
+                                        ctypes.byref(n)) == INVALID
 
 
 def test_unsupported_head_dims():

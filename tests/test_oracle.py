@@ -283,9 +283,10 @@ def test_gradients_match_central_differences(causal, mod, use_mask):
         np.testing.assert_allclose(g, num, atol=1e-8, err_msg=f"d{name}")
 
 
-def _torch_bias(mod, B, H, Sq, Skv, causal, km):
-    """Additive float mask for torch SDPA, written independently of the oracle."""
-    i = torch.arange(Sq, dtype=torch.float64)[:, None]
+def _torch_bias(mod, B, H, Sq, Skv, causal, km, q_offset=0):
+    """Additive float mask for torch SDPA, written independently of the oracle
+    (query row i at position i + q_offset)."""
+    i = torch.arange(Sq, dtype=torch.float64)[:, None] + q_offset
     j = torch.arange(Skv, dtype=torch.float64)[None, :]
     bias = torch.zeros(B, H, Sq, Skv, dtype=torch.float64)
     if mod == MOD_ALIBI:
@@ -302,19 +303,18 @@ def _torch_bias(mod, B, H, Sq, Skv, causal, km):
 
 
 @pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
-@pytest.mark.parametrize("shape", [(2, 3, 33, 33, 16), (1, 2, 17, 40, 8)])
+@pytest.mark.parametrize("shape", [(2, 3, 33, 33, 16, 0), (1, 2, 17, 40, 8, 0), (1, 2, 17, 40, 8, 23),
+                                   (1, 2, 17, 40, 8, 9)])
 def test_against_torch_sdpa_fp64(causal, mod, use_mask, shape):
-    B, H, Sq, Skv, D = shape
-    if causal and Sq != Skv:
-        pytest.skip("causal attention is defined here for seq_q == seq_kv")
+    B, H, Sq, Skv, D, off = shape
     q, k, v, do, km = _case(60, B=B, H=H, Sq=Sq, Skv=Skv, D=D, key_mask=use_mask)
     scale = 1.0 / math.sqrt(D)
-    kw = dict(scale=scale, causal=causal, key_mask=km, mod=mod)
+    kw = dict(scale=scale, causal=causal, key_mask=km, mod=mod, q_offset=off)
     o, lse = oracle.forward(q, k, v, **kw)
     dq, dk, dv = oracle.backward(q, k, v, do, **kw)
 
     tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
-    mask = _torch_bias(mod, B, H, Sq, Skv, causal, km)
+    mask = _torch_bias(mod, B, H, Sq, Skv, causal, km, off)
     to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
     to.backward(torch.from_numpy(do))
     np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-13)
@@ -324,6 +324,44 @@ def test_against_torch_sdpa_fp64(causal, mod, use_mask, shape):
     # lse against torch's logsumexp of the masked, biased scores
     s = torch.matmul(torch.from_numpy(q), torch.from_numpy(k).transpose(-1, -2)) * scale + mask
     np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+# --------------------------------------------------------------------------- query offsets
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", COMBOS)
+def test_offset_rows_are_the_tail_of_the_full_run(causal, mod, use_mask):
+    """Query rows placed at positions q_offset.. of a key sequence give the
+    same outputs as the same rows inside the full-length problem: the
+    attention of a query depends only on its position, its vector and the
+    keys (a KV cache of q_offset keys)."""
+    S, Sq = 20, 7
+    off = S - Sq
+    q, k, v, do, km = _case(90, B=1, H=3, Sq=S, Skv=S, D=4, key_mask=use_mask)
+    kw = dict(scale=0.6, causal=causal, key_mask=km, mod=mod)
+    o, lse = oracle.forward(q, k, v, **kw)
+    o_t, lse_t = oracle.forward(q[:, :, off:], k, v, q_offset=off, **kw)
+    np.testing.assert_allclose(o_t, o[:, :, off:], atol=1e-14)
+    np.testing.assert_allclose(lse_t, lse[:, :, off:], atol=1e-14)
+    do_tail = np.zeros_like(do)
+    do_tail[:, :, off:] = do[:, :, off:]
+    dq, dk, dv = oracle.backward(q, k, v, do_tail, **kw)
+    dq_t, dk_t, dv_t = oracle.backward(q[:, :, off:], k, v, do[:, :, off:], q_offset=off, **kw)
+    np.testing.assert_allclose(dq_t, dq[:, :, off:], atol=1e-14)
+    np.testing.assert_allclose(dk_t, dk, atol=1e-14)
+    np.testing.assert_allclose(dv_t, dv, atol=1e-14)
+
+
+@pytest.mark.parametrize("mod", [MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD])
+def test_decode_with_offset_is_a_causal_row(mod):
+    """Decoding the query at position p with causal masking equals row p of
+    the full causal forward (keys after p ignored, score_mod at position p)."""
+    q, k, v, _, _ = _case(95, B=2, H=2, Sq=12, Skv=12, D=5)
+    o, lse = oracle.forward(q, k, v, scale=0.5, causal=True, mod=mod)
+    for p in (0, 5, 11):
+        od, lsed = oracle.decode(q[:, :, p:p + 1], k, v, scale=0.5, mod=mod, q_offset=p, causal=True)
+        np.testing.assert_allclose(od[:, :, 0], o[:, :, p], atol=1e-14)
+        np.testing.assert_allclose(lsed[:, :, 0], lse[:, :, p], atol=1e-14)
 
 
 # --------------------------------------------------------------------------- row subsets

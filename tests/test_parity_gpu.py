@@ -286,3 +286,66 @@ def test_running_max_grows_on_the_last_visited_tile(gpu_lib, dtype, D, causal, m
     tdt = inputs["q"].dtype
     inputs["q"], inputs["k"] = q.to(tdt), k.to(tdt)
     full_parity(w, backward=False, inputs=inputs)
+
+
+# ------------------------------------------------------------------ query offsets (KV cache)
+
+OFFSET_SHAPES = [(70, 333, 263), (129, 300, 40), (1, 300, 299), (200, 150, 0), (33, 64, 7)]
+
+
+def offset_parity(dtype, D, causal, mod, mask, Sq, Skv, off, wid):
+    """Forward and backward with query row i at key position i + off, every
+    output element against the oracle with the same offset."""
+    w = small(dtype, D, False, mod, mask, Sq=Sq, Skv=Skv, B=1, H=2, wid=wid)
+    inputs = w.make()
+    say(f"[offset] {dtype} D{D} causal={causal} mod={mod} mask={mask} Sq{Sq} Skv{Skv} off{off}")
+    dev = to_dev(inputs)
+    kw = dict(causal=causal, score_mod={W.MOD_NONE: None, W.MOD_ALIBI: "alibi", W.MOD_CHECKERBOARD: "checkerboard"}[mod],
+              scale=w.scale, key_mask=dev.get("key_mask"), q_offset=off)
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+    torch.cuda.synchronize()
+    okw = dict(scale=w.scale, causal=causal, mod=mod, q_offset=off,
+               key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+    o_r, lse_r = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
+    dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
+    check("o", out, o_r, dtype, "o", strict=False)
+    check_lse(lse, lse_r)
+    check("dq", dq, dq_r, dtype, "grad", strict=False)
+    check("dk", dk, dk_r, dtype, "grad", strict=False)
+    check("dv", dv, dv_r, dtype, "grad", strict=False)
+
+
+@pytest.mark.parametrize("Sq,Skv,off", OFFSET_SHAPES)
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("causal,mod,mask", [(True, W.MOD_ALIBI, False), (True, W.MOD_CHECKERBOARD, True),
+                                             (True, W.MOD_NONE, False), (False, W.MOD_ALIBI, True),
+                                             (False, W.MOD_CHECKERBOARD, False)])
+def test_query_offset(gpu_lib, dtype, D, causal, mod, mask, Sq, Skv, off):
+    offset_parity(dtype, D, causal, mod, mask, Sq, Skv, off, wid=130)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64), ("f32", 128), ("f32", 512)])
+def test_query_offset_other_instances(gpu_lib, dtype, D):
+    offset_parity(dtype, D, True, W.MOD_CHECKERBOARD, False, 45, 190, 145, wid=131)
+    offset_parity(dtype, D, True, W.MOD_ALIBI, True, 64, 129, 65, wid=132)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("mod", [W.MOD_NONE, W.MOD_ALIBI, W.MOD_CHECKERBOARD])
+@pytest.mark.parametrize("off", [0, 1000, 4099])
+def test_decode_with_offset(gpu_lib, dtype, mod, off):
+    """Decode of the query at position off: non-causal (score_mod at that
+    position) and causal (keys 0 .. off only)."""
+    Skv, D = 4100, 64
+    w = W.Workload(f"decode offset {dtype}", 133, 2, 3, 1, Skv, D, dtype, mod=mod, backward=False)
+    x = w.make()
+    dev = to_dev(x)
+    name = {W.MOD_NONE: None, W.MOD_ALIBI: "alibi", W.MOD_CHECKERBOARD: "checkerboard"}[mod]
+    for causal in (False, True):
+        say(f"[decode offset] {dtype} mod={mod} off={off} causal={causal}")
+        out, lse = fa.decode(dev["q"], dev["k"], dev["v"], score_mod=name, scale=w.scale, q_offset=off, causal=causal)
+        torch.cuda.synchronize()
+        o_r, lse_r = oracle.decode(x["q"], x["k"], x["v"], scale=w.scale, mod=mod, q_offset=off, causal=causal)
+        check("o", out, o_r, dtype, "o")
+        check_lse(lse, lse_r)

@@ -43,8 +43,10 @@ def _stream(t: torch.Tensor):
 def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
             key_mask: Optional[torch.Tensor] = None, score_mod: Optional[str] = None,
             scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
-            checker: Tuple[float, float] = (0.5, -0.5)) -> _lib.FaProblem:
-    """The C-ABI problem descriptor for these tensors."""
+            checker: Tuple[float, float] = (0.5, -0.5), q_offset: int = 0) -> _lib.FaProblem:
+    """The C-ABI problem descriptor for these tensors.  q_offset is the
+    position of query row 0 among the keys (0 for self-attention; the number
+    of cached keys before the first query with a KV cache)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be (batch, heads, seq, head_dim)")
     if q.dtype not in _DTYPE:
@@ -61,6 +63,7 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     p.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
     p.checker_even, p.checker_odd = float(checker[0]), float(checker[1])
     p.key_mask = None if key_mask is None else key_mask.data_ptr()
+    p.q_offset = int(q_offset)
     return p
 
 
@@ -82,12 +85,12 @@ def _mask_u8(key_mask):
 
 
 def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-            checker=(0.5, -0.5), out=None, lse=None):
+            checker=(0.5, -0.5), q_offset=0, out=None, lse=None):
     """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     lib = _lib.load()
@@ -103,7 +106,7 @@ def backward_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
-             alibi_slopes=None, checker=(0.5, -0.5), workspace=None, grads=None, which="all"):
+             alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, workspace=None, grads=None, which="all"):
     """Gradients (dq, dk, dv) of sum(dout * out).
 
     which="dq" runs only the query pass (dk, dv come back as None), "dkdv"
@@ -113,7 +116,7 @@ def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     need = backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -135,13 +138,14 @@ def decode_workspace_bytes(p: _lib.FaProblem) -> int:
     return int(n.value)
 
 
-def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5),
-           workspace=None, out=None, lse=None):
-    """Single-query attention (seq_q == 1), split over the key axis."""
+def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0,
+           causal=False, workspace=None, out=None, lse=None):
+    """Single-query attention (seq_q == 1, at position q_offset), split over
+    the key axis.  With causal=True only keys 0 .. q_offset count."""
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, key_mask, alibi_slopes)
-    p = problem(q, k, causal=False, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     need = decode_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -168,23 +172,23 @@ def _plan(fn, name, args, keep):
 
 
 def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
-                 alibi_slopes=None, checker=(0.5, -0.5)):
+                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0):
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
     return _plan(lib.fa_forward, "fa_forward", args, (p, q, k, v, out, lse, key_mask, alibi_slopes))
 
 
 def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,
-                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5)):
+                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0):
     """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
@@ -193,11 +197,11 @@ def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=Fals
 
 
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-                checker=(0.5, -0.5)):
+                checker=(0.5, -0.5), q_offset=0, causal=False):
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes)
-    p = problem(q, k, causal=False, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
             _stream(q))

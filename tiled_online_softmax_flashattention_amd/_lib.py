@@ -26,7 +26,7 @@ class FaProblem(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
         ("mod_kind", ctypes.c_int32), ("alibi_slopes", _c_void_p),
         ("checker_even", ctypes.c_float), ("checker_odd", ctypes.c_float),
-        ("key_mask", _c_void_p),
+        ("key_mask", _c_void_p), ("q_offset", ctypes.c_int64),
     ]
 
 

@@ -34,12 +34,13 @@ fa_status validate_problem(const fa_problem* p) {
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARGUMENT;
   if (p->mod_kind == FA_MOD_CHECKERBOARD && (!isfinite(p->checker_even) || !isfinite(p->checker_odd)))
     return FA_ERR_INVALID_ARGUMENT;
-  if (p->causal && p->seq_q != p->seq_kv) return FA_ERR_INVALID_ARGUMENT;
+  if (p->q_offset < 0) return FA_ERR_INVALID_ARGUMENT;
   if (p->alibi_slopes && ((uintptr_t)p->alibi_slopes & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 32-bit per (batch, head) slice
   if (p->batch * p->heads > kMaxI32 / 8) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;
+  if (p->q_offset > kMaxI32 - p->seq_q) return FA_ERR_UNSUPPORTED;
   if (p->batch > kMaxI32 / p->seq_kv) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -69,6 +70,7 @@ fa::AttnArgs make_args(const fa_problem* p) {
   a.even_log2 = p->checker_even * fa::kLog2e;
   a.odd_log2 = p->checker_odd * fa::kLog2e;
   a.causal = p->causal;
+  a.q_off = (int)p->q_offset;
   return a;
 }
 
@@ -87,9 +89,15 @@ BwdLayout bwd_layout(const fa_problem* p) {
   return l;
 }
 
+// Keys a decode query sees: all of them, or with causal only 0 .. q_offset.
+int decode_kv_len(const fa_problem* p) {
+  const int64_t n = p->causal ? (p->q_offset + 1 < p->seq_kv ? p->q_offset + 1 : p->seq_kv) : p->seq_kv;
+  return (int)n;
+}
+
 size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
   const int BH = (int)(p->batch * p->heads);
-  *n_split = fa::decode_choose_split(BH, (int)p->seq_kv, chunk);
+  *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
   return round_up((size_t)BH * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float), 256);
 }
 
@@ -182,7 +190,7 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
   if (!bytes) return FA_ERR_INVALID_ARGUMENT;
-  if (p->seq_q != 1 || p->causal) return FA_ERR_INVALID_ARGUMENT;
+  if (p->seq_q != 1) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   int n_split, chunk;
   *bytes = decode_ws(p, &n_split, &chunk);
@@ -193,7 +201,7 @@ fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const voi
                     void* workspace, size_t workspace_bytes, void* stream) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
-  if (p->seq_q != 1 || p->causal) return FA_ERR_INVALID_ARGUMENT;
+  if (p->seq_q != 1) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
   if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;

@@ -184,9 +184,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
   f32x16 cinit = zero16();
   if constexpr (MOD == MOD_CHECKERBOARD) {
-    // query tiles start at even positions, so register r holds a query of parity (r & 1)
+    // query tiles start at even rows, so register r holds a query at a position of parity ((r + q_off) & 1)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = (((kj + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
+    for (int r = 0; r < 16; ++r) cinit[r] = (((kj + r + a.q_off) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
   f32x16 dk[DT], dv[DT];
@@ -196,7 +196,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     dv[dt] = zero16();
   }
 
-  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  const int off = a.q_off;            // query row q sits at key position q + off
+  const int qt0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
 
   // Direct loads of query tile it.  Rows past seq_q are clamped to the last
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   // Queries 32mt .. 32mt+31 of tile it.
   auto half = [&](int it, int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD) __attribute__((always_inline)) {
     const int qs = it * BQ + 32 * mt;   // first query of the half
-    if (CAUSAL && qs + 31 < kw) return;   // every query precedes every key of this wave
+    if (CAUSAL && qs + off + 31 < kw) return;   // every query precedes every key of this wave
 
     // S' = Q K^T + C and dP = dO V^T, queries as rows
     f32x16 sv = cinit, dpv = zero16();
@@ -228,16 +229,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       }
     }
     // P = 0 for queries before the key (causal) and past seq_q, only on such halves
-    if (__builtin_amdgcn_ballot_w64((CAUSAL && qs < kj) || qs + 31 >= Sq) != 0) {
+    if (__builtin_amdgcn_ballot_w64((CAUSAL && qs + off < kj) || qs + 31 >= Sq) != 0) {
       const int ql = qs + 4 * hi;   // query of register r: ql + 8 (r / 4) + r % 4
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = ql + 8 * (r >> 2) + (r & 3);
-        if ((CAUSAL && q < kj) || q >= Sq) sv[r] = kNegInf;
+        if ((CAUSAL && q + off < kj) || q >= Sq) sv[r] = kNegInf;
       }
     }
     float lb = key_ok ? 0.f : kNegInf;
-    if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ) : kNegInf;
+    if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ - off) : kNegInf;
     const float* lrow = sL + 32 * mt + 4 * hi;
     const float* drow = sD + 32 * mt + 4 * hi;
 #pragma unroll
@@ -336,6 +337,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int q0 = qb * BM;
   const int qw = q0 + 32 * wave;
   const int qi = qw + l32;
+  const int qwp = qw + a.q_off, qpos = qi + a.q_off;   // positions among the keys
   const float c = a.scale_log2;
   const float inv_scale = 1.0f / a.scale;
 
@@ -391,14 +393,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   }
   if constexpr (MOD == MOD_CHECKERBOARD && !MASK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = (((qi + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
+    for (int r = 0; r < 16; ++r) cinit[r] = (((qpos + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
 
-  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
 
   // Key-mask row: one byte per key, converted to an additive row in LDS.
@@ -429,12 +431,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   // Keys 32t .. 32t+31 of tile n.
   auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
     const int k0 = n * BN + 32 * t;   // first key of the half
-    if (CAUSAL && k0 > qw + 31) return;
+    if (CAUSAL && k0 > qwp + 31) return;
 
     // S'^T = K Q^T + C and dP^T = V dO^T, keys as rows
     f32x16 s = cinit, dp = zero16();
     if constexpr (MASK) {
-      const float* row = sB + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+      const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 m4 = *(const f32x4*)(row + 8 * u);
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     // scores past the diagonal or past seq_kv: -inf (only on such halves)
     {
       int lim = 1 << 30;
-      if (CAUSAL && k0 + 31 > qw) lim = qi - k0;
+      if (CAUSAL && k0 + 31 > qwp) lim = qpos - k0;
       if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
       if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
         const int lim_l = lim - 4 * hi;
@@ -477,7 +479,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     }
 
     float nb = -lse2;
-    if constexpr (MOD == MOD_ALIBI) nb = slope2 * (float)(k0 - qi) - lse2;
+    if constexpr (MOD == MOD_ALIBI) nb = slope2 * (float)(k0 - qpos) - lse2;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = exp2_hw(fmaf(s[r], c, nb));

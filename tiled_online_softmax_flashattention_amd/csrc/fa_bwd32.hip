@@ -114,7 +114,8 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
     dv[dt] = zero16();
   }
 
-  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  const int off = a.q_off;   // query row q sits at key position q + off
+  const int qt0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
   for (int it = qt0; it < nqt; ++it) {
     const int q0 = it * BQ;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
       sDl[tid] = ok ? a.delta[(size_t)bh * Sq + q0 + tid] : 0.f;
     }
     __syncthreads();
-    if (DS == 1 && CAUSAL && q0 + BQ - 1 < kw) continue;
+    if (DS == 1 && CAUSAL && q0 + off + BQ - 1 < kw) continue;
 
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
     const float* qrow = sQ + l32 * P + e * DSL + hi * HS;
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
       dp = slice_sum<DS>(dp, sS, wave, g, lane);
     }
 
-    const bool diag = CAUSAL && (q0 < kw + 31);
+    const bool diag = CAUSAL && (q0 + off < kw + 31);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const f32x4 l4 = *(const f32x4*)&sL[8 * u + 4 * hi];
@@ -161,11 +162,11 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
         const int r = 4 * u + c;
         const int qi = q0 + acc_row(r, hi);
         float x = s[r] * a.scale_log2;
-        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi);
-        if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cbo : cbe;
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi - off);
+        if constexpr (MOD == MOD_CHECKERBOARD) x += ((r + off) & 1) ? cbo : cbe;
         float p = exp2_hw(x - l4[c]);
         if (!key_ok) p = 0.f;
-        if (diag && kj > qi) p = 0.f;
+        if (diag && kj > qi + off) p = 0.f;
         s[r] = p;
         dp[r] = p * (dp[r] - d4[c]);
       }
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
   const int q0 = qb * BM;
   const int qw = q0 + 32 * g;
   const int qi = qw + l32;
+  const int qwp = qw + a.q_off, qpos = qi + a.q_off;   // positions among the keys
 
   const float* Qg = (const float*)a.q + (size_t)bh * Sq * D;
   const float* dOg = (const float*)a.dout + (size_t)bh * Sq * D;
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
   float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
   if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
   if constexpr (MOD == MOD_CHECKERBOARD) {
-    const bool qeven = (qi & 1) == 0;
+    const bool qeven = (qpos & 1) == 0;
     cb0 = qeven ? a.even_log2 : a.odd_log2;
     cb1 = qeven ? a.odd_log2 : a.even_log2;
   }
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
 
-  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = j * BN;
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
     }
     __syncthreads();
-    if (DS == 1 && CAUSAL && kv0 > qw + 31) continue;
+    if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
 
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
     const float* krow = sK + l32 * P + e * DSL + hi * HS;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
       dp = slice_sum<DS>(dp, sS, wave, g, lane);
     }
 
-    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
+    const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);
     const bool tail = kv0 + BN > Skv;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
         const int r = 4 * u + c;
         const int kv = kv0 + acc_row(r, hi);
         float x = s[r] * a.scale_log2;
-        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qpos);
         if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
         float p = exp2_hw(x - lse2);
         if constexpr (MASK) {
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
         } else {
           if (tail && kv >= Skv) p = 0.f;
         }
-        if (diag && kv > qi) p = 0.f;
+        if (diag && kv > qpos) p = 0.f;
         dp[r] = p * (dp[r] - delta);
       }
     }

@@ -251,6 +251,7 @@ struct AttnArgs {
   float even_nat;      // checkerboard bias, natural units
   float odd_nat;
   int causal;
+  int q_off;           // position of query row 0 among the keys
   int n_qblocks;
   int n_split;         // decode: number of key chunks
   int chunk;           // decode: keys per chunk

@@ -81,8 +81,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
   const int bh = blockIdx.x / a.n_split;
   const int b = bh / a.H, h = bh - b * a.H;
   const int Skv = a.Skv;
+  // causal: only keys 0 .. q_off exist for the query (the split covers just those)
+  const int kv_len = a.causal ? min(Skv, a.q_off + 1) : Skv;
   const int c0 = split * a.chunk;
-  const int c1 = min(Skv, c0 + a.chunk);
+  const int c1 = min(kv_len, c0 + a.chunk);
 
   const char* Kg = (const char*)a.k + ((size_t)bh * Skv * D) * ES + sub * 16;
   const char* Vg = (const char*)a.v + ((size_t)bh * Skv * D) * ES + sub * 16;
@@ -128,8 +130,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 #pragma unroll
       for (int w = 1; w < LPK; w <<= 1) d += __shfl_xor(d, w);
       const int kv = base + u * KPB;
-      if constexpr (MOD == MOD_ALIBI) d += slope2 * (float)kv;  // -slope * (0 - kv)
-      if constexpr (MOD == MOD_CHECKERBOARD) d += (kv & 1) ? a.odd_log2 : a.even_log2;
+      if constexpr (MOD == MOD_ALIBI) d += slope2 * (float)(kv - a.q_off);  // -slope * (q_off - kv)
+      if constexpr (MOD == MOD_CHECKERBOARD) d += ((kv + a.q_off) & 1) ? a.odd_log2 : a.even_log2;
       bool ok = kv < c1;
       if constexpr (MASK) ok = ok && mrow[min(kv, c1 - 1)] != 0;
       t[u] = ok ? d : kNegInf;

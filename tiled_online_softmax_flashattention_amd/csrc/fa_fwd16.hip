@@ -80,6 +80,8 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   const int q0 = qb * BM;
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
+  // positions among the keys (query row 0 sits at key position q_off)
+  const int qwp = qw + a.q_off, qpos = qi + a.q_off;
   const float c = a.scale_log2;
   const float inv_scale = 1.0f / a.scale;
 
@@ -109,12 +111,12 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     for (int r = 0; r < 16; ++r) cinit[r] = slope * inv_scale * (float)acc_row(r, hi);
   }
   if constexpr (MOD == MOD_CHECKERBOARD && !MASK) {
-    // register r holds a key of parity (r & 1); (qi + kv) is even when the parities agree
+    // register r holds a key of parity (r & 1); (qpos + kv) is even when the parities agree
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = (((qi + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
+    for (int r = 0; r < 16; ++r) cinit[r] = (((qpos + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
-  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
   // Causal: the diagonal tile first, then towards key 0.  ALiBi grows with the
   // key index, so its largest scores also come first when the tiles are
@@ -171,7 +173,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   auto scores = [&](int t, int k0, const uint16_t* sK, const float* sB) __attribute__((always_inline)) {
     f32x16 s = cinit;
     if constexpr (MASK) {
-      const float* row = sB + ((qi & 1) ? BN : 0) + 32 * t + 4 * hi;
+      const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 m4 = *(const f32x4*)(row + 8 * u);
@@ -192,10 +194,10 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, QS, 0);
     }
     // the diagonal and ragged-tail conditions are uniform over the wave
-    const bool diag = CAUSAL && k0 + 31 > qw;
+    const bool diag = CAUSAL && k0 + 31 > qwp;
     const bool tail = !MASK && k0 + 32 > Skv;
     if (diag || tail) {
-      int lim = diag ? qi - k0 : (1 << 30);   // last allowed key position inside the half
+      int lim = diag ? qpos - k0 : (1 << 30);   // last allowed key position inside the half
       if (tail) lim = min(lim, Skv - 1 - k0);
       const int lim_l = lim - 4 * hi;
 #pragma unroll
@@ -210,12 +212,12 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
   auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
     const int k0 = kv_of(n) + 32 * t;   // first key of the half
-    if (CAUSAL && k0 > qw + 31) return;   // every key follows every query of this wave
+    if (CAUSAL && k0 > qwp + 31) return;   // every key follows every query of this wave
 
     f32x16 s = scores(t, k0, sK, sB);
     // per-lane exponent offset (ALiBi: bias of the half's first key)
     float add = 0.f;
-    if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qi);
+    if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qpos);
 
     // Fast path: exponentials against the running max as it stands, valid
     // when every lane has one (have_max, uniform) and no lane's sum over the

@@ -53,6 +53,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   const int q0 = qb * BM;
   const int qw = q0 + 32 * g;
   const int qi = qw + l32;
+  const int qwp = qw + a.q_off, qpos = qi + a.q_off;   // positions among the keys
 
   const float* Qg = (const float*)a.q + (size_t)bh * Sq * D;
   const float* Kg = (const float*)a.k + (size_t)bh * Skv * D;
@@ -74,12 +75,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   float slope2 = 0.f, cb0 = 0.f, cb1 = 0.f;
   if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
   if constexpr (MOD == MOD_CHECKERBOARD) {
-    const bool qeven = (qi & 1) == 0;
+    const bool qeven = (qpos & 1) == 0;
     cb0 = qeven ? a.even_log2 : a.odd_log2;
     cb1 = qeven ? a.odd_log2 : a.even_log2;
   }
 
-  const int kv_end = CAUSAL ? min(Skv, q0 + BM) : Skv;
+  const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   const int ntiles = (kv_end + BN - 1) / BN;
 
   float m_run = kNegInf, l_run = 0.f;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
     }
     __syncthreads();
-    if (DS == 1 && CAUSAL && kv0 > qw + 31) continue;
+    if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
 
     f32x16 s0 = zero16(), s1 = zero16();
     const float* krow = sK + l32 * P + e * DSL + hi * HS;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
       }
     }
 
-    const bool diag = CAUSAL && (kv0 + BN - 1 > qw);
+    const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);
     const bool tail = kv0 + BN > Skv;
     float mx = kNegInf;
 #pragma unroll
@@ -140,14 +141,14 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
         const int r = 4 * u + c;
         const int kv = kv0 + acc_row(r, hi);
         float x = s[r] * a.scale_log2;
-        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qi);
+        if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qpos);
         if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
         if constexpr (MASK) {
           if (((mw >> (8 * c)) & 0xffu) == 0u) x = kNegInf;
         } else {
           if (tail && kv >= Skv) x = kNegInf;
         }
-        if (diag && kv > qi) x = kNegInf;
+        if (diag && kv > qpos) x = kNegInf;
         s[r] = x;
         mx = fmaxf(mx, x);
       }
