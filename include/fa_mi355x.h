@@ -128,15 +128,17 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Bytes of device workspace fa_decode needs for problem p (seq_q must be 1). */
+/* Bytes of device workspace fa_decode needs for problem p (1 <= seq_q <= 64). */
 fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
 
-/* Decode: one query per (batch, head) (seq_q == 1, at position q_offset; with
- * causal only keys 0 .. q_offset count) against seq_kv keys, split over the
- * key axis into chunks whose
- * partial (max, sum, accumulator) are merged exactly.  The flaxattention page
- * (decoding benchmark and TODO list) singles this case out.  f16, bf16 and
- * f32 with head_dim 64 or 128.  Same outputs as fa_forward at seq_q = 1. */
+/* Decode: a short block of queries (1 <= seq_q <= 64, query row i at key
+ * position q_offset + i; with causal only keys up to that position count)
+ * against seq_kv keys, split over the key axis into chunks whose partial
+ * (max, sum, accumulator) are merged exactly.  The flaxattention page
+ * (decoding benchmark and TODO list) singles this case out.  seq_q == 1 runs a
+ * streaming kernel (one group of lanes per key); seq_q > 1 runs the 16-bit
+ * forward kernel on each key chunk (fp32: the forward, unsplit).  f16, bf16 and
+ * f32 with head_dim 64 or 128.  Same outputs as fa_forward. */
 fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);

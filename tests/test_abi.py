@@ -139,10 +139,12 @@ def test_backward_workspace_rules():
 def test_decode_rules():
     lib = _lib.load()
     n = ctypes.c_size_t(0)
-    assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=2, seq_kv=4096)), ctypes.byref(n)) == INVALID
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=65, seq_kv=4096)), ctypes.byref(n)) == INVALID
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=64, seq_kv=4096)), ctypes.byref(n)) == _lib.FA_OK
+    assert n.value >= 2 * 4 * 64 * (64 + 2) * 4   # a partial row per (batch, head, query) and key chunk
     p = prob(seq_q=1, seq_kv=32768)
     assert lib.fa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.FA_OK
     assert n.value > 0 and n.value % 256 == 0
     assert dec(p, ws_bytes=n.value - 1) == WS
-    assert dec(prob(seq_q=2)) == INVALID
+    assert dec(prob(seq_q=65)) == INVALID
     assert dec(prob(seq_q=1, head_dim=512, dtype=_lib.FA_F32)) == UNSUP

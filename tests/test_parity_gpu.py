@@ -349,3 +349,32 @@ def test_decode_with_offset(gpu_lib, dtype, mod, off):
         o_r, lse_r = oracle.decode(x["q"], x["k"], x["v"], scale=w.scale, mod=mod, q_offset=off, causal=causal)
         check("o", out, o_r, dtype, "o")
         check_lse(lse, lse_r)
+
+
+# ------------------------------------------------------------------ short query blocks (split over keys)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("Sq,Skv", [(2, 300), (16, 5000), (33, 4100), (64, 700)])
+@pytest.mark.parametrize("causal,mod,mask", [(True, W.MOD_ALIBI, False), (True, W.MOD_NONE, True),
+                                             (False, W.MOD_CHECKERBOARD, True), (False, W.MOD_NONE, False)])
+def test_decode_short_query_block(gpu_lib, dtype, D, Sq, Skv, causal, mod, mask):
+    """1 < seq_q <= 64 through fa_decode (the forward split over key chunks
+    plus the exact merge), queries after a KV cache (q_offset = seq_kv -
+    seq_q), against the oracle and against fa_forward."""
+    off = Skv - Sq
+    w = small(dtype, D, False, mod, mask, Sq=Sq, Skv=Skv, B=2, H=3, wid=140)
+    x = w.make(with_dout=False)
+    dev = to_dev(x)
+    name = {W.MOD_NONE: None, W.MOD_ALIBI: "alibi", W.MOD_CHECKERBOARD: "checkerboard"}[mod]
+    kw = dict(score_mod=name, scale=w.scale, key_mask=dev.get("key_mask"), q_offset=off, causal=causal)
+    say(f"[short block] {dtype} D{D} Sq{Sq} Skv{Skv} causal={causal} mod={mod} mask={mask}")
+    out, lse = fa.decode(dev["q"], dev["k"], dev["v"], **kw)
+    out_f, lse_f = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
+    torch.cuda.synchronize()
+    o_r, lse_r = oracle.forward(x["q"], x["k"], x["v"], scale=w.scale, causal=causal, mod=mod, q_offset=off,
+                                key_mask=None if x.get("key_mask") is None else x["key_mask"].numpy())
+    check("o", out, o_r, dtype, "o")
+    check_lse(lse, lse_r)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert (out.float() - out_f.float()).abs().max().item() <= tol * max(1.0, out_f.float().abs().max().item())

@@ -140,8 +140,9 @@ def decode_workspace_bytes(p: _lib.FaProblem) -> int:
 
 def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0,
            causal=False, workspace=None, out=None, lse=None):
-    """Single-query attention (seq_q == 1, at position q_offset), split over
-    the key axis.  With causal=True only keys 0 .. q_offset count."""
+    """Attention for a short query block (1 <= seq_q <= 64, row i at key
+    position q_offset + i), split over the key axis.  With causal=True a row
+    sees keys up to its position only."""
     key_mask = _mask_u8(key_mask)
     _check_tensors(q, k, v, key_mask, alibi_slopes)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,

@@ -89,16 +89,31 @@ BwdLayout bwd_layout(const fa_problem* p) {
   return l;
 }
 
-// Keys a decode query sees: all of them, or with causal only 0 .. q_offset.
+constexpr int64_t kMaxDecodeQ = 64;   // longest query block fa_decode takes
+
+// Keys the decode queries see: all of them, or with causal only keys up to
+// the last query's position.
 int decode_kv_len(const fa_problem* p) {
-  const int64_t n = p->causal ? (p->q_offset + 1 < p->seq_kv ? p->q_offset + 1 : p->seq_kv) : p->seq_kv;
+  const int64_t last = p->q_offset + p->seq_q;   // last query position + 1
+  const int64_t n = p->causal ? (last < p->seq_kv ? last : p->seq_kv) : p->seq_kv;
   return (int)n;
 }
 
+// Split of the key axis and workspace bytes (one (D + 2)-float partial per
+// query row and chunk).  fp32 query blocks (seq_q > 1) run the forward
+// unsplit and need no workspace.
 size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
   const int BH = (int)(p->batch * p->heads);
+  if (p->seq_q > 1 && p->dtype == FA_F32) {
+    *n_split = 1;
+    *chunk = (int)p->seq_kv;
+    return 256;
+  }
   *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
-  return round_up((size_t)BH * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float), 256);
+  if (p->seq_q > 1) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
+  *n_split = (decode_kv_len(p) + *chunk - 1) / *chunk;
+  return round_up((size_t)BH * (size_t)p->seq_q * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float),
+                  256);
 }
 
 }  // namespace
@@ -190,7 +205,7 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
   if (!bytes) return FA_ERR_INVALID_ARGUMENT;
-  if (p->seq_q != 1) return FA_ERR_INVALID_ARGUMENT;
+  if (p->seq_q > kMaxDecodeQ) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   int n_split, chunk;
   *bytes = decode_ws(p, &n_split, &chunk);
@@ -201,7 +216,7 @@ fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const voi
                     void* workspace, size_t workspace_bytes, void* stream) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
-  if (p->seq_q != 1) return FA_ERR_INVALID_ARGUMENT;
+  if (p->seq_q > kMaxDecodeQ) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
   if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
@@ -219,8 +234,21 @@ fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const voi
   a.partial = (float*)workspace;
   a.n_split = n_split;
   a.chunk = chunk;
-  hipError_t err = fa::launch_decode(a, p->dtype, (int)p->head_dim, p->mod_kind, p->key_mask != nullptr,
-                                     (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  const int D = (int)p->head_dim;
+  const bool mask = p->key_mask != nullptr, causal = p->causal != 0;
+  hipError_t err;
+  if (p->seq_q == 1) {
+    err = fa::launch_decode(a, p->dtype, D, p->mod_kind, mask, st);
+  } else if (p->dtype == FA_F32) {   // short fp32 query block: the forward, unsplit
+    a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
+    err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st);
+  } else {   // short 16-bit query block: the forward split over the keys, then the merge
+    a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
+    err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
+    if (err == hipSuccess)
+      err = fa::launch_decode_merge(a, p->dtype, D, (int)(p->batch * p->heads * p->seq_q), st);
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 
 constexpr int kMaxSplit = 256;
 
-// One workgroup per (b, h).  The chunks' (max, sum) are read in parallel into
+// One workgroup per output row: (b, h) for decode, (b, h, query) for a query
+// block split over the key axis.  The chunks' (max, sum) are read in parallel into
 // LDS, the weights 2^(m_s - M) computed once, and every thread then issues
 // its accumulator loads for all chunks back to back (no serial chain of
 // dependent loads).
@@ -284,6 +285,19 @@ static hipError_t launch_decode_d(const AttnArgs& a, int mod, bool mask, hipStre
       return mask ? launch_decode_inst<T, D, MOD_CHECKERBOARD, true>(a, st) : launch_decode_inst<T, D, MOD_CHECKERBOARD, false>(a, st);
     default: return mask ? launch_decode_inst<T, D, MOD_NONE, true>(a, st) : launch_decode_inst<T, D, MOD_NONE, false>(a, st);
   }
+}
+
+template <class T>
+static hipError_t launch_merge_t(const AttnArgs& a, int D, int rows, hipStream_t st) {
+  if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<T, 64>), dim3((unsigned)rows), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3((unsigned)rows), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st) {
+  if (dtype == 0) return launch_merge_t<F32>(a, D, rows, st);
+  if (dtype == 2) return launch_merge_t<BF16>(a, D, rows, st);
+  return launch_merge_t<F16>(a, D, rows, st);
 }
 
 template <class T>

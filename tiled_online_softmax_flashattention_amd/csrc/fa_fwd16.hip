@@ -53,9 +53,12 @@ constexpr float kSumLimit = 32768.0f;   // a half's row sum above this forces a 
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// One 128-query block (qb) of one (batch, head) slice (bh).
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb) {
+// One 128-query block (qb) of one (batch, head) slice (bh).  With SPLIT the
+// block covers only key chunk `split` (a.chunk keys) and writes its
+// unnormalised partial (accumulator, running max, sum) to a.partial for the
+// exact merge of the decode path; otherwise it writes O and lse.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT>
+__device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb, const int split) {
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
@@ -116,13 +119,21 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     for (int r = 0; r < 16; ++r) cinit[r] = (((qpos + r) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
   }
 
-  const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  // causal: keys up to the block's last query position
+  const int kv_end = CAUSAL ? min(Skv, min(q0 + BM, Sq) + a.q_off) : Skv;
+  const int ntiles_all = (kv_end + BN - 1) / BN;
+  int t_lo = 0, t_hi = ntiles_all;   // tiles this workgroup visits
+  if constexpr (SPLIT) {
+    const int ct = a.chunk / BN;
+    t_lo = min(split * ct, ntiles_all);
+    t_hi = min(t_lo + ct, ntiles_all);
+  }
+  const int ntiles = t_hi - t_lo;
   // Causal: the diagonal tile first, then towards key 0.  ALiBi grows with the
   // key index, so its largest scores also come first when the tiles are
   // visited from the last one down, and the running max rarely moves.
   constexpr bool REV = CAUSAL || MOD == MOD_ALIBI;
-  auto kv_of = [&](int n) { return (REV ? ntiles - 1 - n : n) * BN; };
+  auto kv_of = [&](int n) { return (REV ? t_hi - 1 - n : t_lo + n) * BN; };
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
   // the last row (finite values whose scores are masked to -inf).
@@ -281,10 +292,12 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   };
 
   // Prologue: tile 0 (and its mask row) requested.
-  load_tile(kv_of(0), sK0, sV0);
-  load_m(kv_of(0));
-  store_m(sB0);
-  load_m(kv_of(min(1, ntiles - 1)));
+  if (ntiles > 0) {
+    load_tile(kv_of(0), sK0, sV0);
+    load_m(kv_of(0));
+    store_m(sB0);
+    load_m(kv_of(min(1, ntiles - 1)));
+  }
 
   // Tile n in buffers (n & 1); tile n+1 is requested into the other buffers
   // right after the barrier that retires tile n-1.
@@ -297,9 +310,11 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       store_m(sBn);
       load_m(kv_of(min(n + 2, ntiles - 1)));
     }
-    half(n, 0, sK, sV, sB);
-    __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: their registers are shared
-    half(n, 1, sK, sV, sB);
+    if (qw < Sq) {   // a wave past the last query only loads its share of the tiles
+      half(n, 0, sK, sV, sB);
+      __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: their registers are shared
+      half(n, 1, sK, sV, sB);
+    }
   };
 
   int n = 0;
@@ -310,6 +325,21 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   if (n < ntiles) tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
 
   const float l_tot = l_run + xor32(l_run);
+  if constexpr (SPLIT) {
+    if (qi < Sq) {
+      float* P = a.partial + (((size_t)bh * Sq + qi) * a.n_split + split) * (D + 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[32 * dt + 8 * (r >> 2) + 4 * hi + (r & 3)] = o[dt][r];   // rows are only 8-byte aligned
+      }
+      if (hi == 0) {
+        P[D] = l_tot > 0.f ? m_run : kNegInf;
+        P[D + 1] = l_tot;
+      }
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < Sq) {
     uint16_t* Og = (uint16_t*)a.o + ((size_t)bh * Sq + qi) * D;
@@ -335,40 +365,60 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_kernel(const AttnA
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int p = blockIdx.x / BH;
-  fwd16_block<T, D, MOD, CAUSAL, MASK>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, false>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p, 0);
+}
+
+// Split over the key axis (short query blocks against a long key sequence):
+// workgroup (bh, query block, key chunk), bh = blockIdx.x mod (batch * heads).
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_split_kernel(const AttnArgs a) {
+  const int BH = a.B * a.H;
+  const int bh = blockIdx.x % BH;
+  const int r = blockIdx.x / BH;
+  fwd16_block<T, D, MOD, CAUSAL, MASK, true>(a, bh, r / a.n_split, r % a.n_split);
+}
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st) {
+  const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H);
+  if (split)
+    hipLaunchKernelGGL((fwd16_split_kernel<T, D, MOD, CAUSAL, MASK>), dim3(blocks * (unsigned)a.n_split), dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, CAUSAL, MASK>), dim3(blocks), dim3(256), 0, st, a);
 }
 
 template <class T, int D, int MOD>
-static hipError_t launch_fwd16_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
-  const dim3 grid((unsigned)(a.n_qblocks * a.B * a.H)), block(256);
+static hipError_t launch_fwd16_mod(const AttnArgs& a, bool causal, bool mask, bool split, hipStream_t st) {
   if (causal) {
-    if (mask) hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, true, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, true, false>), grid, block, 0, st, a);
+    if (mask) launch_fwd16_inst<T, D, MOD, true, true>(a, split, st);
+    else launch_fwd16_inst<T, D, MOD, true, false>(a, split, st);
   } else {
-    if (mask) hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, false, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, false, false>), grid, block, 0, st, a);
+    if (mask) launch_fwd16_inst<T, D, MOD, false, true>(a, split, st);
+    else launch_fwd16_inst<T, D, MOD, false, false>(a, split, st);
   }
   return hipGetLastError();
 }
 
 template <class T, int D>
-static hipError_t launch_fwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
+static hipError_t launch_fwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool split, hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return launch_fwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, st);
-    case MOD_CHECKERBOARD: return launch_fwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, st);
-    default: return launch_fwd16_mod<T, D, MOD_NONE>(a, causal, mask, st);
+    case MOD_ALIBI: return launch_fwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, split, st);
+    case MOD_CHECKERBOARD: return launch_fwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, split, st);
+    default: return launch_fwd16_mod<T, D, MOD_NONE>(a, causal, mask, split, st);
   }
 }
 
 int fwd16_block_q(int) { return 128; }
 
-hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st) {
+hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st,
+                        bool split) {
   if (bf16) {
-    return D == 64 ? launch_fwd16_d<BF16, 64>(a, mod, causal, mask, st)
-                   : launch_fwd16_d<BF16, 128>(a, mod, causal, mask, st);
+    return D == 64 ? launch_fwd16_d<BF16, 64>(a, mod, causal, mask, split, st)
+                   : launch_fwd16_d<BF16, 128>(a, mod, causal, mask, split, st);
   }
-  return D == 64 ? launch_fwd16_d<F16, 64>(a, mod, causal, mask, st)
-                 : launch_fwd16_d<F16, 128>(a, mod, causal, mask, st);
+  return D == 64 ? launch_fwd16_d<F16, 64>(a, mod, causal, mask, split, st)
+                 : launch_fwd16_d<F16, 128>(a, mod, causal, mask, split, st);
 }
 
 }  // namespace fa

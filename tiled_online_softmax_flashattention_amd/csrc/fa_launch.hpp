@@ -7,10 +7,13 @@
 
 namespace fa {
 
-// 16-bit forward (f16 / bf16, head_dim 64 or 128).
+// 16-bit forward (f16 / bf16, head_dim 64 or 128).  With split, each query
+// block is split over a.n_split key chunks of a.chunk keys whose partials go
+// to a.partial (rows (bh, query) x chunks x (D + 2) floats) for
+// launch_decode_merge.
 int fwd16_block_q(int D);
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
-                        hipStream_t st);
+                        hipStream_t st, bool split = false);
 
 // fp32 forward (head_dim 64, 128 or 512).
 int fwd32_block_q(int D);
@@ -32,5 +35,7 @@ hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
 // Split-KV decode and the merge of the partial (max, sum, accumulator).
 int decode_choose_split(int BH, int Skv, int* chunk);
 hipError_t launch_decode(const AttnArgs& a, int dtype, int D, int mod, bool mask, hipStream_t st);
+// Merge of `rows` partial rows (a.n_split chunks each) into O and lse rows.
+hipError_t launch_decode_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st);
 
 }  // namespace fa
