@@ -147,7 +147,8 @@ def measured_traffic(kernel: str):
 
 def extra_workloads(fa, W, torch, reps: int) -> dict:
     """Forward and forward+backward times of the key-padding (bf16) and the
-    long-context (fp32, head_dim 512) workloads."""
+    long-context (fp32, head_dim 512) workloads, and a short query block
+    against a long KV cache (split over keys vs. the plain forward)."""
     res = {}
     for w, kw, peak in ((W.KEYPAD_BF16, dict(score_mod="checkerboard"), PEAK_F16_TFLOPS),
                         (W.LONG_F32, dict(causal=True), PEAK_F32_TFLOPS)):
@@ -172,6 +173,33 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
                        "peak_TFLOP/s": peak, "flop_convention": "causal pairs" if w.causal else "all pairs"}
         del dev, q, k, v, do, out, grads, ws
         torch.cuda.empty_cache()
+
+    # A block of 16 new queries after a 32752-key cache (fp16, causal, ALiBi):
+    # the key-split path of fa_decode against the plain forward; K/V copies
+    # are rotated so reads come from HBM.
+    B, H, Sq, Skv, D = 8, 8, 16, 32768, 64
+    log(f"[bench] extra: short query block {B}x{H}x{Sq} against {Skv} keys")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn(B, H, Sq, D, device="cuda", dtype=torch.float16, generator=gen)
+    kvs = [(torch.randn(B, H, Skv, D, device="cuda", dtype=torch.float16, generator=gen),
+            torch.randn(B, H, Skv, D, device="cuda", dtype=torch.float16, generator=gen)) for _ in range(2)]
+    kw = dict(causal=True, score_mod="alibi", q_offset=Skv - Sq)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.decode_workspace_bytes(fa.problem(q, kvs[0][0], **kw)), dtype=torch.uint8, device="cuda")
+    split = [fa.plan_decode(q, k, v, out, lse, ws, **kw) for k, v in kvs]
+    plain = [fa.plan_forward(q, k, v, out, lse, **kw) for k, v in kvs]
+    for f in split + plain:
+        f()
+    ms_s = time_calls(lambda i: split[i % 2](), max(reps, 4), torch)
+    ms_p = time_calls(lambda i: plain[i % 2](), max(reps, 4), torch)
+    nbytes = 2 * B * H * Skv * D * 2 + 2 * B * H * Sq * D * 2 + B * H * Sq * 4
+    res[f"short query block f16 causal ALiBi ({B},{H},{Sq},{D}) after {Skv - Sq} cached keys"] = {
+        "split_us": round(ms_s * 1e3, 2), "split_GB/s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
+        "split_frac_hbm_peak": round(nbytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "forward_unsplit_us": round(ms_p * 1e3, 2), "bytes": nbytes}
+    del q, kvs, out, lse, ws, split, plain
+    torch.cuda.empty_cache()
     return res
 
 
