@@ -24,6 +24,9 @@ What it computes (the definition the flash kernels reach up to rounding order):
   default; a KV cache of q_offset earlier keys otherwise: the flaxattention
   page's TODO list names decoding with a cache), and both the causal rule and
   the score_mod use that position.
+* block sparsity (the flaxattention page's block mask): with a boolean
+  block_mask (B, H, ceil(Sq/128), ceil(Skv/128)), pair (i, j) is also
+  allowed only when block (i // 128, j // 128) is set (query ROW i, key j).
 * a query row with no allowed key is an empty sum: O_i = 0, lse_i = -inf, and
   its gradients are zero.  (The pages leave this open; the attnax kernel's
   finite ``min`` fill would instead average V.)
@@ -102,6 +105,12 @@ def allowed_pairs(q_idx: np.ndarray, seq_kv: int, causal: bool,
     return ok
 
 
+def _block_allowed(block_mask, b: int, h: int, rows: np.ndarray, seq_kv: int) -> np.ndarray:
+    """Boolean (len(rows), seq_kv): block (row // 128, key // 128) is set."""
+    bm = np.asarray(block_mask, dtype=bool)[b, h]
+    return bm[(np.asarray(rows) // 128)[:, None], (np.arange(seq_kv) // 128)[None, :]]
+
+
 def _probabilities(qb: np.ndarray, kb: np.ndarray, scale: float, bias: np.ndarray,
                    ok: np.ndarray):
     """Scores, lse and P for one (batch, head) and a block of query rows."""
@@ -131,7 +140,7 @@ def _setup(q, k, v, rows, key_mask):
 
 def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
             mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-            rows: Optional[Sequence[int]] = None, q_offset: int = 0):
+            rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None):
     """Exact attention output and log-sum-exp.
 
     Returns ``(o, lse)``: o (B, H, R, D), lse (B, H, R) in fp64, where R are the
@@ -151,14 +160,15 @@ def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
         ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
         for h in range(H):
             bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
-            _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, ok)
+            okh = ok if block_mask is None else ok & _block_allowed(block_mask, b, h, rows, seq_kv)
+            _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, okh)
             o[b, h] = p @ v[b, h]
     return o, lse
 
 
 def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None,
              mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-             rows: Optional[Sequence[int]] = None, q_offset: int = 0):
+             rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None):
     """Analytic gradients of sum(dout * O) with respect to q, k and v.
 
     Returns ``(dq, dk, dv)``: dq (B, H, R, D) for the requested rows; dk and dv
@@ -181,7 +191,8 @@ def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None
         for h in range(H):
             bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
             qb, dob = q[b, h, rows], do[b, h, rows]
-            _, _, p = _probabilities(qb, k[b, h], scale, bias, ok)
+            okh = ok if block_mask is None else ok & _block_allowed(block_mask, b, h, rows, seq_kv)
+            _, _, p = _probabilities(qb, k[b, h], scale, bias, okh)
             dp = dob @ v[b, h].T
             d_row = (p * dp).sum(axis=1)
             ds = p * (dp - d_row[:, None])

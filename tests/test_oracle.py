@@ -364,6 +364,53 @@ def test_decode_with_offset_is_a_causal_row(mod):
         np.testing.assert_allclose(lsed[:, :, 0], lse[:, :, p], atol=1e-14)
 
 
+# --------------------------------------------------------------------------- block masks
+
+
+def _block_mask(B, H, Sq, Skv, seed):
+    """Random 128 x 128 block mask that keeps block (r, 0) for every row block."""
+    nq, nk = -(-Sq // 128), -(-Skv // 128)
+    bm = np.random.default_rng(seed).random((B, H, nq, nk)) < 0.5
+    bm[..., 0] = True
+    return bm
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", [(False, MOD_NONE, False), (True, MOD_ALIBI, False),
+                                                 (False, MOD_CHECKERBOARD, True), (True, MOD_NONE, True)])
+def test_block_mask_against_torch_sdpa(causal, mod, use_mask):
+    """The block mask removes whole 128 x 128 (query row, key) blocks; checked
+    against torch SDPA with the block mask expanded to elements."""
+    B, H, Sq, Skv, D = 1, 2, 300, 400, 8
+    q, k, v, do, km = _case(97, B=B, H=H, Sq=Sq, Skv=Skv, D=D, key_mask=use_mask)
+    bm = _block_mask(B, H, Sq, Skv, 98)
+    kw = dict(scale=0.35, causal=causal, key_mask=km, mod=mod, q_offset=Skv - Sq if causal else 0, block_mask=bm)
+    o, lse = oracle.forward(q, k, v, **kw)
+    dq, dk, dv = oracle.backward(q, k, v, do, **kw)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = _torch_bias(mod, B, H, Sq, Skv, causal, km, Skv - Sq if causal else 0)
+    elem = torch.from_numpy(bm).repeat_interleave(128, dim=2)[:, :, :Sq].repeat_interleave(128, dim=3)[..., :Skv]
+    mask = mask.masked_fill(~elem, float("-inf"))
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.35)
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-13)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+    s_ = torch.matmul(torch.from_numpy(q), torch.from_numpy(k).transpose(-1, -2)) * 0.35 + mask
+    np.testing.assert_allclose(lse, torch.logsumexp(s_, dim=-1).numpy(), atol=1e-12)
+
+
+def test_full_block_mask_changes_nothing():
+    q, k, v, do, _ = _case(99, B=1, H=2, Sq=200, Skv=260, D=4)
+    bm = np.ones((1, 2, 2, 3), dtype=bool)
+    for causal in (False, True):
+        kw = dict(scale=0.5, causal=causal, mod=MOD_ALIBI, q_offset=60 if causal else 0)
+        o, lse = oracle.forward(q, k, v, **kw)
+        o2, lse2 = oracle.forward(q, k, v, block_mask=bm, **kw)
+        np.testing.assert_array_equal(o, o2)
+        np.testing.assert_array_equal(lse, lse2)
+
+
 # --------------------------------------------------------------------------- row subsets
 
 
