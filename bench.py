@@ -200,6 +200,41 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
         "forward_unsplit_us": round(ms_p * 1e3, 2), "bytes": nbytes}
     del q, kvs, out, lse, ws, split, plain
     torch.cuda.empty_cache()
+
+    # Block sparsity: fp16 (8, 8, 8192, 64), causal, ALiBi, with a block mask
+    # of a sliding window of 8 blocks (1024 keys).  Flops count only the pairs
+    # the mask and the causal rule allow.
+    import numpy as np
+    B, H, S, D, win = 8, 8, 8192, 64, 8
+    w = W.Workload("block-sparse prefill", 8, B, H, S, S, D, "f16", causal=True, mod=W.MOD_ALIBI)
+    log(f"[bench] extra: block-sparse {B}x{H}x{S}x{D}, causal ALiBi, window of {win} blocks")
+    x = w.make()
+    q, k, v, do = (x[t].cuda() for t in ("q", "k", "v", "dout"))
+    bm = W.window_block_mask(B, H, S, S, win).cuda()
+    rows = np.arange(S)
+    bmh = bm[0, 0].cpu().numpy() != 0
+    pairs = B * H * int(sum(((np.arange(S)[None, :] <= rows[r0:r0 + 128, None])
+                             & bmh[r0 // 128][np.arange(S) // 128][None, :]).sum() for r0 in range(0, S, 128)))
+    kw = dict(causal=True, score_mod="alibi", block_mask=bm)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device="cuda")
+    run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
+    run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
+    dense_fwd = fa.plan_forward(q, k, v, out, lse, causal=True, score_mod="alibi")
+    run_fwd(); run_bwd(); dense_fwd()
+    ms_f = time_calls(lambda i: run_fwd(), reps, torch)
+    ms_fb = time_calls(lambda i: (run_fwd(), run_bwd()), reps, torch)
+    ms_dense = time_calls(lambda i: dense_fwd(), reps, torch)
+    res[f"block-sparse f16 causal ALiBi ({B},{H},{S},{D}), sliding window of {win} blocks"] = {
+        "forward_ms": round(ms_f, 4), "fwd_bwd_ms": round(ms_fb, 4), "allowed_pairs": pairs,
+        "forward_TFLOP/s": round(4.0 * D * pairs / ms_f / 1e9, 1),
+        "fwd_bwd_TFLOP/s": round(14.0 * D * pairs / ms_fb / 1e9, 1),
+        "dense_causal_forward_ms": round(ms_dense, 4), "peak_TFLOP/s": PEAK_F16_TFLOPS,
+        "flop_convention": "pairs allowed by the block mask and the causal rule"}
+    del q, k, v, do, out, lse, grads, ws, bm
+    torch.cuda.empty_cache()
     return res
 
 

@@ -25,6 +25,7 @@
  *     k, v, dk, dv              (batch, heads, seq_kv, head_dim)
  *     lse                       (batch, heads, seq_q)  float32, natural log
  *     key_mask                  (batch, seq_kv) uint8, nonzero = keep the key
+ *     block_mask                (batch, heads, ceil(seq_q/128), ceil(seq_kv/128)) uint8
  *   q, k, v, out, dout, dq, dk, dv all have the element type ``dtype``.
  * - Every pointer named as a tensor is a DEVICE pointer on the current HIP
  *   device, 16-byte aligned.  The ``fa_problem`` struct itself is a host
@@ -46,7 +47,9 @@
  * self-attention; the number of cached keys before the first query when
  * decoding or prefilling against a KV cache), j is the 0-based key position,
  * and the bias is NOT multiplied by scale.  Key j is allowed for query i when
- * key_mask[b][j] != 0 (or key_mask == NULL) and, if causal, j <= pos_i.
+ * key_mask[b][j] != 0 (or key_mask == NULL), if causal, j <= pos_i, and, with
+ * a block mask, block_mask[b][h][i / 128][j / 128] != 0 (query ROW i, not its
+ * position).
  * lse_i = log sum_{allowed j} exp(s_ij); out_i =
  * sum_{allowed j} exp(s_ij - lse_i) v_j.  A row with no allowed key gets
  * out_i = 0, lse_i = -inf and zero gradients.  Score, softmax and
@@ -63,7 +66,12 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
+
+/* Edge of the blocks of a block mask (query rows and keys), and the longest
+ * seq_q / seq_kv a call with a block mask takes. */
+#define FA_BLOCK_MASK_BLOCK 128
+#define FA_BLOCK_MASK_MAX_SEQ 131072
 
 typedef enum {
   FA_OK = 0,
@@ -94,6 +102,14 @@ typedef struct {
   float checker_odd;
   const uint8_t* key_mask;   /* device uint8 (batch, seq_kv), nonzero = keep; NULL = keep all */
   int64_t q_offset;          /* >= 0: position of query row 0 among the keys (0 = self-attention) */
+  /* Block sparsity (flaxattention page, "Example usage": create_block_mask
+   * over 128 x 128 blocks).  Device uint8 (batch, heads, ceil(seq_q / 128),
+   * ceil(seq_kv / 128)); byte (b, h, r, c) == 0 removes every pair of query
+   * rows 128r .. 128r+127 and keys 128c .. 128c+127, nonzero leaves the
+   * block's pairs to the other rules.  The kernels never load or compute a
+   * removed block.  NULL = no block mask.  Requires seq_q and seq_kv
+   * <= FA_BLOCK_MASK_MAX_SEQ (else FA_ERR_UNSUPPORTED). */
+  const uint8_t* block_mask;
 } fa_problem;
 
 /* Supported: dtype f16 or bf16 with head_dim 64 or 128; dtype f32 with

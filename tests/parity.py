@@ -65,8 +65,11 @@ def kw_of(w: W.Workload) -> dict:
 
 
 def oracle_kw(w: W.Workload, inputs: dict) -> dict:
-    return dict(scale=w.scale, causal=w.causal, mod=w.mod,
-                key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+    kw = dict(scale=w.scale, causal=w.causal, mod=w.mod,
+              key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+    if inputs.get("block_mask") is not None:
+        kw["block_mask"] = inputs["block_mask"].numpy() != 0
+    return kw
 
 
 def to_dev(inputs: dict) -> dict:
@@ -74,13 +77,15 @@ def to_dev(inputs: dict) -> dict:
 
 
 def run_forward(w: W.Workload, dev: dict):
-    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], key_mask=dev.get("key_mask"), **kw_of(w))
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], key_mask=dev.get("key_mask"),
+                          block_mask=dev.get("block_mask"), **kw_of(w))
     torch.cuda.synchronize()
     return out, lse
 
 
 def run_backward(w: W.Workload, dev: dict, out, lse, dout):
-    g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dout, key_mask=dev.get("key_mask"), **kw_of(w))
+    g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dout, key_mask=dev.get("key_mask"),
+                    block_mask=dev.get("block_mask"), **kw_of(w))
     torch.cuda.synchronize()
     return g
 
@@ -106,12 +111,13 @@ def full_parity(w: W.Workload, backward: bool = True, inputs=None, strict: bool 
     return res
 
 
-def sampled_parity(w: W.Workload, n_rows: int, backward: bool = True) -> dict:
+def sampled_parity(w: W.Workload, n_rows: int, backward: bool = True, block_mask=None) -> dict:
     """Large shapes: O, lse and dQ on sampled query rows; all dK, dV rows from
     a second backward whose dO is zero outside the sampled rows (exact, since
     the backward is linear in dO)."""
     say(f"[sampled] {w.name}: generating inputs")
     inputs = w.make(with_dout=backward)
+    inputs["block_mask"] = block_mask
     rows = W.sample_rows(w.seq_q, n_rows, w.workload_id)
     dev = to_dev(inputs)
     say(f"[sampled] {w.name}: forward on GPU")

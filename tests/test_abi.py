@@ -4,6 +4,7 @@ import ctypes
 import glob
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -41,10 +42,29 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == 2
+    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 3
     for s in range(5):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"
+
+
+def test_problem_struct_layout_matches_the_header(tmp_path):
+    """The ctypes view of fa_problem has the size and field offsets that a C
+    compiler gives the header's struct (and the header's constants agree)."""
+    fields = [f for f, _ in _lib.FaProblem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "fa_mi355x.h"\nint main(void) {\n'
+        '  printf("%zu %d %d %d\\n", sizeof(fa_problem), FA_ABI_VERSION, FA_BLOCK_MASK_BLOCK, FA_BLOCK_MASK_MAX_SEQ);\n'
+        + "".join(f'  printf("%zu\\n", offsetof(fa_problem, {f}));\n' for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    size, ver, blk, max_seq = (int(x) for x in out[:4])
+    assert size == ctypes.sizeof(_lib.FaProblem)
+    assert (ver, blk, max_seq) == (_lib.FA_ABI_VERSION, _lib.FA_BLOCK_MASK_BLOCK, _lib.FA_BLOCK_MASK_MAX_SEQ)
+    for f, off in zip(fields, out[4:]):
+        assert getattr(_lib.FaProblem, f).offset == int(off), f
 
 
 def prob(**kw):
@@ -148,3 +168,17 @@ def test_decode_rules():
     assert dec(p, ws_bytes=n.value - 1) == WS
     assert dec(prob(seq_q=65)) == INVALID
     assert dec(prob(seq_q=1, head_dim=512, dtype=_lib.FA_F32)) == UNSUP
+
+
+def test_block_mask_length_limit():
+    """A block mask takes sequences up to FA_BLOCK_MASK_MAX_SEQ (tile lists in
+    LDS); without one the same lengths pass validation."""
+    m = _lib.FA_BLOCK_MASK_MAX_SEQ
+    bm = A[9]
+    assert fwd(prob(seq_q=m + 1, seq_kv=64, block_mask=bm)) == UNSUP
+    assert fwd(prob(seq_q=64, seq_kv=m + 1, block_mask=bm)) == UNSUP
+    assert bwd(prob(seq_q=m + 1, seq_kv=m + 1, block_mask=bm)) == UNSUP
+    assert dec(prob(seq_q=1, seq_kv=m + 1, block_mask=bm)) == UNSUP
+    # at the limit validation passes and the next check (a null tensor) fails
+    assert fwd(prob(seq_q=m, seq_kv=m, block_mask=bm), q=None) == INVALID
+    assert fwd(prob(seq_q=m + 1, seq_kv=64), q=None) == INVALID

@@ -11,7 +11,10 @@ is no CPU or PyTorch fallback, and a missing library raises.
 
 q, k, v: (batch, heads, seq, head_dim) contiguous cuda tensors of one dtype
 (float32, float16 or bfloat16); key_mask: (batch, seq_kv) uint8/bool,
-nonzero = keep; score_mod: None, "alibi" or "checkerboard".
+nonzero = keep; score_mod: None, "alibi" or "checkerboard"; block_mask:
+(batch, heads, ceil(seq_q/128), ceil(seq_kv/128)) uint8/bool, zero removes a
+128 x 128 block of (query row, key) pairs (``block_mask_shape`` gives the
+shape).
 """
 from __future__ import annotations
 
@@ -25,7 +28,7 @@ from . import _lib
 from ._lib import FaError
 
 __all__ = ["forward", "backward", "decode", "backward_workspace_bytes", "decode_workspace_bytes",
-           "FaError", "problem", "plan_forward", "plan_backward", "plan_decode"]
+           "FaError", "problem", "plan_forward", "plan_backward", "plan_decode", "block_mask_shape"]
 
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 _MOD = {None: _lib.FA_MOD_NONE, "none": _lib.FA_MOD_NONE, "alibi": _lib.FA_MOD_ALIBI,
@@ -40,15 +43,26 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def block_mask_shape(batch: int, heads: int, seq_q: int, seq_kv: int) -> Tuple[int, int, int, int]:
+    """Shape of a block mask: one byte per 128 x 128 block of (query row, key)."""
+    n = _lib.FA_BLOCK_MASK_BLOCK
+    return (batch, heads, -(-seq_q // n), -(-seq_kv // n))
+
+
 def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
             key_mask: Optional[torch.Tensor] = None, score_mod: Optional[str] = None,
             scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
-            checker: Tuple[float, float] = (0.5, -0.5), q_offset: int = 0) -> _lib.FaProblem:
+            checker: Tuple[float, float] = (0.5, -0.5), q_offset: int = 0,
+            block_mask: Optional[torch.Tensor] = None) -> _lib.FaProblem:
     """The C-ABI problem descriptor for these tensors.  q_offset is the
     position of query row 0 among the keys (0 for self-attention; the number
     of cached keys before the first query with a KV cache)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be (batch, heads, seq, head_dim)")
+    if block_mask is not None:
+        want = block_mask_shape(q.shape[0], q.shape[1], q.shape[2], k.shape[2])
+        if tuple(block_mask.shape) != want or block_mask.dtype != torch.uint8:
+            raise ValueError(f"block_mask must be uint8 of shape {want}")
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if score_mod not in _MOD:
@@ -64,6 +78,7 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     p.checker_even, p.checker_odd = float(checker[0]), float(checker[1])
     p.key_mask = None if key_mask is None else key_mask.data_ptr()
     p.q_offset = int(q_offset)
+    p.block_mask = None if block_mask is None else block_mask.data_ptr()
     return p
 
 
@@ -85,12 +100,12 @@ def _mask_u8(key_mask):
 
 
 def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-            checker=(0.5, -0.5), q_offset=0, out=None, lse=None):
+            checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None):
     """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, key_mask, alibi_slopes)
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     lib = _lib.load()
@@ -106,17 +121,18 @@ def backward_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
-             alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, workspace=None, grads=None, which="all"):
+             alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, workspace=None, grads=None,
+             which="all"):
     """Gradients (dq, dk, dv) of sum(dout * out).
 
     which="dq" runs only the query pass (dk, dv come back as None), "dkdv"
     only the key/value pass (dq is None), "all" both."""
     if which not in ("all", "dq", "dkdv"):
         raise ValueError(f"which must be 'all', 'dq' or 'dkdv', not {which!r}")
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes)
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     need = backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -139,14 +155,14 @@ def decode_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0,
-           causal=False, workspace=None, out=None, lse=None):
+           causal=False, block_mask=None, workspace=None, out=None, lse=None):
     """Attention for a short query block (1 <= seq_q <= 64, row i at key
     position q_offset + i), split over the key axis.  With causal=True a row
     sees keys up to its position only."""
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, key_mask, alibi_slopes)
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     need = decode_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -173,37 +189,38 @@ def _plan(fn, name, args, keep):
 
 
 def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
-                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0):
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes)
+                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
-    return _plan(lib.fa_forward, "fa_forward", args, (p, q, k, v, out, lse, key_mask, alibi_slopes))
+    return _plan(lib.fa_forward, "fa_forward", args, (p, q, k, v, out, lse, key_mask, alibi_slopes, block_mask))
 
 
 def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,
-                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0):
+                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
     """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes)
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
     return _plan(lib.fa_backward, "fa_backward", args,
-                 (p, q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes))
+                 (p, q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask))
 
 
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-                checker=(0.5, -0.5), q_offset=0, causal=False):
-    key_mask = _mask_u8(key_mask)
-    _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes)
+                checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None):
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
             _stream(q))
-    return _plan(lib.fa_decode, "fa_decode", args, (p, q, k, v, out, lse, workspace, key_mask, alibi_slopes))
+    return _plan(lib.fa_decode, "fa_decode", args,
+                 (p, q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask))

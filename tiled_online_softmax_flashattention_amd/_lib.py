@@ -27,7 +27,12 @@ class FaProblem(ctypes.Structure):
         ("mod_kind", ctypes.c_int32), ("alibi_slopes", _c_void_p),
         ("checker_even", ctypes.c_float), ("checker_odd", ctypes.c_float),
         ("key_mask", _c_void_p), ("q_offset", ctypes.c_int64),
+        ("block_mask", _c_void_p),
     ]
+
+FA_ABI_VERSION = 3
+FA_BLOCK_MASK_BLOCK = 128
+FA_BLOCK_MASK_MAX_SEQ = 131072
 
 
 _P = ctypes.POINTER(FaProblem)

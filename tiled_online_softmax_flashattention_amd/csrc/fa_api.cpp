@@ -42,6 +42,9 @@ fa_status validate_problem(const fa_problem* p) {
   if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;
   if (p->q_offset > kMaxI32 - p->seq_q) return FA_ERR_UNSUPPORTED;
   if (p->batch > kMaxI32 / p->seq_kv) return FA_ERR_UNSUPPORTED;
+  // block-sparse loops keep their tile lists in LDS, sized for this length
+  if (p->block_mask && (p->seq_q > FA_BLOCK_MASK_MAX_SEQ || p->seq_kv > FA_BLOCK_MASK_MAX_SEQ))
+    return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -71,6 +74,9 @@ fa::AttnArgs make_args(const fa_problem* p) {
   a.odd_log2 = p->checker_odd * fa::kLog2e;
   a.causal = p->causal;
   a.q_off = (int)p->q_offset;
+  a.block_mask = p->block_mask;
+  a.bm_rows = (int)((p->seq_q + FA_BLOCK_MASK_BLOCK - 1) / FA_BLOCK_MASK_BLOCK);
+  a.bm_cols = (int)((p->seq_kv + FA_BLOCK_MASK_BLOCK - 1) / FA_BLOCK_MASK_BLOCK);
   return a;
 }
 

@@ -129,8 +129,9 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
 // their chunks carry the permutation that serves both reads.  Each 64-query
 // tile is processed as two 32-query halves, which keeps the live registers
 // (K, V, dK, dV and two score blocks) within the 256 of two waves per SIMD
-// at head_dim 64.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+// at head_dim 64.  With BLK only the query tiles whose 128 x 128 block (row
+// tile / 2, this workgroup's 128 keys) is set in the block mask are visited.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
   constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
   constexpr int BQ = kDkdvBQ;   // queries per tile
@@ -144,6 +145,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   __shared__ __attribute__((aligned(16))) float sL1[BQ];
   __shared__ __attribute__((aligned(16))) float sD0[BQ];
   __shared__ __attribute__((aligned(16))) float sD1[BQ];
+  __shared__ uint16_t sList[BLK ? kBlkMaxSeq / BQ : 1];   // visited query tiles (block-sparse)
+  __shared__ int sCnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -199,6 +202,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int off = a.q_off;            // query row q sits at key position q + off
   const int qt0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
+  // Visit n = n0 .. n_end-1 is query tile it_of(n): the tile itself, or
+  // entry n of the list of tiles whose block is set.
+  int n0 = qt0, n_end = nqt;
+  if constexpr (BLK) {
+    const uint8_t* bcol = a.block_mask + (size_t)bh * a.bm_rows * a.bm_cols + kb;   // BKV = one block column
+    n0 = 0;
+    n_end = compact_tiles(bcol, a.bm_cols, 1, qt0, nqt, sList, sCnt);   // 64-query tile t lies in block row t / 2
+  }
+  auto it_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BLK) return list_at(sList, n);
+    else return n;
+  };
 
   // Direct loads of query tile it.  Rows past seq_q are clamped to the last
   // row; their scores are masked below.
@@ -267,25 +282,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
   };
 
-  // Tile it in the buffers of its parity; tile it+1 is requested into the
-  // other buffers right after the barrier that retires tile it-1.
-  auto tile = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
+  // Visit n in the buffers of its parity; visit n+1 is requested into the
+  // other buffers right after the barrier that retires visit n-1.
+  auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
                   uint16_t* sOn, float* sLn, float* sDn) __attribute__((always_inline)) {
-    wait_direct_loads();   // this wave's loads of tile it are in LDS
-    __syncthreads();       // ... and every other wave's; tile it-1 is retired
-    if (it + 1 < nqt) load_tile(it + 1, sQn, sOn, sLn, sDn);
+    wait_direct_loads();   // this wave's loads of tile n are in LDS
+    __syncthreads();       // ... and every other wave's; tile n-1 is retired
+    if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
+    const int it = it_of(n);
     half(it, 0, sQ, sO, sL, sD);
     __builtin_amdgcn_sched_barrier(0);   // the halves share registers
     half(it, 1, sQ, sO, sL, sD);
   };
 
-  if (qt0 < nqt) load_tile(qt0, sQ0, sO0, sL0, sD0);
-  int it = qt0;
-  for (; it + 1 < nqt; it += 2) {
-    tile(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
-    tile(it + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
+  if (n0 < n_end) load_tile(it_of(n0), sQ0, sO0, sL0, sD0);
+  int n = n0;
+  for (; n + 1 < n_end; n += 2) {
+    tile(n, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+    tile(n + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
   }
-  if (it < nqt) tile(it, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+  if (n < n_end) tile(n, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
 
   if (kj < Skv) {
     uint16_t* dKg = (uint16_t*)a.dk + ((size_t)bh * Skv + kj) * D;
@@ -311,8 +327,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
 // bias (and the key mask row) start the S^T accumulator, masking runs only on
 // diagonal and tail halves, K/V tiles go straight into double-buffered LDS
 // (K permuted for both of its reads: row fragments for S^T, transposed for
-// dQ), and per score one FMA and one exp give P = 2^(S' c + b - lse2).
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+// dQ), and per score one FMA and one exp give P = 2^(S' c + b - lse2).  With
+// BLK only the key tiles whose block (this workgroup's 128 queries, tile / 2)
+// is set in the block mask are visited.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
   constexpr int BM = 128;   // queries per workgroup
   constexpr int BN = 64;    // keys per tile
@@ -324,6 +342,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
   __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN : 4];   // q parity 0 / 1
   __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN : 4];
+  __shared__ uint16_t sList[BLK ? kBlkMaxSeq / BN : 1];   // visited key tiles (block-sparse)
+  __shared__ int sCnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -401,7 +421,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
 
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  int ntiles = (kv_end + BN - 1) / BN;
+  if constexpr (BLK) {
+    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + qb) * a.bm_cols;   // BM = one block row
+    ntiles = compact_tiles(brow, 1, 1, 0, ntiles, sList, sCnt);   // 64-key tile t lies in block t / 2
+  }
+  auto kv_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BLK) return list_at(sList, n) * BN;
+    else return n * BN;
+  };
 
   // Key-mask row: one byte per key, converted to an additive row in LDS.
   uint32_t mreg = 0;
@@ -430,7 +458,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
   // Keys 32t .. 32t+31 of tile n.
   auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
-    const int k0 = n * BN + 32 * t;   // first key of the half
+    const int k0 = kv_of(n) + 32 * t;   // first key of the half
     if (CAUSAL && k0 > qwp + 31) return;
 
     // S'^T = K Q^T + C and dP^T = V dO^T, keys as rows
@@ -505,21 +533,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     wait_direct_loads();   // this wave's loads of tile n are in LDS
     __syncthreads();       // ... and every other wave's; tile n-1 is retired
     if (n + 1 < ntiles) {
-      load_tile_lds<D, BN, SW_BOTH>(Kg, (n + 1) * BN, Skv, sKn, wave, lane);
-      load_tile_lds<D, BN, SW_BOTH>(Vg, (n + 1) * BN, Skv, sVn, wave, lane);
+      load_tile_lds<D, BN, SW_BOTH>(Kg, kv_of(n + 1), Skv, sKn, wave, lane);
+      load_tile_lds<D, BN, SW_BOTH>(Vg, kv_of(n + 1), Skv, sVn, wave, lane);
       store_m(sBn);
-      load_m(min(n + 2, ntiles - 1) * BN);
+      load_m(kv_of(min(n + 2, ntiles - 1)));
     }
     half(n, 0, sK, sV, sB);
     __builtin_amdgcn_sched_barrier(0);   // the halves share registers
     half(n, 1, sK, sV, sB);
   };
 
-  load_tile_lds<D, BN, SW_BOTH>(Kg, 0, Skv, sK0, wave, lane);
-  load_tile_lds<D, BN, SW_BOTH>(Vg, 0, Skv, sV0, wave, lane);
-  load_m(0);
-  store_m(sB0);
-  load_m(min(1, ntiles - 1) * BN);
+  if (!BLK || ntiles > 0) {   // without a block mask there is always a tile
+    load_tile_lds<D, BN, SW_BOTH>(Kg, kv_of(0), Skv, sK0, wave, lane);
+    load_tile_lds<D, BN, SW_BOTH>(Vg, kv_of(0), Skv, sV0, wave, lane);
+    load_m(kv_of(0));
+    store_m(sB0);
+    load_m(kv_of(min(1, ntiles - 1)));
+  }
   int n = 0;
   for (; n + 1 < ntiles; n += 2) {
     tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
@@ -548,26 +578,33 @@ int bwd16_block_q() { return 128; }
 
 // The query pass runs first and writes delta and lse2 for the key/value
 // pass; without it, the preprocess kernel provides them.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + bwd16_block_kv() - 1) / bwd16_block_kv());
   hipError_t err;
   if (want_q) {
-    hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK>), dim3((unsigned)a.n_qblocks * BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3((unsigned)a.n_qblocks * BH), dim3(256), 0,
+                       st, a);
     err = hipGetLastError();
   } else {
     err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI);
   }
   if (err != hipSuccess || !want_kv) return err;
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK>), dim3(nkb * BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(nkb * BH), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_bwd16_blk(const AttnArgs& a, bool kv, bool qq, hipStream_t st) {
+  return a.block_mask ? launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, kv, qq, st)
+                      : launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, kv, qq, st);
 }
 
 template <class T, int D, int MOD>
 static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
-  if (causal) return mask ? launch_bwd16_inst<T, D, MOD, true, true>(a, kv, qq, st) : launch_bwd16_inst<T, D, MOD, true, false>(a, kv, qq, st);
-  return mask ? launch_bwd16_inst<T, D, MOD, false, true>(a, kv, qq, st) : launch_bwd16_inst<T, D, MOD, false, false>(a, kv, qq, st);
+  if (causal) return mask ? launch_bwd16_blk<T, D, MOD, true, true>(a, kv, qq, st) : launch_bwd16_blk<T, D, MOD, true, false>(a, kv, qq, st);
+  return mask ? launch_bwd16_blk<T, D, MOD, false, true>(a, kv, qq, st) : launch_bwd16_blk<T, D, MOD, false, false>(a, kv, qq, st);
 }
 
 template <class T, int D>

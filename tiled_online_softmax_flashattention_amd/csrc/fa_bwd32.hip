@@ -18,6 +18,8 @@ struct B32Cfg {
   static constexpr int P = D + 4;               // LDS pitch (floats)
   // two 32-row tiles + partial-sum exchange + two 32-float row vectors / mask
   static constexpr size_t lds = (size_t)2 * 32 * P * 4 + (DS > 1 ? 4 * 16 * 64 * 4 : 0) + 2 * 32 * 4 + 64;
+  // block-sparse: the list of visited 32-row tiles and 4 counters after everything else
+  static constexpr size_t lds_blk = lds + (size_t)kBlkMaxSeq / 32 * 2 + 16;
 };
 
 // Sum the DS partial accumulators of a row group through LDS (every wave calls it).
@@ -51,7 +53,9 @@ __device__ __forceinline__ void stage32(float* dst, const float* g, int row0, in
 
 // ------------------------------------------------------------- dK / dV pass
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
+// With BLK only the query tiles whose 128 x 128 block is set in the block
+// mask are visited (a workgroup's keys lie in one block column).
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
   using C = B32Cfg<D>;
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
@@ -63,6 +67,8 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
   float* sS = sO + 32 * P;
   float* sL = sS + (DS > 1 ? 4 * 16 * 64 : 0);
   float* sDl = sL + 32;
+  uint16_t* sList = (uint16_t*)((char*)smem + C::lds);
+  int* sCnt = (int*)(sList + kBlkMaxSeq / 32);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -117,8 +123,13 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
   const int off = a.q_off;   // query row q sits at key position q + off
   const int qt0 = CAUSAL ? max(0, k0 - off) / BQ : 0;
   const int nqt = (Sq + BQ - 1) / BQ;
-  for (int it = qt0; it < nqt; ++it) {
-    const int q0 = it * BQ;
+  int nvis = nqt - qt0;
+  if constexpr (BLK) {
+    const uint8_t* bcol = a.block_mask + (size_t)bh * a.bm_rows * a.bm_cols + (k0 >> 7);
+    nvis = compact_tiles(bcol, a.bm_cols, 2, qt0, nqt, sList, sCnt);   // 32-query tile t lies in block row t / 4
+  }
+  for (int n = 0; n < nvis; ++n) {
+    const int q0 = (BLK ? list_at(sList, n) : qt0 + n) * BQ;
     __syncthreads();
     stage32<D>(sQ, Qg, q0, Sq, tid);
     stage32<D>(sO, dOg, q0, Sq, tid);
@@ -204,7 +215,8 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
 
 // ----------------------------------------------------------------- dQ pass
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
+// With BLK only the key tiles whose 128 x 128 block is set are visited.
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
   using C = B32Cfg<D>;
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
@@ -215,6 +227,8 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
   float* sV = sK + 32 * P;
   float* sS = sV + 32 * P;
   uint8_t* sM = (uint8_t*)(sS + (DS > 1 ? 4 * 16 * 64 : 0) + 64);
+  uint16_t* sList = (uint16_t*)((char*)smem + C::lds);
+  int* sCnt = (int*)(sList + kBlkMaxSeq / 32);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -269,9 +283,13 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
 
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  int ntiles = (kv_end + BN - 1) / BN;
+  if constexpr (BLK) {
+    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
+    ntiles = compact_tiles(brow, 1, 2, 0, ntiles, sList, sCnt);   // 32-key tile t lies in block t / 4
+  }
   for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BN;
+    const int kv0 = (BLK ? list_at(sList, j) : j) * BN;
     __syncthreads();
     stage32<D>(sK, Kg, kv0, Skv, tid);
     stage32<D>(sV, Vg, kv0, Skv, tid);
@@ -359,17 +377,24 @@ static hipError_t launch_dyn32(K kern, unsigned grid, size_t lds, hipStream_t st
   return hipGetLastError();
 }
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
-static hipError_t launch_bwd32_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+static hipError_t launch_bwd32_blk(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
   using C = B32Cfg<D>;
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + 32 * C::NG - 1) / (32 * C::NG));
+  const size_t lds = BLK ? C::lds_blk : C::lds;
   if (want_kv) {
-    hipError_t err = launch_dyn32(dkdv32_kernel<D, MOD, CAUSAL, MASK>, nkb * BH, C::lds, st, a);
+    hipError_t err = launch_dyn32(dkdv32_kernel<D, MOD, CAUSAL, MASK, BLK>, nkb * BH, lds, st, a);
     if (err != hipSuccess) return err;
   }
   if (!want_q) return hipSuccess;
-  return launch_dyn32(dq32_kernel<D, MOD, CAUSAL, MASK>, (unsigned)a.n_qblocks * BH, C::lds, st, a);
+  return launch_dyn32(dq32_kernel<D, MOD, CAUSAL, MASK, BLK>, (unsigned)a.n_qblocks * BH, lds, st, a);
+}
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_bwd32_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
+  return a.block_mask ? launch_bwd32_blk<D, MOD, CAUSAL, MASK, true>(a, want_kv, want_q, st)
+                      : launch_bwd32_blk<D, MOD, CAUSAL, MASK, false>(a, want_kv, want_q, st);
 }
 
 template <int D, int MOD>

@@ -255,6 +255,55 @@ struct AttnArgs {
   int n_qblocks;
   int n_split;         // decode: number of key chunks
   int chunk;           // decode: keys per chunk
+  const uint8_t* block_mask;   // (B, H, bm_rows, bm_cols) bytes, 0 = block skipped; NULL = dense
+  int bm_rows, bm_cols;        // ceil(Sq / kBlk), ceil(Skv / kBlk)
 };
+
+// ------------------------------------------------------------ block sparsity
+//
+// A block mask (the flaxattention page's create_block_mask over 128 x 128
+// blocks) removes whole blocks of (query row, key) pairs: block (r, c) covers
+// query rows 128r .. 128r+127 and keys 128c .. 128c+127.  A workgroup first
+// lists the tiles of its loop whose block is set, in ascending order, in LDS,
+// and then runs its usual double-buffered loop over that list, so a skipped
+// block costs neither loads nor arithmetic.
+
+constexpr int kBlk = 128;             // block edge of the block mask (rows and keys)
+constexpr int kBlkMaxSeq = 131072;    // longest seq_q / seq_kv with a block mask (bounds the LDS lists)
+
+// Writes, in ascending order, the tiles t in [t_lo, t_hi) whose block byte
+// bytes[(t >> shift) * stride] is nonzero to list, and returns their number
+// (uniform).  Every thread of the 4-wave workgroup calls it; cnt4 is 4 ints of
+// LDS.  Ends with a barrier, so the list is visible to all waves on return.
+__device__ __forceinline__ int compact_tiles(const uint8_t* bytes, int stride, int shift, int t_lo, int t_hi,
+                                             uint16_t* list, int* cnt4) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int total = 0;
+  for (int base = t_lo; base < t_hi; base += 256) {
+    const int t = base + tid;
+    const bool vis = t < t_hi && bytes[(size_t)(t >> shift) * stride] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (lane == 0) cnt4[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int before = total, sum = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int cw = cnt4[w];
+      sum += cw;
+      if (w < wave) before += cw;
+    }
+    if (vis) list[before + below] = (uint16_t)t;
+    total = __builtin_amdgcn_readfirstlane(total + sum);
+    __syncthreads();
+  }
+  return total;
+}
+
+// Entry n of an LDS tile list, as a uniform value.
+__device__ __forceinline__ int list_at(const uint16_t* list, int n) {
+  return __builtin_amdgcn_readfirstlane((int)list[n]);
+}
 
 }  // namespace fa

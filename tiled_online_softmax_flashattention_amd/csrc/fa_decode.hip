@@ -65,7 +65,9 @@ __device__ __forceinline__ void merge_into(State<EPL>& s, float m2, float l2, co
 
 constexpr int kDecodeUnroll = 2;   // key batches per group in flight: 2 measured fastest (1: 112, 2: 94, 3: 95, 4: 99, 8: 135 us at 32768 keys)
 
-template <class T, int D, int MOD, bool MASK>
+// With BLK, keys whose 128-key block is unset in block row 0 of the block
+// mask are neither loaded nor counted.
+template <class T, int D, int MOD, bool MASK, bool BLK>
 __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
   constexpr int ES = Elem<T>::size;
   constexpr int EPL = 16 / ES;           // elements per lane
@@ -96,6 +98,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
   float slope2 = 0.f;
   if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
   const uint8_t* mrow = MASK ? a.key_mask + (size_t)b * Skv : nullptr;
+  const uint8_t* brow = BLK ? a.block_mask + (size_t)bh * a.bm_rows * a.bm_cols : nullptr;
 
   State<EPL> st;
   st.m = kNegInf;
@@ -111,8 +114,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kv = min(base + u * KPB, c1 - 1);
-      kk[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
-      vv[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
+      if (!BLK || brow[kv >> 7] != 0) {
+        kk[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
+        vv[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
+      } else {
+        kk[u] = u32x4{0u, 0u, 0u, 0u};
+        vv[u] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
   const int base0 = c0 + wave * KPW + grp;
@@ -134,6 +142,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
       if constexpr (MOD == MOD_CHECKERBOARD) d += ((kv + a.q_off) & 1) ? a.odd_log2 : a.even_log2;
       bool ok = kv < c1;
       if constexpr (MASK) ok = ok && mrow[min(kv, c1 - 1)] != 0;
+      if constexpr (BLK) ok = ok && brow[min(kv, c1 - 1) >> 7] != 0;
       t[u] = ok ? d : kNegInf;
     }
     float mx = st.m;
@@ -270,7 +279,12 @@ int decode_choose_split(int BH, int Skv, int* chunk) {
 template <class T, int D, int MOD, bool MASK>
 static hipError_t launch_decode_inst(const AttnArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0, st, a);
+  if (a.block_mask)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, true>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, false>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0,
+                       st, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(256), 0, st, a);

@@ -56,8 +56,10 @@ constexpr int kSchedDsRead = 0x100;
 // One 128-query block (qb) of one (batch, head) slice (bh).  With SPLIT the
 // block covers only key chunk `split` (a.chunk keys) and writes its
 // unnormalised partial (accumulator, running max, sum) to a.partial for the
-// exact merge of the decode path; otherwise it writes O and lse.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT>
+// exact merge of the decode path; otherwise it writes O and lse.  With BLK
+// only the key tiles whose 128 x 128 block is set in a.block_mask are visited
+// (the 128-query block is exactly one block row).
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT, bool BLK>
 __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb, const int split) {
   constexpr int BM = 128;          // queries per workgroup
   constexpr int BN = 64;           // keys per tile
@@ -74,6 +76,8 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
   __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN : 4];  // per-key additive row (q parity 0 / 1)
   __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN : 4];
+  __shared__ uint16_t sList[BLK ? kBlkMaxSeq / BN : 1];   // visited key tiles (block-sparse)
+  __shared__ int sCnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,12 +132,19 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     t_lo = min(split * ct, ntiles_all);
     t_hi = min(t_lo + ct, ntiles_all);
   }
-  const int ntiles = t_hi - t_lo;
+  int ntiles = t_hi - t_lo;
+  if constexpr (BLK) {
+    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
+    ntiles = compact_tiles(brow, 1, 1, t_lo, t_hi, sList, sCnt);   // 64-key tile t lies in block t / 2
+  }
   // Causal: the diagonal tile first, then towards key 0.  ALiBi grows with the
   // key index, so its largest scores also come first when the tiles are
   // visited from the last one down, and the running max rarely moves.
   constexpr bool REV = CAUSAL || MOD == MOD_ALIBI;
-  auto kv_of = [&](int n) { return (REV ? t_hi - 1 - n : t_lo + n) * BN; };
+  auto kv_of = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BLK) return list_at(sList, REV ? ntiles - 1 - n : n) * BN;
+    else return (REV ? t_hi - 1 - n : t_lo + n) * BN;
+  };
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
   // the last row (finite values whose scores are masked to -inf).
@@ -360,42 +371,48 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
 // with batch * heads a multiple of 8 all blocks of one slice run on one XCD
 // (workgroups are dealt to the 8 XCDs round robin) and share its L2.  Causal
 // query blocks are dispatched longest first.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_kernel(const AttnArgs a) {
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int p = blockIdx.x / BH;
-  fwd16_block<T, D, MOD, CAUSAL, MASK, false>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p, 0);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, false, BLK>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p, 0);
 }
 
 // Split over the key axis (short query blocks against a long key sequence):
 // workgroup (bh, query block, key chunk), bh = blockIdx.x mod (batch * heads).
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_split_kernel(const AttnArgs a) {
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
   const int r = blockIdx.x / BH;
-  fwd16_block<T, D, MOD, CAUSAL, MASK, true>(a, bh, r / a.n_split, r % a.n_split);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, true, BLK>(a, bh, r / a.n_split, r % a.n_split);
 }
 
-template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st) {
   const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H);
   if (split)
-    hipLaunchKernelGGL((fwd16_split_kernel<T, D, MOD, CAUSAL, MASK>), dim3(blocks * (unsigned)a.n_split), dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL((fwd16_split_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(blocks * (unsigned)a.n_split),
+                       dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, CAUSAL, MASK>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((fwd16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(blocks), dim3(256), 0, st, a);
+}
+
+template <class T, int D, int MOD, bool CAUSAL, bool MASK>
+static void launch_fwd16_blk(const AttnArgs& a, bool split, hipStream_t st) {
+  if (a.block_mask) launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, split, st);
+  else launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, split, st);
 }
 
 template <class T, int D, int MOD>
 static hipError_t launch_fwd16_mod(const AttnArgs& a, bool causal, bool mask, bool split, hipStream_t st) {
   if (causal) {
-    if (mask) launch_fwd16_inst<T, D, MOD, true, true>(a, split, st);
-    else launch_fwd16_inst<T, D, MOD, true, false>(a, split, st);
+    if (mask) launch_fwd16_blk<T, D, MOD, true, true>(a, split, st);
+    else launch_fwd16_blk<T, D, MOD, true, false>(a, split, st);
   } else {
-    if (mask) launch_fwd16_inst<T, D, MOD, false, true>(a, split, st);
-    else launch_fwd16_inst<T, D, MOD, false, false>(a, split, st);
+    if (mask) launch_fwd16_blk<T, D, MOD, false, true>(a, split, st);
+    else launch_fwd16_blk<T, D, MOD, false, false>(a, split, st);
   }
   return hipGetLastError();
 }

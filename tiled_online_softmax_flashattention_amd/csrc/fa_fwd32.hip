@@ -24,9 +24,13 @@ struct F32Cfg {
   static constexpr int BN = 32;
   static constexpr int P = D + 4;               // LDS pitch of the K and V tiles (floats)
   static constexpr size_t lds = (size_t)2 * BN * P * 4 + (DS > 1 ? 4 * 16 * 64 * 4 : 0) + 64;
+  // block-sparse: the list of visited 32-key tiles and 4 counters after the tiles
+  static constexpr size_t lds_blk = lds + (size_t)kBlkMaxSeq / BN * 2 + 16;
 };
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
+// With BLK only the key tiles whose 128 x 128 block is set in the block mask
+// are visited (a workgroup's queries lie in one block row).
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   using C = F32Cfg<D>;
   constexpr int DS = C::DS, BM = C::BM, BN = C::BN, P = C::P;
@@ -40,6 +44,8 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   float* sV = sK + BN * P;
   float* sS = sV + BN * P;
   uint8_t* sM = (uint8_t*)(sS + (DS > 1 ? 4 * 16 * 64 : 0));
+  uint16_t* sList = (uint16_t*)((char*)smem + C::lds);
+  int* sCnt = (int*)(sList + kBlkMaxSeq / BN);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -81,7 +87,11 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  int ntiles = (kv_end + BN - 1) / BN;
+  if constexpr (BLK) {
+    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
+    ntiles = compact_tiles(brow, 1, 2, 0, ntiles, sList, sCnt);   // 32-key tile t lies in block t / 4
+  }
 
   float m_run = kNegInf, l_run = 0.f;
   f32x16 o[DT];
@@ -89,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
   for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = j * BN;
+    const int kv0 = (BLK ? list_at(sList, j) : j) * BN;
     __syncthreads();
 #pragma unroll 4
     for (int i = 0; i < NCH; ++i) {
@@ -195,16 +205,22 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 }
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
-static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
-  auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK>;
-  const size_t lds = F32Cfg<D>::lds;
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+static hipError_t launch_one_blk(const AttnArgs& a, hipStream_t st) {
+  auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK, BLK>;
+  const size_t lds = BLK ? F32Cfg<D>::lds_blk : F32Cfg<D>::lds;
   if (lds > 65536) {
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_qblocks * a.B * a.H)), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+template <int D, int MOD, bool CAUSAL, bool MASK>
+static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
+  return a.block_mask ? launch_one_blk<D, MOD, CAUSAL, MASK, true>(a, st)
+                      : launch_one_blk<D, MOD, CAUSAL, MASK, false>(a, st);
 }
 
 template <int D, int MOD>

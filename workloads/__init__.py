@@ -24,7 +24,10 @@ import torch
 SEED = 42
 
 # tensor ids of the per-tensor streams
-Q, K, V, DOUT, MASK, ROWS = 0, 1, 2, 3, 4, 5
+Q, K, V, DOUT, MASK, ROWS, BLOCKS = 0, 1, 2, 3, 4, 5, 6
+
+# edge of a block-mask block (query rows and keys)
+BLOCK = 128
 
 # score_mod kinds; the numbering matches the C-ABI enum
 MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD = 0, 1, 2
@@ -62,6 +65,30 @@ def bernoulli_key_mask(batch: int, seq_kv: int, workload_id: int, p_keep: float 
                 break
         rows.append(r)
     return torch.from_numpy(np.stack(rows)).contiguous()
+
+
+def block_grid(seq_q: int, seq_kv: int) -> Tuple[int, int]:
+    """Number of 128-row and 128-key blocks."""
+    return -(-seq_q // BLOCK), -(-seq_kv // BLOCK)
+
+
+def bernoulli_block_mask(batch: int, heads: int, seq_q: int, seq_kv: int, workload_id: int,
+                         p_keep: float = 0.5, seed: int = SEED) -> torch.Tensor:
+    """(batch, heads, ceil(seq_q/128), ceil(seq_kv/128)) uint8 block mask, 1 =
+    the block's pairs may attend, each entry Bernoulli(p_keep)."""
+    nq, nk = block_grid(seq_q, seq_kv)
+    r = _rng(workload_id, BLOCKS, seed).random((batch, heads, nq, nk)) < p_keep
+    return torch.from_numpy(r.astype(np.uint8)).contiguous()
+
+
+def window_block_mask(batch: int, heads: int, seq_q: int, seq_kv: int, window: int) -> torch.Tensor:
+    """Block mask of a sliding window of whole blocks: block (r, c) is set
+    when r - window < c <= r (the diagonal block and the window - 1 before it)."""
+    nq, nk = block_grid(seq_q, seq_kv)
+    r = np.arange(nq)[:, None]
+    c = np.arange(nk)[None, :]
+    m = ((c <= r) & (c > r - window)).astype(np.uint8)
+    return torch.from_numpy(np.broadcast_to(m, (batch, heads, nq, nk)).copy()).contiguous()
 
 
 def sample_rows(seq: int, n: int, workload_id: int, seed: int = SEED) -> np.ndarray:
