@@ -95,7 +95,7 @@ typedef struct {
   int64_t batch, heads, seq_q, seq_kv, head_dim;
   int32_t dtype;             /* fa_dtype */
   int32_t causal;            /* 0 or 1: key j allowed only when j <= i + q_offset */
-  float scale;               /* multiplies q.k; pass 1/sqrt(head_dim) for the usual scaling */
+  float scale;               /* multiplies q.k, > 0 (else FA_ERR_UNSUPPORTED); 1/sqrt(head_dim) usually */
   int32_t mod_kind;          /* fa_mod_kind */
   const float* alibi_slopes; /* device float[heads] or NULL (FA_MOD_ALIBI only) */
   float checker_even;        /* FA_MOD_CHECKERBOARD only */

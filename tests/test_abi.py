@@ -132,6 +132,13 @@ def test_unsupported_head_dims():
     assert fwd(prob(head_dim=256, dtype=_lib.FA_F32)) == UNSUP
 
 
+def test_scale_must_be_positive():
+    assert fwd(prob(scale=0.0)) == UNSUP
+    assert fwd(prob(scale=-0.125)) == UNSUP
+    assert bwd(prob(scale=-1.0)) == UNSUP
+    assert dec(prob(seq_q=1, scale=0.0)) == UNSUP
+
+
 def test_checkerboard_needs_finite_values():
     assert fwd(prob(mod_kind=2, checker_even=float("nan"))) == INVALID
 

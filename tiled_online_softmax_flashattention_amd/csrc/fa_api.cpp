@@ -32,6 +32,9 @@ fa_status validate_problem(const fa_problem* p) {
   if (p->mod_kind != FA_MOD_NONE && p->mod_kind != FA_MOD_ALIBI && p->mod_kind != FA_MOD_CHECKERBOARD)
     return FA_ERR_INVALID_ARGUMENT;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARGUMENT;
+  // the kernels mask scores as -inf before multiplying by scale and keep the
+  // backward's log-sum-exp in units of scale * q.k: scale must be positive
+  if (!(p->scale > 0.f)) return FA_ERR_UNSUPPORTED;
   if (p->mod_kind == FA_MOD_CHECKERBOARD && (!isfinite(p->checker_even) || !isfinite(p->checker_odd)))
     return FA_ERR_INVALID_ARGUMENT;
   if (p->q_offset < 0) return FA_ERR_INVALID_ARGUMENT;

@@ -36,11 +36,14 @@ namespace fa {
 constexpr int kDkdvBQ = 64;
 
 // delta_i = sum_d dO_id * O_id; lse2_i = lse_i * log2(e), +inf for an empty
-// row (so that exp2(s - lse2) = 0 there).  With fold_alibi, lse2_i also
-// carries the query's share of the ALiBi bias relative to its 64-query tile,
-// slope * log2(e) * (i mod 64), as the 16-bit key/value pass expects.
+// row (so that exp2(s - lse2) = 0 there).  For the 16-bit key/value pass
+// (kv16) the rows are stored as that pass consumes them: -delta_i, and
+// -lse2_i / c in units of q.k (c = scale * log2(e) > 0), with lse2_i carrying
+// the query's share of the ALiBi bias relative to its 64-query tile,
+// slope * log2(e) * (i mod 64).  Both then serve as the initial values of
+// the dP and S accumulators.
 template <int ES, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtype, int fold_alibi) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtype, int kv16) {
   constexpr int EPL = 16 / ES;                        // elements per 16-byte load
   constexpr int LPR = (D * ES / 16) < 64 ? (D * ES / 16) : 64;  // lanes per row
   constexpr int IT = D * ES / 16 / LPR;               // loads per lane
@@ -77,32 +80,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtyp
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
   if (row < rows && sub == 0) {
-    a.delta[row] = acc;
     const float l = a.lse[row];
     float l2 = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
-    if (fold_alibi) {
-      const int64_t bhr = row / a.Sq;
-      const int qrow = (int)(row - bhr * a.Sq);
-      l2 += alibi_slope(a.alibi_slopes, (int)(bhr % a.H), a.H) * kLog2e * (float)(qrow & (kDkdvBQ - 1));
+    if (kv16) {
+      if (kv16 == 2) {   // ALiBi
+        const int64_t bhr = row / a.Sq;
+        const int qrow = (int)(row - bhr * a.Sq);
+        l2 += alibi_slope(a.alibi_slopes, (int)(bhr % a.H), a.H) * kLog2e * (float)(qrow & (kDkdvBQ - 1));
+      }
+      a.delta[row] = -acc;
+      a.lse2[row] = -l2 / a.scale_log2;
+    } else {
+      a.delta[row] = acc;
+      a.lse2[row] = l2;
     }
-    a.lse2[row] = l2;
   }
   (void)EPL;
 }
 
-hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, bool fold_alibi) {
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, int kv16) {
   const int64_t rows = (int64_t)a.B * a.H * a.Sq;
   const int es = dtype == 0 ? 4 : 2;
   const int lpr = (D * es / 16) < 64 ? (D * es / 16) : 64;
   const int rpb = 256 / lpr;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (es == 4) {
-    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<4, 64>), grid, block, 0, st, a, dtype, (int)fold_alibi);
-    else if (D == 128) hipLaunchKernelGGL((bwd_pre_kernel<4, 128>), grid, block, 0, st, a, dtype, (int)fold_alibi);
-    else hipLaunchKernelGGL((bwd_pre_kernel<4, 512>), grid, block, 0, st, a, dtype, (int)fold_alibi);
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<4, 64>), grid, block, 0, st, a, dtype, kv16);
+    else if (D == 128) hipLaunchKernelGGL((bwd_pre_kernel<4, 128>), grid, block, 0, st, a, dtype, kv16);
+    else hipLaunchKernelGGL((bwd_pre_kernel<4, 512>), grid, block, 0, st, a, dtype, kv16);
   } else {
-    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<2, 64>), grid, block, 0, st, a, dtype, (int)fold_alibi);
-    else hipLaunchKernelGGL((bwd_pre_kernel<2, 128>), grid, block, 0, st, a, dtype, (int)fold_alibi);
+    if (D == 64) hipLaunchKernelGGL((bwd_pre_kernel<2, 64>), grid, block, 0, st, a, dtype, kv16);
+    else hipLaunchKernelGGL((bwd_pre_kernel<2, 128>), grid, block, 0, st, a, dtype, kv16);
   }
   return hipGetLastError();
 }
@@ -117,13 +125,15 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
 
 // ------------------------------------------------------------- dK / dV pass
 
-// Key-stationary dK/dV pass.  The ALiBi bias slope (k - q) splits into the
-// query's part relative to its tile start, which arrives folded into the
-// lse2 row, and a per-lane term slope (k - tile start) that joins the key
-// mask (-inf) in one exponent offset; the checkerboard bias starts the S
-// accumulator per register.  Per score the work is one subtraction of the
-// row's lse2, one FMA and one exp for P and a subtraction and a multiply for
-// dS.  Query tiles (Q, dO and their
+// Key-stationary dK/dV pass.  The S accumulator starts from the query row's
+// -lse2 / c and the dP accumulator from -delta (rows stored that way by the
+// query pass or the preprocess), so the MFMAs produce S - lse2 / c and
+// dP - delta directly.  The ALiBi bias slope (k - q) splits into the query's
+// part relative to its tile start, which arrives folded into the lse2 row,
+// and a per-lane term slope (k - tile start) that joins the key mask (-inf)
+// and the checkerboard bias (two per-lane values by register parity) in one
+// exponent offset.  Per score the work is one FMA and one exp for P and one
+// multiply for dS.  Query tiles (Q, dO and their
 // lse2 and delta rows) go from HBM straight into double-buffered LDS; both
 // 16-bit tiles are read as row fragments (S, dP) and transposed (dV, dK), so
 // their chunks carry the permutation that serves both reads.  Each 64-query
@@ -160,7 +170,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int kw = k0 + 32 * wave;
   const int kj = kw + l32;            // this lane's key
   const float c = a.scale_log2;
-  const float inv_scale = 1.0f / a.scale;
 
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
   const uint16_t* dOg = (const uint16_t*)a.dout + (size_t)bh * Sq * D;
@@ -185,11 +194,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   if constexpr (MASK) key_ok = key_ok && a.key_mask[(size_t)b * Skv + min(kj, Skv - 1)] != 0;
   float slope2 = 0.f;
   if constexpr (MOD == MOD_ALIBI) slope2 = alibi_slope(a.alibi_slopes, h, a.H) * kLog2e;
-  f32x16 cinit = zero16();
+  // checkerboard bias (log2 units) of registers r even / odd: query tiles
+  // start at even rows, so register r holds a query at a position of parity
+  // ((r + q_off) & 1)
+  float cb0 = 0.f, cb1 = 0.f;
   if constexpr (MOD == MOD_CHECKERBOARD) {
-    // query tiles start at even rows, so register r holds a query at a position of parity ((r + q_off) & 1)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = (((kj + r + a.q_off) & 1) == 0 ? a.even_nat : a.odd_nat) * inv_scale;
+    const bool kev = ((kj + a.q_off) & 1) == 0;
+    cb0 = kev ? a.even_log2 : a.odd_log2;
+    cb1 = kev ? a.odd_log2 : a.even_log2;
   }
 
   f32x16 dk[DT], dv[DT];
@@ -232,8 +244,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     const int qs = it * BQ + 32 * mt;   // first query of the half
     if (CAUSAL && qs + off + 31 < kw) return;   // every query precedes every key of this wave
 
-    // S' = Q K^T + C and dP = dO V^T, queries as rows
-    f32x16 sv = cinit, dpv = zero16();
+    // S' = Q K^T - lse2 / c and dP' = dO V^T - delta, queries as rows: the
+    // accumulators start from the rows' stored values
+    const float* lrow = sL + 32 * mt + 4 * hi;
+    const float* drow = sD + 32 * mt + 4 * hi;
+    f32x16 sv, dpv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
+      const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        sv[4 * u + cc] = l4[cc];
+        dpv[4 * u + cc] = d4[cc];
+      }
+    }
     {
       const int qr = 32 * mt + l32;
 #pragma unroll
@@ -254,19 +279,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
     float lb = key_ok ? 0.f : kNegInf;
     if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ - off) : kNegInf;
-    const float* lrow = sL + 32 * mt + 4 * hi;
-    const float* drow = sD + 32 * mt + 4 * hi;
+    const float lb0 = lb + cb0, lb1 = lb + cb1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
-      const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int r = 4 * u + cc;
-        const float p = exp2_hw(fmaf(sv[r], c, lb - l4[cc]));
-        sv[r] = p;
-        dpv[r] = p * (dpv[r] - d4[cc]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_hw(fmaf(sv[r], c, (r & 1) ? lb1 : lb0));
+      sv[r] = p;
+      dpv[r] *= p;
     }
     // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
 #pragma unroll
@@ -395,11 +413,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     lse2 = (ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();   // empty rows and rows past seq_q: P = 0
     delta = ok ? dsum : 0.f;
     if (ok && hi == 0) {
-      float l2 = lse2;   // for the key/value pass: with the query's ALiBi share (see bwd_pre_kernel)
+      // for the key/value pass, as it consumes them (see bwd_pre_kernel):
+      // -delta, and -lse2 / c with the query's ALiBi share folded in
+      float l2 = lse2;
       if constexpr (MOD == MOD_ALIBI)
         l2 += alibi_slope(a.alibi_slopes, h, a.H) * kLog2e * (float)(qi & (kDkdvBQ - 1));
-      a.delta[(size_t)bh * Sq + qi] = delta;
-      a.lse2[(size_t)bh * Sq + qi] = l2;
+      a.delta[(size_t)bh * Sq + qi] = -delta;
+      a.lse2[(size_t)bh * Sq + qi] = -l2 / a.scale_log2;
     }
   }
 
@@ -419,6 +439,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = zero16();
+  // initial value of the dP^T accumulator: -delta in every register, so the
+  // MFMAs produce dP - delta directly
+  f32x16 dneg;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dneg[r] = -delta;
 
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   int ntiles = (kv_end + BN - 1) / BN;
@@ -461,8 +486,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     const int k0 = kv_of(n) + 32 * t;   // first key of the half
     if (CAUSAL && k0 > qwp + 31) return;
 
-    // S'^T = K Q^T + C and dP^T = V dO^T, keys as rows
-    f32x16 s = cinit, dp = zero16();
+    // S'^T = K Q^T + C and dP'^T = V dO^T - delta, keys as rows
+    f32x16 s = cinit, dp = dneg;
     if constexpr (MASK) {
       const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
@@ -511,7 +536,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = exp2_hw(fmaf(s[r], c, nb));
-      dp[r] = p * (dp[r] - delta);
+      dp[r] *= p;
     }
 
     // dQ^T += K^T dS^T over the half's 32 keys (K^T fragments requested first)
@@ -588,7 +613,7 @@ static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q
                        st, a);
     err = hipGetLastError();
   } else {
-    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI);
+    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI ? 2 : 1);
   }
   if (err != hipSuccess || !want_kv) return err;
   hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(nkb * BH), dim3(256), 0, st, a);

@@ -21,8 +21,10 @@ size_t fwd32_lds_bytes(int D);
 hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st);
 
 // Backward: preprocess (delta = rowsum(dO * O), lse in base 2), then the
-// key-stationary dK/dV pass and the query-stationary dQ pass.
-hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, bool fold_alibi = false);
+// key-stationary dK/dV pass and the query-stationary dQ pass.  kv16 = 0: the
+// rows as the fp32 passes read them; 1: as the 16-bit key/value pass reads
+// them (-delta, -lse2 / c); 2: the same with the ALiBi query share folded in.
+hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, int kv16 = 0);
 int bwd16_block_kv();
 int bwd16_block_q();
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
