@@ -488,13 +488,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
     // S'^T = K Q^T + C and dP'^T = V dO^T - delta, keys as rows
     f32x16 s = cinit, dp = dneg;
-    if constexpr (MASK) {
+    if constexpr (MASK) {   // the row starts the accumulator (cinit is nonzero only for ALiBi)
       const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 m4 = *(const f32x4*)(row + 8 * u);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] += m4[cc];
+        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] = MOD == MOD_ALIBI ? cinit[4 * u + cc] + m4[cc] : m4[cc];
       }
     }
     {

@@ -195,12 +195,14 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   auto scores = [&](int t, int k0, const uint16_t* sK, const float* sB) __attribute__((always_inline)) {
     f32x16 s = cinit;
     if constexpr (MASK) {
+      // the row starts the accumulator (plus the ALiBi offsets, the only
+      // nonzero cinit with a mask: the checkerboard values are in the row)
       const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 m4 = *(const f32x4*)(row + 8 * u);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] += m4[cc];
+        for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] = MOD == MOD_ALIBI ? cinit[4 * u + cc] + m4[cc] : m4[cc];
       }
     }
     {
