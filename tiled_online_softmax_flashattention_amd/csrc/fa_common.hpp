@@ -182,11 +182,16 @@ __device__ __forceinline__ u32x4 read_a_tr_tile(const uint16_t* tile, int p0, in
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// Cache-policy bits of a direct load: 0, or the non-temporal hint for data
+// read exactly once (a key chunk of the split decode path).
+constexpr int kCpolNone = 0;
+constexpr int kCpolNT = 2;
+
 // Direct load (global_load_lds_dwordx4) of a ROWS x D 16-bit tile into an LDS
 // tile by the NW waves of a workgroup: wave w issues the 1 KiB blocks
 // w*NJ .. w*NJ+NJ-1, each lane fetching the global chunk that belongs at its
 // LDS slot.  Rows past nrows are clamped to the last row.
-template <int D, int ROWS, int SW, int NW = 4>
+template <int D, int ROWS, int SW, int NW = 4, int CPOL = kCpolNone>
 __device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int nrows, uint16_t* tile, int wave,
                                               int lane) {
   constexpr int NJ = ROWS * D * 2 / 1024 / NW;
@@ -198,14 +203,14 @@ __device__ __forceinline__ void load_tile_lds(const uint16_t* g, int row0, int n
     const int row = e / D, pch = (e % D) >> 3;
     const int lch = pch ^ chunk_perm<D, SW>(row);
     __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)min(row0 + row, nrows - 1) * D + (lch << 3)),
-                                     (lds_void_ptr)(tile + blk * 512), 16, 0, 0);
+                                     (lds_void_ptr)(tile + blk * 512), 16, 0, CPOL);
   }
 }
 
 // The same load for a tile whose rows all exist (row0 + ROWS <= nrows): a
 // uniform base address plus a per-lane 32-bit byte offset, so the address
 // arithmetic per tile is scalar.
-template <int D, int ROWS, int SW, int NW = 4>
+template <int D, int ROWS, int SW, int NW = 4, int CPOL = kCpolNone>
 __device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint16_t* tile, int wave, int lane) {
   constexpr int NJ = ROWS * D * 2 / 1024 / NW;
   static_assert(NJ * NW * 1024 == ROWS * D * 2, "tile must split into 1 KiB blocks per wave");
@@ -216,7 +221,7 @@ __device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint1
     const int row = e / D, pch = (e % D) >> 3;
     const uint32_t off = (uint32_t)(row * D + ((pch ^ chunk_perm<D, SW>(row)) << 3)) * 2u;
     __builtin_amdgcn_global_load_lds((const void*)((const char*)g_row0 + off), (lds_void_ptr)(tile + blk * 512), 16,
-                                     0, 0);
+                                     0, CPOL);
   }
 }
 

@@ -108,15 +108,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 
   // Software prefetch: the next batch of U keys per group is requested before
   // the current one is used (rows past the chunk are clamped to its last key
-  // and masked), so two batches are in flight per lane.
+  // and masked), so two batches are in flight per lane.  K and V are read
+  // exactly once, so the loads carry the non-temporal hint (measured at 32768
+  // keys: 95 -> 86 us).
   u32x4 kx[U], vx[U], kn[U], vn[U];
   auto load_batch = [&](int base, u32x4* kk, u32x4* vv) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kv = min(base + u * KPB, c1 - 1);
       if (!BLK || brow[kv >> 7] != 0) {
-        kk[u] = *(const u32x4*)(Kg + (size_t)kv * D * ES);
-        vv[u] = *(const u32x4*)(Vg + (size_t)kv * D * ES);
+        kk[u] = __builtin_nontemporal_load((const u32x4*)(Kg + (size_t)kv * D * ES));
+        vv[u] = __builtin_nontemporal_load((const u32x4*)(Vg + (size_t)kv * D * ES));
       } else {
         kk[u] = u32x4{0u, 0u, 0u, 0u};
         vv[u] = u32x4{0u, 0u, 0u, 0u};

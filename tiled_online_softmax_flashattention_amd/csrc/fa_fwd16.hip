@@ -147,14 +147,17 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   };
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
-  // the last row (finite values whose scores are masked to -inf).
+  // the last row (finite values whose scores are masked to -inf).  A split
+  // workgroup (a short query block) is the only reader of its key chunk, so
+  // those loads carry the non-temporal hint.
+  constexpr int CPOL = SPLIT ? kCpolNT : kCpolNone;
   auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) __attribute__((always_inline)) {
     if (kv0 + BN <= Skv) {
-      load_full_tile_lds<D, BN, SW_BOTH>(Kg + (size_t)kv0 * D, sK, wave, lane);
-      load_full_tile_lds<D, BN, VSW>(Vg + (size_t)kv0 * D, sV, wave, lane);
+      load_full_tile_lds<D, BN, SW_BOTH, 4, CPOL>(Kg + (size_t)kv0 * D, sK, wave, lane);
+      load_full_tile_lds<D, BN, VSW, 4, CPOL>(Vg + (size_t)kv0 * D, sV, wave, lane);
     } else {
-      load_tile_lds<D, BN, SW_BOTH>(Kg, kv0, Skv, sK, wave, lane);
-      load_tile_lds<D, BN, VSW>(Vg, kv0, Skv, sV, wave, lane);
+      load_tile_lds<D, BN, SW_BOTH, 4, CPOL>(Kg, kv0, Skv, sK, wave, lane);
+      load_tile_lds<D, BN, VSW, 4, CPOL>(Vg, kv0, Skv, sV, wave, lane);
     }
   };
   // Key-mask row: one byte per key, converted to an additive row in LDS.
