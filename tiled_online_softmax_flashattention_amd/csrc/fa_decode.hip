@@ -63,18 +63,21 @@ __device__ __forceinline__ void merge_into(State<EPL>& s, float m2, float l2, co
   s.m = M;
 }
 
-constexpr int kDecodeUnroll = 2;   // key batches per group in flight: 2 measured fastest (1: 112, 2: 94, 3: 95, 4: 99, 8: 135 us at 32768 keys)
+// Keys per lane group per step (U), chosen per launch by the chunk length:
+// with non-temporal loads, 4096-key chunks (32768 keys, 8 x 8 heads) measured
+// U = 1: 104.5, 2: 85.7, 3: 86.4, 4: 82.2 us, and 256-key chunks (2048 keys)
+// U = 1: 12.7, 2: 11.5, 3: 12.0, 4: 12.5 us.
+constexpr int kDecodeLongChunk = 2048;   // chunks this long use U = 4, shorter ones U = 2
 
 // With BLK, keys whose 128-key block is unset in block row 0 of the block
 // mask are neither loaded nor counted.
-template <class T, int D, int MOD, bool MASK, bool BLK>
+template <class T, int D, int MOD, bool MASK, bool BLK, int U>
 __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
   constexpr int ES = Elem<T>::size;
   constexpr int EPL = 16 / ES;           // elements per lane
   constexpr int LPK = D / EPL;           // lanes per key
   constexpr int KPW = 64 / LPK;          // keys per wave per step
   constexpr int KPB = 4 * KPW;           // keys per workgroup per step
-  constexpr int U = kDecodeUnroll;
   __shared__ float sPart[4][D + 2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -278,15 +281,20 @@ int decode_choose_split(int BH, int Skv, int* chunk) {
   return (int)((Skv + c - 1) / c);
 }
 
+template <class T, int D, int MOD, bool MASK, bool BLK>
+static void launch_decode_split(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)(a.B * a.H * a.n_split));
+  if (a.chunk >= kDecodeLongChunk)
+    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, BLK, 4>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, BLK, 2>), grid, dim3(256), 0, st, a);
+}
+
 template <class T, int D, int MOD, bool MASK>
 static hipError_t launch_decode_inst(const AttnArgs& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  if (a.block_mask)
-    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, true>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0,
-                       st, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<T, D, MOD, MASK, false>), dim3((unsigned)(BH * a.n_split)), dim3(256), 0,
-                       st, a);
+  if (a.block_mask) launch_decode_split<T, D, MOD, MASK, true>(a, st);
+  else launch_decode_split<T, D, MOD, MASK, false>(a, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(256), 0, st, a);
