@@ -246,6 +246,23 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     float add = 0.f;
     if constexpr (MOD == MOD_ALIBI) add = slope2 * (float)(k0 - qpos);
 
+    // P rounded to the 16-bit type and packed in pairs (the B operand of the
+    // P V product), packed right after the exponentials so that the fp32
+    // values are dead before the V fragments are read, and its fp32 row sum
+    // over the half.  (Summing the packed fp16 pairs with v_dot2 measured
+    // slower, and bf16's 2^-9 rounding would be too coarse for lse.)
+    u32x4 pb[2];
+    auto pack_sum = [&]() __attribute__((always_inline)) {
+      float l4[4];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l4[r & 3] = r < 4 ? s[r] : l4[r & 3] + s[r];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        pb[u] = u32x4{pack2<T>(s[8 * u + 0], s[8 * u + 1]), pack2<T>(s[8 * u + 2], s[8 * u + 3]),
+                      pack2<T>(s[8 * u + 4], s[8 * u + 5]), pack2<T>(s[8 * u + 6], s[8 * u + 7])};
+      return (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    };
+
     // Fast path: exponentials against the running max as it stands, valid
     // when every lane has one (have_max, uniform) and no lane's sum over the
     // half exceeds 2^15 (so every P fits fp16).  Otherwise (a row's first
@@ -255,13 +272,9 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     bool ok = have_max;
     if (ok) {
       const float nb = MOD == MOD_ALIBI ? add - m_run : neg_m;
-      float l4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = exp2_hw(fmaf(s[r], c, nb));
-        l4[r & 3] = r < 4 ? s[r] : l4[r & 3] + s[r];
-      }
-      ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+      for (int r = 0; r < 16; ++r) s[r] = exp2_hw(fmaf(s[r], c, nb));
+      ls = pack_sum();
       ok = __builtin_amdgcn_ballot_w64(!(ls <= kSumLimit)) == 0;
     }
     if (!ok) {
@@ -281,13 +294,9 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       neg_m = -m_run;
       have_max = __builtin_amdgcn_ballot_w64(m_run == kNegInf) == 0;
       const float nb = add - m_use;
-      float l4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = exp2_hw(fmaf(s[r], c, nb));
-        l4[r & 3] = r < 4 ? s[r] : l4[r & 3] + s[r];
-      }
-      ls = (l4[0] + l4[1]) + (l4[2] + l4[3]);
+      for (int r = 0; r < 16; ++r) s[r] = exp2_hw(fmaf(s[r], c, nb));
+      ls = pack_sum();
     }
     l_run += ls;
 
@@ -300,10 +309,8 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       for (int dt = 0; dt < DT; ++dt) vfr[u][dt] = read_a_tr_tile<D, VSW>(sV, 32 * t + 16 * u, 32 * dt, lane);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const u32x4 pb = {pack2<T>(s[8 * u + 0], s[8 * u + 1]), pack2<T>(s[8 * u + 2], s[8 * u + 3]),
-                        pack2<T>(s[8 * u + 4], s[8 * u + 5]), pack2<T>(s[8 * u + 6], s[8 * u + 7])};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(vfr[u][dt], pb, o[dt]);
+      for (int dt = 0; dt < DT; ++dt) o[dt] = mma16<T>(vfr[u][dt], pb[u], o[dt]);
     }
   };
 
