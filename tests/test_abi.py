@@ -189,3 +189,21 @@ def test_block_mask_length_limit():
     # at the limit validation passes and the next check (a null tensor) fails
     assert fwd(prob(seq_q=m, seq_kv=m, block_mask=bm), q=None) == INVALID
     assert fwd(prob(seq_q=m + 1, seq_kv=64), q=None) == INVALID
+
+
+def test_binding_block_mask_shape_and_pointer():
+    """The binding takes a (batch, heads, ceil(Sq/128), ceil(Skv/128)) uint8
+    block mask, rejects any other shape or dtype, and passes its address."""
+    import torch
+    import tiled_online_softmax_flashattention_amd as fa
+    q = torch.zeros(2, 3, 300, 64, dtype=torch.float16)
+    k = torch.zeros(2, 3, 129, 64, dtype=torch.float16)
+    assert fa.block_mask_shape(2, 3, 300, 129) == (2, 3, 3, 2)
+    bm = torch.ones(2, 3, 3, 2, dtype=torch.uint8)
+    p = fa.problem(q, k, block_mask=bm)
+    assert p.block_mask == bm.data_ptr()
+    assert fa.problem(q, k).block_mask is None
+    for bad in (torch.ones(2, 3, 2, 2, dtype=torch.uint8), torch.ones(2, 3, 3, 3, dtype=torch.uint8),
+                torch.ones(2, 3, 3, 2, dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            fa.problem(q, k, block_mask=bad)
