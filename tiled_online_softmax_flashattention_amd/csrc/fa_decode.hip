@@ -212,59 +212,55 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
 
 constexpr int kMaxSplit = 256;
 
-// One workgroup per output row: (b, h) for decode, (b, h, query) for a query
-// block split over the key axis.  The chunks' (max, sum) are read in parallel into
-// LDS, the weights 2^(m_s - M) computed once, and every thread then issues
-// its accumulator loads for all chunks back to back (no serial chain of
-// dependent loads).
+// One workgroup of D threads per output row: (b, h) for decode, (b, h, query)
+// for a query block split over the key axis.  Thread d reads, for 8 chunks at
+// a time, each chunk's (max, sum) and its own accumulator element together
+// (the max and sum addresses are the same for every thread: one broadcast),
+// so a batch of chunks costs one round of independent loads; batches merge
+// online, rescaled to the running max.  No LDS, no barrier.
+constexpr int kMergeBatch = 8;
+
 template <class T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const AttnArgs a) {
-  __shared__ float sw[kMaxSplit];
-  __shared__ float sl[kMaxSplit];
-  __shared__ float sM;
+__global__ __launch_bounds__(D) void decode_merge_kernel(const AttnArgs a) {
   const int bh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int d = threadIdx.x;
   const int ns = a.n_split;
   const float* part = a.partial + (size_t)bh * ns * (D + 2);
-  for (int sp = tid; sp < ns; sp += 256) {
-    sw[sp] = part[(size_t)sp * (D + 2) + D];
-    sl[sp] = part[(size_t)sp * (D + 2) + D + 1];
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float m = kNegInf;
-    for (int sp = tid; sp < ns; sp += 64) m = fmaxf(m, sw[sp]);
+  float M = kNegInf, L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
 #pragma unroll
-    for (int w = 1; w < 64; w <<= 1) m = fmaxf(m, __shfl_xor(m, w));
-    if (tid == 0) sM = m;
-  }
-  __syncthreads();
-  const float M = sM;
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  for (int sp = tid; sp < ns; sp += 256) sw[sp] = exp2_hw(sw[sp] - Mu);
-  __syncthreads();
-  float L = 0.f;
-  for (int sp = 0; sp < ns; ++sp) L += sw[sp] * sl[sp];
-  const int d = tid;
-  if (d < D) {
-    float acc = 0.f;
-    int sp = 0;
-    for (; sp + 4 <= ns; sp += 4) {
-      const float x0 = part[(size_t)(sp + 0) * (D + 2) + d], x1 = part[(size_t)(sp + 1) * (D + 2) + d];
-      const float x2 = part[(size_t)(sp + 2) * (D + 2) + d], x3 = part[(size_t)(sp + 3) * (D + 2) + d];
-      acc += sw[sp] * x0 + sw[sp + 1] * x1 + sw[sp + 2] * x2 + sw[sp + 3] * x3;
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool ok = s0 + j < ns;
+      const float* pj = part + (size_t)(ok ? s0 + j : s0) * (D + 2);
+      mv[j] = ok ? pj[D] : kNegInf;
+      lv[j] = ok ? pj[D + 1] : 0.f;
+      av[j] = ok ? pj[d] : 0.f;
     }
-    for (; sp < ns; ++sp) acc += sw[sp] * part[(size_t)sp * (D + 2) + d];
-    const float o = L > 0.f ? acc / L : 0.f;
-    if constexpr (__is_same(T, F32)) {
-      ((float*)a.o)[(size_t)bh * D + d] = o;
-    } else if constexpr (__is_same(T, F16)) {
-      ((_Float16*)a.o)[(size_t)bh * D + d] = (_Float16)o;
-    } else {
-      ((__bf16*)a.o)[(size_t)bh * D + d] = (__bf16)o;
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, mv[j]);
+    const float mu = (mb == kNegInf) ? 0.f : mb;
+    const float sc = exp2_hw(M - mu);
+    L *= sc;
+    acc *= sc;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = exp2_hw(mv[j] - mu);
+      L += w * lv[j];
+      acc += w * av[j];
     }
+    M = mb;
   }
-  if (tid == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+  const float o = L > 0.f ? acc / L : 0.f;
+  if constexpr (__is_same(T, F32)) {
+    ((float*)a.o)[(size_t)bh * D + d] = o;
+  } else if constexpr (__is_same(T, F16)) {
+    ((_Float16*)a.o)[(size_t)bh * D + d] = (_Float16)o;
+  } else {
+    ((__bf16*)a.o)[(size_t)bh * D + d] = (__bf16)o;
+  }
+  if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
 int decode_choose_split(int BH, int Skv, int* chunk) {
@@ -276,7 +272,7 @@ int decode_choose_split(int BH, int Skv, int* chunk) {
   if (c < 256) c = 256;
   if (c > 4096) c = 4096;
   if (c > Skv) c = (Skv + 63) / 64 * 64;
-  if ((Skv + c - 1) / c > kMaxSplit) c = (Skv + kMaxSplit - 1) / kMaxSplit;  // the merge holds at most kMaxSplit chunks
+  if ((Skv + c - 1) / c > kMaxSplit) c = (Skv + kMaxSplit - 1) / kMaxSplit;  // bounds the merge's serial batches
   *chunk = (int)c;
   return (int)((Skv + c - 1) / c);
 }
@@ -297,7 +293,7 @@ static hipError_t launch_decode_inst(const AttnArgs& a, hipStream_t st) {
   else launch_decode_split<T, D, MOD, MASK, false>(a, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3((unsigned)BH), dim3(D), 0, st, a);
   return hipGetLastError();
 }
 
@@ -313,8 +309,8 @@ static hipError_t launch_decode_d(const AttnArgs& a, int mod, bool mask, hipStre
 
 template <class T>
 static hipError_t launch_merge_t(const AttnArgs& a, int D, int rows, hipStream_t st) {
-  if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<T, 64>), dim3((unsigned)rows), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3((unsigned)rows), dim3(256), 0, st, a);
+  if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<T, 64>), dim3((unsigned)rows), dim3(64), 0, st, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<T, 128>), dim3((unsigned)rows), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
