@@ -148,3 +148,31 @@ def test_block_mask_long_fp32_d512(gpu_lib):
                    causal=True)
     bm = W.bernoulli_block_mask(1, 1, 131072, 131072, 207)
     sampled_parity(w, 64, block_mask=bm)
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
+def test_block_mask_with_query_offset(gpu_lib, dtype, D):
+    """Block mask plus a KV-cache offset: 300 queries at positions 100..399
+    against 400 keys, causal, ALiBi.  Block rows index query ROWS (0..2), not
+    positions; forward and backward against the oracle."""
+    Sq, Skv, off = 300, 400, 100
+    w = W.Workload("block-sparse with offset", 208, 2, 2, Sq, Skv, D, dtype, causal=True, mod=W.MOD_ALIBI)
+    inputs = w.make()
+    bm = W.bernoulli_block_mask(2, 2, Sq, Skv, 208, p_keep=0.6)
+    bm[..., 0] = 1   # key block 0 is allowed for every row (no query row is empty)
+    inputs["block_mask"] = bm
+    dev = to_dev(inputs)
+    kw = dict(causal=True, score_mod="alibi", q_offset=off, block_mask=dev["block_mask"])
+    say(f"[block offset] {dtype} D{D}")
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+    torch.cuda.synchronize()
+    okw = dict(oracle_kw(w, inputs), q_offset=off)
+    o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
+    dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
+    strict = dtype != "f32"
+    check("o", out, o_ref, dtype, "o", strict)
+    check_lse(lse, lse_ref)
+    check("dq", dq, dq_r, dtype, "grad", strict)
+    check("dk", dk, dk_r, dtype, "grad", strict)
+    check("dv", dv, dv_r, dtype, "grad", strict)
