@@ -231,6 +231,31 @@ __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt
 __device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
 
+// A 32-row fp32 tile (rows row0 .., D floats each) held in registers by the
+// 256 threads of a workgroup (thread tid holds the 16-byte chunks tid + 256 i),
+// so the next tile of an fp32 loop can be loaded while the current one
+// computes and stored to LDS (pitch D + 4) after the barrier that frees it.
+// Rows past nrows are clamped to the last row (finite; the kernels mask them).
+template <int D>
+struct Rows32 {
+  static constexpr int N = 32 * D / 4 / 256;
+  f32x4 x[N];
+  __device__ __forceinline__ void load(const float* g, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4);
+      x[i] = *(const f32x4*)(g + (size_t)min(row0 + row, nrows - 1) * D + 4 * ch);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4);
+      *(f32x4*)&dst[row * (D + 4) + 4 * ch] = x[i];
+    }
+  }
+};
+
 // Launch arguments of every attention kernel (tensors contiguous BHSD).
 struct AttnArgs {
   const void* q;
