@@ -131,8 +131,14 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
   for (int n = 0; n < nvis; ++n) {
     const int q0 = (BLK ? list_at(sList, n) : qt0 + n) * BQ;
     __syncthreads();
-    stage32<D>(sQ, Qg, q0, Sq, tid);
-    stage32<D>(sO, dOg, q0, Sq, tid);
+    if constexpr (D * 4 % 1024 == 0) {   // head_dim 512: direct loads, one wait
+      stage32_direct<D>(sQ, Qg, q0, Sq, wave, lane);
+      stage32_direct<D>(sO, dOg, q0, Sq, wave, lane);
+      wait_direct_loads();
+    } else {
+      stage32<D>(sQ, Qg, q0, Sq, tid);
+      stage32<D>(sO, dOg, q0, Sq, tid);
+    }
     if (tid < 32) {
       const bool ok = q0 + tid < Sq;
       sL[tid] = ok ? a.lse2[(size_t)bh * Sq + q0 + tid] : __builtin_inff();

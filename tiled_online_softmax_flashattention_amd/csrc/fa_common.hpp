@@ -256,6 +256,28 @@ struct Rows32 {
   }
 };
 
+// The same 32-row fp32 tile (pitch D + 4 floats) staged with direct loads
+// (global_load_lds_dwordx4), for rows of a whole number of 1 KiB blocks
+// (head_dim 512: two per row): each instruction fills one block of one row,
+// wave w the rows 8w .. 8w+7, no registers held and every load of the tile in
+// flight at once.  The caller waits (wait_direct_loads) and synchronises the
+// workgroup before reading the tile.
+template <int D>
+__device__ __forceinline__ void stage32_direct(float* dst, const float* g, int row0, int nrows, int wave, int lane) {
+  static_assert(D * 4 % 1024 == 0, "rows must be whole 1 KiB blocks");
+  constexpr int BPR = D * 4 / 1024;   // blocks per row
+  const int w = __builtin_amdgcn_readfirstlane(wave);   // the LDS address (M0) is uniform
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int row = w * 8 + r;
+    const float* src = g + (size_t)min(row0 + row, nrows - 1) * D + lane * 4;
+#pragma unroll
+    for (int hb = 0; hb < BPR; ++hb)
+      __builtin_amdgcn_global_load_lds((const void*)(src + hb * 256), (lds_void_ptr)(dst + row * (D + 4) + hb * 256),
+                                       16, 0, 0);
+  }
+}
+
 // Launch arguments of every attention kernel (tensors contiguous BHSD).
 struct AttnArgs {
   const void* q;

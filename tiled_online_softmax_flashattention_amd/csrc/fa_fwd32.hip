@@ -101,14 +101,20 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = (BLK ? list_at(sList, j) : j) * BN;
     __syncthreads();
+    if constexpr (D * 4 % 1024 == 0) {   // head_dim 512: direct loads, one wait
+      stage32_direct<D>(sK, Kg, kv0, Skv, wave, lane);
+      stage32_direct<D>(sV, Vg, kv0, Skv, wave, lane);
+      wait_direct_loads();
+    } else {
 #pragma unroll 4
-    for (int i = 0; i < NCH; ++i) {
-      // rows past seq_kv: the last row (finite; its scores are masked to -inf)
-      const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4), kv = min(kv0 + row, Skv - 1);
-      const f32x4 kx = *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch);
-      const f32x4 vx = *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch);
-      *(f32x4*)&sK[row * P + 4 * ch] = kx;
-      *(f32x4*)&sV[row * P + 4 * ch] = vx;
+      for (int i = 0; i < NCH; ++i) {
+        // rows past seq_kv: the last row (finite; its scores are masked to -inf)
+        const int c = tid + 256 * i, row = c / (D / 4), ch = c % (D / 4), kv = min(kv0 + row, Skv - 1);
+        const f32x4 kx = *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch);
+        const f32x4 vx = *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch);
+        *(f32x4*)&sK[row * P + 4 * ch] = kx;
+        *(f32x4*)&sV[row * P + 4 * ch] = vx;
+      }
     }
     if constexpr (MASK) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
