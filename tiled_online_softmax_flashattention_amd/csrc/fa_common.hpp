@@ -227,6 +227,8 @@ __device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint1
 
 // Wait until this wave's direct loads have landed (vmcnt(0)).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+// Wait until at most 16 of this wave's vector memory loads are in flight.
+__device__ __forceinline__ void wait_vmcnt_le16() { __builtin_amdgcn_s_waitcnt(0x3f70 | (16 & 15) | ((16 >> 4) << 14)); }
 
 __device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
@@ -262,7 +264,18 @@ struct Rows32 {
 // wave w the rows 8w .. 8w+7, no registers held and every load of the tile in
 // flight at once.  The caller waits (wait_direct_loads) and synchronises the
 // workgroup before reading the tile.
-template <int D>
+// One direct load (global_load_lds_dwordx4: lane i's 16 bytes from g land at
+// lds_blk + 16 i) issued from inline assembly, so the compiler does not track
+// it: a pipelined loop then waits with its own vmcnt counts instead of the
+// compiler draining every load in flight before each LDS read.  The
+// instruction has no register result (its address registers are read at
+// issue); the caller's waits and barriers order it.
+__device__ __forceinline__ void direct_load16_untracked(const void* g, const void* lds_blk) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_ptr)lds_blk;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0v), "v"(g) : "memory", "m0");
+}
+
+template <int D, bool UNTRACKED = false>
 __device__ __forceinline__ void stage32_direct(float* dst, const float* g, int row0, int nrows, int wave, int lane) {
   static_assert(D * 4 % 1024 == 0, "rows must be whole 1 KiB blocks");
   constexpr int BPR = D * 4 / 1024;   // blocks per row
@@ -272,9 +285,13 @@ __device__ __forceinline__ void stage32_direct(float* dst, const float* g, int r
     const int row = w * 8 + r;
     const float* src = g + (size_t)min(row0 + row, nrows - 1) * D + lane * 4;
 #pragma unroll
-    for (int hb = 0; hb < BPR; ++hb)
-      __builtin_amdgcn_global_load_lds((const void*)(src + hb * 256), (lds_void_ptr)(dst + row * (D + 4) + hb * 256),
-                                       16, 0, 0);
+    for (int hb = 0; hb < BPR; ++hb) {
+      if constexpr (UNTRACKED)
+        direct_load16_untracked(src + hb * 256, dst + row * (D + 4) + hb * 256);
+      else
+        __builtin_amdgcn_global_load_lds((const void*)(src + hb * 256),
+                                         (lds_void_ptr)(dst + row * (D + 4) + hb * 256), 16, 0, 0);
+    }
   }
 }
 

@@ -98,13 +98,30 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero16();
 
+  // head_dim 512: K and V tiles arrive by direct loads (16 per wave and
+  // tensor), pipelined over the two LDS buffers: K of tile j+1 is requested
+  // once the partial scores of tile j are exchanged (K_j is then dead) and
+  // lands during the softmax and P V of tile j; V of tile j+1 is requested
+  // when P V of tile j is done and lands during the scores of tile j+1.  Each
+  // wait counts the wave's own direct loads still allowed in flight.
+  constexpr bool PIPE = D * 4 % 1024 == 0;
+  auto tile_kv = [&](int j) __attribute__((always_inline)) { return (BLK ? list_at(sList, j) : j) * BN; };
+  if constexpr (PIPE) {
+    if (ntiles > 0) stage32_direct<D, true>(sK, Kg, tile_kv(0), Skv, wave, lane);
+  }
   for (int j = 0; j < ntiles; ++j) {
-    const int kv0 = (BLK ? list_at(sList, j) : j) * BN;
-    __syncthreads();
-    if constexpr (D * 4 % 1024 == 0) {   // head_dim 512: direct loads, one wait
-      stage32_direct<D>(sK, Kg, kv0, Skv, wave, lane);
-      stage32_direct<D>(sV, Vg, kv0, Skv, wave, lane);
-      wait_direct_loads();
+    const int kv0 = tile_kv(j);
+    __syncthreads();   // every wave is done with tile j-1 (its P V read V)
+    if constexpr (PIPE) {
+      uint8_t mb = 0;
+      if constexpr (MASK) {   // issued before V_j, so the wait below covers it
+        if (tid < BN) mb = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+      }
+      stage32_direct<D, true>(sV, Vg, kv0, Skv, wave, lane);
+      wait_vmcnt_le16();   // K_j (and the mask bytes) landed; V_j may be in flight
+      if constexpr (MASK) {
+        if (tid < BN) sM[tid] = mb;
+      }
     } else {
 #pragma unroll 4
       for (int i = 0; i < NCH; ++i) {
@@ -116,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
         *(f32x4*)&sV[row * P + 4 * ch] = vx;
       }
     }
-    if constexpr (MASK) {
+    if constexpr (MASK && !PIPE) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
     }
     __syncthreads();
@@ -136,7 +153,10 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     if constexpr (DS > 1) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = s[r];
-      __syncthreads();
+      __syncthreads();   // every wave's partial scores are in: K_j is dead
+      if constexpr (PIPE) {
+        if (j + 1 < ntiles) stage32_direct<D, true>(sK, Kg, tile_kv(j + 1), Skv, wave, lane);
+      }
       s = zero16();
 #pragma unroll
       for (int e2 = 0; e2 < DS; ++e2) {
@@ -184,6 +204,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+
+    if constexpr (PIPE) {   // V_j landed (K_{j+1} may be in flight) in every wave
+      if (j + 1 < ntiles) wait_vmcnt_le16();
+      else wait_direct_loads();
+      __syncthreads();
+    }
 
     // O^T += V^T P^T: step t pairs register t of the probabilities (key
     // acc_row(t, hi)) with that key's V row, one key per lane group.
