@@ -290,8 +290,8 @@ def main() -> int:
         return counters_pass()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every box has one GPU); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads and batches shard with no "
+              "communication; see the multi-GPU design notes); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
