@@ -23,16 +23,26 @@ struct B32Cfg {
 };
 
 // Sum the DS partial accumulators of a row group through LDS (every wave calls it).
-template <int DS>
+// VEC: the 16-byte swizzled exchange (a quarter of the LDS instructions);
+// otherwise one dword per value, which needs fewer registers in flight (the
+// dQ pass at head_dim 512 has none to spare).
+template <int DS, bool VEC>
 __device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g, int lane) {
+  f32x16 s;
+  if constexpr (VEC) {
+    slice_put(sS, x, wave, lane);
+    __syncthreads();
+    s = slice_gather<DS>(sS, g, lane);
+  } else {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = x[r];
-  __syncthreads();
-  f32x16 s = zero16();
+    for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = x[r];
+    __syncthreads();
+    s = zero16();
 #pragma unroll
-  for (int e2 = 0; e2 < DS; ++e2) {
+    for (int e2 = 0; e2 < DS; ++e2) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
+      for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
+    }
   }
   __syncthreads();
   return s;
@@ -165,8 +175,8 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
     if constexpr (DS > 1) {
-      s = slice_sum<DS>(s, sS, wave, g, lane);
-      dp = slice_sum<DS>(dp, sS, wave, g, lane);
+      s = slice_sum<DS, true>(s, sS, wave, g, lane);
+      dp = slice_sum<DS, true>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (q0 + off < kw + 31);
@@ -340,8 +350,8 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
     if constexpr (DS > 1) {
-      s = slice_sum<DS>(s, sS, wave, g, lane);
-      dp = slice_sum<DS>(dp, sS, wave, g, lane);
+      s = slice_sum<DS, false>(s, sS, wave, g, lane);
+      dp = slice_sum<DS, false>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);

@@ -297,6 +297,36 @@ __device__ __forceinline__ void stage32_direct(float* dst, const float* g, int r
   }
 }
 
+// Exchange of partial 32x32 accumulators between the waves that split a
+// head's dims (fp32 head_dim 512): wave w stores its 16 values per lane at
+// sS[w * 1024 + lane * 16 ..] as four 16-byte chunks, chunk c at position
+// c ^ ((lane >> 2) & 3), so a 16-lane pass of 16-byte accesses touches 16
+// distinct 4-bank groups; after a barrier every wave of group g sums the DS
+// partials of waves g*DS .. g*DS+DS-1.
+__device__ __forceinline__ void slice_put(float* sS, const f32x16& x, int wave, int lane) {
+  float* base = sS + wave * 1024 + lane * 16;
+  const int sw = (lane >> 2) & 3;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    *(f32x4*)(base + 4 * (c ^ sw)) = f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]};
+}
+
+template <int DS>
+__device__ __forceinline__ f32x16 slice_gather(const float* sS, int g, int lane) {
+  f32x16 s;
+  const int sw = (lane >> 2) & 3;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int e2 = 0; e2 < DS; ++e2) {
+      const f32x4 v = *(const f32x4*)(sS + (g * DS + e2) * 1024 + lane * 16 + 4 * (c ^ sw));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * c + i] = e2 == 0 ? v[i] : s[4 * c + i] + v[i];
+    }
+  }
+  return s;
+}
+
 // Launch arguments of every attention kernel (tensors contiguous BHSD).
 struct AttnArgs {
   const void* q;

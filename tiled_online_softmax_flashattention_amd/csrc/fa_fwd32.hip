@@ -151,18 +151,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     }
     f32x16 s = s0 + s1;
     if constexpr (DS > 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = s[r];
+      slice_put(sS, s, wave, lane);
       __syncthreads();   // every wave's partial scores are in: K_j is dead
       if constexpr (PIPE) {
         if (j + 1 < ntiles) stage32_direct<D, true>(sK, Kg, tile_kv(j + 1), Skv, wave, lane);
       }
-      s = zero16();
-#pragma unroll
-      for (int e2 = 0; e2 < DS; ++e2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
-      }
+      s = slice_gather<DS>(sS, g, lane);
     }
 
     const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);
