@@ -26,7 +26,9 @@ struct B32Cfg {
 // VEC: the 16-byte swizzled exchange (a quarter of the LDS instructions);
 // otherwise one dword per value, which needs fewer registers in flight (the
 // dQ pass at head_dim 512 has none to spare).
-template <int DS, bool VEC>
+// TRAIL: end with a barrier (sS is reused at once); without it the caller
+// guarantees a barrier before the next write to sS.
+template <int DS, bool VEC, bool TRAIL = true>
 __device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g, int lane) {
   f32x16 s;
   if constexpr (VEC) {
@@ -44,7 +46,7 @@ __device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g
       for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
     }
   }
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
   return s;
 }
 
@@ -174,9 +176,9 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
       p1 = mma_f32(y[3], vf[kk + 3], p1);
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
-    if constexpr (DS > 1) {
+    if constexpr (DS > 1) {   // the two barriers around the next tile's staging order the next exchange
       s = slice_sum<DS, true>(s, sS, wave, g, lane);
-      dp = slice_sum<DS, true>(dp, sS, wave, g, lane);
+      dp = slice_sum<DS, true, false>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (q0 + off < kw + 31);
@@ -304,54 +306,98 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
     const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
     ntiles = compact_tiles(brow, 1, 2, 0, ntiles, sList, sCnt);   // 32-key tile t lies in block t / 4
   }
-  // K, V tile j+1 (and its key-mask bytes) are loaded into registers while
-  // tile j computes, and stored to LDS after the barrier that retires tile j
-  // (long fp32 workload: dQ pass 408 -> 342 ms).  The forward and the dK/dV
-  // pass keep staging in place: the same prefetch measured 1 % slower in the
-  // forward and made the dK/dV pass spill.
+  // head_dim 512: K and V tiles arrive by direct loads (16 per wave and
+  // tensor) issued from inline assembly and waited with per-wave counts: V of
+  // tile j+1 is requested as soon as K of tile j has landed (every wave has
+  // then read V_j for dP), K of tile j+1 once the dQ products of tile j are
+  // issued; each step computes dP = dO V^T first, while its K lands.
+  // Otherwise K, V tile j+1 (and its key-mask bytes) are loaded into
+  // registers while tile j computes and stored to LDS after the barrier that
+  // retires tile j (long fp32 workload at head_dim 512: dQ pass 408 -> 342 ms
+  // before the direct loads).
+  constexpr bool PIPE = D * 4 % 1024 == 0;
   auto tile_kv = [&](int j) __attribute__((always_inline)) { return (BLK ? list_at(sList, j) : j) * BN; };
   Rows32<D> rk, rv;
   uint8_t mnext = 0;
   auto fetch = [&](int kv0) __attribute__((always_inline)) {
-    rk.load(Kg, kv0, Skv, tid);
-    rv.load(Vg, kv0, Skv, tid);
-    if constexpr (MASK) {
-      if (tid < BN) mnext = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+    if constexpr (!PIPE) {
+      rk.load(Kg, kv0, Skv, tid);
+      rv.load(Vg, kv0, Skv, tid);
+      if constexpr (MASK) {
+        if (tid < BN) mnext = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+      }
     }
   };
-  if (ntiles > 0) fetch(tile_kv(0));
+  if (ntiles > 0) {
+    if constexpr (PIPE) {
+      stage32_direct<D, true>(sV, Vg, tile_kv(0), Skv, wave, lane);
+      stage32_direct<D, true>(sK, Kg, tile_kv(0), Skv, wave, lane);
+    } else {
+      fetch(tile_kv(0));
+    }
+  }
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = tile_kv(j);
-    __syncthreads();
-    rk.store(sK, tid);
-    rv.store(sV, tid);
-    if constexpr (MASK) {
-      if (tid < BN) sM[tid] = mnext;
-    }
-    if (j + 1 < ntiles) fetch(tile_kv(j + 1));
-    __syncthreads();
-    if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
-
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
     const float* krow = sK + l32 * P + e * DSL + hi * HS;
     const float* vrow = sV + l32 * P + e * DSL + hi * HS;
+    if constexpr (PIPE) {
+      uint8_t mb = 0;
+      if constexpr (MASK) {   // the compiler waits for this load (and so for K_j) before the store
+        if (tid < BN) mb = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+      }
+      wait_vmcnt_le16();   // V_j landed; K_j may be in flight
+      if constexpr (MASK) {
+        if (tid < BN) sM[tid] = mb;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < HS; kk += 4) {
-      const f32x4 x = *(const f32x4*)(krow + kk);
-      const f32x4 y = *(const f32x4*)(vrow + kk);
-      s0 = mma_f32(x[0], qf[kk + 0], s0);
-      s1 = mma_f32(x[1], qf[kk + 1], s1);
-      p0 = mma_f32(y[0], of[kk + 0], p0);
-      p1 = mma_f32(y[1], of[kk + 1], p1);
-      s0 = mma_f32(x[2], qf[kk + 2], s0);
-      s1 = mma_f32(x[3], qf[kk + 3], s1);
-      p0 = mma_f32(y[2], of[kk + 2], p0);
-      p1 = mma_f32(y[3], of[kk + 3], p1);
+      for (int kk = 0; kk < HS; kk += 4) {
+        const f32x4 y = *(const f32x4*)(vrow + kk);
+        p0 = mma_f32(y[0], of[kk + 0], p0);
+        p1 = mma_f32(y[1], of[kk + 1], p1);
+        p0 = mma_f32(y[2], of[kk + 2], p0);
+        p1 = mma_f32(y[3], of[kk + 3], p1);
+      }
+      wait_direct_loads();   // K_j landed
+      __syncthreads();       // and V_j is dead in every wave
+      if (j + 1 < ntiles) stage32_direct<D, true>(sV, Vg, tile_kv(j + 1), Skv, wave, lane);
+#pragma unroll
+      for (int kk = 0; kk < HS; kk += 4) {
+        const f32x4 x = *(const f32x4*)(krow + kk);
+        s0 = mma_f32(x[0], qf[kk + 0], s0);
+        s1 = mma_f32(x[1], qf[kk + 1], s1);
+        s0 = mma_f32(x[2], qf[kk + 2], s0);
+        s1 = mma_f32(x[3], qf[kk + 3], s1);
+      }
+    } else {
+      __syncthreads();
+      rk.store(sK, tid);
+      rv.store(sV, tid);
+      if constexpr (MASK) {
+        if (tid < BN) sM[tid] = mnext;
+      }
+      if (j + 1 < ntiles) fetch(tile_kv(j + 1));
+      __syncthreads();
+      if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
+#pragma unroll
+      for (int kk = 0; kk < HS; kk += 4) {
+        const f32x4 x = *(const f32x4*)(krow + kk);
+        const f32x4 y = *(const f32x4*)(vrow + kk);
+        s0 = mma_f32(x[0], qf[kk + 0], s0);
+        s1 = mma_f32(x[1], qf[kk + 1], s1);
+        p0 = mma_f32(y[0], of[kk + 0], p0);
+        p1 = mma_f32(y[1], of[kk + 1], p1);
+        s0 = mma_f32(x[2], qf[kk + 2], s0);
+        s1 = mma_f32(x[3], qf[kk + 3], s1);
+        p0 = mma_f32(y[2], of[kk + 2], p0);
+        p1 = mma_f32(y[3], of[kk + 3], p1);
+      }
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
-    if constexpr (DS > 1) {
-      s = slice_sum<DS, false>(s, sS, wave, g, lane);
-      dp = slice_sum<DS, false>(dp, sS, wave, g, lane);
+    if constexpr (DS > 1) {   // with PIPE the barrier before K_{j+1} orders the next exchange
+      s = slice_sum<DS, PIPE>(s, sS, wave, g, lane);
+      dp = slice_sum<DS, PIPE, !PIPE>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);
@@ -384,6 +430,10 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
       const float* krw = sK + acc_row(t, hi) * P + e * DSL + l32;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_f32(krw[32 * dt], dp[t], dq[dt]);
+    }
+    if constexpr (PIPE) {
+      __syncthreads();   // K_j is dead in every wave
+      if (j + 1 < ntiles) stage32_direct<D, true>(sK, Kg, tile_kv(j + 1), Skv, wave, lane);
     }
   }
 
