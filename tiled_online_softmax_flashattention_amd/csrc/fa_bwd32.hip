@@ -22,30 +22,14 @@ struct B32Cfg {
   static constexpr size_t lds_blk = lds + (size_t)kBlkMaxSeq / 32 * 2 + 16;
 };
 
-// Sum the DS partial accumulators of a row group through LDS (every wave calls it).
-// VEC: the 16-byte swizzled exchange (a quarter of the LDS instructions);
-// otherwise one dword per value, which needs fewer registers in flight (the
-// dQ pass at head_dim 512 has none to spare).
-// TRAIL: end with a barrier (sS is reused at once); without it the caller
-// guarantees a barrier before the next write to sS.
-template <int DS, bool VEC, bool TRAIL = true>
+// Sum the DS partial accumulators of a row group through LDS (every wave calls
+// it; 16-byte swizzled chunks).  TRAIL: end with a barrier (sS is reused at
+// once); without it the caller guarantees a barrier before the next write to sS.
+template <int DS, bool TRAIL = true>
 __device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g, int lane) {
-  f32x16 s;
-  if constexpr (VEC) {
-    slice_put(sS, x, wave, lane);
-    __syncthreads();
-    s = slice_gather<DS>(sS, g, lane);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sS[(wave * 16 + r) * 64 + lane] = x[r];
-    __syncthreads();
-    s = zero16();
-#pragma unroll
-    for (int e2 = 0; e2 < DS; ++e2) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] += sS[((g * DS + e2) * 16 + r) * 64 + lane];
-    }
-  }
+  slice_put(sS, x, wave, lane);
+  __syncthreads();
+  const f32x16 s = slice_gather<DS>(sS, g, lane);
   if constexpr (TRAIL) __syncthreads();
   return s;
 }
@@ -177,8 +161,8 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
     if constexpr (DS > 1) {   // the two barriers around the next tile's staging order the next exchange
-      s = slice_sum<DS, true>(s, sS, wave, g, lane);
-      dp = slice_sum<DS, true, false>(dp, sS, wave, g, lane);
+      s = slice_sum<DS>(s, sS, wave, g, lane);
+      dp = slice_sum<DS, false>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (q0 + off < kw + 31);
@@ -396,8 +380,8 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
     }
     f32x16 s = s0 + s1, dp = p0 + p1;
     if constexpr (DS > 1) {   // with PIPE the barrier before K_{j+1} orders the next exchange
-      s = slice_sum<DS, PIPE>(s, sS, wave, g, lane);
-      dp = slice_sum<DS, PIPE, !PIPE>(dp, sS, wave, g, lane);
+      s = slice_sum<DS>(s, sS, wave, g, lane);
+      dp = slice_sum<DS, !PIPE>(dp, sS, wave, g, lane);
     }
 
     const bool diag = CAUSAL && (kv0 + BN - 1 > qwp);
