@@ -41,6 +41,15 @@ def test_f32_d512_small(gpu_lib, causal, mod, mask):
     full_parity(small("f32", 512, causal, mod, mask, Sq=80, Skv=130, B=1, H=2))
 
 
+@pytest.mark.parametrize("Skv", [1, 31, 32, 33, 64, 65, 97])
+@pytest.mark.parametrize("mask", [False, True])
+def test_f32_d512_key_tile_edges(gpu_lib, Skv, mask):
+    """head_dim 512 stages 32-key (and 32-query) tiles through two LDS buffers
+    with the next tile's loads in flight: one, two and three tiles, full and
+    ragged, with and without a key mask (the mask bytes load in the step)."""
+    full_parity(small("f32", 512, False, W.MOD_ALIBI, mask, Sq=45, Skv=Skv, B=1, H=2, wid=108), strict=False)
+
+
 @pytest.mark.parametrize("S", [1, 17, 63, 64, 65, 127, 129, 255, 257])
 @pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 512)])
 def test_ragged_causal_lengths(gpu_lib, S, dtype, D):
