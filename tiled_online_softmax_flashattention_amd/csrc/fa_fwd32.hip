@@ -196,8 +196,13 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     }
     l_run = l_run * alpha + ls;
     m_run = m_new;
+    // alpha is exactly 1 wherever the running max did not move: skip the
+    // rescale when that holds for the whole wave (the usual case once a
+    // row's largest scores are in)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
 
     if constexpr (PIPE) {   // V_j landed (K_{j+1} may be in flight) in every wave
       if (j + 1 < ntiles) wait_vmcnt_le16();
