@@ -207,3 +207,92 @@ def test_binding_block_mask_shape_and_pointer():
                 torch.ones(2, 3, 3, 2, dtype=torch.int32)):
         with pytest.raises(ValueError):
             fa.problem(q, k, block_mask=bad)
+
+
+def _cpu_inputs(B=2, H=3, Sq=50, Skv=70, D=64, dtype=None):
+    import torch
+    dtype = dtype or torch.float16
+    q = torch.zeros(B, H, Sq, D, dtype=dtype)
+    k = torch.zeros(B, H, Skv, D, dtype=dtype)
+    v = torch.zeros(B, H, Skv, D, dtype=dtype)
+    return q, k, v
+
+
+def _bad_cases():
+    """(entry point, keyword overrides) pairs that the binding must reject
+    with ValueError before anything reaches the library: every tensor's shape
+    and dtype is checked against q and k."""
+    import torch
+    q, k, v = _cpu_inputs()
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    f16, f32, u8 = torch.float16, torch.float32, torch.uint8
+    return [
+        ("forward", dict(k=torch.zeros(B, H + 1, Skv, D, dtype=f16))),          # heads differ
+        ("forward", dict(k=torch.zeros(B + 1, H, Skv, D, dtype=f16))),          # batch differs
+        ("forward", dict(k=torch.zeros(B, H, Skv, 128, dtype=f16))),            # head_dim differs
+        ("forward", dict(k=torch.zeros(B, H, Skv, D, dtype=torch.bfloat16))),   # dtype differs
+        ("forward", dict(v=torch.zeros(B, H, Skv + 1, D, dtype=f16))),          # v.shape != k.shape
+        ("forward", dict(v=torch.zeros(B, H, Skv, D, dtype=f32))),
+        ("forward", dict(key_mask=torch.ones(B, Skv + 1, dtype=u8))),           # key mask (B, Skv)
+        ("forward", dict(key_mask=torch.ones(B + 1, Skv, dtype=u8))),
+        ("forward", dict(alibi_slopes=torch.ones(H - 1, dtype=f32), score_mod="alibi")),   # too few slopes
+        ("forward", dict(alibi_slopes=torch.ones(H, dtype=torch.float64), score_mod="alibi")),
+        ("forward", dict(out=torch.zeros(B, H, Sq - 1, D, dtype=f16))),         # caller's out too small
+        ("forward", dict(out=torch.zeros(B, H, Sq, D, dtype=f32))),
+        ("forward", dict(lse=torch.zeros(B, H, Sq - 1, dtype=f32))),            # caller's lse too small
+        ("forward", dict(lse=torch.zeros(B, H, Sq, dtype=f16))),
+        ("forward", dict(block_mask=torch.ones(B, H, 1, 2, dtype=u8))),
+        ("backward", dict(dout=torch.zeros(B, H, Sq, D - 32, dtype=f16))),
+        ("backward", dict(dout=torch.zeros(B, H, Sq, D, dtype=f32))),
+        ("backward", dict(out=torch.zeros(B, H, Sq + 1, D, dtype=f16))),
+        ("backward", dict(lse=torch.zeros(B, H, Sq + 1, dtype=f32))),
+        ("backward", dict(grads=(torch.zeros(B, H, Sq - 1, D, dtype=f16), torch.zeros_like(k), torch.zeros_like(v)))),
+        ("backward", dict(grads=(torch.zeros_like(q), torch.zeros(B, H, Skv - 1, D, dtype=f16), torch.zeros_like(v)))),
+        ("backward", dict(grads=(torch.zeros_like(q), torch.zeros_like(k), torch.zeros(B, H, Skv, D, dtype=f32)))),
+        ("backward", dict(workspace=torch.zeros(1024, dtype=f32))),            # bytes counted from numel
+        ("decode", dict(out=torch.zeros(B, H, Sq, D + 64, dtype=f16))),
+        ("decode", dict(lse=torch.zeros(B, H, 1, dtype=f32))),
+        ("decode", dict(k=torch.zeros(B, H, Skv, D, dtype=f32))),
+    ]
+
+
+@pytest.mark.parametrize("case", range(26))
+def test_binding_rejects_mismatched_tensors(case):
+    """A mismatched k, v, key mask, slope vector, dout or caller-supplied out,
+    lse, gradient or workspace tensor raises ValueError in the binding (it
+    would otherwise reach the kernels as an out-of-bounds read or write)."""
+    import torch
+    import tiled_online_softmax_flashattention_amd as fa
+    cases = _bad_cases()
+    assert len(cases) == 26
+    fn_name, over = cases[case]
+    q, k, v = _cpu_inputs()
+    B, H, Sq, D = q.shape
+    args = dict(q=q, k=k, v=v)
+    for name in ("q", "k", "v"):
+        if name in over:
+            args[name] = over.pop(name)
+    if fn_name == "forward":
+        call = lambda: fa.forward(args["q"], args["k"], args["v"], **over)
+    elif fn_name == "backward":
+        out = over.pop("out", torch.zeros_like(q))
+        lse = over.pop("lse", torch.zeros(B, H, Sq, dtype=torch.float32))
+        dout = over.pop("dout", torch.zeros_like(q))
+        call = lambda: fa.backward(args["q"], args["k"], args["v"], out, lse, dout, **over)
+    else:
+        call = lambda: fa.decode(args["q"], args["k"], args["v"], **over)
+    with pytest.raises(ValueError):
+        call()
+
+
+def test_binding_accepts_matching_cpu_tensors_until_the_device_check():
+    """Well-formed tensors pass the shape checks and are then refused only
+    because they are not on a GPU (the library is never called)."""
+    import torch
+    import tiled_online_softmax_flashattention_amd as fa
+    q, k, v = _cpu_inputs()
+    B, H, Sq, D = q.shape
+    with pytest.raises(ValueError, match="cuda"):
+        fa.forward(q, k, v, key_mask=torch.ones(B, k.shape[2], dtype=torch.uint8),
+                   out=torch.zeros_like(q), lse=torch.zeros(B, H, Sq, dtype=torch.float32))

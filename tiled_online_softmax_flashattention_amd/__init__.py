@@ -60,9 +60,8 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be (batch, heads, seq, head_dim)")
     if block_mask is not None:
-        want = block_mask_shape(q.shape[0], q.shape[1], q.shape[2], k.shape[2])
-        if tuple(block_mask.shape) != want or block_mask.dtype != torch.uint8:
-            raise ValueError(f"block_mask must be uint8 of shape {want}")
+        _expect(block_mask, "block_mask", block_mask_shape(q.shape[0], q.shape[1], q.shape[2], k.shape[2]),
+                torch.uint8)
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if score_mod not in _MOD:
@@ -93,6 +92,45 @@ def _check_tensors(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, name, shape, dtype):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+
+
+def _validate(q, k, v, *, key_mask=None, alibi_slopes=None, block_mask=None, out=None, lse=None, dout=None,
+              grads=(None, None, None), workspace=None):
+    """Shapes and dtypes of every tensor against q and k, so that no
+    mismatched tensor reaches the library as an out-of-bounds read or write.
+    Pure metadata checks (they run on CPU tensors too)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None or t.dim() != 4:
+            raise ValueError(f"{name} must be (batch, heads, seq, head_dim)")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    _expect(k, "k", (B, H, Skv, D), q.dtype)
+    _expect(v, "v", (B, H, Skv, D), q.dtype)
+    _expect(key_mask, "key_mask", (B, Skv), torch.uint8)
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.dim() != 1 or alibi_slopes.numel() < H:
+            raise ValueError(f"alibi_slopes must be a float32 vector of at least {H} entries")
+    _expect(block_mask, "block_mask", block_mask_shape(B, H, Sq, Skv), torch.uint8)
+    _expect(out, "out", (B, H, Sq, D), q.dtype)
+    _expect(lse, "lse", (B, H, Sq), torch.float32)
+    _expect(dout, "dout", (B, H, Sq, D), q.dtype)
+    dq, dk, dv = grads
+    _expect(dq, "dq", (B, H, Sq, D), q.dtype)
+    _expect(dk, "dk", (B, H, Skv, D), q.dtype)
+    _expect(dv, "dv", (B, H, Skv, D), q.dtype)
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor (its numel is the byte count)")
+
+
 def _mask_u8(key_mask):
     if key_mask is None:
         return None
@@ -103,7 +141,8 @@ def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None,
             checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None):
     """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
-    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     out = torch.empty_like(q) if out is None else out
@@ -130,7 +169,10 @@ def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=
     if which not in ("all", "dq", "dkdv"):
         raise ValueError(f"which must be 'all', 'dq' or 'dkdv', not {which!r}")
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
-    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              dout=dout, grads=grads if grads is not None else (None, None, None), workspace=workspace)
+    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask, workspace,
+                   *(grads if grads is not None else ()))
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     need = backward_workspace_bytes(p)
@@ -160,7 +202,9 @@ def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=N
     position q_offset + i), split over the key axis.  With causal=True a row
     sees keys up to its position only."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
-    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              workspace=workspace)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, workspace)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
     need = decode_workspace_bytes(p)
@@ -191,6 +235,7 @@ def _plan(fn, name, args, keep):
 def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
                  alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
     _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
@@ -203,6 +248,8 @@ def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=Fals
                   score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
     """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              dout=dout, grads=(dq, dk, dv), workspace=workspace)
     _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
@@ -216,6 +263,8 @@ def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=Fals
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
                 checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None):
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              workspace=workspace)
     _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
