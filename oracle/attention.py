@@ -211,3 +211,65 @@ def decode(q, k, v, *, scale: float, key_mask=None, mod: int = MOD_NONE, alibi_s
         raise ValueError("decode takes seq_q = 1")
     return forward(q, k, v, scale=scale, causal=causal, key_mask=key_mask, mod=mod,
                    alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset)
+
+
+def magnitudes(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None,
+               mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
+               rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None):
+    """Magnitudes that bound the rounding error of an fp32 evaluation of the
+    forward and backward, per output element.
+
+    An fp32 kernel forms every output as sums of products (dot products of
+    length head_dim for the scores and dP, sums over keys or queries for O, dQ,
+    dK, dV), and each rounding error is at most u = 2^-24 times the magnitude
+    of the quantity it rounds.  Carrying absolute values through the same
+    formulas gives, for every output element, the magnitude M that its
+    accumulated rounding error is proportional to:
+
+    * a_ij = scale * sum_d |q_id| |k_jd| + |bias_ij|: magnitude of the score,
+      whose rounding moves P_ij by a relative amount proportional to a_ij, and
+      lse_i by the P-weighted mean abar_i of a_ij; r_ij = 1 + a_ij + abar_i is
+      the relative error weight of P_ij (the 1 for the exponential and the
+      normalisation themselves);
+    * M_o = (P o r) |V|,  M_dv = (P o r)^T |dO|;
+    * the error of dS_ij = P_ij (dP_ij - D_i) is weighted by
+      T_ij = P_ij (r_ij |dP_ij - D_i| + b_ij + c_i) with b_ij = sum_d |dO_id| |v_jd|
+      (magnitude of dP_ij) and c_i = sum_d |dO_id| (M_o,id + |O_id|)
+      (magnitude of D_i = <dO_i, O_i> including the error O carries);
+    * M_dq = scale * T |K|,  M_dk = scale * T^T |Q|.
+
+    Returns (M_o, M_dq, M_dk, M_dv) with the shapes of (o, dq, dk, dv) from
+    forward/backward with the same ``rows``.  Every M is at least the absolute
+    value of the corresponding result (r >= 1 and T_ij >= |dS_ij|).
+    """
+    q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
+    do = as_f64(dout)
+    B, H, _, D = q.shape
+    seq_kv = k.shape[2]
+    m_o = np.zeros((B, H, len(rows), v.shape[3]))
+    m_dq = np.zeros((B, H, len(rows), D))
+    m_dk = np.zeros_like(k)
+    m_dv = np.zeros_like(v)
+    kv_idx = np.arange(seq_kv)
+    pos = rows + int(q_offset)
+    for b in range(B):
+        ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
+        for h in range(H):
+            bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
+            qb, dob = q[b, h, rows], do[b, h, rows]
+            okh = ok if block_mask is None else ok & _block_allowed(block_mask, b, h, rows, seq_kv)
+            _, _, p = _probabilities(qb, k[b, h], scale, bias, okh)
+            a = scale * (np.abs(qb) @ np.abs(k[b, h]).T) + np.abs(bias)
+            abar = (p * a).sum(axis=1)
+            pr = p * (1.0 + a + abar[:, None])
+            o = p @ v[b, h]
+            m_o[b, h] = pr @ np.abs(v[b, h])
+            dp = dob @ v[b, h].T
+            d_row = (p * dp).sum(axis=1)
+            bmag = np.abs(dob) @ np.abs(v[b, h]).T
+            cmag = (np.abs(dob) * (m_o[b, h] + np.abs(o))).sum(axis=1)
+            t = pr * np.abs(dp - d_row[:, None]) + p * (bmag + cmag[:, None])
+            m_dq[b, h] = scale * (t @ np.abs(k[b, h]))
+            m_dk[b, h] = scale * (t.T @ np.abs(qb))
+            m_dv[b, h] = pr.T @ np.abs(dob)
+    return m_o, m_dq, m_dk, m_dv

@@ -11,8 +11,8 @@ Removing blocks (with a key mask on top) leaves each query few keys, so the
 probabilities concentrate and dK, dV grow to about 10 (oracle: max|dV| = 10.3
 for fp32 D = 128 with a key mask); a 300-term fp32 sum of that size resolves
 to about 1e-6 of it, above the absolute 1e-5.  The fp32 small cases therefore
-take the bars scaled by max(1, max|ref|) (the ragged-shape convention of
-parity.err); the long sampled cases stay strict.
+pass either within the absolute bars or within the per-element bound derived
+from the accumulation (tests/bounds.py); the long sampled cases stay strict.
 """
 import numpy as np
 import pytest
@@ -21,7 +21,7 @@ import torch
 import oracle
 import tiled_online_softmax_flashattention_amd as fa
 import workloads as W
-from parity import check, check_lse, full_parity, oracle_kw, sampled_parity, say, to_dev
+from parity import check, check_case, check_lse, full_parity, oracle_kw, sampled_parity, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -168,11 +168,4 @@ def test_block_mask_with_query_offset(gpu_lib, dtype, D):
     dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
     torch.cuda.synchronize()
     okw = dict(oracle_kw(w, inputs), q_offset=off)
-    o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
-    dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
-    strict = dtype != "f32"
-    check("o", out, o_ref, dtype, "o", strict)
-    check_lse(lse, lse_ref)
-    check("dq", dq, dq_r, dtype, "grad", strict)
-    check("dk", dk, dk_r, dtype, "grad", strict)
-    check("dv", dv, dv_r, dtype, "grad", strict)
+    check_case(dtype, inputs, okw, out, lse, (dq, dk, dv), strict=dtype != "f32")

@@ -510,3 +510,95 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(oracle, "backward", bad_backward)
     with pytest.raises(AssertionError):
         test_gradients_match_central_differences(False, MOD_NONE, False)
+
+
+# --------------------------------------------------------------------------- error magnitudes
+
+from bounds import U32, kappa, within  # noqa: E402
+
+
+def _mag_case(causal, mod, use_mask, B=2, H=2, Sq=9, Skv=13, D=6, seed=70):
+    q, k, v, do = (_rand((B, H, Sq if i in (0, 3) else Skv, D), seed + i) for i in range(4))
+    km = None
+    if use_mask:
+        km = (np.random.default_rng(seed + 9).random((B, Skv)) < 0.6).astype(np.uint8)
+        km[:, 0] = 1
+    if causal:
+        Skv = Sq
+        k, v = k[:, :, :Sq], v[:, :, :Sq]
+        km = None if km is None else km[:, :Sq]
+    kw = dict(scale=0.4, causal=causal, mod=mod, key_mask=km)
+    return q, k, v, do, kw
+
+
+@pytest.mark.parametrize("causal,mod,use_mask", [(False, MOD_NONE, False), (True, MOD_ALIBI, False),
+                                                 (False, MOD_CHECKERBOARD, True), (True, MOD_NONE, True)])
+def test_magnitudes_bound_the_results(causal, mod, use_mask):
+    """Every magnitude is at least the absolute value of the result it
+    belongs to (triangle inequality on the same sums)."""
+    q, k, v, do, kw = _mag_case(causal, mod, use_mask)
+    o, _ = oracle.forward(q, k, v, **kw)
+    g = oracle.backward(q, k, v, do, **kw)
+    for m, r in zip(oracle.magnitudes(q, k, v, do, **kw), (o,) + tuple(g)):
+        assert np.all(m >= np.abs(r) - 1e-12)
+
+
+def test_magnitudes_closed_forms():
+    """q = 0 and v >= 0 with no score_mod: every score is 0, so a_ij = 0,
+    r_ij = 1 and M_o equals O = mean of V exactly; dO >= 0 makes M_dv = dV.
+    A single kept key j*: P is one-hot, r = 1 + 2 a_ij*, so
+    M_o,i = (1 + 2 scale sum_d |q_id| |k_j*d|) |v_j*|."""
+    B, H, S, D = 1, 2, 7, 5
+    v = np.abs(_rand((B, H, S, D), 80))
+    k = _rand((B, H, S, D), 81)
+    do = np.abs(_rand((B, H, S, D), 82))
+    q0 = np.zeros((B, H, S, D))
+    mo, _, _, mdv = oracle.magnitudes(q0, k, v, do, scale=0.3)
+    o, _ = oracle.forward(q0, k, v, scale=0.3)
+    _, _, dv = oracle.backward(q0, k, v, do, scale=0.3)
+    np.testing.assert_allclose(mo, np.broadcast_to(v.mean(axis=2, keepdims=True), mo.shape), atol=1e-14)
+    np.testing.assert_allclose(mo, o, atol=1e-14)
+    np.testing.assert_allclose(mdv, dv, atol=1e-14)
+    q = _rand((B, H, S, D), 83)
+    km = np.zeros((B, S), dtype=np.uint8)
+    km[0, 4] = 1
+    mo1, _, _, _ = oracle.magnitudes(q, k, v, do, scale=0.3, key_mask=km)
+    a = 0.3 * (np.abs(q) * np.abs(k[:, :, 4:5])).sum(axis=3, keepdims=True)
+    np.testing.assert_allclose(mo1, (1 + 2 * a) * np.abs(v[:, :, 4:5]), rtol=1e-14)
+
+
+@pytest.mark.parametrize("causal,mod,use_mask,D", [(False, MOD_CHECKERBOARD, True, 64), (True, MOD_ALIBI, False, 64),
+                                                   (False, MOD_NONE, False, 128), (True, MOD_NONE, True, 32)])
+def test_fp32_evaluation_stays_within_the_derived_bound(causal, mod, use_mask, D):
+    """An independent fp32 evaluation of the definition (torch CPU float32:
+    matmul, softmax and autograd) against the fp64 oracle: every element of O,
+    dQ, dK and dV is within kappa u M of the exact value."""
+    B, H, Sq, Skv = 1, 2, 150, 230
+    if causal:
+        Skv = Sq
+    rng = np.random.default_rng(90)
+    q, k, v, do = (rng.standard_normal((B, H, Sq if i in (0, 3) else Skv, D)).astype(np.float32) for i in range(4))
+    km = (rng.random((B, Skv)) < 0.5).astype(np.uint8) if use_mask else None
+    if km is not None:
+        km[:, 0] = 1
+    scale = 1.0 / math.sqrt(D)
+    kw = dict(scale=scale, causal=causal, mod=mod, key_mask=km)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    pos, kj = np.arange(Sq), np.arange(Skv)
+    bias = torch.from_numpy(np.stack([oracle.score_bias(mod, h, pos, kj, H) for h in range(H)])).float()
+    s = scale * (tq @ tk.transpose(-1, -2)) + bias[None]
+    ok = torch.ones(B, 1, Sq, Skv, dtype=torch.bool)
+    if km is not None:
+        ok &= torch.from_numpy(km != 0)[:, None, None, :]
+    if causal:
+        ok &= torch.from_numpy(kj[None, :] <= pos[:, None])[None, None]
+    o32 = torch.softmax(s.masked_fill(~ok, float("-inf")), dim=-1) @ tv
+    o32.backward(torch.from_numpy(do))
+    o, _ = oracle.forward(q, k, v, **kw)
+    g = oracle.backward(q, k, v, do, **kw)
+    mags = oracle.magnitudes(q, k, v, do, **kw)
+    kap = kappa(Sq, Skv, D)
+    for name, got, ref, m in zip(("o", "dq", "dk", "dv"), (o32.detach(), tq.grad, tk.grad, tv.grad), (o,) + tuple(g),
+                                 mags):
+        ok_, ratio = within(np.abs(got.double().numpy() - ref), 0.0, kap, m)
+        assert ok_, f"{name}: error / (kappa u M) = {ratio:.3f}"

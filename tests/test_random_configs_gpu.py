@@ -4,18 +4,18 @@ block mask, forward and backward, each case against the fp64 oracle.
 
 The cases are drawn once from a fixed seed (the list is the same on every
 run).  Bars as elsewhere: 16-bit max-abs-err / max|ref| <= 2e-2 (O) and 5e-2
-(gradients); fp32 1e-4 (O) and 1e-5 (gradients), scaled by max(1, max|ref|)
-as for the other edge-shape cases (random masks can leave a row a handful of
-keys, so dK and dV grow past 1); lse within 1e-3 + 1e-5 |lse|.
+(gradients); fp32 1e-4 (O) and 1e-5 (gradients) absolute, or, where random
+masks leave a row a handful of keys and dK, dV grow past 1, the per-element
+bound derived from the accumulation (tests/bounds.py); lse within
+1e-3 + 1e-5 |lse|.
 """
 import numpy as np
 import pytest
 import torch
 
-import oracle
 import tiled_online_softmax_flashattention_amd as fa
 import workloads as W
-from parity import MOD_NAME, check, check_lse, say, to_dev
+from parity import MOD_NAME, check_case, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,4 @@ def test_random_config(gpu_lib, case):
     okw = dict(scale=w.scale, causal=c["causal"], mod=c["mod"], q_offset=c["off"],
                key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy(),
                block_mask=None if inputs.get("block_mask") is None else inputs["block_mask"].numpy() != 0)
-    o_ref, lse_ref = oracle.forward(inputs["q"], inputs["k"], inputs["v"], **okw)
-    dq_r, dk_r, dv_r = oracle.backward(inputs["q"], inputs["k"], inputs["v"], inputs["dout"], **okw)
-    check("o", out, o_ref, c["dtype"], "o", strict=False)
-    check_lse(lse, lse_ref)
-    for name, g, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
-        check(name, g, r, c["dtype"], "grad", strict=False)
+    check_case(c["dtype"], inputs, okw, out, lse, (dq, dk, dv), strict=False)

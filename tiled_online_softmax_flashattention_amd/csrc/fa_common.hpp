@@ -269,9 +269,9 @@ struct Rows32 {
 // it: a pipelined loop then waits with its own vmcnt counts instead of the
 // compiler draining every load in flight before each LDS read.  The
 // instruction has no register result (its address registers are read at
-// issue); the caller's waits and barriers order it.  It overwrites M0, so a
-// kernel using it must not keep anything else in M0 (the only user, the
-// head_dim 512 fp32 forward, has no other M0 access in its ISA).
+// issue); the caller's waits and barriers order it.  It writes M0 and says so
+// (an m0 clobber), so the compiler re-establishes any other value it keeps in
+// M0 after it.  Users: the head_dim 512 fp32 forward and dQ pass.
 __device__ __forceinline__ void direct_load16_untracked(const void* g, const void* lds_blk) {
   const uint32_t m0v = (uint32_t)(uintptr_t)(lds_void_ptr)lds_blk;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0v), "v"(g) : "memory", "m0");
