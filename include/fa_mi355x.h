@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Edge of the blocks of a block mask (query rows and keys), and the longest
  * seq_q / seq_kv a call with a block mask takes. */
@@ -78,7 +78,8 @@ typedef enum {
   FA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad enum, bad shape */
   FA_ERR_UNSUPPORTED = 2,        /* valid request outside what the kernels implement */
   FA_ERR_WORKSPACE_TOO_SMALL = 3,
-  FA_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+  FA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+  FA_ERR_SCRATCH_LIMIT = 5       /* fa_decode_noalloc: the problem needs more than FA_DECODE_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -158,6 +159,23 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
 fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Bytes of the fixed device scratch behind fa_decode_noalloc (per device). */
+#define FA_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* fa_decode without a workspace argument, for callers that cannot allocate
+ * device memory at call time (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same problems, arguments and
+ * results as fa_decode; the per-chunk partials go to a fixed scratch array
+ * of FA_DECODE_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends.  A problem whose fa_decode_workspace_size
+ * exceeds that returns FA_ERR_SCRATCH_LIMIT (nothing launched).  The call
+ * allocates nothing.  Every call on one device shares that device's scratch
+ * (the last call's partials stay in it): calls that overlap on one device,
+ * e.g. on two streams, race and give undefined results; calls on one stream
+ * are ordered and safe.  Nothing in the scratch needs to start at zero. */
+fa_status fa_decode_noalloc(const fa_problem* p, const void* q, const void* k, const void* v,
+                            void* out, float* lse, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

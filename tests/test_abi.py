@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 3
-    for s in range(5):
+    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 4
+    for s in range(6):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"
 
@@ -296,3 +296,22 @@ def test_binding_accepts_matching_cpu_tensors_until_the_device_check():
     with pytest.raises(ValueError, match="cuda"):
         fa.forward(q, k, v, key_mask=torch.ones(B, k.shape[2], dtype=torch.uint8),
                    out=torch.zeros_like(q), lse=torch.zeros(B, H, Sq, dtype=torch.float32))
+
+
+def test_decode_noalloc_rules():
+    """fa_decode_noalloc validates like fa_decode (no workspace argument) and
+    refuses a problem whose partials exceed its fixed scratch, before any
+    HIP call."""
+    lib = _lib.load()
+    nd = lambda p: lib.fa_decode_noalloc(ctypes.byref(p), A[0], A[1], A[2], A[3], A[4], None)
+    assert lib.fa_decode_noalloc(None, A[0], A[1], A[2], A[3], A[4], None) == INVALID
+    assert nd(prob(seq_q=65)) == INVALID
+    assert nd(prob(seq_q=1, head_dim=512, dtype=_lib.FA_F32)) == UNSUP
+    assert nd(prob(seq_q=1, scale=0.0)) == UNSUP
+    assert lib.fa_decode_noalloc(ctypes.byref(prob(seq_q=1)), None, A[1], A[2], A[3], A[4], None) == INVALID
+    big = prob(batch=4, heads=32, seq_q=64, seq_kv=32768, head_dim=128)
+    n = ctypes.c_size_t(0)
+    assert lib.fa_decode_workspace_size(ctypes.byref(big), ctypes.byref(n)) == _lib.FA_OK
+    assert n.value > _lib.FA_DECODE_SCRATCH_BYTES
+    assert nd(big) == _lib.FA_ERR_SCRATCH_LIMIT
+    assert b"scratch" in lib.fa_status_string(_lib.FA_ERR_SCRATCH_LIMIT)

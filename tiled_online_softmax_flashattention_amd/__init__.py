@@ -27,7 +27,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["forward", "backward", "decode", "backward_workspace_bytes", "decode_workspace_bytes",
+__all__ = ["forward", "backward", "decode", "decode_noalloc", "backward_workspace_bytes", "decode_workspace_bytes",
            "FaError", "problem", "plan_forward", "plan_backward", "plan_decode", "block_mask_shape"]
 
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
@@ -215,6 +215,25 @@ def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=N
     lib = _lib.load()
     _lib.check(lib.fa_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                              workspace.numel(), _stream(q)), "fa_decode")
+    return out, lse
+
+
+def decode_noalloc(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5),
+                   q_offset=0, causal=False, block_mask=None, out=None, lse=None):
+    """decode() through fa_decode_noalloc: no workspace, the library's fixed
+    per-device scratch instead (for callers that cannot allocate at call time;
+    pass out and lse to allocate nothing here either).  Calls that overlap on
+    one device race on that scratch."""
+    key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse)
+    p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = _lib.load()
+    _lib.check(lib.fa_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q)),
+               "fa_decode_noalloc")
     return out, lse
 
 

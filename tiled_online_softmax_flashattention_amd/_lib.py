@@ -11,7 +11,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa_mi355x.so")
 
-FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP = range(5)
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP, FA_ERR_SCRATCH_LIMIT = range(6)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MOD_NONE, FA_MOD_ALIBI, FA_MOD_CHECKERBOARD = 0, 1, 2
 
@@ -30,9 +30,10 @@ class FaProblem(ctypes.Structure):
         ("block_mask", _c_void_p),
     ]
 
-FA_ABI_VERSION = 3
+FA_ABI_VERSION = 4
 FA_BLOCK_MASK_BLOCK = 128
 FA_BLOCK_MASK_MAX_SEQ = 131072
+FA_DECODE_SCRATCH_BYTES = 16 << 20
 
 
 _P = ctypes.POINTER(FaProblem)
@@ -42,6 +43,7 @@ SIGNATURES = {
     "fa_backward": (ctypes.c_int, [_P] + [_c_void_p] * 10 + [ctypes.c_size_t, _c_void_p]),
     "fa_decode_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_decode": (ctypes.c_int, [_P] + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
+    "fa_decode_noalloc": (ctypes.c_int, [_P] + [_c_void_p] * 6),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_abi_version": (ctypes.c_int, []),
 }

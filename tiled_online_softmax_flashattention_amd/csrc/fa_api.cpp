@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa_mi355x.h"
 #include "fa_launch.hpp"
 
@@ -221,26 +223,35 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes) {
   return FA_OK;
 }
 
-fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both decode entry points (pure host logic).
+fa_status validate_decode(const fa_problem* p, const void* q, const void* k, const void* v, void* out,
+                          float* lse) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
   if (p->seq_q > kMaxDecodeQ) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
   if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
-  if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
-  int n_split, chunk;
-  const size_t need = decode_ws(p, &n_split, &chunk);
-  if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  return FA_OK;
+}
 
+// The decode launches on a validated problem with `ws` holding at least
+// decode_ws(p) bytes.
+fa_status decode_launch(const fa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                        void* ws, void* stream) {
+  int n_split, chunk;
+  decode_ws(p, &n_split, &chunk);
   fa::AttnArgs a = make_args(p);
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = out;
   a.lse = lse;
-  a.partial = (float*)workspace;
+  a.partial = (float*)ws;
   a.n_split = n_split;
   a.chunk = chunk;
   hipStream_t st = (hipStream_t)stream;
@@ -261,6 +272,59 @@ fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const voi
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Fixed device scratch of fa_decode_noalloc: the per-chunk partials live in
+// this array instead of a caller workspace.  Every device the library runs
+// on holds its own copy (module-scope device memory) until the process ends.
+// Host code never uses the array's name as an address: its device address
+// is taken once per device with hipGetSymbolAddress and kept below.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first
+// call on that device (with that device current).
+fa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status s = validate_decode(p, q, k, v, out, lse);
+  if (s != FA_OK) return s;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
+  int n_split, chunk;
+  if (workspace_bytes < decode_ws(p, &n_split, &chunk)) return FA_ERR_WORKSPACE_TOO_SMALL;
+  return decode_launch(p, q, k, v, out, lse, workspace, stream);
+}
+
+fa_status fa_decode_noalloc(const fa_problem* p, const void* q, const void* k, const void* v, void* out,
+                            float* lse, void* stream) {
+  fa_status s = validate_decode(p, q, k, v, out, lse);
+  if (s != FA_OK) return s;
+  int n_split, chunk;
+  if (decode_ws(p, &n_split, &chunk) > (size_t)FA_DECODE_SCRATCH_BYTES) return FA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != FA_OK) return s;
+  return decode_launch(p, q, k, v, out, lse, ws, stream);
+}
+
 const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
@@ -268,6 +332,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "unsupported problem (dtype, head_dim or size)";
     case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_SCRATCH_LIMIT: return "problem needs more than the fixed scratch of the allocation-free entry point";
   }
   return "unknown status";
 }
