@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 /* Edge of the blocks of a block mask (query rows and keys), and the longest
  * seq_q / seq_kv a call with a block mask takes. */
@@ -92,6 +92,12 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  *                       checker_odd (the workloads use +0.5 / -0.5). */
 typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2 } fa_mod_kind;
 
+/* dQ formation of the backward (fa_problem.dq_mode). */
+typedef enum { FA_DQ_AUTO = 0, FA_DQ_SEPARATE = 1, FA_DQ_ATOMIC = 2 } fa_dq_mode;
+
+/* Most key chunks fa_decode splits into (fa_problem.kv_splits). */
+#define FA_MAX_KV_SPLITS 256
+
 typedef struct {
   int64_t batch, heads, seq_q, seq_kv, head_dim;
   int32_t dtype;             /* fa_dtype */
@@ -111,6 +117,21 @@ typedef struct {
    * removed block.  NULL = no block mask.  Requires seq_q and seq_kv
    * <= FA_BLOCK_MASK_MAX_SEQ (else FA_ERR_UNSUPPORTED). */
   const uint8_t* block_mask;
+  /* How fa_backward forms dQ when dq, dk and dv are all requested (fa_dq_mode).
+   * FA_DQ_AUTO: the library's measured choice for the dtype and head_dim.
+   * FA_DQ_SEPARATE: a query-stationary pass that recomputes the scores and
+   *   dP; no atomics, bitwise-repeatable.
+   * FA_DQ_ATOMIC: the key/value pass also adds scale * dS K into an fp32
+   *   workspace with atomics, then a conversion kernel writes dq; saves the
+   *   recomputation, but the order of the additions (and so the last bits of
+   *   dq) varies between calls.  f16 and bf16 only, and seq_q * head_dim
+   *   below 2^28 (else FA_ERR_UNSUPPORTED).
+   * A call that skips the query or the key/value pass ignores the mode. */
+  int32_t dq_mode;
+  /* fa_decode: 0 = the library's split of the key axis; n > 0 = about n key
+   * chunks (1 <= n <= FA_MAX_KV_SPLITS; a 16-bit query block rounds chunks up
+   * to whole 64-key tiles).  The results do not depend on it beyond rounding. */
+  int32_t kv_splits;
 } fa_problem;
 
 /* Supported: dtype f16 or bf16 with head_dim 64 or 128; dtype f32 with
@@ -138,8 +159,12 @@ fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes);
  * at least one pass must be requested, and dk, dv are NULL together or not
  * at all.
  * The workspace (>= fa_backward_workspace_size bytes, 256-byte aligned) is
- * scratch: its contents on entry are ignored and on exit undefined.  Every
- * kernel is deterministic: repeated calls give bitwise-equal results. */
+ * scratch: its contents on entry are ignored and on exit undefined.  Its size
+ * depends on p->dq_mode (the atomic mode adds seq_q * head_dim floats per
+ * (batch, head)).  With dq_mode FA_DQ_SEPARATE every kernel is deterministic:
+ * repeated calls give bitwise-equal results; FA_DQ_ATOMIC (or FA_DQ_AUTO
+ * where it picks the atomic mode) gives bitwise-equal dk, dv and a dq that
+ * varies in its last bits. */
 fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const void* v,
                       const void* out, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,

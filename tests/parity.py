@@ -99,9 +99,9 @@ def run_forward(w: W.Workload, dev: dict):
     return out, lse
 
 
-def run_backward(w: W.Workload, dev: dict, out, lse, dout):
+def run_backward(w: W.Workload, dev: dict, out, lse, dout, dq_mode: str = "auto"):
     g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dout, key_mask=dev.get("key_mask"),
-                    block_mask=dev.get("block_mask"), **kw_of(w))
+                    block_mask=dev.get("block_mask"), dq_mode=dq_mode, **kw_of(w))
     torch.cuda.synchronize()
     return g
 
@@ -138,8 +138,10 @@ def check_case(dtype: str, inputs: dict, okw: dict, out, lse, grads=None, strict
     return res
 
 
-def full_parity(w: W.Workload, backward: bool = True, inputs=None, strict: bool = True) -> dict:
-    """Every output element against the oracle (sizes the oracle finishes quickly)."""
+def full_parity(w: W.Workload, backward: bool = True, inputs=None, strict: bool = True,
+                dq_modes=("auto",)) -> dict:
+    """Every output element against the oracle (sizes the oracle finishes
+    quickly); the backward once per dQ mode in dq_modes, against one oracle run."""
     say(f"[parity] {w.name} B{w.batch} H{w.heads} Sq{w.seq_q} Skv{w.seq_kv} D{w.head_dim} {w.dtype} "
         f"causal={w.causal} mod={w.mod} mask={w.key_mask}")
     inputs = inputs or w.make(with_dout=backward)
@@ -151,10 +153,13 @@ def full_parity(w: W.Workload, backward: bool = True, inputs=None, strict: bool 
     res = {"o": check("o", out, o_ref, w.dtype, "o", strict, None if mags is None else mags[0], kap)}
     check_lse(lse, lse_ref)
     if backward:
-        grads = run_backward(w, dev, out, lse, dev["dout"])
-        for i, name in enumerate(("dq", "dk", "dv")):
-            res[name] = check(name, grads[i], g_ref[i], w.dtype, "grad", strict,
-                              None if mags is None else mags[i + 1], kap)
+        for mode in dq_modes:
+            grads = run_backward(w, dev, out, lse, dev["dout"], dq_mode=mode)
+            sfx = "" if mode == "auto" else f" ({mode} dQ)"
+            for i, name in enumerate(("dq", "dk", "dv")):
+                res[name + sfx] = check(name + sfx, grads[i], g_ref[i], w.dtype, "grad", strict,
+                                        None if mags is None else mags[i + 1], kap)
+            del grads
     say(f"[parity] ok {res}")
     return res
 

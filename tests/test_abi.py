@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 4
+    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 5
     for s in range(6):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"

@@ -54,6 +54,16 @@ def test_block_mask_every_instance(gpu_lib, dtype, D, causal, mod, mask):
     full_parity(w, inputs=inputs, strict=dtype != "f32")
 
 
+@pytest.mark.parametrize("dtype,D,causal,mod,mask", [("f16", 64, True, W.MOD_ALIBI, False),
+                                                     ("bf16", 128, False, W.MOD_CHECKERBOARD, True),
+                                                     ("f16", 128, True, W.MOD_NONE, True),
+                                                     ("bf16", 64, False, W.MOD_NONE, False)])
+def test_block_mask_atomic_dq(gpu_lib, dtype, D, causal, mod, mask):
+    """Block-sparse backward with dQ from atomics in the key/value pass."""
+    w, inputs = block_case(dtype, D, causal, mod, mask, wid=209)
+    full_parity(w, inputs=inputs, dq_modes=("atomic",))
+
+
 @pytest.mark.parametrize("causal,mod,mask", [(False, W.MOD_NONE, False), (True, W.MOD_ALIBI, False),
                                              (False, W.MOD_CHECKERBOARD, True), (True, W.MOD_NONE, True)])
 def test_block_mask_f32_d512(gpu_lib, causal, mod, mask):
@@ -82,7 +92,8 @@ def test_block_mask_empty_rows_and_columns(gpu_lib, dtype, D):
                                             ("f32", 512, False)])
 def test_full_block_mask_is_the_dense_result(gpu_lib, dtype, D, causal):
     """A block mask with every block set visits the dense tiles in the dense
-    order, so every output is bitwise equal to the call without one."""
+    order, so every output is bitwise equal to the call without one (dQ from
+    the deterministic separate pass)."""
     Sq = 333 if D < 512 else 150
     w = W.Workload("full block mask", 203, 2, 2, Sq, Sq, D, dtype, causal=causal, mod=W.MOD_ALIBI)
     dev = to_dev(w.make())
@@ -92,7 +103,7 @@ def test_full_block_mask_is_the_dense_result(gpu_lib, dtype, D, causal):
     for bm in (None, ones):
         kw = dict(causal=causal, score_mod="alibi", block_mask=bm)
         out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
-        g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+        g = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], dq_mode="separate", **kw)
         res.append((out, lse) + tuple(g))
     torch.cuda.synchronize()
     for a, b in zip(*res):

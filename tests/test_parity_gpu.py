@@ -36,6 +36,13 @@ def test_every_instance_small(gpu_lib, dtype, D, causal, mod, mask):
     full_parity(small(dtype, D, causal, mod, mask))
 
 
+@pytest.mark.parametrize("dtype,D,causal,mod,mask", [x for x in INSTANCES if x[0] != "f32"])
+def test_every_16bit_instance_both_dq_modes(gpu_lib, dtype, D, causal, mod, mask):
+    """The backward with dQ from the separate query pass and from fp32
+    atomics in the key/value pass, each against the oracle."""
+    full_parity(small(dtype, D, causal, mod, mask, wid=109), dq_modes=("separate", "atomic"))
+
+
 @pytest.mark.parametrize("causal,mod,mask", [(c, m, k) for c in (False, True) for m in MODS for k in (False, True)])
 def test_f32_d512_small(gpu_lib, causal, mod, mask):
     full_parity(small("f32", 512, causal, mod, mask, Sq=80, Skv=130, B=1, H=2))
@@ -94,14 +101,16 @@ def test_masked_keys_with_garbage_are_ignored(gpu_lib, dtype):
 
 
 def test_backward_is_deterministic(gpu_lib):
+    """With the separate dQ pass (no atomics) repeated calls are bitwise equal."""
     for dtype, D, causal in (("f16", 64, True), ("bf16", 128, False), ("f32", 512, True)):
         w = small(dtype, D, causal, W.MOD_ALIBI, False, Sq=150, B=1, H=2, wid=105)
         say(f"[determinism] {dtype} D{D} causal={causal}")
         dev = to_dev(w.make())
+        kw = dict(causal=causal, score_mod="alibi", dq_mode="separate")
         out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, score_mod="alibi")
-        g1 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], causal=causal, score_mod="alibi")
+        g1 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
         out2, lse2 = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, score_mod="alibi")
-        g2 = fa.backward(dev["q"], dev["k"], dev["v"], out2, lse2, dev["dout"], causal=causal, score_mod="alibi")
+        g2 = fa.backward(dev["q"], dev["k"], dev["v"], out2, lse2, dev["dout"], **kw)
         torch.cuda.synchronize()
         assert torch.equal(out, out2) and torch.equal(lse, lse2)
         for a, b in zip(g1, g2):
@@ -114,7 +123,7 @@ def test_backward_single_pass_matches_full(gpu_lib, dtype, D):
     dev = to_dev(w.make())
     kw = dict(causal=True, score_mod="alibi")
     out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
-    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], dq_mode="separate", **kw)
     dq1, n1, n2 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], which="dq", **kw)
     n3, dk1, dv1 = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], which="dkdv", **kw)
     torch.cuda.synchronize()
@@ -252,15 +261,16 @@ def test_workload_tiny_f32_exact(gpu_lib):
 def test_workload_prefill_f16_causal_alibi(gpu_lib):
     """The prefill workload at its full size (8, 8, 2048, 64), dense dO:
     every element of O, lse, dQ, dK and dV against the oracle (flash-attention-jax
-    page, value_and_grad_difference: plain against flash on o, dq, dk, dv)."""
-    full_parity(W.PREFILL_F16)
+    page, value_and_grad_difference: plain against flash on o, dq, dk, dv),
+    with both dQ modes."""
+    full_parity(W.PREFILL_F16, dq_modes=("separate", "atomic"))
 
 
 @pytest.mark.timeout(900)
 def test_workload_keypad_bf16_checkerboard(gpu_lib):
     """The key-padding workload at its full size (4, 16, 4096, 128), dense dO:
-    every element against the oracle."""
-    full_parity(W.KEYPAD_BF16)
+    every element against the oracle, with both dQ modes."""
+    full_parity(W.KEYPAD_BF16, dq_modes=("separate", "atomic"))
 
 
 @pytest.mark.parametrize("w", [W.DECODE_F16_2K, W.DECODE_F16_32K], ids=["2k", "32k"])

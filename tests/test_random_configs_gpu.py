@@ -54,7 +54,9 @@ def test_random_config(gpu_lib, case):
     kw = dict(causal=c["causal"], score_mod=MOD_NAME[c["mod"]], scale=w.scale, q_offset=c["off"],
               key_mask=dev.get("key_mask"), block_mask=dev.get("block_mask"))
     out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
-    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+    # 16-bit cases alternate between the two dQ modes
+    mode = "separate" if c["dtype"] == "f32" or c["id"] % 2 else "atomic"
+    dq, dk, dv = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], dq_mode=mode, **kw)
     torch.cuda.synchronize()
     okw = dict(scale=w.scale, causal=c["causal"], mod=c["mod"], q_offset=c["off"],
                key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy(),

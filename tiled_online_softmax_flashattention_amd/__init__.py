@@ -33,6 +33,7 @@ __all__ = ["forward", "backward", "decode", "decode_noalloc", "backward_workspac
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 _MOD = {None: _lib.FA_MOD_NONE, "none": _lib.FA_MOD_NONE, "alibi": _lib.FA_MOD_ALIBI,
         "checkerboard": _lib.FA_MOD_CHECKERBOARD}
+_DQ_MODE = {"auto": _lib.FA_DQ_AUTO, "separate": _lib.FA_DQ_SEPARATE, "atomic": _lib.FA_DQ_ATOMIC}
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -53,10 +54,13 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
             key_mask: Optional[torch.Tensor] = None, score_mod: Optional[str] = None,
             scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
             checker: Tuple[float, float] = (0.5, -0.5), q_offset: int = 0,
-            block_mask: Optional[torch.Tensor] = None) -> _lib.FaProblem:
+            block_mask: Optional[torch.Tensor] = None, dq_mode: str = "auto",
+            kv_splits: int = 0) -> _lib.FaProblem:
     """The C-ABI problem descriptor for these tensors.  q_offset is the
     position of query row 0 among the keys (0 for self-attention; the number
-    of cached keys before the first query with a KV cache)."""
+    of cached keys before the first query with a KV cache).  dq_mode ("auto",
+    "separate" or "atomic") picks how the backward forms dQ; kv_splits (0 =
+    the library's choice) the number of key chunks of a decode."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be (batch, heads, seq, head_dim)")
     if block_mask is not None:
@@ -78,6 +82,10 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     p.key_mask = None if key_mask is None else key_mask.data_ptr()
     p.q_offset = int(q_offset)
     p.block_mask = None if block_mask is None else block_mask.data_ptr()
+    if dq_mode not in _DQ_MODE:
+        raise ValueError(f"dq_mode must be one of {sorted(_DQ_MODE)}, not {dq_mode!r}")
+    p.dq_mode = _DQ_MODE[dq_mode]
+    p.kv_splits = int(kv_splits)
     return p
 
 
@@ -161,11 +169,13 @@ def backward_workspace_bytes(p: _lib.FaProblem) -> int:
 
 def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
              alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, workspace=None, grads=None,
-             which="all"):
+             which="all", dq_mode="auto"):
     """Gradients (dq, dk, dv) of sum(dout * out).
 
     which="dq" runs only the query pass (dk, dv come back as None), "dkdv"
-    only the key/value pass (dq is None), "all" both."""
+    only the key/value pass (dq is None), "all" both.  dq_mode: "separate"
+    (deterministic query pass), "atomic" (fp32 atomics in the key/value pass)
+    or "auto" (the library's measured choice)."""
     if which not in ("all", "dq", "dkdv"):
         raise ValueError(f"which must be 'all', 'dq' or 'dkdv', not {which!r}")
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
@@ -174,7 +184,8 @@ def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=
     _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask, workspace,
                    *(grads if grads is not None else ()))
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                dq_mode=dq_mode)
     need = backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -197,16 +208,18 @@ def decode_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0,
-           causal=False, block_mask=None, workspace=None, out=None, lse=None):
+           causal=False, block_mask=None, workspace=None, out=None, lse=None, kv_splits=0):
     """Attention for a short query block (1 <= seq_q <= 64, row i at key
-    position q_offset + i), split over the key axis.  With causal=True a row
-    sees keys up to its position only."""
+    position q_offset + i), split over the key axis (into about kv_splits
+    chunks; 0 = the library's choice).  With causal=True a row sees keys up
+    to its position only."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               workspace=workspace)
     _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, workspace)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                kv_splits=kv_splits)
     need = decode_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -264,14 +277,16 @@ def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=No
 
 
 def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,
-                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
+                  score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None,
+                  dq_mode="auto"):
     """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               dout=dout, grads=(dq, dk, dv), workspace=workspace)
     _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                dq_mode=dq_mode)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
@@ -280,13 +295,14 @@ def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=Fals
 
 
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-                checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None):
+                checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None, kv_splits=0):
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               workspace=workspace)
     _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                kv_splits=kv_splits)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
             _stream(q))

@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(PKG, "libfa_mi355x.so")
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_HIP, FA_ERR_SCRATCH_LIMIT = range(6)
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_MOD_NONE, FA_MOD_ALIBI, FA_MOD_CHECKERBOARD = 0, 1, 2
+FA_DQ_AUTO, FA_DQ_SEPARATE, FA_DQ_ATOMIC = 0, 1, 2
+FA_MAX_KV_SPLITS = 256
 
 # every function the header declares, with (restype, argtypes)
 _c_void_p = ctypes.c_void_p
@@ -28,9 +30,10 @@ class FaProblem(ctypes.Structure):
         ("checker_even", ctypes.c_float), ("checker_odd", ctypes.c_float),
         ("key_mask", _c_void_p), ("q_offset", ctypes.c_int64),
         ("block_mask", _c_void_p),
+        ("dq_mode", ctypes.c_int32), ("kv_splits", ctypes.c_int32),
     ]
 
-FA_ABI_VERSION = 4
+FA_ABI_VERSION = 5
 FA_BLOCK_MASK_BLOCK = 128
 FA_BLOCK_MASK_MAX_SEQ = 131072
 FA_DECODE_SCRATCH_BYTES = 16 << 20

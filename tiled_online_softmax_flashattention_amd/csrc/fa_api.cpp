@@ -50,6 +50,40 @@ fa_status validate_problem(const fa_problem* p) {
   // block-sparse loops keep their tile lists in LDS, sized for this length
   if (p->block_mask && (p->seq_q > FA_BLOCK_MASK_MAX_SEQ || p->seq_kv > FA_BLOCK_MASK_MAX_SEQ))
     return FA_ERR_UNSUPPORTED;
+  if (p->dq_mode != FA_DQ_AUTO && p->dq_mode != FA_DQ_SEPARATE && p->dq_mode != FA_DQ_ATOMIC)
+    return FA_ERR_INVALID_ARGUMENT;
+  if (p->kv_splits < 0) return FA_ERR_INVALID_ARGUMENT;
+  if (p->kv_splits > FA_MAX_KV_SPLITS) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// The atomic dQ mode's buffer descriptors bound a (batch, head) slice of the
+// fp32 accumulator by a 32-bit byte count.
+bool dq_atomic_fits(const fa_problem* p) {
+  return p->dtype != FA_F32 && p->seq_q * p->head_dim < ((int64_t)1 << 28);
+}
+
+// Measured choice of FA_DQ_AUTO per (dtype, head_dim): true = atomic.  The
+// atomic key/value pass loses at both 16-bit head dims on MI355X: its fp32
+// atomics (B*H*Sq*D per 128-key block) run at about 2 TB/s of L2 atomic
+// throughput, so the pass takes 233 vs 80 us (prefill f16 8x8x2048x64,
+// causal) and 3.28 vs 1.40 ms (key-padding bf16 4x16x4096x128), more than the
+// separate query pass it replaces (63 us, 0.99 ms).
+bool dq_atomic_by_default(const fa_problem* p) {
+  (void)p;
+  return false;
+}
+
+// Whether fa_backward forms dQ with atomics for this problem (when both
+// passes run).  FA_ERR_UNSUPPORTED for an explicit atomic request it cannot
+// serve.
+fa_status resolve_dq_atomic(const fa_problem* p, bool* atomic) {
+  if (p->dq_mode == FA_DQ_ATOMIC) {
+    if (!dq_atomic_fits(p)) return FA_ERR_UNSUPPORTED;
+    *atomic = true;
+  } else {
+    *atomic = p->dq_mode == FA_DQ_AUTO && dq_atomic_fits(p) && dq_atomic_by_default(p);
+  }
   return FA_OK;
 }
 
@@ -88,15 +122,18 @@ fa::AttnArgs make_args(const fa_problem* p) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct BwdLayout {
-  size_t delta_off, lse2_off, total;
+  size_t delta_off, lse2_off, dq_acc_off, total;
 };
 
-BwdLayout bwd_layout(const fa_problem* p) {
+// Workspace: delta and lse2 rows, and in the atomic dQ mode the fp32 dQ
+// accumulator (B, H, Sq, D).
+BwdLayout bwd_layout(const fa_problem* p, bool dq_atomic) {
   const size_t rows = (size_t)p->batch * p->heads * p->seq_q;
   BwdLayout l;
   l.delta_off = 0;
   l.lse2_off = round_up(rows * sizeof(float), 256);
-  l.total = l.lse2_off + round_up(rows * sizeof(float), 256);
+  l.dq_acc_off = l.lse2_off + round_up(rows * sizeof(float), 256);
+  l.total = l.dq_acc_off + (dq_atomic ? round_up(rows * (size_t)p->head_dim * sizeof(float), 256) : 0);
   return l;
 }
 
@@ -120,7 +157,12 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
     *chunk = (int)p->seq_kv;
     return 256;
   }
-  *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
+  if (p->kv_splits > 0) {   // the caller's split: about kv_splits chunks
+    const int len = decode_kv_len(p);
+    *chunk = (len + p->kv_splits - 1) / p->kv_splits;
+  } else {
+    *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
+  }
   if (p->seq_q > 1) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
   *n_split = (decode_kv_len(p) + *chunk - 1) / *chunk;
   return round_up((size_t)BH * (size_t)p->seq_q * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float),
@@ -161,7 +203,10 @@ fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
   if (!bytes) return FA_ERR_INVALID_ARGUMENT;
-  *bytes = bwd_layout(p).total;
+  bool atomic = false;
+  s = resolve_dq_atomic(p, &atomic);
+  if (s != FA_OK) return s;
+  *bytes = bwd_layout(p, atomic).total;
   return FA_OK;
 }
 
@@ -178,7 +223,11 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   if (want_kv && !tensors_ok({dk, dv})) return FA_ERR_INVALID_ARGUMENT;
   if (!lse || ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
-  const BwdLayout lay = bwd_layout(p);
+  bool atomic = false;
+  s = resolve_dq_atomic(p, &atomic);
+  if (s != FA_OK) return s;
+  atomic = atomic && want_q && want_kv;   // a single pass has no dQ to share
+  const BwdLayout lay = bwd_layout(p, atomic);
   if (workspace_bytes < lay.total) return FA_ERR_WORKSPACE_TOO_SMALL;
   const int D = (int)p->head_dim;
   const bool f32 = p->dtype == FA_F32;
@@ -198,6 +247,7 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   a.dv = dv;
   a.delta = (float*)((char*)workspace + lay.delta_off);
   a.lse2 = (float*)((char*)workspace + lay.lse2_off);
+  a.dq_acc = atomic ? (float*)((char*)workspace + lay.dq_acc_off) : nullptr;
   a.n_qblocks = (int)nqb;
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
@@ -207,7 +257,7 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
     err = fa::launch_bwd32(a, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr, want_kv, want_q, st);
   } else {     // 16-bit: the query pass computes the preprocess itself
     err = fa::launch_bwd16(a, p->dtype == FA_BF16, D, p->mod_kind, p->causal != 0, p->key_mask != nullptr,
-                           want_kv, want_q, st);
+                           want_kv, want_q, atomic, st);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -8,7 +8,7 @@
 // pallas_flash_attention docstring) and time it (flaxattention benchmark
 // table); this is the hand-written counterpart.
 //
-// Two deterministic passes, no atomics:
+// Two modes for dQ.  Separate (deterministic, no atomics): two passes,
 //  * dkdv16_kernel: key-stationary.  Each wave keeps 32 keys' K and V rows in
 //    registers and their dK^T, dV^T accumulators, and loops over 64-query
 //    tiles whose Q and dO go straight from HBM into LDS.  S and dP are formed
@@ -21,6 +21,12 @@
 //    LDS; S^T and dP^T are formed with keys as rows so the lane holds one
 //    query, and dQ^T = K^T dS^T accumulates in registers (K^T fragments
 //    through the transposing LDS read).
+// Atomic: the preprocess kernel writes the row statistics and zeroes an fp32
+// dQ accumulator; the key/value pass (DQA) also stores each query tile's dS^T
+// in LDS and adds dS K over its 128 keys into the accumulator with fp32
+// atomics; a convert kernel scales and rounds it to dQ.  This removes the
+// query pass's recomputation of S and dP (4 D of its 6 D flop per pair); the
+// order of the atomic additions varies, so dQ is not bitwise repeatable.
 // The LDS tiles are unpadded rows with permuted 16-byte chunks (tswz), which
 // keeps both the row-fragment and the transposing reads free of bank
 // conflicts.
@@ -79,6 +85,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const AttnArgs a, int dtyp
   }
 #pragma unroll
   for (int w = 1; w < LPR; w <<= 1) acc += __shfl_xor(acc, w);
+  if (a.dq_acc && row < rows) {   // atomic dQ mode: the key/value pass adds into these rows
+    float* z = a.dq_acc + row * D;
+#pragma unroll
+    for (int c = sub; c < D / 4; c += LPR) *(f32x4*)(z + 4 * c) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (row < rows && sub == 0) {
     const float l = a.lse[row];
     float l2 = (l == kNegInf) ? __builtin_inff() : l * kLog2e;
@@ -141,12 +152,16 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
 // (K, V, dK, dV and two score blocks) within the 256 of two waves per SIMD
 // at head_dim 64.  With BLK only the query tiles whose 128 x 128 block (row
 // tile / 2, this workgroup's 128 keys) is set in the block mask are visited.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool DQA>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
   constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
   constexpr int BQ = kDkdvBQ;   // queries per tile
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = BQ * D;
+  // atomic dQ mode: the workgroup's K rows and each query tile's dS^T (128
+  // keys x 64 queries, 16-bit) in LDS, read transposed by the dQ products
+  __shared__ __attribute__((aligned(16))) uint16_t sKd[DQA ? BKV * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sDS[DQA ? BKV * BQ : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sQ0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sQ1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sO0[TILE];
@@ -187,6 +202,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       kf[kk] = *(const u32x4*)(Kg + off + 16 * kk);
       vf[kk] = *(const u32x4*)(Vg + off + 16 * kk);
     }
+  }
+  if constexpr (DQA) {   // K rows of the workgroup for the dQ products (visible after the first barrier)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) lds_write16(sKd + tile_off<D, SW_TR>(32 * wave + l32, 16 * kk + 8 * hi), kf[kk]);
   }
   // per-lane exponent term: the key's share of the bias, or -inf for a
   // masked key or a key past seq_kv (its dK, dV rows are not stored)
@@ -239,10 +258,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       __builtin_amdgcn_global_load_lds((const void*)(deltag + min(q0 + lane, Sq - 1)), (lds_void_ptr)sD, 4, 0, 0);
   };
 
+  // dS^T of queries 32mt + 16u .. +15 held by this lane (its key, 8 queries
+  // in accumulator order) into the LDS tile of the dQ products: row = key,
+  // position p = 32mt + 16u + 8hi + j for register 8u + j, i.e. query
+  // swap23(p) of the tile (bits 2 and 3 of the position exchanged).
+  auto put_ds = [&](int mt, int u, u32x4 db) __attribute__((always_inline)) {
+    if constexpr (DQA) lds_write16(sDS + tile_off<64, SW_BOTH>(32 * wave + l32, 32 * mt + 16 * u + 8 * hi), db);
+  };
+
   // Queries 32mt .. 32mt+31 of tile it.
   auto half = [&](int it, int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD) __attribute__((always_inline)) {
     const int qs = it * BQ + 32 * mt;   // first query of the half
-    if (CAUSAL && qs + off + 31 < kw) return;   // every query precedes every key of this wave
+    // every query precedes every key of this wave: nothing to add (in the
+    // atomic dQ mode the half still runs, masked to P = 0, so its dS^T rows
+    // of the LDS tile are zeros; such halves occur only in a key block's
+    // first query tile)
+    if (!DQA && CAUSAL && qs + off + 31 < kw) return;
 
     // S' = Q K^T - lse2 / c and dP' = dO V^T - delta, queries as rows: the
     // accumulators start from the rows' stored values
@@ -292,6 +323,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       const int p0 = 32 * mt + 16 * u;
       const u32x4 pb = pack8<T>(sv, u);
       const u32x4 db = pack8<T>(dpv, u);
+      put_ds(mt, u, db);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         dv[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sO, p0, 32 * dt, lane), pb, dv[dt]);
@@ -300,17 +332,69 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
   };
 
+  // Atomic dQ mode, after every wave has stored its dS^T of query tile it:
+  // dQ_tile += dS K over the workgroup's 128 keys, as (64 queries x D) / 4
+  // waves of 32 x 32 MFMA tiles (wave w: queries 32 (w >> 1) .., dims
+  // 32 ((w & 1) NT + t) ..), both operands through the transposing LDS read,
+  // then added into the fp32 accumulator rows with buffer atomics whose
+  // descriptor bounds the slice (lanes past seq_q are dropped by the
+  // hardware, so every wave issues exactly NA atomics per tile).
+  constexpr int NT = DQA ? D / 64 : 1;
+  __amdgpu_buffer_rsrc_t dq_rsrc;
+  if constexpr (DQA)
+    dq_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.dq_acc + (size_t)bh * Sq * D, 0, Sq * D * 4, 0x00020000);
+  auto dq_tile = [&](int it) __attribute__((always_inline)) {
+    if constexpr (DQA) {
+      const int qh = wave >> 1;
+      f32x16 cq[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) cq[t] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < BKV / 16; ++ks) {
+        const u32x4 af = read_a_tr_tile<64, SW_BOTH>(sDS, 16 * ks, 32 * qh, lane);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          cq[t] = mma16<T>(af, read_a_tr_tile<D, SW_TR>(sKd, 16 * ks, 32 * ((wave & 1) * NT + t), lane), cq[t]);
+      }
+      // register r holds position 32qh + 8(r/4) + 4hi + r%4, i.e. query
+      // 32qh + 16(r/8) + 8hi + 4((r/4)%2) + r%4 of the tile
+      const int qb = it * BQ + 32 * qh + 8 * hi;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int dcol = 32 * ((wave & 1) * NT + t) + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb + 16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3);
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(cq[t][r], dq_rsrc, (q * D + dcol) * 4, 0, 0);
+        }
+      }
+    }
+  };
+
   // Visit n in the buffers of its parity; visit n+1 is requested into the
   // other buffers right after the barrier that retires visit n-1.
   auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
                   uint16_t* sOn, float* sLn, float* sDn) __attribute__((always_inline)) {
-    wait_direct_loads();   // this wave's loads of tile n are in LDS
-    __syncthreads();       // ... and every other wave's; tile n-1 is retired
+    // this wave's loads of tile n are in LDS; in the atomic dQ mode the NA
+    // atomics of tile n-1, issued after those loads, may still be in flight
+    // (vector memory operations complete in issue order)
+    if constexpr (DQA) {
+      if (n == n0) wait_direct_loads();
+      else wait_vmcnt_le<16 * NT>();
+      barrier_lds();       // ... and every other wave's; tile n-1 is retired
+    } else {
+      wait_direct_loads();
+      __syncthreads();
+    }
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
     const int it = it_of(n);
     half(it, 0, sQ, sO, sL, sD);
     __builtin_amdgcn_sched_barrier(0);   // the halves share registers
     half(it, 1, sQ, sO, sL, sD);
+    if constexpr (DQA) {
+      barrier_lds_loads_in_flight();   // every wave's dS^T of tile n is in sDS; tile n+1's loads stay in flight
+      dq_tile(it);
+    }
   };
 
   if (n0 < n_end) load_tile(it_of(n0), sQ0, sO0, sL0, sD0);
@@ -596,18 +680,45 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   }
 }
 
+// ----------------------------------------------------------- dQ conversion
+
+// Atomic dQ mode: dQ = scale * dQacc rounded to the 16-bit type, 8 elements
+// per thread (two 16-byte loads, one 16-byte store).
+template <class T>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const AttnArgs a, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 x = *(const f32x4*)(a.dq_acc + 8 * i);
+  const f32x4 y = *(const f32x4*)(a.dq_acc + 8 * i + 4);
+  const float sc = a.scale;
+  *(u32x4*)((uint16_t*)a.dq + 8 * i) = u32x4{pack2<T>(x[0] * sc, x[1] * sc), pack2<T>(x[2] * sc, x[3] * sc),
+                                             pack2<T>(y[0] * sc, y[1] * sc), pack2<T>(y[2] * sc, y[3] * sc)};
+}
+
 // ----------------------------------------------------------------- launchers
 
 int bwd16_block_kv() { return 128; }
 int bwd16_block_q() { return 128; }
 
-// The query pass runs first and writes delta and lse2 for the key/value
-// pass; without it, the preprocess kernel provides them.
+// Separate mode: the query pass runs first and writes delta and lse2 for the
+// key/value pass; without it, the preprocess kernel provides them.  Atomic
+// mode (dq_atomic, both passes wanted): preprocess (row statistics, zeroed
+// accumulator), the key/value pass with the dQ products, the conversion.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
-static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, hipStream_t st) {
+static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q, bool dq_atomic, hipStream_t st) {
   const int BH = a.B * a.H;
   const unsigned nkb = (unsigned)((a.Skv + bwd16_block_kv() - 1) / bwd16_block_kv());
   hipError_t err;
+  if (dq_atomic && want_q && want_kv) {
+    err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI ? 2 : 1);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK, true>), dim3(nkb * BH), dim3(256), 0, st, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t n8 = (int64_t)BH * a.Sq * D / 8;
+    hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, a, n8);
+    return hipGetLastError();
+  }
   if (want_q) {
     hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3((unsigned)a.n_qblocks * BH), dim3(256), 0,
                        st, a);
@@ -616,36 +727,43 @@ static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q
     err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI ? 2 : 1);
   }
   if (err != hipSuccess || !want_kv) return err;
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(nkb * BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK, false>), dim3(nkb * BH), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-static hipError_t launch_bwd16_blk(const AttnArgs& a, bool kv, bool qq, hipStream_t st) {
-  return a.block_mask ? launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, kv, qq, st)
-                      : launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, kv, qq, st);
+static hipError_t launch_bwd16_blk(const AttnArgs& a, bool kv, bool qq, bool at, hipStream_t st) {
+  return a.block_mask ? launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, kv, qq, at, st)
+                      : launch_bwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, kv, qq, at, st);
 }
 
 template <class T, int D, int MOD>
-static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
-  if (causal) return mask ? launch_bwd16_blk<T, D, MOD, true, true>(a, kv, qq, st) : launch_bwd16_blk<T, D, MOD, true, false>(a, kv, qq, st);
-  return mask ? launch_bwd16_blk<T, D, MOD, false, true>(a, kv, qq, st) : launch_bwd16_blk<T, D, MOD, false, false>(a, kv, qq, st);
+static hipError_t launch_bwd16_mod(const AttnArgs& a, bool causal, bool mask, bool kv, bool qq, bool at,
+                                   hipStream_t st) {
+  if (causal)
+    return mask ? launch_bwd16_blk<T, D, MOD, true, true>(a, kv, qq, at, st)
+                : launch_bwd16_blk<T, D, MOD, true, false>(a, kv, qq, at, st);
+  return mask ? launch_bwd16_blk<T, D, MOD, false, true>(a, kv, qq, at, st)
+              : launch_bwd16_blk<T, D, MOD, false, false>(a, kv, qq, at, st);
 }
 
 template <class T, int D>
-static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool kv, bool qq, hipStream_t st) {
+static hipError_t launch_bwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool kv, bool qq, bool at,
+                                 hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return launch_bwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, kv, qq, st);
-    case MOD_CHECKERBOARD: return launch_bwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, kv, qq, st);
-    default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, kv, qq, st);
+    case MOD_ALIBI: return launch_bwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, kv, qq, at, st);
+    case MOD_CHECKERBOARD: return launch_bwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, kv, qq, at, st);
+    default: return launch_bwd16_mod<T, D, MOD_NONE>(a, causal, mask, kv, qq, at, st);
   }
 }
 
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, bool kv, bool qq,
-                        hipStream_t st) {
+                        bool dq_atomic, hipStream_t st) {
   if (bf16)
-    return D == 64 ? launch_bwd16_d<BF16, 64>(a, mod, causal, mask, kv, qq, st) : launch_bwd16_d<BF16, 128>(a, mod, causal, mask, kv, qq, st);
-  return D == 64 ? launch_bwd16_d<F16, 64>(a, mod, causal, mask, kv, qq, st) : launch_bwd16_d<F16, 128>(a, mod, causal, mask, kv, qq, st);
+    return D == 64 ? launch_bwd16_d<BF16, 64>(a, mod, causal, mask, kv, qq, dq_atomic, st)
+                   : launch_bwd16_d<BF16, 128>(a, mod, causal, mask, kv, qq, dq_atomic, st);
+  return D == 64 ? launch_bwd16_d<F16, 64>(a, mod, causal, mask, kv, qq, dq_atomic, st)
+                 : launch_bwd16_d<F16, 128>(a, mod, causal, mask, kv, qq, dq_atomic, st);
 }
 
 }  // namespace fa

@@ -227,8 +227,35 @@ __device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint1
 
 // Wait until this wave's direct loads have landed (vmcnt(0)).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
-// Wait until at most 16 of this wave's vector memory loads are in flight.
-__device__ __forceinline__ void wait_vmcnt_le16() { __builtin_amdgcn_s_waitcnt(0x3f70 | (16 & 15) | ((16 >> 4) << 14)); }
+// Wait until at most N (<= 63) of this wave's vector memory operations are in
+// flight (they complete in issue order, so the older ones have).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmcnt_le16() { wait_vmcnt_le<16>(); }
+
+// Workgroup barrier ordering LDS only: each wave's LDS operations complete,
+// then all waves meet.  Unlike __syncthreads() (a release fence on all of
+// memory), it does not wait for the wave's global stores, atomics or direct
+// loads still in flight; a caller that needs its direct loads in LDS waits
+// for them (vmcnt) first.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The same barrier while this wave's direct loads into other LDS buffers are
+// in flight: the fence of barrier_lds makes the compiler complete every
+// pending direct load first, so this form waits for the wave's own LDS
+// instructions (lgkmcnt) in the same asm block as the barrier, whose memory
+// clobber keeps the compiler from moving memory accesses across it.  The
+// caller must not read the buffers those loads write before waiting for them.
+__device__ __forceinline__ void barrier_lds_loads_in_flight() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
@@ -341,6 +368,7 @@ struct AttnArgs {
   float* delta;     // backward workspace: rowsum(dO * O), (B, H, Sq)
   float* lse2;      // backward workspace: lse * log2(e), +inf for empty rows (16-bit ALiBi: plus the
                     // query's bias share within its 64-query tile)
+  float* dq_acc;    // backward workspace of the atomic dQ mode: fp32 (B, H, Sq, D) sums of dS K
   const uint8_t* key_mask;
   const float* alibi_slopes;
   float* partial;   // decode workspace

@@ -27,8 +27,10 @@ hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
 hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, int kv16 = 0);
 int bwd16_block_kv();
 int bwd16_block_q();
+// dq_atomic (with both passes wanted): dQ from fp32 atomics in the key/value
+// pass (a.dq_acc, B*H*Sq*D floats) instead of the query pass.
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
-                        bool want_kv, bool want_q, hipStream_t st);
+                        bool want_kv, bool want_q, bool dq_atomic, hipStream_t st);
 int bwd32_block_kv(int D);
 int bwd32_block_q(int D);
 hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, bool want_kv, bool want_q,
