@@ -5,17 +5,28 @@ A step is one forward plus one full backward (dQ, dK, dV) of the prefill
 workload: fp16 q, k, v ~ N(0, 1) of shape (8, 8, 2048, 64), causal, ALiBi
 score_mod, dO ~ N(0, 1).  The headline value is forward+backward TFLOP/s on
 the algorithmic flop count (causal pairs S(S+1)/2 per head; 4*D flop per pair
-forward, 10*D backward).  The same JSON line also carries the forward alone,
-the split-KV decode (fp16, (8, 8, 1, 64) against 2048 and 32768 keys, GB/s
-of K + V + q + O + lse with K/V copies rotated so reads come from HBM), the
-roofline of the dominant kernel, and the fp64 oracle timed on a bounded
-sample on the host cores.
+forward, 10*D backward).  The same JSON line also carries the other
+workloads, each timed with HIP events on the library's stream:
+
+* tiny fp32 (1, 2, 256, 64): forward and forward+backward (latency-bound);
+* key-padding bf16 (4, 16, 4096, 128), Bernoulli(0.5) key mask and
+  checkerboard: forward and forward+backward (all pairs evaluated);
+* long-context fp32 (1, 1, 131072, 512), causal: forward and
+  forward+backward against the fp32 matrix peak;
+* split-KV decode, fp16 (8, 8, 1, 64) against 2048 and 32768 keys, GB/s of
+  K + V + q + O + lse with K/V copies rotated so reads come from HBM;
+
+plus the backward of both 16-bit workloads in each dQ mode (separate query
+pass and atomics), the roofline of the headline's dominant kernel (with its
+average duration from the committed rocprofv3 trace beside the event-derived
+one), and the fp64 oracle timed on a bounded sample on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-s SECONDS]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,7 +45,7 @@ def log(msg: str) -> None:
 
 
 def time_calls(fn, reps: int, torch) -> float:
-    """Average milliseconds per call of fn() from HIP events on the current
+    """Average milliseconds per call of fn(i) from HIP events on the current
     stream (the stream the library launches on)."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -46,17 +57,64 @@ def time_calls(fn, reps: int, torch) -> float:
     return start.elapsed_time(end) / reps
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_f16_causal_alibi.json")
-KERNEL_SOURCES = {"fwd16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
-                  "dq16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
-                  "dkdv16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip"}
+def settle(fn, seconds: float, torch) -> int:
+    """Calls fn(i) untimed for `seconds` (the GPU clock ramps up over the
+    first tens of milliseconds of load); returns the number of calls."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()
+
+
+SOURCES = {"fwd16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
+           "dq16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+           "dkdv16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+           "bwd_pre_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+           "dq_convert_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+           "fwd32_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd32.hip",
+           "dq32_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd32.hip",
+           "dkdv32_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd32.hip",
+           "decode_split_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_decode.hip",
+           "decode_merge_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_decode.hip",
+           "fwd16_split_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip"}
+
+
+def source_of(kernel_name: str):
+    """Source file of a kernel from its (demangled) rocprof name."""
+    for short, src in SOURCES.items():
+        if f"::{short}<" in kernel_name or kernel_name.startswith(short):
+            return src
+    return None
+
+
+# The headline's dominant kernel, as rocprofv3 names it.
+DKDV_PREFILL = "void fa::dkdv16_kernel<fa::F16, 64, 1, true, false, false, false>(fa::AttnArgs)"
+TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_bench.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bench.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bench.json")
 COPY_BYTES = 256 * 1024 * 1024    # the calibration copy of --counters
+
+
+# ------------------------------------------------------------------ profiles
+#
+# The summaries under profiles/ come from rocprofv3 runs of this script and
+# are written by the summary modes below; each records the command that made
+# it and the sha256 of every kernel's source, and bench.py reports a figure
+# from them only while that source is unchanged.
 
 
 def counters_pass() -> int:
     """What the rocprofv3 --pmc runs profile: a device copy of COPY_BYTES (the
     counters' calibration), then two forward + backward steps of the prefill
-    workload."""
+    and of the key-padding workload and one of the long-context workload."""
     import torch
 
     import tiled_online_softmax_flashattention_amd as fa
@@ -66,114 +124,263 @@ def counters_pass() -> int:
     y = torch.empty_like(x)
     for _ in range(2):
         y.copy_(x)
-    w = W.PREFILL_F16
-    d = w.make()
-    q, k, v, do = (d[t].cuda() for t in ("q", "k", "v", "dout"))
-    kw = dict(causal=True, score_mod="alibi", scale=w.scale)
-    out, lse = fa.forward(q, k, v, **kw)
-    for _ in range(2):
-        fa.forward(q, k, v, out=out, lse=lse, **kw)
-        fa.backward(q, k, v, out, lse, do, **kw)
-    torch.cuda.synchronize()
+    del x, y
+    for w, kw, n in ((W.PREFILL_F16, dict(causal=True, score_mod="alibi"), 2),
+                     (W.KEYPAD_BF16, dict(score_mod="checkerboard"), 2),
+                     (W.LONG_F32, dict(causal=True), 1)):
+        d = {k: (None if t is None else t.cuda()) for k, t in w.make().items()}
+        kw = dict(kw, key_mask=d["key_mask"], scale=w.scale)
+        q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+        out, lse = fa.forward(q, k, v, **kw)
+        for _ in range(n):
+            fa.forward(q, k, v, out=out, lse=lse, **kw)
+            fa.backward(q, k, v, out, lse, do, **kw)
+        torch.cuda.synchronize()
+        del d, q, k, v, do, out, lse
+        torch.cuda.empty_cache()
     print("counters pass done", flush=True)
     return 0
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, command: str) -> int:
-    """Writes TRAFFIC_FILE from the counter_collection CSVs of the two
-    rocprofv3 passes over --counters: per-dispatch FETCH_SIZE / WRITE_SIZE
-    (KiB, summed over the device) of each kernel, scaled by what the same
-    counters read for the calibration copy, with the source hash of each
-    kernel."""
+def _per_dispatch(path: str):
+    """{dispatch id: (kernel name, {counter: value summed over the device})}."""
     import csv
-    import hashlib
     from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(path)):
+        d = int(r["Dispatch_Id"])
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    return {d: (names[d], vals[d]) for d in vals}
 
-    def per_kernel(path, counter):
-        vals = defaultdict(list)
-        by_dispatch = defaultdict(float)
-        names = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            key = r["Dispatch_Id"]
-            by_dispatch[key] += float(r["Counter_Value"])
-            names[key] = r["Kernel_Name"]
-        for key, v in by_dispatch.items():
-            vals[names[key]].append(v)
-        return vals
 
-    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+def traffic_summary(fetch_csv: str, write_csv: str, command: str) -> int:
+    """Writes the HBM traffic summary from the counter_collection CSVs of the
+    two rocprofv3 passes over --counters: per-dispatch FETCH_SIZE / WRITE_SIZE
+    (KiB, summed over the device) of each kernel (median over its dispatches),
+    scaled by what the same counters read for the calibration copy."""
+    from collections import defaultdict
+    fetch, write = _per_dispatch(fetch_csv), _per_dispatch(write_csv)
 
-    def find(vals, frag):
-        got = [v for n, v in vals.items() if frag in n]
-        return sorted(x for lst in got for x in lst)
+    def by_kernel(disp, counter):
+        out = defaultdict(list)
+        for name, c in disp.values():
+            out[name].append(c[counter])
+        return out
 
+    fk, wk = by_kernel(fetch, "FETCH_SIZE"), by_kernel(write, "WRITE_SIZE")
     copy_kib = COPY_BYTES / 1024
-    cf = find(fetch, "copyBuffer") or find(fetch, "elementwise") or find(fetch, "copy")
-    cw = find(write, "copyBuffer") or find(write, "elementwise") or find(write, "copy")
-    fetch_factor = copy_kib / max(cf)
-    write_factor = copy_kib / max(cw)
-    out = {"command": command, "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": max(cf), "write_kib": max(cw),
-                                                    "fetch_factor": round(fetch_factor, 4),
-                                                    "write_factor": round(write_factor, 4)},
+    cf = max(v for n, lst in fk.items() if "copyBuffer" in n or "elementwise" in n for v in lst)
+    cw = max(v for n, lst in wk.items() if "copyBuffer" in n or "elementwise" in n for v in lst)
+    out = {"command": command, "copy_calibration": {"bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                                                    "fetch_factor": round(copy_kib / cf, 4),
+                                                    "write_factor": round(copy_kib / cw, 4)},
            "kernels": {}}
-    for kern, src in KERNEL_SOURCES.items():
-        f, wv = find(fetch, kern), find(write, kern)
-        if not f or not wv:
+    for name in sorted(fk):
+        src = source_of(name)
+        if src is None or name not in wk:
             continue
-        fk, wk = f[len(f) // 2], wv[len(wv) // 2]
-        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
-        out["kernels"][kern] = {"fetch_kib": fk, "write_kib": wk,
-                                "hbm_bytes": int(round((fk * fetch_factor + wk * write_factor) * 1024)),
-                                "source": src, "source_sha256": sha}
+        f = sorted(fk[name])[len(fk[name]) // 2]
+        wv = sorted(wk[name])[len(wk[name]) // 2]
+        out["kernels"][name] = {"fetch_kib": f, "write_kib": wv, "dispatches": len(fk[name]),
+                                "hbm_bytes": int(round((f * copy_kib / cf + wv * copy_kib / cw) * 1024)),
+                                "source": src, "source_sha256": source_sha(src)}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
+    rows = [(n, r["dispatches"], round(r["fetch_kib"] / 1024, 1), round(r["write_kib"] / 1024, 1),
+             round(r["hbm_bytes"] / 1e6, 1)) for n, r in sorted(out["kernels"].items())]
+    _write_md(TRAFFIC_FILE[:-5] + ".md", "traffic-summary", "L2-to-memory traffic per dispatch (rocprofv3 FETCH_SIZE, WRITE_SIZE)",
+              command, ("kernel", "dispatches", "FETCH_SIZE MiB", "WRITE_SIZE MiB", "bytes (calibrated), MB"), rows,
+              f"`bench.py --counters`: a {COPY_BYTES >> 20} MiB device copy, then untimed forward + backward steps of "
+              f"the prefill, key-padding and long-context workloads; the median dispatch of each kernel. "
+              f"Calibration on the copy: FETCH_SIZE reads {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB for "
+              f"{copy_kib:.0f} KiB moved, so fetch counts are scaled by {copy_kib / cf:.4f} and write counts by "
+              f"{copy_kib / cw:.4f}. These count bytes between L2 and the memory fabric (the on-package cache "
+              f"included), an upper bound on HBM bytes.")
     print(json.dumps(out, indent=1))
     return 0
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel's source has changed since then."""
-    import hashlib
+def _write_md(path: str, mode: str, title: str, command: str, header, rows, notes: str = "") -> None:
+    """A short markdown table beside a JSON summary (same figures)."""
+    lines = [f"# {title}", "", "Command (from the repository root on the GPU box, `R` = that root), then "
+             f"`python bench.py --{mode} ...` on its CSVs:", "", "```",
+             command, "```", ""]
+    if notes:
+        lines += [notes, ""]
+    lines.append("| " + " | ".join(header) + " |")
+    lines.append("|" + "---|" * len(header))
+    lines += ["| " + " | ".join(str(c) for c in r) + " |" for r in rows]
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def trace_summary(stats_csv: str, command: str) -> int:
+    """Writes the kernel-duration summary from rocprofv3's kernel_stats.csv."""
+    import csv
+    out = {"command": command, "kernels": {}}
+    for r in csv.DictReader(open(stats_csv)):
+        src = source_of(r["Name"])
+        rec = {"calls": int(r["Calls"]), "average_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
+               "max_ns": float(r["MaxNs"]), "share_percent": float(r["Percentage"])}
+        if src:
+            rec.update(source=src, source_sha256=source_sha(src))
+        out["kernels"][r["Name"]] = rec
+    with open(TRACE_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    rows = [(n, r["calls"], round(r["average_ns"] / 1e3, 2), round(r["min_ns"] / 1e3, 2), round(r["max_ns"] / 1e3, 2),
+             f'{r["share_percent"]:.2f} %')
+            for n, r in sorted(out["kernels"].items(), key=lambda kv: -kv[1]["share_percent"])]
+    _write_md(TRACE_FILE[:-5] + ".md", "trace-summary", "Kernel durations of bench.py (rocprofv3 kernel trace)", command,
+              ("kernel", "calls", "average us", "min us", "max us", "share of traced time"), rows,
+              "The traced run is the default bench without the CPU baseline: every workload of the JSON line, "
+              "each timed loop after its clock settle.")
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def counter_summary(csv1: str, csv2: str, csv3: str, command: str) -> int:
+    """Shader-counter summary (last dispatch of each kernel) from the three
+    rocprofv3 --pmc passes over --counters.  cycles = GRBM_GUI_ACTIVE / 8
+    (summed over the 8 XCDs); SIMD-cycle shares divide by cycles x 1024 SIMDs:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES, VALU busy = 4 SQ_ACTIVE_INST_VALU
+    (quad-cycles), both in one cycle = SQ_VALU_MFMA_COEXEC_CYCLES; waves per
+    CU = 4 SQ_WAVE_CYCLES / cycles / 256; VALU instructions per MFMA =
+    (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; exp per MFMA =
+    SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA; s_waitcnt share =
+    SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS bank-conflict share =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    merged = {}
+    for path in (csv1, csv2, csv3):
+        disp = _per_dispatch(path)
+        last = {}
+        for d, (name, c) in sorted(disp.items()):
+            last[name] = c
+        for name, c in last.items():
+            merged.setdefault(name, {}).update(c)
+    out = {"command": command, "kernels": {}}
+    print("| kernel | cycles | MFMA busy | VALU busy | MFMA and VALU in one cycle | waves per CU | VALU instr "
+          "per MFMA | exp per MFMA | wave time in s_waitcnt | LDS bank-conflict share |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for name, c in sorted(merged.items()):
+        src = source_of(name)
+        need = ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_WAVE_CYCLES")
+        if src is None or any(k not in c for k in need) or c["SQ_INSTS_MFMA"] == 0:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / 8
+        simd = cyc * 1024
+        rec = {"cycles": cyc, "mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd,
+               "valu_busy": 4 * c.get("SQ_ACTIVE_INST_VALU", 0) / simd,
+               "coexec": c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / simd,
+               "waves_per_cu": 4 * c["SQ_WAVE_CYCLES"] / cyc / 256,
+               "valu_per_mfma": (c.get("SQ_INSTS_VALU", 0) - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"],
+               "exp_per_mfma": c.get("SQ_INSTS_VALU_TRANS_F32", 0) / c["SQ_INSTS_MFMA"],
+               "waitcnt_share": c.get("SQ_WAIT_INST_ANY", 0) / c["SQ_WAVE_CYCLES"],
+               "lds_conflict_share": c.get("SQ_LDS_BANK_CONFLICT", 0) / max(1.0, c.get("SQ_LDS_IDX_ACTIVE", 0)),
+               "source": src, "source_sha256": source_sha(src), "raw": dict(c)}
+        out["kernels"][name] = rec
+        print(f"| {name} | {cyc:.0f} | {100 * rec['mfma_busy']:.1f} % | {100 * rec['valu_busy']:.1f} % | "
+              f"{100 * rec['coexec']:.1f} % | {rec['waves_per_cu']:.1f} | {rec['valu_per_mfma']:.1f} | "
+              f"{rec['exp_per_mfma']:.2f} | {100 * rec['waitcnt_share']:.0f} % | "
+              f"{100 * rec['lds_conflict_share']:.0f} % |")
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    rows = [(n, f'{r["cycles"]:.0f}', f'{100 * r["mfma_busy"]:.1f} %', f'{100 * r["valu_busy"]:.1f} %',
+             f'{100 * r["coexec"]:.1f} %', f'{r["waves_per_cu"]:.1f}', f'{r["valu_per_mfma"]:.1f}',
+             f'{r["exp_per_mfma"]:.2f}', f'{100 * r["waitcnt_share"]:.0f} %', f'{100 * r["lds_conflict_share"]:.0f} %')
+            for n, r in sorted(out["kernels"].items())]
+    _write_md(COUNTERS_FILE[:-5] + ".md", "counter-summary", "Shader counters per kernel (rocprofv3 --pmc, three passes)", command,
+              ("kernel", "cycles", "MFMA busy", "VALU busy", "MFMA and VALU in one cycle", "waves per CU",
+               "VALU instr per MFMA", "exp per MFMA", "wave time in s_waitcnt", "LDS bank-conflict share"), rows,
+              "Last dispatch of each kernel in `bench.py --counters`. " + " ".join(counter_summary.__doc__.split()))
+    return 0
+
+
+def _from_summary(path: str, kernel: str, field: str):
+    """A kernel's figure from a committed summary, or None when the file,
+    the kernel or its unchanged source is missing."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))["kernels"][kernel]
-        sha = hashlib.sha256(open(os.path.join(ROOT, rec["source"]), "rb").read()).hexdigest()
+        rec = json.load(open(path))["kernels"][kernel]
+        if rec["source_sha256"] != source_sha(rec["source"]):
+            return None
+        return rec[field]
     except (OSError, KeyError, ValueError):
         return None
-    return rec["hbm_bytes"] if sha == rec["source_sha256"] else None
 
+
+
+# ------------------------------------------------------------------ workloads
+
+
+def dense_workload(fa, W, torch, w, kw: dict, peak: float, reps: int, settle_s: float, dq_modes=("auto",)) -> dict:
+    """Forward and forward+backward of one workload (inputs resident in HBM),
+    and the backward alone in each dQ mode asked for."""
+    d = {k: (None if t is None else t.cuda()) for k, t in w.make().items()}
+    kw = dict(kw, key_mask=d["key_mask"], scale=w.scale)
+    q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
+    bwd = {}
+    for mode in dq_modes:
+        ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, dq_mode=mode, **kw)), dtype=torch.uint8,
+                         device=q.device)
+        bwd[mode] = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, dq_mode=mode, **kw)
+    run_bwd = bwd[dq_modes[0]]
+    run_fwd()
+    for f in bwd.values():
+        f()
+    settle(lambda i: (run_fwd(), run_bwd()), settle_s, torch)
+    ms_f = time_calls(lambda i: run_fwd(), reps, torch)
+    ms_fb = time_calls(lambda i: (run_fwd(), run_bwd()), reps, torch)
+    ff, fb = w.fwd_flops(), w.fwd_flops() + w.bwd_flops()
+    res = {"forward": {"ms": round(ms_f, 4), "TFLOP/s": round(ff / ms_f / 1e9, 2),
+                       "frac_peak": round(ff / ms_f / 1e9 / peak, 4)},
+           "fwd_bwd": {"ms": round(ms_fb, 4), "TFLOP/s": round(fb / ms_fb / 1e9, 2),
+                       "frac_peak": round(fb / ms_fb / 1e9 / peak, 4)},
+           "peak_TFLOP/s": peak, "calls_timed": reps,
+           "flop_convention": "causal pairs" if w.causal else "all pairs evaluated"}
+    if len(dq_modes) > 1:
+        res["backward_ms_by_dq_mode"] = {m: round(time_calls(lambda i: f(), reps, torch), 4) for m, f in bwd.items()}
+    del d, q, k, v, do, out, lse, grads, bwd, run_fwd, run_bwd
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_workloads(fa, W, torch, reps: int, settle_s: float) -> dict:
+    """Split-KV decode at 2048 and 32768 keys; K/V copies are rotated (>= 1
+    GiB in all) so every call reads from HBM, after a clock settle."""
+    res = {}
+    for wd in (W.DECODE_F16_2K, W.DECODE_F16_32K):
+        per = 2 * wd.batch * wd.heads * wd.seq_kv * wd.head_dim * 2
+        n_sets = max(2, -(-(1 << 30) // per))
+        xd = wd.make()
+        qd = xd["q"].cuda()
+        ks = [xd["k"].cuda() for _ in range(n_sets)]
+        vs = [xd["v"].cuda() for _ in range(n_sets)]
+        od = torch.empty_like(qd)
+        ld = torch.empty(qd.shape[:3], dtype=torch.float32, device=qd.device)
+        wsd = torch.empty(fa.decode_workspace_bytes(fa.problem(qd, ks[0], scale=wd.scale)), dtype=torch.uint8,
+                          device=qd.device)
+        plans = [fa.plan_decode(qd, ks[j], vs[j], od, ld, wsd, scale=wd.scale) for j in range(n_sets)]
+        call = lambda i: plans[i % n_sets]()
+        settled = settle(call, settle_s, torch)
+        ms = time_calls(call, max(reps, 4 * n_sets), torch)
+        nbytes = per + wd.batch * wd.heads * wd.head_dim * 2 * 2 + wd.batch * wd.heads * 4
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[str(wd.seq_kv)] = {"GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                               "us": round(ms * 1e3, 2), "bytes": nbytes, "kv_copies_rotated": n_sets,
+                               "settle_calls": settled}
+        del ks, vs, plans
+        torch.cuda.empty_cache()
+    return res
 
 def extra_workloads(fa, W, torch, reps: int) -> dict:
-    """Forward and forward+backward times of the key-padding (bf16) and the
-    long-context (fp32, head_dim 512) workloads, and a short query block
-    against a long KV cache (split over keys vs. the plain forward)."""
+    """A short query block against a long KV cache (split over keys vs. the
+    plain forward) and a block-sparse prefill (sliding window of blocks)."""
     res = {}
-    for w, kw, peak in ((W.KEYPAD_BF16, dict(score_mod="checkerboard"), PEAK_F16_TFLOPS),
-                        (W.LONG_F32, dict(causal=True), PEAK_F32_TFLOPS)):
-        log(f"[bench] extra: {w.name}")
-        x = w.make()
-        dev = {k2: (None if t is None else t.cuda()) for k2, t in x.items()}
-        kw = dict(kw, key_mask=dev["key_mask"], scale=w.scale)
-        q, k, v, do = dev["q"], dev["k"], dev["v"], dev["dout"]
-        out = torch.empty_like(q)
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-        ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device=q.device)
-        run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
-        run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
-        run_fwd(); run_bwd()
-        n = reps if w.head_dim < 512 else 2
-        ms_f = time_calls(lambda i: run_fwd(), n, torch)
-        ms_fb = time_calls(lambda i: (run_fwd(), run_bwd()), n, torch)
-        res[w.name] = {"forward_ms": round(ms_f, 3), "fwd_bwd_ms": round(ms_fb, 3),
-                       "forward_TFLOP/s": round(w.fwd_flops() / ms_f / 1e9, 1),
-                       "fwd_bwd_TFLOP/s": round((w.fwd_flops() + w.bwd_flops()) / ms_fb / 1e9, 1),
-                       "peak_TFLOP/s": peak, "flop_convention": "causal pairs" if w.causal else "all pairs"}
-        del dev, q, k, v, do, out, grads, ws
-        torch.cuda.empty_cache()
-
     # A block of 16 new queries after a 32752-key cache (fp16, causal, ALiBi):
     # the key-split path of fa_decode against the plain forward; K/V copies
     # are rotated so reads come from HBM.
@@ -268,24 +475,35 @@ def cpu_baseline(w, heads: int) -> dict:
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--settle-s", type=float, default=0.3,
-                    help="seconds of untimed steps before the warmup, so the GPU clock has left its ramp")
+                    help="seconds of untimed calls before each timed loop, so the GPU clock has left its ramp")
     ap.add_argument("--reps", type=int, default=20, help="calls per per-kernel timing loop")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) slices in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", action="store_true", help="also time the key-padding and long-context workloads")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time a short query block against a KV cache and a block-sparse prefill")
     ap.add_argument("--counters", action="store_true",
-                    help="only run the calibration copy and two untimed steps (for rocprofv3 --pmc)")
+                    help="only run the calibration copy and untimed steps (for rocprofv3 --pmc)")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write the HBM traffic summary from two rocprofv3 counter CSVs of --counters")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"),
+                    help="write the kernel-duration summary from a rocprofv3 kernel_stats.csv of this script")
+    ap.add_argument("--counter-summary", nargs=4, metavar=("CSV1", "CSV2", "CSV3", "COMMAND"),
+                    help="write the shader-counter summary from three rocprofv3 --pmc CSVs of --counters")
     args = ap.parse_args()
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.trace_summary:
+        return trace_summary(*args.trace_summary)
+    if args.counter_summary:
+        return counter_summary(*args.counter_summary)
     if args.counters:
         return counters_pass()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -311,27 +529,21 @@ def main() -> int:
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, dq_mode="atomic", **kw)), dtype=torch.uint8,
+                     device=dev)
 
     run_fwd = fa.plan_forward(q, k, v, out, lse, **kw)
     run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
     run_q = fa.plan_backward(q, k, v, out, lse, do, grads[0], None, None, ws, **kw)
+    run_sep = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, dq_mode="separate", **kw)
+    run_atomic = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, dq_mode="atomic", **kw)
 
     def step(_i=0):
         run_fwd()
         run_bwd()
 
-    # The GPU clock ramps up over the first few tens of milliseconds of load
-    # (the first 100 steps run about a third slower than the rest), so steps
-    # are run untimed for settle_s seconds before the W warmup steps.
     log(f"[bench] settle {args.settle_s} s, warmup {args.warmup}")
-    settle_steps = 0
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle_s:
-        for _ in range(50):
-            step()
-        settle_steps += 50
-        torch.cuda.synchronize()
+    settle_steps = settle(step, args.settle_s, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -353,9 +565,12 @@ def main() -> int:
     ms_fwd = time_calls(lambda i: run_fwd(), args.reps, torch)
     ms_q = time_calls(lambda i: run_q(), args.reps, torch)
     ms_bwd = time_calls(lambda i: run_bwd(), args.reps, torch)
-    # A full 16-bit backward launches the query kernel (which also writes the
-    # row statistics) and then the key/value kernel on one stream, so the
-    # key/value kernel's time is the difference of the two timings.
+    ms_sep = time_calls(lambda i: run_sep(), args.reps, torch)
+    ms_atomic = time_calls(lambda i: run_atomic(), args.reps, torch)
+    # The backward (dQ mode "auto" = the separate query pass) launches the
+    # query kernel, which also writes the row statistics, and then the
+    # key/value kernel on one stream, so the key/value kernel's time is the
+    # difference of the two timings.
     ms_kv = ms_bwd - ms_q
     pairs = w.pairs()
     D = w.head_dim
@@ -368,34 +583,29 @@ def main() -> int:
     dom = max(kernels, key=lambda n: kernels[n][1])
     dom_flops, dom_ms = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": measured_traffic(dom),
-                "avg_ms": round(dom_ms, 4)}
+    full = {"dkdv16_kernel": DKDV_PREFILL,
+            "dq16_kernel": "void fa::dq16_kernel<fa::F16, 64, 1, true, false, false>(fa::AttnArgs)",
+            "fwd16_kernel": "void fa::fwd16_kernel<fa::F16, 64, 1, true, false, false>(fa::AttnArgs)"}[dom]
+    traced_ns = _from_summary(TRACE_FILE, full, "average_ns")
+    roofline = {"bound": "mfma", "kernel": full, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                "traffic": _from_summary(TRAFFIC_FILE, full, "hbm_bytes"),
+                "algorithmic_flop_per_launch": dom_flops, "avg_ms": round(dom_ms, 4),
+                "rocprof_avg_ms": None if traced_ns is None else round(traced_ns * 1e-6, 4)}
+    if traced_ns is not None:
+        roofline["frac_from_rocprof_avg"] = round(dom_flops / (traced_ns * 1e-9) / 1e12 / PEAK_F16_TFLOPS, 4)
+    del q, k, v, do, out, lse, grads, ws, run_fwd, run_bwd, run_q, run_sep, run_atomic
+    torch.cuda.empty_cache()
 
     log("[bench] decode")
-    decode = {}
-    for wd in (W.DECODE_F16_2K, W.DECODE_F16_32K):
-        per = 2 * wd.batch * wd.heads * wd.seq_kv * wd.head_dim * 2
-        n_sets = max(2, -(-(1 << 30) // per))
-        xd = wd.make()
-        qd = xd["q"].to(dev)
-        ks = [xd["k"].to(dev) for _ in range(n_sets)]
-        vs = [xd["v"].to(dev) for _ in range(n_sets)]
-        od = torch.empty_like(qd)
-        ld = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
-        wsd = torch.empty(fa.decode_workspace_bytes(fa.problem(qd, ks[0], scale=wd.scale)), dtype=torch.uint8,
-                          device=dev)
-        plans = [fa.plan_decode(qd, ks[j], vs[j], od, ld, wsd, scale=wd.scale) for j in range(n_sets)]
-        call = lambda i: plans[i % n_sets]()
-        for i in range(3):
-            call(i)
-        ms = time_calls(call, max(args.reps, 2 * n_sets), torch)
-        nbytes = per + wd.batch * wd.heads * wd.head_dim * 2 * 2 + wd.batch * wd.heads * 4
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        decode[str(wd.seq_kv)] = {"GB/s": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-                                  "us": round(ms * 1e3, 2), "bytes": nbytes, "kv_copies_rotated": n_sets}
-        del ks, vs, plans
-        torch.cuda.empty_cache()
+    decode = decode_workloads(fa, W, torch, args.reps, args.settle_s)
+    log("[bench] tiny fp32")
+    tiny = dense_workload(fa, W, torch, W.TINY_F32, {}, PEAK_F32_TFLOPS, 200, 0.05)
+    log("[bench] key-padding bf16")
+    keypad = dense_workload(fa, W, torch, W.KEYPAD_BF16, dict(score_mod="checkerboard"), PEAK_F16_TFLOPS,
+                            args.reps, args.settle_s, dq_modes=("auto", "atomic"))
+    log("[bench] long-context fp32")
+    long32 = dense_workload(fa, W, torch, W.LONG_F32, dict(causal=True), PEAK_F32_TFLOPS, 2, 0.0)
 
     result = {
         "metric": "attention TFLOP/s fwd & fwd+bwd (% MFMA peak); decode GB/s (% HBM peak)",
@@ -418,8 +628,10 @@ def main() -> int:
         "forward": {"TFLOP/s": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12, 2),
                     "frac_mfma_peak": round(w.fwd_flops() / (ms_fwd * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
                     "ms": round(ms_fwd, 4)},
-        "backward_ms": {"all": round(ms_bwd, 4), "dq16_kernel": round(ms_q, 4), "dkdv16_kernel": round(ms_kv, 4)},
+        "backward_ms": {"all": round(ms_bwd, 4), "dq16_kernel": round(ms_q, 4), "dkdv16_kernel": round(ms_kv, 4),
+                        "by_dq_mode": {"separate": round(ms_sep, 4), "atomic": round(ms_atomic, 4)}},
         "decode": decode,
+        "workloads": {W.TINY_F32.name: tiny, W.KEYPAD_BF16.name: keypad, W.LONG_F32.name: long32},
         "roofline": roofline,
     }
     if args.extra:

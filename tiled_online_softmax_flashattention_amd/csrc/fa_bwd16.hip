@@ -177,8 +177,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int kb = blockIdx.x / BH;     // low kb = most query tiles under causal: dispatched first
+  // low kb = most query tiles under causal: dispatched first
+  const BlockCoord bc = block_coord(blockIdx.x, BH, (a.Skv + BKV - 1) / BKV, CAUSAL);
+  const int bh = bc.bh, kb = bc.blk;
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int k0 = kb * BKV;
@@ -451,9 +452,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
-  if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+  const BlockCoord bc = block_coord(blockIdx.x, BH, a.n_qblocks, CAUSAL);
+  const int bh = bc.bh;
+  const int qb = CAUSAL ? a.n_qblocks - 1 - bc.blk : bc.blk;
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM;

@@ -354,6 +354,27 @@ __device__ __forceinline__ f32x16 slice_gather(const float* sS, int g, int lane)
   return s;
 }
 
+// Workgroup order.  Workgroups are dealt to the 8 XCDs round robin (block i
+// runs on XCD i mod 8), each XCD with its own 4 MB L2.  Block i of a grid of
+// BH * nblk blocks gets (bh, blk):
+//  * causal (blocks of unequal length): bh = i mod BH, blk = i / BH, so with
+//    BH a multiple of 8 each head stays on one XCD and the blocks of every
+//    head are dealt in the same order (the kernels turn blk into
+//    longest-first);
+//  * otherwise, with BH a multiple of 8: XCD x = i mod 8 takes heads
+//    x, x + 8, ... one after the other, blk = (i / 8) mod nblk, so the blocks
+//    resident on an XCD span one or two heads and share their K/V (or Q/dO)
+//    in its L2 (8 heads at once would not fit at 4096 x 128);
+//  * otherwise the first rule.
+struct BlockCoord {
+  int bh, blk;
+};
+__device__ __forceinline__ BlockCoord block_coord(int i, int BH, int nblk, bool causal) {
+  if (causal || (BH & 7) != 0) return BlockCoord{i % BH, i / BH};
+  const int x = i & 7, j = i >> 3;
+  return BlockCoord{x + 8 * (j / nblk), j % nblk};
+}
+
 // Launch arguments of every attention kernel (tensors contiguous BHSD).
 struct AttnArgs {
   const void* q;

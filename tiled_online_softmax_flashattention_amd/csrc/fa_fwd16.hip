@@ -379,16 +379,13 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   }
 }
 
-// Workgroup blockIdx.x handles slice bh = blockIdx.x mod (batch * heads), so
-// with batch * heads a multiple of 8 all blocks of one slice run on one XCD
-// (workgroups are dealt to the 8 XCDs round robin) and share its L2.  Causal
-// query blocks are dispatched longest first.
+// Workgroup order: block_coord (each head's blocks on one XCD, non-causal
+// heads one after the other per XCD).  Causal query blocks are dispatched
+// longest first.
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_kernel(const AttnArgs a) {
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int p = blockIdx.x / BH;
-  fwd16_block<T, D, MOD, CAUSAL, MASK, false, BLK>(a, bh, CAUSAL ? a.n_qblocks - 1 - p : p, 0);
+  const BlockCoord c = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, CAUSAL);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, false, BLK>(a, c.bh, CAUSAL ? a.n_qblocks - 1 - c.blk : c.blk, 0);
 }
 
 // Split over the key axis (short query blocks against a long key sequence):
