@@ -381,32 +381,34 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
     """A short query block against a long KV cache (split over keys vs. the
     plain forward) and a block-sparse prefill (sliding window of blocks)."""
     res = {}
-    # A block of 16 new queries after a 32752-key cache (fp16, causal, ALiBi):
-    # the key-split path of fa_decode against the plain forward; K/V copies
-    # are rotated so reads come from HBM.
-    B, H, Sq, Skv, D = 8, 8, 16, 32768, 64
-    log(f"[bench] extra: short query block {B}x{H}x{Sq} against {Skv} keys")
-    gen = torch.Generator(device="cuda").manual_seed(7)
-    q = torch.randn(B, H, Sq, D, device="cuda", dtype=torch.float16, generator=gen)
-    kvs = [(torch.randn(B, H, Skv, D, device="cuda", dtype=torch.float16, generator=gen),
-            torch.randn(B, H, Skv, D, device="cuda", dtype=torch.float16, generator=gen)) for _ in range(2)]
-    kw = dict(causal=True, score_mod="alibi", q_offset=Skv - Sq)
-    out = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-    ws = torch.empty(fa.decode_workspace_bytes(fa.problem(q, kvs[0][0], **kw)), dtype=torch.uint8, device="cuda")
-    split = [fa.plan_decode(q, k, v, out, lse, ws, **kw) for k, v in kvs]
-    plain = [fa.plan_forward(q, k, v, out, lse, **kw) for k, v in kvs]
-    for f in split + plain:
-        f()
-    ms_s = time_calls(lambda i: split[i % 2](), max(reps, 4), torch)
-    ms_p = time_calls(lambda i: plain[i % 2](), max(reps, 4), torch)
-    nbytes = 2 * B * H * Skv * D * 2 + 2 * B * H * Sq * D * 2 + B * H * Sq * 4
-    res[f"short query block f16 causal ALiBi ({B},{H},{Sq},{D}) after {Skv - Sq} cached keys"] = {
-        "split_us": round(ms_s * 1e3, 2), "split_GB/s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
-        "split_frac_hbm_peak": round(nbytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "forward_unsplit_us": round(ms_p * 1e3, 2), "bytes": nbytes}
-    del q, kvs, out, lse, ws, split, plain
-    torch.cuda.empty_cache()
+    # A block of 16 new queries after a 32752-key cache (causal, ALiBi), fp16
+    # and fp32: the key-split path of fa_decode against the plain forward on
+    # the same problem; K/V copies are rotated so reads come from HBM.
+    for dt, tdt, es in (("f16", torch.float16, 2), ("f32", torch.float32, 4)):
+        B, H, Sq, Skv, D = 8, 8, 16, 32768, 64
+        log(f"[bench] extra: short query block {dt} {B}x{H}x{Sq} against {Skv} keys")
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        q = torch.randn(B, H, Sq, D, device="cuda", dtype=tdt, generator=gen)
+        kvs = [(torch.randn(B, H, Skv, D, device="cuda", dtype=tdt, generator=gen),
+                torch.randn(B, H, Skv, D, device="cuda", dtype=tdt, generator=gen)) for _ in range(2)]
+        kw = dict(causal=True, score_mod="alibi", q_offset=Skv - Sq)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        ws = torch.empty(fa.decode_workspace_bytes(fa.problem(q, kvs[0][0], **kw)), dtype=torch.uint8, device="cuda")
+        split = [fa.plan_decode(q, k, v, out, lse, ws, **kw) for k, v in kvs]
+        plain = [fa.plan_forward(q, k, v, out, lse, **kw) for k, v in kvs]
+        for f in split + plain:
+            f()
+        settle(lambda i: split[i % 2](), 0.2, torch)
+        ms_s = time_calls(lambda i: split[i % 2](), max(reps, 4), torch)
+        ms_p = time_calls(lambda i: plain[i % 2](), max(reps, 4), torch)
+        nbytes = 2 * B * H * Skv * D * es + 2 * B * H * Sq * D * es + B * H * Sq * 4
+        res[f"short query block {dt} causal ALiBi ({B},{H},{Sq},{D}) after {Skv - Sq} cached keys"] = {
+            "split_us": round(ms_s * 1e3, 2), "split_GB/s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
+            "split_frac_hbm_peak": round(nbytes / (ms_s * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "forward_unsplit_us": round(ms_p * 1e3, 2), "bytes": nbytes}
+        del q, kvs, out, lse, ws, split, plain
+        torch.cuda.empty_cache()
 
     # Block sparsity: fp16 (8, 8, 8192, 64), causal, ALiBi, with a block mask
     # of a sliding window of 8 blocks (1024 keys).  Flops count only the pairs

@@ -178,9 +178,9 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
  * against seq_kv keys, split over the key axis into chunks whose partial
  * (max, sum, accumulator) are merged exactly.  The flaxattention page
  * (decoding benchmark and TODO list) singles this case out.  seq_q == 1 runs a
- * streaming kernel (one group of lanes per key); seq_q > 1 runs the 16-bit
- * forward kernel on each key chunk (fp32: the forward, unsplit).  f16, bf16 and
- * f32 with head_dim 64 or 128.  Same outputs as fa_forward. */
+ * streaming kernel (one group of lanes per key); seq_q > 1 runs the forward
+ * kernel of the dtype on each key chunk.  f16, bf16 and f32 with head_dim 64
+ * or 128.  Same outputs as fa_forward. */
 fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);

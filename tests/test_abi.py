@@ -315,3 +315,29 @@ def test_decode_noalloc_rules():
     assert n.value > _lib.FA_DECODE_SCRATCH_BYTES
     assert nd(big) == _lib.FA_ERR_SCRATCH_LIMIT
     assert b"scratch" in lib.fa_status_string(_lib.FA_ERR_SCRATCH_LIMIT)
+
+
+def test_dq_mode_and_kv_splits_rules():
+    """dq_mode must name a mode; the atomic mode is for 16-bit types and adds
+    an fp32 accumulator to the workspace; kv_splits is 0 (automatic) or
+    1 .. FA_MAX_KV_SPLITS."""
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    sizes = {}
+    for mode in (_lib.FA_DQ_AUTO, _lib.FA_DQ_SEPARATE, _lib.FA_DQ_ATOMIC):
+        assert lib.fa_backward_workspace_size(ctypes.byref(prob(dq_mode=mode)), ctypes.byref(n)) == _lib.FA_OK
+        sizes[mode] = n.value
+    assert sizes[_lib.FA_DQ_ATOMIC] >= sizes[_lib.FA_DQ_SEPARATE] + 2 * 4 * 100 * 64 * 4
+    assert sizes[_lib.FA_DQ_AUTO] == sizes[_lib.FA_DQ_SEPARATE]
+    assert lib.fa_backward_workspace_size(ctypes.byref(prob(dq_mode=3)), ctypes.byref(n)) == INVALID
+    assert lib.fa_backward_workspace_size(ctypes.byref(prob(dq_mode=_lib.FA_DQ_ATOMIC, dtype=_lib.FA_F32)),
+                                          ctypes.byref(n)) == UNSUP
+    assert bwd(prob(dq_mode=_lib.FA_DQ_ATOMIC), ws_bytes=sizes[_lib.FA_DQ_SEPARATE]) == WS
+    assert fwd(prob(kv_splits=-1)) == INVALID
+    assert fwd(prob(kv_splits=_lib.FA_MAX_KV_SPLITS + 1)) == UNSUP
+    one = prob(seq_q=1, seq_kv=4096, kv_splits=1)
+    seven = prob(seq_q=1, seq_kv=4096, kv_splits=7)
+    assert lib.fa_decode_workspace_size(ctypes.byref(one), ctypes.byref(n)) == _lib.FA_OK
+    n1 = n.value
+    assert lib.fa_decode_workspace_size(ctypes.byref(seven), ctypes.byref(n)) == _lib.FA_OK
+    assert n.value >= 7 * 2 * 4 * (64 + 2) * 4 and n1 >= 2 * 4 * (64 + 2) * 4 and n.value > n1

@@ -250,6 +250,34 @@ def test_decode_independent_of_split(gpu_lib):
     check_lse(l1, lse_ref)
 
 
+@pytest.mark.parametrize("dtype,Sq", [("f16", 1), ("bf16", 1), ("f32", 1), ("f16", 16), ("bf16", 16)])
+def test_decode_explicit_key_splits(gpu_lib, dtype, Sq):
+    """The same decode split into 1, 2, 7 and the most (FA_MAX_KV_SPLITS
+    requested) key chunks: every split against the oracle, and the splits
+    against each other (they differ only in the order of the exact merge)."""
+    Skv, D = 5000, 64
+    w = W.Workload(f"decode splits {dtype}", 122, 2, 3, Sq, Skv, D, dtype, mod=W.MOD_ALIBI, key_mask=True,
+                   backward=False)
+    x = w.make()
+    dev = to_dev(x)
+    off = Skv - Sq
+    o_r, lse_r = oracle.forward(x["q"], x["k"], x["v"], scale=w.scale, mod=W.MOD_ALIBI, q_offset=off, causal=True,
+                                key_mask=x["key_mask"].numpy())
+    outs = []
+    for n in (1, 2, 7, 256):
+        say(f"[decode splits] {dtype} Sq{Sq} kv_splits={n}")
+        out, lse = fa.decode(dev["q"], dev["k"], dev["v"], key_mask=dev["key_mask"], score_mod="alibi",
+                             scale=w.scale, q_offset=off, causal=True, kv_splits=n)
+        torch.cuda.synchronize()
+        check("o", out, o_r, dtype, "o")
+        check_lse(lse, lse_r)
+        outs.append((out.float(), lse))
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    for o, l in outs[1:]:
+        assert (o - outs[0][0]).abs().max().item() <= tol * max(1.0, outs[0][0].abs().max().item())
+        assert (l - outs[0][1]).abs().max().item() < 1e-4
+
+
 # ------------------------------------------------------------- the workloads
 
 

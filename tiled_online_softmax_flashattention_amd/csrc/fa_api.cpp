@@ -148,15 +148,9 @@ int decode_kv_len(const fa_problem* p) {
 }
 
 // Split of the key axis and workspace bytes (one (D + 2)-float partial per
-// query row and chunk).  fp32 query blocks (seq_q > 1) run the forward
-// unsplit and need no workspace.
+// query row and chunk).
 size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
   const int BH = (int)(p->batch * p->heads);
-  if (p->seq_q > 1 && p->dtype == FA_F32) {
-    *n_split = 1;
-    *chunk = (int)p->seq_kv;
-    return 256;
-  }
   if (p->kv_splits > 0) {   // the caller's split: about kv_splits chunks
     const int len = decode_kv_len(p);
     *chunk = (len + p->kv_splits - 1) / p->kv_splits;
@@ -310,12 +304,10 @@ fa_status decode_launch(const fa_problem* p, const void* q, const void* k, const
   hipError_t err;
   if (p->seq_q == 1) {
     err = fa::launch_decode(a, p->dtype, D, p->mod_kind, mask, st);
-  } else if (p->dtype == FA_F32) {   // short fp32 query block: the forward, unsplit
+  } else {   // short query block: the forward split over the keys, then the merge
     a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
-    err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st);
-  } else {   // short 16-bit query block: the forward split over the keys, then the merge
-    a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
-    err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
+    if (p->dtype == FA_F32) err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true);
+    else err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
     if (err == hipSuccess)
       err = fa::launch_decode_merge(a, p->dtype, D, (int)(p->batch * p->heads * p->seq_q), st);
   }

@@ -29,8 +29,12 @@ struct F32Cfg {
 };
 
 // With BLK only the key tiles whose 128 x 128 block is set in the block mask
-// are visited (a workgroup's queries lie in one block row).
-template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+// are visited (a workgroup's queries lie in one block row).  With SPLIT
+// (head_dim <= 128; a short query block against a long key sequence) the
+// grid is (batch * heads) x query blocks x a.n_split key chunks of a.chunk
+// keys, and each workgroup writes its rows' unnormalised partial
+// (accumulator, running max, sum) to a.partial for the decode merge.
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   using C = F32Cfg<D>;
   constexpr int DS = C::DS, BM = C::BM, BN = C::BN, P = C::P;
@@ -50,10 +54,16 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = wave / DS, e = wave % DS;
+  static_assert(!SPLIT || DS == 1, "the key split is built for head_dim <= 128");
   const int BH = a.B * a.H;
   const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
-  if (CAUSAL) qb = a.n_qblocks - 1 - qb;
+  int qb = blockIdx.x / BH, split = 0;
+  if constexpr (SPLIT) {
+    split = qb % a.n_split;
+    qb /= a.n_split;
+  } else if (CAUSAL) {
+    qb = a.n_qblocks - 1 - qb;
+  }
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM;
@@ -87,10 +97,17 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
-  int ntiles = (kv_end + BN - 1) / BN;
+  const int ntiles_all = (kv_end + BN - 1) / BN;
+  int t_lo = 0, t_hi = ntiles_all;   // the 32-key tiles this workgroup visits
+  if constexpr (SPLIT) {
+    const int ct = a.chunk / BN;
+    t_lo = min(split * ct, ntiles_all);
+    t_hi = min(t_lo + ct, ntiles_all);
+  }
+  int ntiles = t_hi - t_lo;
   if constexpr (BLK) {
     const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
-    ntiles = compact_tiles(brow, 1, 2, 0, ntiles, sList, sCnt);   // 32-key tile t lies in block t / 4
+    ntiles = compact_tiles(brow, 1, 2, t_lo, t_hi, sList, sCnt);   // 32-key tile t lies in block t / 4
   }
 
   float m_run = kNegInf, l_run = 0.f;
@@ -105,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   // when P V of tile j is done and lands during the scores of tile j+1.  Each
   // wait counts the wave's own direct loads still allowed in flight.
   constexpr bool PIPE = D * 4 % 1024 == 0;
-  auto tile_kv = [&](int j) __attribute__((always_inline)) { return (BLK ? list_at(sList, j) : j) * BN; };
+  auto tile_kv = [&](int j) __attribute__((always_inline)) { return (BLK ? list_at(sList, j) : t_lo + j) * BN; };
   if constexpr (PIPE) {
     if (ntiles > 0) stage32_direct<D, true>(sK, Kg, tile_kv(0), Skv, wave, lane);
   }
@@ -221,6 +238,21 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 
   const float l_tot = l_run + xor32(l_run);
+  if constexpr (SPLIT) {
+    if (qi < Sq) {
+      float* Pp = a.partial + (((size_t)bh * Sq + qi) * a.n_split + split) * (D + 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Pp[32 * dt + 8 * (r >> 2) + 4 * hi + (r & 3)] = o[dt][r];
+      }
+      if (hi == 0) {
+        Pp[D] = l_tot > 0.f ? m_run : kNegInf;
+        Pp[D + 1] = l_tot;
+      }
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < Sq) {
     float* Og = (float*)a.o + ((size_t)bh * Sq + qi) * D + e * DSL;
@@ -236,36 +268,38 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 }
 
-template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT>
 static hipError_t launch_one_blk(const AttnArgs& a, hipStream_t st) {
-  auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK, BLK>;
+  auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK, BLK, SPLIT>;
   const size_t lds = BLK ? F32Cfg<D>::lds_blk : F32Cfg<D>::lds;
   if (lds > 65536) {
     hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(a.n_qblocks * a.B * a.H)), dim3(256), lds, st, a);
+  const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H) * (SPLIT ? (unsigned)a.n_split : 1u);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
-template <int D, int MOD, bool CAUSAL, bool MASK>
+template <int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
-  return a.block_mask ? launch_one_blk<D, MOD, CAUSAL, MASK, true>(a, st)
-                      : launch_one_blk<D, MOD, CAUSAL, MASK, false>(a, st);
+  return a.block_mask ? launch_one_blk<D, MOD, CAUSAL, MASK, true, SPLIT>(a, st)
+                      : launch_one_blk<D, MOD, CAUSAL, MASK, false, SPLIT>(a, st);
 }
 
-template <int D, int MOD>
+template <int D, int MOD, bool SPLIT>
 static hipError_t launch_fwd32_mod(const AttnArgs& a, bool causal, bool mask, hipStream_t st) {
-  if (causal) return mask ? launch_one<D, MOD, true, true>(a, st) : launch_one<D, MOD, true, false>(a, st);
-  return mask ? launch_one<D, MOD, false, true>(a, st) : launch_one<D, MOD, false, false>(a, st);
+  if (causal)
+    return mask ? launch_one<D, MOD, true, true, SPLIT>(a, st) : launch_one<D, MOD, true, false, SPLIT>(a, st);
+  return mask ? launch_one<D, MOD, false, true, SPLIT>(a, st) : launch_one<D, MOD, false, false, SPLIT>(a, st);
 }
 
-template <int D>
+template <int D, bool SPLIT>
 static hipError_t launch_fwd32_d(const AttnArgs& a, int mod, bool causal, bool mask, hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return launch_fwd32_mod<D, MOD_ALIBI>(a, causal, mask, st);
-    case MOD_CHECKERBOARD: return launch_fwd32_mod<D, MOD_CHECKERBOARD>(a, causal, mask, st);
-    default: return launch_fwd32_mod<D, MOD_NONE>(a, causal, mask, st);
+    case MOD_ALIBI: return launch_fwd32_mod<D, MOD_ALIBI, SPLIT>(a, causal, mask, st);
+    case MOD_CHECKERBOARD: return launch_fwd32_mod<D, MOD_CHECKERBOARD, SPLIT>(a, causal, mask, st);
+    default: return launch_fwd32_mod<D, MOD_NONE, SPLIT>(a, causal, mask, st);
   }
 }
 
@@ -277,10 +311,12 @@ size_t fwd32_lds_bytes(int D) {
   return D == 512 ? F32Cfg<512>::lds : D == 128 ? F32Cfg<128>::lds : F32Cfg<64>::lds;
 }
 
-hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st) {
-  if (D == 64) return launch_fwd32_d<64>(a, mod, causal, mask, st);
-  if (D == 128) return launch_fwd32_d<128>(a, mod, causal, mask, st);
-  return launch_fwd32_d<512>(a, mod, causal, mask, st);
+hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st, bool split) {
+  if (split) return D == 64 ? launch_fwd32_d<64, true>(a, mod, causal, mask, st)
+                            : launch_fwd32_d<128, true>(a, mod, causal, mask, st);
+  if (D == 64) return launch_fwd32_d<64, false>(a, mod, causal, mask, st);
+  if (D == 128) return launch_fwd32_d<128, false>(a, mod, causal, mask, st);
+  return launch_fwd32_d<512, false>(a, mod, causal, mask, st);
 }
 
 }  // namespace fa

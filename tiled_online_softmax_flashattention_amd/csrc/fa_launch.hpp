@@ -15,10 +15,13 @@ int fwd16_block_q(int D);
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
                         hipStream_t st, bool split = false);
 
-// fp32 forward (head_dim 64, 128 or 512).
+// fp32 forward (head_dim 64, 128 or 512).  With split (head_dim <= 128), each
+// query block is split over a.n_split key chunks of a.chunk keys (a multiple
+// of 32) whose partials go to a.partial, as launch_fwd16 does.
 int fwd32_block_q(int D);
 size_t fwd32_lds_bytes(int D);
-hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st);
+hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st,
+                        bool split = false);
 
 // Backward: preprocess (delta = rowsum(dO * O), lse in base 2), then the
 // key-stationary dK/dV pass and the query-stationary dQ pass.  kv16 = 0: the
