@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 /* Edge of the blocks of a block mask (query rows and keys), and the longest
  * seq_q / seq_kv a call with a block mask takes. */
@@ -79,18 +79,28 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 2,        /* valid request outside what the kernels implement */
   FA_ERR_WORKSPACE_TOO_SMALL = 3,
   FA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
-  FA_ERR_SCRATCH_LIMIT = 5       /* fa_decode_noalloc: the problem needs more than FA_DECODE_SCRATCH_BYTES */
+  FA_ERR_SCRATCH_LIMIT = 5,      /* fa_decode_noalloc: the problem needs more than FA_DECODE_SCRATCH_BYTES */
+  FA_ERR_COMPILE = 6             /* a caller-defined score_mod failed to compile */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
-/* score_mod kinds (flaxattention page: example and benchmark).
+/* score_mod kinds (flaxattention page: example and benchmark; attnax
+ * pallas_flash_attention page: score_mod, a callable on the scaled scores with
+ * global indices).
  *  FA_MOD_ALIBI:        bias = -slope_h * (pos_i - j).  slope_h comes from
  *                       alibi_slopes[h] (device float[heads]) or, when that is
  *                       NULL, slope_h = 2^(-8 (h + 1) / heads).
  *  FA_MOD_CHECKERBOARD: bias = checker_even when (pos_i + j) is even, otherwise
- *                       checker_odd (the workloads use +0.5 / -0.5). */
-typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2 } fa_mod_kind;
+ *                       checker_odd (the workloads use +0.5 / -0.5).
+ *  FA_MOD_CUSTOM:       s_ij = mod(scale * <q_i, k_j>, b, h, pos_i, j) with the
+ *                       caller's device function (fa_score_mod_create); f16
+ *                       and bf16 with head_dim 64 or 128, fa_forward and
+ *                       fa_backward (fa_decode returns FA_ERR_UNSUPPORTED). */
+typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2, FA_MOD_CUSTOM = 3 } fa_mod_kind;
+
+/* A caller-defined score_mod compiled for the device (fa_score_mod_create). */
+typedef struct fa_score_mod_s* fa_score_mod;
 
 /* dQ formation of the backward (fa_problem.dq_mode). */
 typedef enum { FA_DQ_AUTO = 0, FA_DQ_SEPARATE = 1, FA_DQ_ATOMIC = 2 } fa_dq_mode;
@@ -132,6 +142,10 @@ typedef struct {
    * chunks (1 <= n <= FA_MAX_KV_SPLITS; a 16-bit query block rounds chunks up
    * to whole 64-key tiles).  The results do not depend on it beyond rounding. */
   int32_t kv_splits;
+  /* FA_MOD_CUSTOM: the compiled score_mod and its parameter array (device
+   * floats handed to the caller's functions as `params`, or NULL). */
+  fa_score_mod custom_mod;
+  const float* mod_params;
 } fa_problem;
 
 /* Supported: dtype f16 or bf16 with head_dim 64 or 128; dtype f32 with
@@ -184,6 +198,31 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
 fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Caller-defined score_mod (attnax pallas_flash_attention page: score_mod is
+ * a callable traced into the inner loop, applied to the scaled scores with
+ * global indices; its gradient there comes from tracing).  `source` is HIP
+ * device code defining
+ *
+ *   __device__ float fa_score_mod(float score, int b, int h, int q_idx, int kv_idx,
+ *                                 const float* params);
+ *   __device__ float fa_score_mod_grad(float score, int b, int h, int q_idx, int kv_idx,
+ *                                      const float* params);
+ *
+ * score = scale * <q_i, k_j> (natural units), b and h the batch and head,
+ * q_idx = i + q_offset and kv_idx = j the global positions, params the
+ * problem's mod_params; fa_score_mod returns the modified score (before any
+ * mask: masked pairs are dropped whatever it returns) and fa_score_mod_grad
+ * its derivative with respect to score, which the backward multiplies into dS.
+ * The library compiles the source with hipRTC into its generic attention
+ * kernels: once here for the target, to report errors (FA_ERR_COMPILE, with
+ * the compiler's log in `log` (log_bytes, NUL-terminated) when log != NULL),
+ * and again for each (device, dtype, head_dim, causal, key mask, block mask)
+ * configuration on its first use (seconds; cached in the handle).  The handle
+ * is freed with fa_score_mod_destroy once no call using it is in flight;
+ * concurrent calls may share it. */
+fa_status fa_score_mod_create(const char* source, fa_score_mod* mod, char* log, size_t log_bytes);
+fa_status fa_score_mod_destroy(fa_score_mod mod);
 
 /* Bytes of the fixed device scratch behind fa_decode_noalloc (per device). */
 #define FA_DECODE_SCRATCH_BYTES (16u << 20)

@@ -35,6 +35,16 @@ What it computes (the definition the flash kernels reach up to rounding order):
   dP = dO V^T, D_i = sum_j P_ij dP_ij (= <dO_i, O_i>), dS = P * (dP - D),
   dQ = scale * dS K, dK = scale * dS^T Q, dV = P^T dO.
 
+A caller-defined score_mod (mod = MOD_CUSTOM, attnax pallas_flash_attention
+page: score_mod is a callable applied to the scaled scores with global
+indices, before the mask) is a pair custom = (fn, dfn) of numpy functions
+fn(s, b, h, q_idx, kv_idx) -> modified scores and dfn(...) -> d fn / d s,
+evaluated on the (rows, keys) matrix of s = scale <q_i, k_j> with q_idx a
+column and kv_idx a row of global positions.  Then s'_ij = fn(s_ij, ...),
+P = softmax of s' over the allowed keys, and by the chain rule
+dS_ij = P_ij (dP_ij - D_i) dfn(s_ij, ...) in dQ = scale dS K and
+dK = scale dS^T Q (the page obtains the same derivative by tracing).
+
 score_mod kinds (the pages name them but do not define them; the readings
 are the workloads' own definitions):
 
@@ -59,7 +69,7 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD = 0, 1, 2
+MOD_NONE, MOD_ALIBI, MOD_CHECKERBOARD, MOD_CUSTOM = 0, 1, 2, 3
 
 
 def as_f64(x) -> np.ndarray:
@@ -114,7 +124,18 @@ def _block_allowed(block_mask, b: int, h: int, rows: np.ndarray, seq_kv: int) ->
 def _probabilities(qb: np.ndarray, kb: np.ndarray, scale: float, bias: np.ndarray,
                    ok: np.ndarray):
     """Scores, lse and P for one (batch, head) and a block of query rows."""
-    s = scale * (qb @ kb.T) + bias
+    return _softmax_rows(scale * (qb @ kb.T) + bias, ok)
+
+
+def _custom_scores(qb, kb, scale, custom, b, h, pos, kv_idx):
+    """(s, s') for a caller-defined score_mod: s = scale q.k, s' = fn(s, ...)."""
+    s = scale * (qb @ kb.T)
+    return s, np.asarray(custom[0](s, b, h, np.asarray(pos)[:, None], np.asarray(kv_idx)[None, :]),
+                         dtype=np.float64) * np.ones_like(s)
+
+
+def _softmax_rows(s: np.ndarray, ok: np.ndarray):
+    """lse and P of the allowed entries of each row of s (empty rows: -inf, 0)."""
     s_allowed = np.where(ok, s, -np.inf)
     m = s_allowed.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
     any_ok = np.isfinite(m)
@@ -140,7 +161,7 @@ def _setup(q, k, v, rows, key_mask):
 
 def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
             mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-            rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None):
+            rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None, custom=None):
     """Exact attention output and log-sum-exp.
 
     Returns ``(o, lse)``: o (B, H, R, D), lse (B, H, R) in fp64, where R are the
@@ -159,16 +180,20 @@ def forward(q, k, v, *, scale: float, causal: bool = False, key_mask=None,
     for b in range(B):
         ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
         for h in range(H):
-            bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
             okh = ok if block_mask is None else ok & _block_allowed(block_mask, b, h, rows, seq_kv)
-            _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, okh)
+            if mod == MOD_CUSTOM:
+                _, s_mod = _custom_scores(q[b, h, rows], k[b, h], scale, custom, b, h, pos, kv_idx)
+                _, lse[b, h], p = _softmax_rows(s_mod, okh)
+            else:
+                bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
+                _, lse[b, h], p = _probabilities(q[b, h, rows], k[b, h], scale, bias, okh)
             o[b, h] = p @ v[b, h]
     return o, lse
 
 
 def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None,
              mod: int = MOD_NONE, alibi_slopes=None, checker=(0.5, -0.5),
-             rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None):
+             rows: Optional[Sequence[int]] = None, q_offset: int = 0, block_mask=None, custom=None):
     """Analytic gradients of sum(dout * O) with respect to q, k and v.
 
     Returns ``(dq, dk, dv)``: dq (B, H, R, D) for the requested rows; dk and dv
@@ -189,13 +214,20 @@ def backward(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=None
     for b in range(B):
         ok = allowed_pairs(pos, seq_kv, causal, None if km is None else km[b])
         for h in range(H):
-            bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
             qb, dob = q[b, h, rows], do[b, h, rows]
             okh = ok if block_mask is None else ok & _block_allowed(block_mask, b, h, rows, seq_kv)
-            _, _, p = _probabilities(qb, k[b, h], scale, bias, okh)
+            if mod == MOD_CUSTOM:
+                s_raw, s_mod = _custom_scores(qb, k[b, h], scale, custom, b, h, pos, kv_idx)
+                _, _, p = _softmax_rows(s_mod, okh)
+            else:
+                bias = score_bias(mod, h, pos, kv_idx, H, alibi_slopes, checker)
+                _, _, p = _probabilities(qb, k[b, h], scale, bias, okh)
             dp = dob @ v[b, h].T
             d_row = (p * dp).sum(axis=1)
             ds = p * (dp - d_row[:, None])
+            if mod == MOD_CUSTOM:   # chain rule through the caller's mod (allowed pairs only)
+                ds = np.where(okh, ds * (np.asarray(custom[1](s_raw, b, h, pos[:, None], kv_idx[None, :]),
+                                                    dtype=np.float64) * np.ones_like(s_raw)), 0.0)
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ qb)
             dv[b, h] = p.T @ dob
@@ -242,6 +274,8 @@ def magnitudes(q, k, v, dout, *, scale: float, causal: bool = False, key_mask=No
     forward/backward with the same ``rows``.  Every M is at least the absolute
     value of the corresponding result (r >= 1 and T_ij >= |dS_ij|).
     """
+    if mod == MOD_CUSTOM:
+        raise NotImplementedError("error magnitudes are defined for the built-in score_mods")
     q, k, v, rows, km = _setup(q, k, v, rows, key_mask)
     do = as_f64(dout)
     B, H, _, D = q.shape

@@ -62,6 +62,7 @@ def check(name: str, gpu: torch.Tensor, ref: np.ndarray, dtype: str, kind: str, 
             f"worst ratio {ratio:.3f}")
         assert ok, f"{name}: error above the derived bound (worst ratio {ratio:.3f})"
         return e
+    say(f"[{name}] {dtype} max-abs-err / max|ref| {e:.3e} <= {tol:.0e}" if e <= tol else f"[{name}] {e:.3e}")
     assert e <= tol, f"{name}: error {e:.3e} > {tol:.1e}"
     return e
 

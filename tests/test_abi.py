@@ -42,8 +42,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 5
-    for s in range(6):
+    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 6
+    for s in range(7):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"
 
@@ -96,7 +96,7 @@ INVALID, UNSUP, WS = _lib.FA_ERR_INVALID_ARGUMENT, _lib.FA_ERR_UNSUPPORTED, _lib
 
 
 @pytest.mark.parametrize("field,value", [("batch", 0), ("heads", -1), ("seq_q", 0), ("seq_kv", 0),
-                                         ("head_dim", 0), ("dtype", 7), ("causal", 2), ("mod_kind", 3),
+                                         ("head_dim", 0), ("dtype", 7), ("causal", 2), ("mod_kind", 4),
                                          ("scale", float("nan")), ("scale", float("inf"))])
 def test_invalid_problem_fields(field, value):
     assert fwd(prob(**{field: value})) == INVALID
@@ -341,3 +341,29 @@ def test_dq_mode_and_kv_splits_rules():
     n1 = n.value
     assert lib.fa_decode_workspace_size(ctypes.byref(seven), ctypes.byref(n)) == _lib.FA_OK
     assert n.value >= 7 * 2 * 4 * (64 + 2) * 4 and n1 >= 2 * 4 * (64 + 2) * 4 and n.value > n1
+
+
+def test_score_mod_create_compiles_and_reports_errors():
+    """fa_score_mod_create compiles the caller's functions into the generic
+    kernels with the run-time compiler (no GPU needed for that) and returns
+    FA_ERR_COMPILE with the compiler's log for a broken source."""
+    lib = _lib.load()
+    good = b"""
+    __device__ float fa_score_mod(float s, int b, int h, int q, int k, const float* p) { return s * 0.5f + p[0]; }
+    __device__ float fa_score_mod_grad(float s, int b, int h, int q, int k, const float* p) { return 0.5f; }
+    """
+    h = ctypes.c_void_p()
+    log = ctypes.create_string_buffer(1 << 14)
+    assert lib.fa_score_mod_create(good, ctypes.byref(h), log, len(log)) == _lib.FA_OK
+    assert h.value
+    assert lib.fa_score_mod_destroy(h) == _lib.FA_OK
+    bad = b"__device__ float fa_score_mod(float s) { return s + ; }"
+    h2 = ctypes.c_void_p()
+    assert lib.fa_score_mod_create(bad, ctypes.byref(h2), log, len(log)) == _lib.FA_ERR_COMPILE
+    assert not h2.value and b"error" in log.value
+    assert lib.fa_score_mod_create(None, ctypes.byref(h2), None, 0) == INVALID
+    assert lib.fa_score_mod_destroy(None) == INVALID
+    # a custom mod needs its handle, and is refused for fp32
+    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM)) == INVALID
+    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32)) == UNSUP
+    assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10])) == UNSUP

@@ -7,6 +7,7 @@ analytic backward, invariants, and an independent library attention routine
 (torch's fp64 CPU ``scaled_dot_product_attention`` with autograd).
 """
 import json
+import sys
 import math
 import os
 
@@ -602,3 +603,96 @@ def test_fp32_evaluation_stays_within_the_derived_bound(causal, mod, use_mask, D
                                  mags):
         ok_, ratio = within(np.abs(got.double().numpy() - ref), 0.0, kap, m)
         assert ok_, f"{name}: error / (kappa u M) = {ratio:.3f}"
+
+
+# --------------------------------------------------------------------------- caller-defined score_mods
+
+from oracle import MOD_CUSTOM  # noqa: E402
+
+CAP = 1.5   # soft-cap of the tanh score_mod below
+
+
+def softcap(s, b, h, qi, kj):
+    return CAP * np.tanh(s / CAP)
+
+
+def softcap_grad(s, b, h, qi, kj):
+    return 1.0 - np.tanh(s / CAP) ** 2
+
+
+@pytest.mark.parametrize("causal,use_mask", [(False, False), (True, False), (False, True), (True, True)])
+def test_custom_identity_and_additive_alibi_are_the_builtin_mods(causal, use_mask):
+    """A custom mod returning the score unchanged is MOD_NONE, and one adding
+    -slope_h (q_idx - kv_idx) is MOD_ALIBI, for the output, lse and every
+    gradient (the derivative of an additive mod is 1)."""
+    B, H, Sq, Skv, D, off = 2, 3, 13, 21, 4, 8
+    q, k, v, do, km = _case(75, B=B, H=H, Sq=Sq, Skv=Skv, D=D, key_mask=use_mask)
+    slopes = 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
+    ident = (lambda s, b, h, qi, kj: s, lambda s, b, h, qi, kj: np.ones_like(s))
+    alibi = (lambda s, b, h, qi, kj: s - slopes[h] * (qi - kj), lambda s, b, h, qi, kj: np.ones_like(s))
+    for builtin, custom in ((MOD_NONE, ident), (MOD_ALIBI, alibi)):
+        base = dict(scale=0.7, causal=causal, key_mask=km, q_offset=off)
+        o0, l0 = oracle.forward(q, k, v, mod=builtin, **base)
+        o1, l1 = oracle.forward(q, k, v, mod=MOD_CUSTOM, custom=custom, **base)
+        np.testing.assert_allclose(o1, o0, atol=1e-14)
+        np.testing.assert_allclose(l1, l0, atol=1e-13)
+        for g0, g1 in zip(oracle.backward(q, k, v, do, mod=builtin, **base),
+                          oracle.backward(q, k, v, do, mod=MOD_CUSTOM, custom=custom, **base)):
+            np.testing.assert_allclose(g1, g0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,use_mask,off", [(False, False, 0), (True, False, 0), (True, True, 9),
+                                                 (False, True, 5)])
+def test_custom_softcap_against_torch_autograd(causal, use_mask, off):
+    """A score-dependent mod (tanh soft-cap of the scaled scores) against an
+    independent torch fp64 evaluation: scores, tanh, masks, softmax, P V, and
+    torch's autograd for the gradients."""
+    B, H, Sq, Skv, D = 2, 2, 17, 26, 8
+    q, k, v, do, km = _case(76, B=B, H=H, Sq=Sq, Skv=Skv, D=D, key_mask=use_mask)
+    q, k = 2.0 * q, 2.0 * k   # scores well into tanh's bend
+    scale = 1.0 / math.sqrt(D)
+    kw = dict(scale=scale, causal=causal, key_mask=km, q_offset=off, mod=MOD_CUSTOM, custom=(softcap, softcap_grad))
+    o, lse = oracle.forward(q, k, v, **kw)
+    dq, dk, dv = oracle.backward(q, k, v, do, **kw)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = CAP * torch.tanh(scale * (tq @ tk.transpose(-1, -2)) / CAP)
+    s = s + _torch_bias(MOD_NONE, B, H, Sq, Skv, causal, km, off)
+    to = torch.softmax(s, dim=-1) @ tv
+    to.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, to.detach().numpy(), atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).detach().numpy(), atol=1e-12)
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), atol=1e-12)
+
+
+def test_custom_softcap_gradients_match_central_differences():
+    B, H, S, D = 1, 2, 5, 3
+    q, k, v, do, km = _case(77, B=B, H=H, Sq=S, Skv=S, D=D, key_mask=True)
+    kw = dict(scale=2.0, causal=True, key_mask=km, mod=MOD_CUSTOM, custom=(softcap, softcap_grad))
+    grads = oracle.backward(q, k, v, do, **kw)
+    h = 1e-5
+    for name, x, g in zip(("q", "k", "v"), (q, k, v), grads):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args = [{"q": q, "k": k, "v": v}, {"q": q, "k": k, "v": v}]
+            for sgn, a in zip((1, -1), args):
+                xx = x.copy()
+                xx[idx] += sgn * h
+                a[name] = xx
+            num[idx] = (_loss(args[0]["q"], args[0]["k"], args[0]["v"], do, kw)
+                        - _loss(args[1]["q"], args[1]["k"], args[1]["v"], do, kw)) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=1e-8, err_msg=f"d{name}")
+
+
+def test_custom_pins_catch_a_dropped_chain_rule_factor(monkeypatch):
+    """Plant a mistake (the backward forgets the mod's derivative) and check
+    that the autograd pin rejects it."""
+    import oracle.attention as A
+    real = softcap_grad
+    monkeypatch.setattr(sys.modules[__name__], "softcap_grad", lambda s, b, h, qi, kj: np.ones_like(s))
+    with pytest.raises(AssertionError):
+        test_custom_softcap_against_torch_autograd(False, False, 0)
+    monkeypatch.setattr(sys.modules[__name__], "softcap_grad", real)
+    assert A.MOD_CUSTOM == MOD_CUSTOM

@@ -11,7 +11,8 @@ is no CPU or PyTorch fallback, and a missing library raises.
 
 q, k, v: (batch, heads, seq, head_dim) contiguous cuda tensors of one dtype
 (float32, float16 or bfloat16); key_mask: (batch, seq_kv) uint8/bool,
-nonzero = keep; score_mod: None, "alibi" or "checkerboard"; block_mask:
+nonzero = keep; score_mod: None, "alibi", "checkerboard" or a ScoreMod (caller-defined, with
+mod_params); block_mask:
 (batch, heads, ceil(seq_q/128), ceil(seq_kv/128)) uint8/bool, zero removes a
 128 x 128 block of (query row, key) pairs (``block_mask_shape`` gives the
 shape).
@@ -27,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["forward", "backward", "decode", "decode_noalloc", "backward_workspace_bytes", "decode_workspace_bytes",
+__all__ = ["forward", "backward", "decode", "decode_noalloc", "ScoreMod", "backward_workspace_bytes", "decode_workspace_bytes",
            "FaError", "problem", "plan_forward", "plan_backward", "plan_decode", "block_mask_shape"]
 
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
@@ -44,6 +45,50 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+class ScoreMod:
+    """A caller-defined score_mod, compiled by the library (hipRTC).
+
+    ``source`` is HIP device code defining
+
+        __device__ float fa_score_mod(float score, int b, int h, int q_idx, int kv_idx,
+                                      const float* params);
+        __device__ float fa_score_mod_grad(float score, int b, int h, int q_idx, int kv_idx,
+                                           const float* params);
+
+    (the modified score of score = scale * q.k at global positions, and its
+    derivative with respect to score).  Pass the object as ``score_mod=`` and
+    its parameters as ``mod_params=`` (a float32 cuda tensor) to forward and
+    backward.  Compile errors raise FaError with the compiler's log."""
+
+    def __init__(self, source: str):
+        lib = _lib.load()
+        handle = ctypes.c_void_p()
+        log = ctypes.create_string_buffer(1 << 16)
+        st = lib.fa_score_mod_create(source.encode(), ctypes.byref(handle), log, len(log))
+        if st != _lib.FA_OK:
+            raise FaError(st, "fa_score_mod_create", log.value.decode(errors="replace"))
+        self.source = source
+        self._handle = handle
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._handle is None:
+            raise ValueError("ScoreMod has been closed")
+        return self._handle
+
+    def close(self) -> None:
+        """Releases the compiled code (no call using it may be in flight)."""
+        if getattr(self, "_handle", None) is not None:
+            _lib.load().fa_score_mod_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def block_mask_shape(batch: int, heads: int, seq_q: int, seq_kv: int) -> Tuple[int, int, int, int]:
     """Shape of a block mask: one byte per 128 x 128 block of (query row, key)."""
     n = _lib.FA_BLOCK_MASK_BLOCK
@@ -55,7 +100,7 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
             scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
             checker: Tuple[float, float] = (0.5, -0.5), q_offset: int = 0,
             block_mask: Optional[torch.Tensor] = None, dq_mode: str = "auto",
-            kv_splits: int = 0) -> _lib.FaProblem:
+            kv_splits: int = 0, mod_params: Optional[torch.Tensor] = None) -> _lib.FaProblem:
     """The C-ABI problem descriptor for these tensors.  q_offset is the
     position of query row 0 among the keys (0 for self-attention; the number
     of cached keys before the first query with a KV cache).  dq_mode ("auto",
@@ -68,7 +113,7 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
                 torch.uint8)
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
-    if score_mod not in _MOD:
+    if not isinstance(score_mod, ScoreMod) and score_mod not in _MOD:
         raise ValueError(f"unknown score_mod {score_mod!r}")
     B, H, Sq, D = q.shape
     p = _lib.FaProblem()
@@ -76,7 +121,15 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     p.dtype = _DTYPE[q.dtype]
     p.causal = int(bool(causal))
     p.scale = float(1.0 / math.sqrt(D) if scale is None else scale)
-    p.mod_kind = _MOD[score_mod]
+    if isinstance(score_mod, ScoreMod):
+        p.mod_kind = _lib.FA_MOD_CUSTOM
+        p.custom_mod = score_mod.handle
+    else:
+        p.mod_kind = _MOD[score_mod]
+    if mod_params is not None:
+        if mod_params.dtype != torch.float32 or not mod_params.is_contiguous():
+            raise ValueError("mod_params must be a contiguous float32 tensor")
+        p.mod_params = mod_params.data_ptr()
     p.alibi_slopes = None if alibi_slopes is None else alibi_slopes.data_ptr()
     p.checker_even, p.checker_odd = float(checker[0]), float(checker[1])
     p.key_mask = None if key_mask is None else key_mask.data_ptr()
@@ -146,13 +199,14 @@ def _mask_u8(key_mask):
 
 
 def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-            checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None):
+            checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None, mod_params=None):
     """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
-    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, mod_params)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                mod_params=mod_params)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     lib = _lib.load()
@@ -169,7 +223,7 @@ def backward_workspace_bytes(p: _lib.FaProblem) -> int:
 
 def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=None, scale=None,
              alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, workspace=None, grads=None,
-             which="all", dq_mode="auto"):
+             which="all", dq_mode="auto", mod_params=None):
     """Gradients (dq, dk, dv) of sum(dout * out).
 
     which="dq" runs only the query pass (dk, dv come back as None), "dkdv"
@@ -181,11 +235,11 @@ def backward(q, k, v, out, lse, dout, *, causal=False, key_mask=None, score_mod=
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               dout=dout, grads=grads if grads is not None else (None, None, None), workspace=workspace)
-    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask, workspace,
+    _check_tensors(q, k, v, out, lse, dout, key_mask, alibi_slopes, block_mask, workspace, mod_params,
                    *(grads if grads is not None else ()))
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                dq_mode=dq_mode)
+                dq_mode=dq_mode, mod_params=mod_params)
     need = backward_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -208,7 +262,7 @@ def decode_workspace_bytes(p: _lib.FaProblem) -> int:
 
 
 def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0,
-           causal=False, block_mask=None, workspace=None, out=None, lse=None, kv_splits=0):
+           causal=False, block_mask=None, workspace=None, out=None, lse=None, kv_splits=0, mod_params=None):
     """Attention for a short query block (1 <= seq_q <= 64, row i at key
     position q_offset + i), split over the key axis (into about kv_splits
     chunks; 0 = the library's choice).  With causal=True a row sees keys up
@@ -219,7 +273,7 @@ def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=N
     _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, workspace)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                kv_splits=kv_splits)
+                kv_splits=kv_splits, mod_params=mod_params)
     need = decode_workspace_bytes(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -265,33 +319,36 @@ def _plan(fn, name, args, keep):
 
 
 def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
-                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None):
+                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, mod_params=None):
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
-    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask)
+    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask, mod_params)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                mod_params=mod_params)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
-    return _plan(lib.fa_forward, "fa_forward", args, (p, q, k, v, out, lse, key_mask, alibi_slopes, block_mask))
+    return _plan(lib.fa_forward, "fa_forward", args,
+                 (p, q, k, v, out, lse, key_mask, alibi_slopes, block_mask, score_mod, mod_params))
 
 
 def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,
                   score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None,
-                  dq_mode="auto"):
+                  dq_mode="auto", mod_params=None):
     """dq may be None (key/value pass only); dk and dv may both be None (query pass only)."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               dout=dout, grads=(dq, dk, dv), workspace=workspace)
-    _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask)
+    _check_tensors(q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask, mod_params)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                dq_mode=dq_mode)
+                dq_mode=dq_mode, mod_params=mod_params)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q))
     return _plan(lib.fa_backward, "fa_backward", args,
-                 (p, q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask))
+                 (p, q, k, v, out, lse, dout, dq, dk, dv, workspace, key_mask, alibi_slopes, block_mask, score_mod,
+                  mod_params))
 
 
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,

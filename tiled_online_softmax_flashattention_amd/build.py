@@ -21,13 +21,16 @@ OUT = os.path.join(PKG, "libfa_mi355x.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_bwd16.hip", "fa_bwd32.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_rtc.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_bwd16.hip", "fa_bwd32.hip",
+           "fa_decode.hip"]
+# headers compiled again at run time (caller-defined score_mods), embedded as strings
+RTC_EMBED = (("kRtcCommon", "fa_common.hpp"), ("kRtcCustom", "fa_custom.hpp"))
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-I", BUILD,
     "-Wno-unused-command-line-argument",
 ]
 
@@ -49,15 +52,33 @@ def _compile(src: str) -> str:
     return obj
 
 
+def write_rtc_sources() -> None:
+    """fa_rtc_sources.inc: the headers the run-time compiler needs, as raw
+    string literals."""
+    delim = "FA_RTC_SRC"
+    parts = []
+    for name, fname in RTC_EMBED:
+        text = open(os.path.join(CSRC, fname)).read()
+        if f"){delim}" in text:
+            raise RuntimeError(f"{fname} contains the raw-string delimiter")
+        parts.append(f'static const char {name}[] = R"{delim}({text}){delim}";\n')
+    path = os.path.join(BUILD, "fa_rtc_sources.inc")
+    new = "".join(parts)
+    if not os.path.exists(path) or open(path).read() != new:
+        with open(path, "w") as fh:
+            fh.write(new)
+
+
 def build(jobs: int = 0, verbose: bool = True) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
+    write_rtc_sources()
     t0 = time.time()
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lhiprtc"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

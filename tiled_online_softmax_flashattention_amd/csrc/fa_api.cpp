@@ -10,6 +10,7 @@
 
 #include "../../include/fa_mi355x.h"
 #include "fa_launch.hpp"
+#include "fa_rtc.hpp"
 
 namespace {
 
@@ -31,8 +32,11 @@ fa_status validate_problem(const fa_problem* p) {
     return FA_ERR_INVALID_ARGUMENT;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return FA_ERR_INVALID_ARGUMENT;
-  if (p->mod_kind != FA_MOD_NONE && p->mod_kind != FA_MOD_ALIBI && p->mod_kind != FA_MOD_CHECKERBOARD)
+  if (p->mod_kind != FA_MOD_NONE && p->mod_kind != FA_MOD_ALIBI && p->mod_kind != FA_MOD_CHECKERBOARD &&
+      p->mod_kind != FA_MOD_CUSTOM)
     return FA_ERR_INVALID_ARGUMENT;
+  if (p->mod_kind == FA_MOD_CUSTOM && !p->custom_mod) return FA_ERR_INVALID_ARGUMENT;
+  if (p->mod_params && ((uintptr_t)p->mod_params & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARGUMENT;
   // the kernels mask scores as -inf before multiplying by scale and keep the
   // backward's log-sum-exp in units of scale * q.k: scale must be positive
@@ -42,6 +46,8 @@ fa_status validate_problem(const fa_problem* p) {
   if (p->q_offset < 0) return FA_ERR_INVALID_ARGUMENT;
   if (p->alibi_slopes && ((uintptr_t)p->alibi_slopes & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
+  // caller-defined score_mods run the generic 16-bit kernels (head_dim 64, 128)
+  if (p->mod_kind == FA_MOD_CUSTOM && p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 32-bit per (batch, head) slice
   if (p->batch * p->heads > kMaxI32 / 8) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;
@@ -78,6 +84,11 @@ bool dq_atomic_by_default(const fa_problem* p) {
 // passes run).  FA_ERR_UNSUPPORTED for an explicit atomic request it cannot
 // serve.
 fa_status resolve_dq_atomic(const fa_problem* p, bool* atomic) {
+  if (p->mod_kind == FA_MOD_CUSTOM) {   // the caller-defined score_mod kernels have the separate passes only
+    if (p->dq_mode == FA_DQ_ATOMIC) return FA_ERR_UNSUPPORTED;
+    *atomic = false;
+    return FA_OK;
+  }
   if (p->dq_mode == FA_DQ_ATOMIC) {
     if (!dq_atomic_fits(p)) return FA_ERR_UNSUPPORTED;
     *atomic = true;
@@ -116,6 +127,7 @@ fa::AttnArgs make_args(const fa_problem* p) {
   a.block_mask = p->block_mask;
   a.bm_rows = (int)((p->seq_q + FA_BLOCK_MASK_BLOCK - 1) / FA_BLOCK_MASK_BLOCK);
   a.bm_cols = (int)((p->seq_kv + FA_BLOCK_MASK_BLOCK - 1) / FA_BLOCK_MASK_BLOCK);
+  a.mod_params = p->mod_params;
   return a;
 }
 
@@ -184,6 +196,9 @@ fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const vo
   a.lse = lse;
   a.n_qblocks = (int)nqb;
   hipStream_t st = (hipStream_t)stream;
+  if (p->mod_kind == FA_MOD_CUSTOM)
+    return fa::custom_launch(p->custom_mod, 0, p->dtype, (int)p->head_dim, p->causal != 0, p->key_mask != nullptr,
+                             p->block_mask != nullptr, a, (unsigned)(nqb * p->batch * p->heads), st);
   hipError_t err;
   if (p->dtype == FA_F32)
     err = fa::launch_fwd32(a, (int)p->head_dim, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
@@ -245,6 +260,21 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   a.n_qblocks = (int)nqb;
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
+  if (p->mod_kind == FA_MOD_CUSTOM) {   // preprocess (plain rows), then the run-time compiled passes
+    err = fa::launch_bwd_pre(a, p->dtype, D, st, 0);
+    if (err != hipSuccess) return FA_ERR_HIP;
+    const bool causal = p->causal != 0, mask = p->key_mask != nullptr, blk = p->block_mask != nullptr;
+    const unsigned bh = (unsigned)(p->batch * p->heads);
+    if (want_q) {
+      s = fa::custom_launch(p->custom_mod, 1, p->dtype, D, causal, mask, blk, a,
+                            (unsigned)ceil_div(p->seq_q, 128) * bh, st);
+      if (s != FA_OK) return s;
+    }
+    if (want_kv)
+      s = fa::custom_launch(p->custom_mod, 2, p->dtype, D, causal, mask, blk, a,
+                            (unsigned)ceil_div(p->seq_kv, 128) * bh, st);
+    return s;
+  }
   if (f32) {   // fp32: preprocess kernel, then the passes
     err = fa::launch_bwd_pre(a, p->dtype, D, st);
     if (err != hipSuccess) return FA_ERR_HIP;
@@ -276,6 +306,7 @@ fa_status validate_decode(const fa_problem* p, const void* q, const void* k, con
                           float* lse) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
+  if (p->mod_kind == FA_MOD_CUSTOM) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxDecodeQ) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
@@ -367,6 +398,12 @@ fa_status fa_decode_noalloc(const fa_problem* p, const void* q, const void* k, c
   return decode_launch(p, q, k, v, out, lse, ws, stream);
 }
 
+fa_status fa_score_mod_create(const char* source, fa_score_mod* mod, char* log, size_t log_bytes) {
+  return fa::custom_create(source, mod, log, log_bytes);
+}
+
+fa_status fa_score_mod_destroy(fa_score_mod mod) { return fa::custom_destroy(mod); }
+
 const char* fa_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "ok";
@@ -375,6 +412,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_SCRATCH_LIMIT: return "problem needs more than the fixed scratch of the allocation-free entry point";
+    case FA_ERR_COMPILE: return "the caller-defined score_mod failed to compile";
   }
   return "unknown status";
 }

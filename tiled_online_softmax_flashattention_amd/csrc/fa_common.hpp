@@ -8,8 +8,19 @@
 // plus its partner lane l ^ 32.
 #pragma once
 
+#ifdef __HIPCC_RTC__
+// Compiled at run time (hipRTC, the caller-defined score_mod kernels): the
+// runtime header is implicit and the fixed-width types live in its namespace.
+typedef __hip_internal::uint8_t uint8_t;
+typedef __hip_internal::uint16_t uint16_t;
+typedef __hip_internal::uint32_t uint32_t;
+typedef __hip_internal::uint64_t uint64_t;
+typedef __hip_internal::int64_t int64_t;
+typedef __UINTPTR_TYPE__ uintptr_t;
+#else
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#endif
 
 namespace fa {
 
@@ -407,6 +418,7 @@ struct AttnArgs {
   int chunk;           // decode: keys per chunk
   const uint8_t* block_mask;   // (B, H, bm_rows, bm_cols) bytes, 0 = block skipped; NULL = dense
   int bm_rows, bm_cols;        // ceil(Sq / kBlk), ceil(Skv / kBlk)
+  const float* mod_params;     // caller-defined score_mod: its parameter array (device), or NULL
 };
 
 // ------------------------------------------------------------ block sparsity

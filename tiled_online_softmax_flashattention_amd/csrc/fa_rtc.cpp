@@ -1,0 +1,154 @@
+// Caller-defined score_mods: run-time compilation (hipRTC) of the generic
+// kernels of fa_custom.hpp around the caller's device functions, a cache of
+// the loaded code objects per device and kernel configuration, and their
+// launches.  The kernel sources are embedded in the library at build time
+// (fa_rtc_sources.inc, generated from fa_common.hpp and fa_custom.hpp).
+#include <hip/hip_runtime.h>
+#include <hip/hiprtc.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/fa_mi355x.h"
+#include "fa_rtc.hpp"
+
+#include "fa_rtc_sources.inc"   // kRtcCommon, kRtcCustom
+
+struct fa_score_mod_s {
+  std::string source;
+  std::mutex mu;
+  struct Loaded {
+    hipModule_t module;
+    hipFunction_t fn[3];   // forward, query pass, key/value pass
+  };
+  std::map<std::tuple<int, int, int, int, int, int>, Loaded> cache;   // device, dtype, D, causal, mask, block
+};
+
+namespace fa {
+namespace {
+
+const char* kKernelNames[3] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv"};
+
+// The translation unit: the caller's functions, then the kernel templates and
+// one instantiation of each pass for the configuration.
+std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, bool mask, bool blk) {
+  const char* T = dtype == FA_BF16 ? "fa::BF16" : "fa::F16";
+  const int lb = D == 64 ? 2 : 1;   // workgroups per CU the registers allow
+  char inst[1024];
+  const char* tf[2] = {"false", "true"};
+  snprintf(inst, sizeof(inst),
+           "\n#include \"fa_custom.hpp\"\n"
+           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_fwd(const fa::AttnArgs a) "
+           "{ fa::fwd_custom<%s, %d, %s, %s, %s>(a); }\n"
+           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_dq(const fa::AttnArgs a) "
+           "{ fa::dq_custom<%s, %d, %s, %s, %s>(a); }\n"
+           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_dkdv(const fa::AttnArgs a) "
+           "{ fa::dkdv_custom<%s, %d, %s, %s, %s>(a); }\n",
+           lb, T, D, tf[causal], tf[mask], tf[blk], lb, T, D, tf[causal], tf[mask], tf[blk], lb, T, D, tf[causal],
+           tf[mask], tf[blk]);
+  return user + "\n" + inst;
+}
+
+// Compiles one configuration for `arch`; returns the code object or an
+// empty vector with the compiler log in *log.
+std::vector<char> rtc_compile(const std::string& unit, const std::string& arch, std::string* log) {
+  hiprtcProgram prog;
+  const char* headers[2] = {kRtcCommon, kRtcCustom};
+  const char* names[2] = {"fa_common.hpp", "fa_custom.hpp"};
+  if (hiprtcCreateProgram(&prog, unit.c_str(), "fa_score_mod.hip", 2, headers, names) != HIPRTC_SUCCESS) {
+    *log = "hiprtcCreateProgram failed";
+    return {};
+  }
+  const std::string arch_opt = "--offload-arch=" + arch;
+  // no packed fp32 VALU instructions, as in the library's own build
+  const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                        "-packed-fp32-ops"};
+  const hiprtcResult r = hiprtcCompileProgram(prog, (int)(sizeof(opts) / sizeof(opts[0])), opts);
+  size_t n = 0;
+  hiprtcGetProgramLogSize(prog, &n);
+  log->assign(n, '\0');
+  if (n) hiprtcGetProgramLog(prog, &(*log)[0]);
+  std::vector<char> code;
+  if (r == HIPRTC_SUCCESS) {
+    size_t cs = 0;
+    hiprtcGetCodeSize(prog, &cs);
+    code.resize(cs);
+    hiprtcGetCode(prog, code.data());
+  }
+  hiprtcDestroyProgram(&prog);
+  return code;
+}
+
+std::string device_arch(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return "gfx950";
+  std::string a = prop.gcnArchName;
+  const size_t colon = a.find(':');
+  return colon == std::string::npos ? a : a.substr(0, colon);
+}
+
+}  // namespace
+
+fa_status custom_create(const char* source, fa_score_mod* out, char* log, size_t log_bytes) {
+  if (!source || !out) return FA_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  // one configuration compiled for the target, so that errors in the
+  // caller's source surface here, with the compiler's log
+  std::string msg;
+  const std::vector<char> code = rtc_compile(rtc_unit(source, FA_F16, 64, false, false, false), "gfx950", &msg);
+  if (log && log_bytes) {
+    const size_t m = msg.size() < log_bytes - 1 ? msg.size() : log_bytes - 1;
+    memcpy(log, msg.data(), m);
+    log[m] = '\0';
+  }
+  if (code.empty()) return FA_ERR_COMPILE;
+  fa_score_mod_s* s = new fa_score_mod_s;
+  s->source = source;
+  *out = s;
+  return FA_OK;
+}
+
+fa_status custom_destroy(fa_score_mod mod) {
+  if (!mod) return FA_ERR_INVALID_ARGUMENT;
+  for (auto& kv : mod->cache) hipModuleUnload(kv.second.module);
+  delete mod;
+  return FA_OK;
+}
+
+fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causal, bool mask, bool blk,
+                        const AttnArgs& a, unsigned grid, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  const auto key = std::make_tuple(dev, dtype, D, (int)causal, (int)mask, (int)blk);
+  hipFunction_t fn;
+  {
+    std::lock_guard<std::mutex> lock(mod->mu);
+    auto it = mod->cache.find(key);
+    if (it == mod->cache.end()) {
+      std::string log;
+      const std::vector<char> code = rtc_compile(rtc_unit(mod->source, dtype, D, causal, mask, blk), device_arch(dev), &log);
+      if (code.empty()) return FA_ERR_COMPILE;
+      fa_score_mod_s::Loaded l;
+      if (hipModuleLoadData(&l.module, code.data()) != hipSuccess) return FA_ERR_HIP;
+      for (int i = 0; i < 3; ++i) {
+        if (hipModuleGetFunction(&l.fn[i], l.module, kKernelNames[i]) != hipSuccess) {
+          hipModuleUnload(l.module);
+          return FA_ERR_HIP;
+        }
+      }
+      it = mod->cache.emplace(key, l).first;
+    }
+    fn = it->second.fn[pass];
+  }
+  AttnArgs args = a;
+  void* params[] = {&args};
+  if (hipModuleLaunchKernel(fn, grid, 1, 1, 256, 1, 1, 0, st, params, nullptr) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // namespace fa
