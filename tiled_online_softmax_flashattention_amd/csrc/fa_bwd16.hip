@@ -128,6 +128,11 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, i
 
 // ------------------------------------------------------------ shared helpers
 
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 template <class T>
 __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
   return u32x4{pack2<T>(x[8 * u + 0], x[8 * u + 1]), pack2<T>(x[8 * u + 2], x[8 * u + 3]),
@@ -267,20 +272,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     if constexpr (DQA) lds_write16(sDS + tile_off<64, SW_BOTH>(32 * wave + l32, 32 * mt + 16 * u + 8 * hi), db);
   };
 
-  // Queries 32mt .. 32mt+31 of tile it.
-  auto half = [&](int it, int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD) __attribute__((always_inline)) {
-    const int qs = it * BQ + 32 * mt;   // first query of the half
-    // every query precedes every key of this wave: nothing to add (in the
-    // atomic dQ mode the half still runs, masked to P = 0, so its dS^T rows
-    // of the LDS tile are zeros; such halves occur only in a key block's
-    // first query tile)
-    if (!DQA && CAUSAL && qs + off + 31 < kw) return;
-
-    // S' = Q K^T - lse2 / c and dP' = dO V^T - delta, queries as rows: the
-    // accumulators start from the rows' stored values
+  // Queries 32mt .. 32mt+31 of tile it, in two steps: the score products,
+  // then the probabilities, dS and the dV, dK products.
+  // every query precedes every key of this wave: nothing to add (in the
+  // atomic dQ mode the half still runs, masked to P = 0, so its dS^T rows
+  // of the LDS tile are zeros; such halves occur only in a key block's
+  // first query tile)
+  auto half_runs = [&](int it, int mt) __attribute__((always_inline)) {
+    return DQA || !CAUSAL || it * BQ + 32 * mt + off + 31 >= kw;
+  };
+  // S' = Q K^T - lse2 / c and dP' = dO V^T - delta, queries as rows: the
+  // accumulators start from the rows' stored values
+  auto scores = [&](int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, f32x16& sv,
+                    f32x16& dpv) __attribute__((always_inline)) {
     const float* lrow = sL + 32 * mt + 4 * hi;
     const float* drow = sD + 32 * mt + 4 * hi;
-    f32x16 sv, dpv;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
@@ -291,16 +297,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
         dpv[4 * u + cc] = d4[cc];
       }
     }
-    {
-      const int qr = 32 * mt + l32;
+    const int qr = 32 * mt + l32;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int off = tile_off<D, SW_BOTH>(qr, 16 * kk + 8 * hi);
-        sv = mma16<T>(lds_read16(sQ + off), kf[kk], sv);
-        dpv = mma16<T>(lds_read16(sO + off), vf[kk], dpv);
-      }
+    for (int kk = 0; kk < KS; ++kk) {
+      const int off = tile_off<D, SW_BOTH>(qr, 16 * kk + 8 * hi);
+      sv = mma16<T>(lds_read16(sQ + off), kf[kk], sv);
+      dpv = mma16<T>(lds_read16(sO + off), vf[kk], dpv);
     }
-    // P = 0 for queries before the key (causal) and past seq_q, only on such halves
+  };
+  // P = 0 for queries before the key (causal) and past seq_q, only on such halves
+  auto mask_scores = [&](int it, int mt, f32x16& sv) __attribute__((always_inline)) {
+    const int qs = it * BQ + 32 * mt;   // first query of the half
     if (__builtin_amdgcn_ballot_w64((CAUSAL && qs + off < kj) || qs + 31 >= Sq) != 0) {
       const int ql = qs + 4 * hi;   // query of register r: ql + 8 (r / 4) + r % 4
 #pragma unroll
@@ -309,6 +316,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
         if ((CAUSAL && q + off < kj) || q >= Sq) sv[r] = kNegInf;
       }
     }
+  };
+  // P and dS = P (dP - delta), rounded and packed as MFMA B operands
+  auto probs = [&](int it, f32x16& sv, f32x16& dpv, u32x4* pb, u32x4* db) __attribute__((always_inline)) {
     float lb = key_ok ? 0.f : kNegInf;
     if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ - off) : kNegInf;
     const float lb0 = lb + cb0, lb1 = lb + cb1;
@@ -318,20 +328,45 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       sv[r] = p;
       dpv[r] *= p;
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pb[u] = pack8<T>(sv, u);
+      db[u] = pack8<T>(dpv, u);
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+  auto products = [&](int mt, const u32x4* pb, const u32x4* db, const uint16_t* sQ, const uint16_t* sO)
+                      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int p0 = 32 * mt + 16 * u;
-      const u32x4 pb = pack8<T>(sv, u);
-      const u32x4 db = pack8<T>(dpv, u);
-      put_ds(mt, u, db);
+      put_ds(mt, u, db[u]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dv[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sO, p0, 32 * dt, lane), pb, dv[dt]);
-        dk[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sQ, p0, 32 * dt, lane), db, dk[dt]);
+        dv[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sO, p0, 32 * dt, lane), pb[u], dv[dt]);
+        dk[dt] = mma16<T>(read_a_tr_tile<D, SW_BOTH>(sQ, p0, 32 * dt, lane), db[u], dk[dt]);
       }
     }
   };
+  auto finish = [&](int it, int mt, f32x16& sv, f32x16& dpv, const uint16_t* sQ, const uint16_t* sO)
+                    __attribute__((always_inline)) {
+    mask_scores(it, mt, sv);
+    u32x4 pb[2], db[2];
+    probs(it, sv, dpv, pb, db);
+    products(mt, pb, db, sQ, sO);
+  };
+  auto half = [&](int it, int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD) __attribute__((always_inline)) {
+    if (!half_runs(it, mt)) return;
+    f32x16 sv, dpv;
+    scores(mt, sQ, sO, sL, sD, sv, dpv);
+    finish(it, mt, sv, dpv, sQ, sO);
+  };
+  // head_dim 128 runs one wave per SIMD, so no other wave fills the matrix
+  // cores while a wave works through its exponentials: both halves' score
+  // products are issued first, and the first half's probabilities are
+  // computed while the second half's products run (and its dV, dK products
+  // while the second half's probabilities are computed).
+  constexpr bool PAIRED = D == 128 && !DQA;
 
   // Atomic dQ mode, after every wave has stored its dS^T of query tile it:
   // dQ_tile += dS K over the workgroup's 128 keys, as (64 queries x D) / 4
@@ -389,9 +424,47 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
     const int it = it_of(n);
-    half(it, 0, sQ, sO, sL, sD);
-    __builtin_amdgcn_sched_barrier(0);   // the halves share registers
-    half(it, 1, sQ, sO, sL, sD);
+    if (PAIRED && half_runs(it, 0) && half_runs(it, 1)) {
+      // In-order issue: the second half's score products and the first
+      // half's probabilities share one straight-line region, scheduled as
+      // MFMA / VALU alternation, and likewise the first half's dV, dK
+      // products and the second half's probabilities.
+      f32x16 sv0, dp0, sv1, dp1;
+      u32x4 pb0[2], db0[2], pb1[2], db1[2];
+      scores(0, sQ, sO, sL, sD, sv0, dp0);
+      mask_scores(it, 0, sv0);
+      __builtin_amdgcn_sched_barrier(0);
+      scores(1, sQ, sO, sL, sD, sv1, dp1);
+      probs(it, sv0, dp0, pb0, db0);
+      // 8 row reads and 2 KS fragment reads feed 2 KS MFMAs: the first 12
+      // reads up front, then one read ahead of each MFMA
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mask_scores(it, 1, sv1);
+      __builtin_amdgcn_sched_barrier(0);
+      products(0, pb0, db0, sQ, sO);
+      probs(it, sv1, dp1, pb1, db1);
+      // 2 transposing reads per MFMA: 8 up front, then 2 ahead of each MFMA
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * DT; ++i) {
+        if (i < 4 * DT - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      products(1, pb1, db1, sQ, sO);
+    } else {
+      half(it, 0, sQ, sO, sL, sD);
+      __builtin_amdgcn_sched_barrier(0);   // the halves share registers
+      half(it, 1, sQ, sO, sL, sD);
+    }
     if constexpr (DQA) {
       barrier_lds_loads_in_flight();   // every wave's dS^T of tile n is in sDS; tile n+1's loads stay in flight
       dq_tile(it);
@@ -566,13 +639,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     }
   };
 
-  // Keys 32t .. 32t+31 of tile n.
-  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
-    const int k0 = kv_of(n) + 32 * t;   // first key of the half
-    if (CAUSAL && k0 > qwp + 31) return;
-
-    // S'^T = K Q^T + C and dP'^T = V dO^T - delta, keys as rows
-    f32x16 s = cinit, dp = dneg;
+  // Keys 32t .. 32t+31 of tile n, in two steps: the score products, then the
+  // probabilities, dS and the dQ products.
+  auto half_runs = [&](int n, int t) __attribute__((always_inline)) {
+    return !CAUSAL || kv_of(n) + 32 * t <= qwp + 31;
+  };
+  // S'^T = K Q^T + C and dP'^T = V dO^T - delta, keys as rows
+  auto scores = [&](int t, const uint16_t* sK, const uint16_t* sV, const float* sB, f32x16& s, f32x16& dp)
+                    __attribute__((always_inline)) {
+    s = cinit;
+    dp = dneg;
     if constexpr (MASK) {   // the row starts the accumulator (cinit is nonzero only for ALiBi)
       const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
 #pragma unroll
@@ -582,25 +658,25 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
         for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] = MOD == MOD_ALIBI ? cinit[4 * u + cc] + m4[cc] : m4[cc];
       }
     }
-    {
-      // every K and V fragment is requested before the first MFMA
-      const int kr = 32 * t + l32;
-      u32x4 kfr[KS], vfr[KS];
+    // every K and V fragment is requested before the first MFMA
+    const int kr = 32 * t + l32;
+    u32x4 kfr[KS], vfr[KS];
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int off = tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi);
-        kfr[kk] = lds_read16(sK + off);
-        vfr[kk] = lds_read16(sV + off);
-      }
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        s = mma16<T>(kfr[kk], qf[kk], s);
-        dp = mma16<T>(vfr[kk], of[kk], dp);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // MFMAs
+    for (int kk = 0; kk < KS; ++kk) {
+      const int off = tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi);
+      kfr[kk] = lds_read16(sK + off);
+      vfr[kk] = lds_read16(sV + off);
     }
-
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      s = mma16<T>(kfr[kk], qf[kk], s);
+      dp = mma16<T>(vfr[kk], of[kk], dp);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);   // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);   // MFMAs
+  };
+  auto finish = [&](int n, int t, f32x16& s, f32x16& dp, const uint16_t* sK) __attribute__((always_inline)) {
+    const int k0 = kv_of(n) + 32 * t;   // first key of the half
     // scores past the diagonal or past seq_kv: -inf (only on such halves)
     {
       int lim = 1 << 30;
@@ -637,6 +713,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       for (int dt = 0; dt < DT; ++dt) dq[dt] = mma16<T>(kt[u][dt], db, dq[dt]);
     }
   };
+  auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
+    if (!half_runs(n, t)) return;
+    f32x16 s, dp;
+    scores(t, sK, sV, sB, s, dp);
+    finish(n, t, s, dp, sK);
+  };
+  // head_dim 128 runs one wave per SIMD: both halves' score products first,
+  // so the second half's products run while the first half's probabilities
+  // are computed (as in the key/value pass).
+  constexpr bool PAIRED = D == 128;
 
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB, uint16_t* sKn, uint16_t* sVn,
                   float* sBn) __attribute__((always_inline)) {
@@ -648,9 +734,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       store_m(sBn);
       load_m(kv_of(min(n + 2, ntiles - 1)));
     }
-    half(n, 0, sK, sV, sB);
-    __builtin_amdgcn_sched_barrier(0);   // the halves share registers
-    half(n, 1, sK, sV, sB);
+    if constexpr (PAIRED) {
+      const bool r0 = half_runs(n, 0), r1 = half_runs(n, 1);
+      f32x16 s0, dp0, s1, dp1;
+      if (r0) scores(0, sK, sV, sB, s0, dp0);
+      if (r1) scores(1, sK, sV, sB, s1, dp1);
+      if (r0) finish(n, 0, s0, dp0, sK);
+      if (r1) finish(n, 1, s1, dp1, sK);
+    } else {
+      half(n, 0, sK, sV, sB);
+      __builtin_amdgcn_sched_barrier(0);   // the halves share registers
+      half(n, 1, sK, sV, sB);
+    }
   };
 
   if (!BLK || ntiles > 0) {   // without a block mask there is always a tile
