@@ -396,7 +396,7 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
         ws = torch.empty(fa.decode_workspace_bytes(fa.problem(q, kvs[0][0], **kw)), dtype=torch.uint8, device="cuda")
         split = [fa.plan_decode(q, k, v, out, lse, ws, **kw) for k, v in kvs]
-        plain = [fa.plan_forward(q, k, v, out, lse, **kw) for k, v in kvs]
+        plain = [fa.plan_forward(q, k, v, out, lse, kv_splits=1, **kw) for k, v in kvs]
         for f in split + plain:
             f()
         settle(lambda i: split[i % 2](), 0.2, torch)
@@ -409,6 +409,33 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
             "forward_unsplit_us": round(ms_p * 1e3, 2), "bytes": nbytes}
         del q, kvs, out, lse, ws, split, plain
         torch.cuda.empty_cache()
+
+    # One long head: fp16 (1, 1, 32768, 128), causal, ALiBi.  Its 256 query
+    # blocks alone leave the device idle (the last, longest ones finish
+    # alone); forward() splits the key axis by the library's per-shape table
+    # (fa_forward_split), timed against the unsplit fa_forward.
+    B, H, S, D = 1, 1, 32768, 128
+    log(f"[bench] extra: long single head {B}x{H}x{S}x{D} f16 causal ALiBi, split vs unsplit forward")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    q, k, v = (torch.randn(B, H, S, D, device="cuda", dtype=torch.float16, generator=gen) for _ in range(3))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    kw = dict(causal=True, score_mod="alibi")
+    chunks = fa.forward_split_workspace_bytes(fa.problem(q, k, **kw)) // (B * H * S * (D + 2) * 4)
+    run_split = fa.plan_forward(q, k, v, out, lse, **kw)
+    run_whole = fa.plan_forward(q, k, v, out, lse, kv_splits=1, **kw)
+    run_split(); run_whole()
+    settle(lambda i: run_split(), 0.2, torch)
+    ms_s = time_calls(lambda i: run_split(), reps, torch)
+    ms_w = time_calls(lambda i: run_whole(), reps, torch)
+    flop = 4.0 * D * B * H * S * (S + 1) / 2
+    res[f"long single head f16 causal ALiBi ({B},{H},{S},{D}), forward split over keys"] = {
+        "key_chunks": int(chunks), "split_ms": round(ms_s, 4), "split_TFLOP/s": round(flop / ms_s / 1e9, 1),
+        "split_frac_peak": round(flop / ms_s / 1e9 / PEAK_F16_TFLOPS, 4),
+        "unsplit_ms": round(ms_w, 4), "unsplit_TFLOP/s": round(flop / ms_w / 1e9, 1),
+        "flop_convention": "causal pairs"}
+    del q, k, v, out, lse, run_split, run_whole
+    torch.cuda.empty_cache()
 
     # Block sparsity: fp16 (8, 8, 8192, 64), causal, ALiBi, with a block mask
     # of a sliding window of 8 blocks (1024 keys).  Flops count only the pairs

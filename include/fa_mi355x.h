@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 /* Edge of the blocks of a block mask (query rows and keys), and the longest
  * seq_q / seq_kv a call with a block mask takes. */
@@ -105,7 +105,7 @@ typedef struct fa_score_mod_s* fa_score_mod;
 /* dQ formation of the backward (fa_problem.dq_mode). */
 typedef enum { FA_DQ_AUTO = 0, FA_DQ_SEPARATE = 1, FA_DQ_ATOMIC = 2 } fa_dq_mode;
 
-/* Most key chunks fa_decode splits into (fa_problem.kv_splits). */
+/* Most key chunks fa_decode and fa_forward_split split into (fa_problem.kv_splits). */
 #define FA_MAX_KV_SPLITS 256
 
 typedef struct {
@@ -138,9 +138,10 @@ typedef struct {
    *   below 2^28 (else FA_ERR_UNSUPPORTED).
    * A call that skips the query or the key/value pass ignores the mode. */
   int32_t dq_mode;
-  /* fa_decode: 0 = the library's split of the key axis; n > 0 = about n key
-   * chunks (1 <= n <= FA_MAX_KV_SPLITS; a 16-bit query block rounds chunks up
-   * to whole 64-key tiles).  The results do not depend on it beyond rounding. */
+  /* fa_decode and fa_forward_split: 0 = the library's split of the key axis;
+   * n > 0 = about n key chunks (1 <= n <= FA_MAX_KV_SPLITS; query blocks of
+   * more than one row round chunks up to whole 64-key tiles).  The results do
+   * not depend on it beyond rounding.  Other calls ignore it. */
   int32_t kv_splits;
   /* FA_MOD_CUSTOM: the compiled score_mod and its parameter array (device
    * floats handed to the caller's functions as `params`, or NULL). */
@@ -160,6 +161,30 @@ typedef struct {
  * backward needs lse. */
 fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const void* v,
                      void* out, float* lse, void* stream);
+
+/* Bytes of device workspace fa_forward_split needs for problem p (written to
+ * *bytes); 0 when the call runs unsplit. */
+fa_status fa_forward_split_workspace_size(const fa_problem* p, size_t* bytes);
+
+/* Forward with the key axis split into chunks, for shapes whose query blocks
+ * alone do not fill the device (few (batch, head) slices of long sequences;
+ * with causal the last query blocks are the longest and would finish alone).
+ * Every (query block, key chunk) pair is a workgroup that runs the forward's
+ * online-softmax loop over its chunk and stores the unnormalised partial
+ * (running max, sum, accumulator) of each row in the workspace; a second
+ * kernel merges a row's partials exactly, rescaling each to the common max
+ * as the loop itself does from tile to tile (attnax pallas_flash_attention
+ * page, kernel body).  The flaxattention page's TODO list asks for default
+ * configurations per input shape: with p->kv_splits == 0 the library's
+ * per-shape table picks the chunk count, and where it keeps the forward
+ * whole (enough query blocks, or too few keys per chunk to pay for the merge)
+ * the call is exactly fa_forward.  Same outputs as fa_forward up to rounding.
+ * The workspace (>= fa_forward_split_workspace_size bytes, 256-byte aligned)
+ * is scratch; it may be NULL when that size is 0.  Not split: head_dim 512
+ * and FA_MOD_CUSTOM (kv_splits > 1 gives FA_ERR_UNSUPPORTED for them). */
+fa_status fa_forward_split(const fa_problem* p, const void* q, const void* k, const void* v,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Bytes of device workspace fa_backward needs for problem p (written to *bytes). */
 fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes);

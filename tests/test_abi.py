@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 6
+    assert lib.fa_abi_version() == _lib.FA_ABI_VERSION == 7
     for s in range(7):
         assert lib.fa_status_string(s)
     assert lib.fa_status_string(99) == b"unknown status"
@@ -341,6 +341,52 @@ def test_dq_mode_and_kv_splits_rules():
     n1 = n.value
     assert lib.fa_decode_workspace_size(ctypes.byref(seven), ctypes.byref(n)) == _lib.FA_OK
     assert n.value >= 7 * 2 * 4 * (64 + 2) * 4 and n1 >= 2 * 4 * (64 + 2) * 4 and n.value > n1
+
+
+def test_forward_split_table_and_rules():
+    """fa_forward_split: the per-shape table keeps the forward whole where its
+    query blocks fill the device (every workload shape) or where chunks would
+    be short, and splits few long sequences; an explicit kv_splits sets the
+    chunk count; every error is returned before any HIP call."""
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+
+    def ws(p):
+        assert lib.fa_forward_split_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.FA_OK
+        return n.value
+
+    f16, bf16, f32 = _lib.FA_F16, _lib.FA_BF16, _lib.FA_F32
+    assert ws(prob(batch=8, heads=8, seq_q=2048, seq_kv=2048, causal=1, mod_kind=1)) == 0      # prefill
+    assert ws(prob(batch=4, heads=16, seq_q=4096, seq_kv=4096, head_dim=128, dtype=bf16)) == 0
+    assert ws(prob(batch=1, heads=2, seq_q=256, seq_kv=256, dtype=f32)) == 0
+    assert ws(prob(batch=1, heads=1, seq_q=131072, seq_kv=131072, head_dim=512, dtype=f32, causal=1)) == 0
+    assert ws(prob(batch=1, heads=1, seq_q=1000, seq_kv=1000, causal=1)) == 0                 # short chunks
+    long_row = 1 * 2 * 16384 * (128 + 2) * 4                                                   # one chunk's partials
+    big = ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1))
+    assert big >= 2 * long_row and big % 256 == 0
+    assert ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1, kv_splits=1)) == 0
+    assert ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1, kv_splits=4)) == \
+        4 * long_row
+    # chunks are whole 64-key tiles: 5 chunks of 80 keys become 128-key chunks, 4 in all
+    assert ws(prob(seq_q=100, seq_kv=400, kv_splits=5)) == 2 * 4 * 100 * 4 * (64 + 2) * 4
+    assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(head_dim=512, dtype=f32, kv_splits=4)),
+                                               ctypes.byref(n)) == UNSUP
+    assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10],
+                                                                 kv_splits=4)), ctypes.byref(n)) == UNSUP
+    assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(kv_splits=-1)), ctypes.byref(n)) == INVALID
+    assert lib.fa_forward_split_workspace_size(ctypes.byref(prob()), None) == INVALID
+
+    def fs(p, ws_ptr=A[11], ws_bytes=1 << 30, q=A[0]):
+        return lib.fa_forward_split(ctypes.byref(p), q, A[1], A[2], A[3], A[4], ws_ptr, ws_bytes, None)
+
+    split = prob(seq_q=100, seq_kv=400, kv_splits=4)
+    need = ws(split)
+    assert fs(split, ws_bytes=need - 1) == WS
+    assert fs(split, ws_ptr=None) == INVALID
+    assert fs(split, ws_ptr=ctypes.c_void_p(0x10010)) == INVALID     # not 256-byte aligned
+    assert fs(split, q=None) == INVALID
+    assert fs(prob(seq_q=100, seq_kv=400, kv_splits=4, scale=0.0)) == UNSUP
+    assert fs(prob(head_dim=512, dtype=f32, kv_splits=4)) == UNSUP
 
 
 def test_score_mod_create_compiles_and_reports_errors():

@@ -28,7 +28,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["forward", "backward", "decode", "decode_noalloc", "ScoreMod", "backward_workspace_bytes", "decode_workspace_bytes",
+__all__ = ["forward", "backward", "decode", "decode_noalloc", "ScoreMod", "forward_split_workspace_bytes",
+           "backward_workspace_bytes", "decode_workspace_bytes",
            "FaError", "problem", "plan_forward", "plan_backward", "plan_decode", "block_mask_shape"]
 
 _DTYPE = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
@@ -105,7 +106,8 @@ def problem(q: torch.Tensor, k: torch.Tensor, *, causal: bool = False,
     position of query row 0 among the keys (0 for self-attention; the number
     of cached keys before the first query with a KV cache).  dq_mode ("auto",
     "separate" or "atomic") picks how the backward forms dQ; kv_splits (0 =
-    the library's choice) the number of key chunks of a decode."""
+    the library's choice) the number of key chunks of fa_decode and
+    fa_forward_split."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be (batch, heads, seq, head_dim)")
     if block_mask is not None:
@@ -198,20 +200,40 @@ def _mask_u8(key_mask):
     return key_mask.to(torch.uint8).contiguous() if key_mask.dtype != torch.uint8 else key_mask.contiguous()
 
 
+def forward_split_workspace_bytes(p: _lib.FaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().fa_forward_split_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+               "fa_forward_split_workspace_size")
+    return int(n.value)
+
+
 def forward(q, k, v, *, causal=False, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-            checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None, mod_params=None):
-    """Attention output (q's dtype) and log-sum-exp (float32, natural log)."""
+            checker=(0.5, -0.5), q_offset=0, block_mask=None, out=None, lse=None, mod_params=None, kv_splits=0,
+            workspace=None):
+    """Attention output (q's dtype) and log-sum-exp (float32, natural log).
+
+    kv_splits: 0 = the library's per-shape choice (fa_forward_split: the key
+    axis is split and merged where the query blocks alone leave the device
+    idle), 1 = never split (fa_forward), n > 1 = about n key chunks."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
-    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
-    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, mod_params)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              workspace=workspace)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, mod_params, workspace)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                mod_params=mod_params)
+                mod_params=mod_params, kv_splits=kv_splits)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     lib = _lib.load()
-    _lib.check(lib.fa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q)),
-               "fa_forward")
+    need = 0 if kv_splits == 1 else forward_split_workspace_bytes(p)
+    if need == 0:
+        _lib.check(lib.fa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q)),
+                   "fa_forward")
+        return out, lse
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _lib.check(lib.fa_forward_split(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), workspace.numel(), _stream(q)), "fa_forward_split")
     return out, lse
 
 
@@ -319,17 +341,28 @@ def _plan(fn, name, args, keep):
 
 
 def plan_forward(q, k, v, out, lse, *, causal=False, key_mask=None, score_mod=None, scale=None,
-                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, mod_params=None):
+                 alibi_slopes=None, checker=(0.5, -0.5), q_offset=0, block_mask=None, mod_params=None,
+                 kv_splits=0, workspace=None):
+    """kv_splits as in forward(); a split plan allocates its workspace now
+    unless one is passed."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
-    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
-    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask, mod_params)
+    _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
+              workspace=workspace)
+    _check_tensors(q, k, v, out, lse, key_mask, alibi_slopes, block_mask, mod_params, workspace)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                mod_params=mod_params)
+                mod_params=mod_params, kv_splits=kv_splits)
     lib = _lib.load()
-    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
-    return _plan(lib.fa_forward, "fa_forward", args,
-                 (p, q, k, v, out, lse, key_mask, alibi_slopes, block_mask, score_mod, mod_params))
+    keep = (p, q, k, v, out, lse, key_mask, alibi_slopes, block_mask, score_mod, mod_params)
+    need = 0 if kv_splits == 1 else forward_split_workspace_bytes(p)
+    if need == 0:
+        args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q))
+        return _plan(lib.fa_forward, "fa_forward", args, keep)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+            _stream(q))
+    return _plan(lib.fa_forward_split, "fa_forward_split", args, keep + (workspace,))
 
 
 def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=False, key_mask=None,

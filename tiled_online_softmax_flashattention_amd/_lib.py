@@ -35,7 +35,7 @@ class FaProblem(ctypes.Structure):
         ("custom_mod", _c_void_p), ("mod_params", _c_void_p),
     ]
 
-FA_ABI_VERSION = 6
+FA_ABI_VERSION = 7
 FA_BLOCK_MASK_BLOCK = 128
 FA_BLOCK_MASK_MAX_SEQ = 131072
 FA_DECODE_SCRATCH_BYTES = 16 << 20
@@ -44,6 +44,8 @@ FA_DECODE_SCRATCH_BYTES = 16 << 20
 _P = ctypes.POINTER(FaProblem)
 SIGNATURES = {
     "fa_forward": (ctypes.c_int, [_P, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "fa_forward_split_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
+    "fa_forward_split": (ctypes.c_int, [_P] + [_c_void_p] * 6 + [ctypes.c_size_t, _c_void_p]),
     "fa_backward_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_backward": (ctypes.c_int, [_P] + [_c_void_p] * 10 + [ctypes.c_size_t, _c_void_p]),
     "fa_decode_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),

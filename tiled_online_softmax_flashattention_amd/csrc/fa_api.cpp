@@ -175,6 +175,91 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
                   256);
 }
 
+// Workgroups of the forward resident on the device at once (256 CUs times
+// the workgroups per CU that the kernel's registers allow).
+int64_t forward_slots(const fa_problem* p) {
+  if (p->dtype == FA_F32) return 256;
+  return p->head_dim == 64 ? 3 * 256 : 2 * 256;
+}
+
+// Per-shape table of fa_forward_split (kv_splits = 0): how many key chunks,
+// from sweeps of the chunk count on MI355X over 16-bit and fp32 shapes with
+// 64 .. 1024 query blocks and 4096 .. 32768 keys.  R is the ratio of the
+// device's workgroup slots to the query blocks (with causal twice that: a
+// causal block averages half the keys), i.e. about how many times the
+// longest block's work exceeds one slot's fair share.
+//  * 16-bit, causal, R >= 4: R - 1 chunks.  The non-empty (block, chunk)
+//    pairs, about blocks (n + 1) / 2, then just fit in the slots and start
+//    together; one more chunk starts the last full chunks in a second round
+//    (1 x 1 x 32768 x 128: 421 us at 3 chunks, 588 at 4, 700 unsplit).
+//  * 16-bit, causal, 2 <= R < 4, long sequences (>= 16384 keys at head_dim
+//    128, >= 8192 at 64): 5 chunks, fine grains over several rounds
+//    (1 x 4 x 16384 x 128: 351 us vs 404 unsplit); shorter sequences stay
+//    whole (2 x 8 x 4096 x 128: 110 us unsplit, 117 at 2 chunks).
+//  * 16-bit, not causal: R chunks when R >= 2 (1 x 2 x 8192 x 128: 90 us at
+//    4 chunks vs 169 unsplit).
+//  * fp32 (one workgroup per CU, 4x the time per key): 2R chunks with causal,
+//    R without, when R >= 2 (1 x 1 x 8192 x 64 causal: 128 us at 16 chunks
+//    vs 816 unsplit).
+//  * Chunks of at least kMinSplitChunk keys (fp32: a quarter), so that the
+//    partials' write and merge stay small against the chunk's arithmetic.
+// Everything else (R < 2: the query blocks already fill the device, e.g.
+// 8 x 8 x 2048 x 64, where 2 chunks cost 83 us against 54) stays whole, and
+// so do sequences shorter than the sweeps went (kMinSplitKeys).
+constexpr int kMinSplitChunk = 512;
+constexpr int kMinSplitKeys = 4096;
+
+int forward_choose_split(const fa_problem* p, int len) {
+  if (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128 || len < kMinSplitKeys) return 1;
+  const int64_t blocks = p->batch * p->heads * ceil_div(p->seq_q, block_q_fwd(p));
+  const int64_t R = (p->causal ? 2 : 1) * forward_slots(p) / blocks;
+  if (R < 2) return 1;
+  int64_t n;
+  if (p->dtype == FA_F32) n = p->causal ? 2 * R : R;
+  else if (!p->causal) n = R;
+  else if (R >= 4) n = R - 1;
+  else n = len >= (p->head_dim == 128 ? 16384 : 8192) ? 5 : 1;
+  const int64_t most = len / (p->dtype == FA_F32 ? kMinSplitChunk / 4 : kMinSplitChunk);
+  if (n > most) n = most;
+  if (n > FA_MAX_KV_SPLITS) n = FA_MAX_KV_SPLITS;
+  return n < 2 ? 1 : (int)n;
+}
+
+// Key split of fa_forward_split and its workspace bytes: one (D + 2)-float
+// partial per query row and chunk; 0 bytes when the forward stays whole.
+size_t forward_split_ws(const fa_problem* p, int* n_split, int* chunk) {
+  const int len = decode_kv_len(p);   // keys the last query row sees
+  const int n = p->kv_splits > 0 ? p->kv_splits : forward_choose_split(p, len);
+  int c = (len + n - 1) / n;
+  c = (c + 63) / 64 * 64;   // whole 64-key tiles
+  *chunk = c;
+  *n_split = (len + c - 1) / c;
+  if (*n_split <= 1) return 0;
+  return round_up((size_t)(p->batch * p->heads) * (size_t)p->seq_q * (size_t)(*n_split) *
+                      (size_t)(p->head_dim + 2) * sizeof(float),
+                  256);
+}
+
+// The forward over key chunks, then the merge of each row's partials, on a
+// validated problem with `ws` holding n_split partials per row (many_rows:
+// the forward's merge with several rows per workgroup; else the decode's).
+hipError_t split_forward_launch(const fa_problem* p, fa::AttnArgs a, int n_split, int chunk, void* ws,
+                                hipStream_t st, bool many_rows) {
+  const int D = (int)p->head_dim;
+  const bool mask = p->key_mask != nullptr, causal = p->causal != 0;
+  a.partial = (float*)ws;
+  a.n_split = n_split;
+  a.chunk = chunk;
+  a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
+  hipError_t err;
+  if (p->dtype == FA_F32) err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true);
+  else err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
+  if (err != hipSuccess) return err;
+  const int rows = (int)(p->batch * p->heads * p->seq_q);
+  return many_rows ? fa::launch_split_merge(a, p->dtype, D, rows, st)
+                   : fa::launch_decode_merge(a, p->dtype, D, rows, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,6 +290,40 @@ fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const vo
   else
     err = fa::launch_fwd16(a, p->dtype == FA_BF16, (int)p->head_dim, p->mod_kind, p->causal != 0,
                            p->key_mask != nullptr, st);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_forward_split_workspace_size(const fa_problem* p, size_t* bytes) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (!bytes) return FA_ERR_INVALID_ARGUMENT;
+  if (p->kv_splits > 1 && (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128)) return FA_ERR_UNSUPPORTED;
+  int n_split, chunk;
+  *bytes = forward_split_ws(p, &n_split, &chunk);
+  return FA_OK;
+}
+
+fa_status fa_forward_split(const fa_problem* p, const void* q, const void* k, const void* v, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status s = validate_problem(p);
+  if (s != FA_OK) return s;
+  if (p->kv_splits > 1 && (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128)) return FA_ERR_UNSUPPORTED;
+  int n_split, chunk;
+  const size_t need = forward_split_ws(p, &n_split, &chunk);
+  if (need == 0) return fa_forward(p, q, k, v, out, lse, stream);
+  if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return FA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  if (ceil_div(p->seq_q, block_q_fwd(p)) * p->batch * p->heads * n_split > kMaxI32) return FA_ERR_UNSUPPORTED;
+  if (p->batch * p->heads * p->seq_q > kMaxI32) return FA_ERR_UNSUPPORTED;   // merge grid
+  fa::AttnArgs a = make_args(p);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  const hipError_t err = split_forward_launch(p, a, n_split, chunk, workspace, (hipStream_t)stream, true);
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -331,16 +450,12 @@ fa_status decode_launch(const fa_problem* p, const void* q, const void* k, const
   a.chunk = chunk;
   hipStream_t st = (hipStream_t)stream;
   const int D = (int)p->head_dim;
-  const bool mask = p->key_mask != nullptr, causal = p->causal != 0;
+  const bool mask = p->key_mask != nullptr;
   hipError_t err;
   if (p->seq_q == 1) {
     err = fa::launch_decode(a, p->dtype, D, p->mod_kind, mask, st);
   } else {   // short query block: the forward split over the keys, then the merge
-    a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
-    if (p->dtype == FA_F32) err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true);
-    else err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
-    if (err == hipSuccess)
-      err = fa::launch_decode_merge(a, p->dtype, D, (int)(p->batch * p->heads * p->seq_q), st);
+    err = split_forward_launch(p, a, n_split, chunk, ws, st, false);
   }
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -386,6 +386,27 @@ __device__ __forceinline__ BlockCoord block_coord(int i, int BH, int nblk, bool 
   return BlockCoord{x + 8 * (j / nblk), j % nblk};
 }
 
+// Order of a forward split over the key axis: query blocks longest first
+// (with causal, the last blocks: their chunks are full), the chunks of one
+// block next to each other, so that the longest pieces of work start first
+// and the short ones (diagonal chunks; chunks past the diagonal, which exit at
+// once) fill in at the end.  bh is the fastest index, as in block_coord.
+// Workgroup i runs on XCD i mod 8; with chunk j of every block's group on the
+// same XCD, the XCDs holding the first chunks would get most of the causal
+// work.  So the chunk also turns with the block: the (j, k) pairs of one XCD
+// recur every g = 8 / gcd(BH * n_split, 8) blocks, and chunk
+// (j + k / g) mod n_split runs through every chunk on every XCD.
+struct SplitCoord {
+  int bh, qb, split;
+};
+__device__ __forceinline__ SplitCoord split_coord(int i, int BH, int nq, int n_split, bool causal) {
+  const int bh = i % BH, r = i / BH;
+  const int k = r / n_split, j = r - k * n_split;   // k-th longest block
+  const int m = (BH * n_split) & 7;                   // BH n_split mod 8
+  const int g = m == 0 ? 1 : (m & 1) ? 8 : (m & 3) ? 4 : 2;
+  return SplitCoord{bh, causal ? nq - 1 - k : k, (j + k / g) % n_split};
+}
+
 // Launch arguments of every attention kernel (tensors contiguous BHSD).
 struct AttnArgs {
   const void* q;

@@ -217,15 +217,22 @@ constexpr int kMaxSplit = 256;
 // a time, each chunk's (max, sum) and its own accumulator element together
 // (the max and sum addresses are the same for every thread: one broadcast),
 // so a batch of chunks costs one round of independent loads; batches merge
-// online, rescaled to the running max.  No LDS, no barrier.
+// online, rescaled to the running max.  No LDS, no barrier.  With causal a
+// row reads only the chunks that hold keys up to its position (the split
+// forward writes no partial for a chunk past its query block's last key).
 constexpr int kMergeBatch = 8;
 
 template <class T, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(const AttnArgs a) {
   const int bh = blockIdx.x;
   const int d = threadIdx.x;
-  const int ns = a.n_split;
-  const float* part = a.partial + (size_t)bh * ns * (D + 2);
+  int ns = a.n_split;
+  if (a.causal) {
+    const int qpos = bh % a.Sq + a.q_off;
+    const int kv_end = min(a.Skv, qpos + 1);
+    ns = min(ns, (kv_end + a.chunk - 1) / a.chunk);
+  }
+  const float* part = a.partial + (size_t)bh * a.n_split * (D + 2);
   float M = kNegInf, L = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch], av[kMergeBatch];
@@ -261,6 +268,77 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const AttnArgs a) {
     ((__bf16*)a.o)[(size_t)bh * D + d] = (__bf16)o;
   }
   if (d == 0 && a.lse) a.lse[bh] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+// Merge for the forward split over keys (many rows): D / 2 threads per row,
+// two dims per thread with 8-byte loads (a partial row of D + 2 floats is
+// 8-byte aligned), 256 / (D / 2) rows per workgroup; otherwise the same
+// batched online merge as decode_merge_kernel.
+template <class T, int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const AttnArgs a, int rows) {
+  constexpr int TPR = D / 2, RPW = 256 / TPR;
+  const int t = threadIdx.x % TPR;
+  const int row = blockIdx.x * RPW + threadIdx.x / TPR;
+  if (row >= rows) return;
+  int ns = a.n_split;
+  if (a.causal) {   // chunks holding keys up to the row's position
+    const int kv_end = min(a.Skv, row % a.Sq + a.q_off + 1);
+    ns = min(ns, (kv_end + a.chunk - 1) / a.chunk);
+  }
+  const float* part = a.partial + (size_t)row * a.n_split * (D + 2);
+  float M = kNegInf, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    float2 av[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool ok = s0 + j < ns;
+      const float* pj = part + (size_t)(ok ? s0 + j : s0) * (D + 2);
+      mv[j] = ok ? pj[D] : kNegInf;
+      lv[j] = ok ? pj[D + 1] : 0.f;
+      const float2 x = *(const float2*)(pj + 2 * t);
+      av[j] = ok ? x : float2{0.f, 0.f};
+    }
+    float mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) mb = fmaxf(mb, mv[j]);
+    const float mu = (mb == kNegInf) ? 0.f : mb;
+    const float sc = exp2_hw(M - mu);
+    L *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float w = exp2_hw(mv[j] - mu);
+      L += w * lv[j];
+      acc0 += w * av[j].x;
+      acc1 += w * av[j].y;
+    }
+    M = mb;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const size_t o = (size_t)row * D + 2 * t;
+  if constexpr (__is_same(T, F32)) {
+    *(float2*)((float*)a.o + o) = float2{acc0 * inv, acc1 * inv};
+  } else {
+    *(uint32_t*)((uint16_t*)a.o + o) = pack2<T>(acc0 * inv, acc1 * inv);
+  }
+  if (t == 0 && a.lse) a.lse[row] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+}
+
+template <class T>
+static hipError_t launch_split_merge_t(const AttnArgs& a, int D, int rows, hipStream_t st) {
+  const unsigned rpw = 256u / (unsigned)(D / 2);
+  const dim3 grid(((unsigned)rows + rpw - 1) / rpw);
+  if (D == 64) hipLaunchKernelGGL((split_merge_kernel<T, 64>), grid, dim3(256), 0, st, a, rows);
+  else hipLaunchKernelGGL((split_merge_kernel<T, 128>), grid, dim3(256), 0, st, a, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st) {
+  if (dtype == 0) return launch_split_merge_t<F32>(a, D, rows, st);
+  if (dtype == 2) return launch_split_merge_t<BF16>(a, D, rows, st);
+  return launch_split_merge_t<F16>(a, D, rows, st);
 }
 
 int decode_choose_split(int BH, int Skv, int* chunk) {

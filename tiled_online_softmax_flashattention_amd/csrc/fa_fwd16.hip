@@ -131,6 +131,9 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     const int ct = a.chunk / BN;
     t_lo = min(split * ct, ntiles_all);
     t_hi = min(t_lo + ct, ntiles_all);
+    // a chunk past the block's last key (causal): no row of the block reads
+    // its partial, so none is written
+    if (t_lo >= ntiles_all) return;
   }
   int ntiles = t_hi - t_lo;
   if constexpr (BLK) {
@@ -147,17 +150,26 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   };
 
   // Direct loads of tile kv0 into (sK, sV).  Rows past seq_kv are clamped to
-  // the last row (finite values whose scores are masked to -inf).  A split
-  // workgroup (a short query block) is the only reader of its key chunk, so
-  // those loads carry the non-temporal hint.
-  constexpr int CPOL = SPLIT ? kCpolNT : kCpolNone;
+  // the last row (finite values whose scores are masked to -inf).  The split
+  // workgroups of a short query block (the only query block) are the only
+  // readers of their key chunks, so those loads carry the non-temporal hint;
+  // the query blocks of a longer split sequence share each chunk through L2.
+  const bool nt = SPLIT && a.n_qblocks == 1;
   auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV) __attribute__((always_inline)) {
-    if (kv0 + BN <= Skv) {
-      load_full_tile_lds<D, BN, SW_BOTH, 4, CPOL>(Kg + (size_t)kv0 * D, sK, wave, lane);
-      load_full_tile_lds<D, BN, VSW, 4, CPOL>(Vg + (size_t)kv0 * D, sV, wave, lane);
+    if (nt) {
+      if (kv0 + BN <= Skv) {
+        load_full_tile_lds<D, BN, SW_BOTH, 4, kCpolNT>(Kg + (size_t)kv0 * D, sK, wave, lane);
+        load_full_tile_lds<D, BN, VSW, 4, kCpolNT>(Vg + (size_t)kv0 * D, sV, wave, lane);
+      } else {
+        load_tile_lds<D, BN, SW_BOTH, 4, kCpolNT>(Kg, kv0, Skv, sK, wave, lane);
+        load_tile_lds<D, BN, VSW, 4, kCpolNT>(Vg, kv0, Skv, sV, wave, lane);
+      }
+    } else if (kv0 + BN <= Skv) {
+      load_full_tile_lds<D, BN, SW_BOTH, 4, kCpolNone>(Kg + (size_t)kv0 * D, sK, wave, lane);
+      load_full_tile_lds<D, BN, VSW, 4, kCpolNone>(Vg + (size_t)kv0 * D, sV, wave, lane);
     } else {
-      load_tile_lds<D, BN, SW_BOTH, 4, CPOL>(Kg, kv0, Skv, sK, wave, lane);
-      load_tile_lds<D, BN, VSW, 4, CPOL>(Vg, kv0, Skv, sV, wave, lane);
+      load_tile_lds<D, BN, SW_BOTH, 4, kCpolNone>(Kg, kv0, Skv, sK, wave, lane);
+      load_tile_lds<D, BN, VSW, 4, kCpolNone>(Vg, kv0, Skv, sV, wave, lane);
     }
   };
   // Key-mask row: one byte per key, converted to an additive row in LDS.
@@ -388,14 +400,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_kernel(const AttnA
   fwd16_block<T, D, MOD, CAUSAL, MASK, false, BLK>(a, c.bh, CAUSAL ? a.n_qblocks - 1 - c.blk : c.blk, 0);
 }
 
-// Split over the key axis (short query blocks against a long key sequence):
-// workgroup (bh, query block, key chunk), bh = blockIdx.x mod (batch * heads).
+// Split over the key axis (short query blocks against a long key sequence,
+// and sequences whose query blocks alone leave the device idle): workgroup
+// (bh, query block, key chunk) in the order of split_coord (longest blocks
+// first, chunks rotated over the XCDs).
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_split_kernel(const AttnArgs a) {
-  const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
-  const int r = blockIdx.x / BH;
-  fwd16_block<T, D, MOD, CAUSAL, MASK, true, BLK>(a, bh, r / a.n_split, r % a.n_split);
+  const SplitCoord c = split_coord(blockIdx.x, a.B * a.H, a.n_qblocks, a.n_split, CAUSAL);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, true, BLK>(a, c.bh, c.qb, c.split);
 }
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>

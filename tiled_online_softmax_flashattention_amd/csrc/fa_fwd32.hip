@@ -56,11 +56,13 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   const int g = wave / DS, e = wave % DS;
   static_assert(!SPLIT || DS == 1, "the key split is built for head_dim <= 128");
   const int BH = a.B * a.H;
-  const int bh = blockIdx.x % BH;
+  int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH, split = 0;
   if constexpr (SPLIT) {
-    split = qb % a.n_split;
-    qb /= a.n_split;
+    const SplitCoord c = split_coord(blockIdx.x, BH, a.n_qblocks, a.n_split, CAUSAL);
+    bh = c.bh;
+    qb = c.qb;
+    split = c.split;
   } else if (CAUSAL) {
     qb = a.n_qblocks - 1 - qb;
   }
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
     const int ct = a.chunk / BN;
     t_lo = min(split * ct, ntiles_all);
     t_hi = min(t_lo + ct, ntiles_all);
+    if (t_lo >= ntiles_all) return;   // past the block's last key: no row reads this partial
   }
   int ntiles = t_hi - t_lo;
   if constexpr (BLK) {

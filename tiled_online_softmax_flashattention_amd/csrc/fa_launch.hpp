@@ -44,5 +44,8 @@ int decode_choose_split(int BH, int Skv, int* chunk);
 hipError_t launch_decode(const AttnArgs& a, int dtype, int D, int mod, bool mask, hipStream_t st);
 // Merge of `rows` partial rows (a.n_split chunks each) into O and lse rows.
 hipError_t launch_decode_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st);
+// The same merge for the forward split over keys (many rows; several rows
+// per workgroup).
+hipError_t launch_split_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st);
 
 }  // namespace fa
