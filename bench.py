@@ -437,6 +437,55 @@ def extra_workloads(fa, W, torch, reps: int) -> dict:
     del q, k, v, out, lse, run_split, run_whole
     torch.cuda.empty_cache()
 
+    # Caller-defined score_mods at the prefill shape, fp16 (8, 8, 2048, 64),
+    # causal: ALiBi written as a caller mod (slopes from mod_params) against
+    # the built-in ALiBi kernels, and a tanh soft cap (a score-dependent mod,
+    # whose backward multiplies dS by its derivative).  The first call
+    # compiles each configuration; it runs before the timed loops.
+    B, H, S, D = 8, 8, 2048, 64
+    log(f"[bench] extra: caller-defined score_mods {B}x{H}x{S}x{D} f16 causal")
+    alibi_src = """
+__device__ float fa_score_mod(float s, int b, int h, int q, int k, const float* p) { return s - p[h] * (float)(q - k); }
+__device__ float fa_score_mod_grad(float s, int b, int h, int q, int k, const float* p) { return 1.0f; }
+"""
+    softcap_src = """
+__device__ float fa_score_mod(float s, int b, int h, int q, int k, const float* p) { return p[0] * tanhf(s / p[0]); }
+__device__ float fa_score_mod_grad(float s, int b, int h, int q, int k, const float* p) {
+  const float t = tanhf(s / p[0]);
+  return 1.0f - t * t;
+}
+"""
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    q, k, v, do = (torch.randn(B, H, S, D, device="cuda", dtype=torch.float16, generator=gen) for _ in range(4))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32, device="cuda")
+    cap = torch.tensor([20.0], dtype=torch.float32, device="cuda")
+    flop_f = 4.0 * D * B * H * S * (S + 1) / 2
+    mods = {"built-in ALiBi": (None, "alibi", None), "ALiBi as a caller mod": (alibi_src, None, slopes),
+            "tanh soft cap (caller mod)": (softcap_src, None, cap)}
+    row = {}
+    for name, (src, builtin, params) in mods.items():
+        mod = fa.ScoreMod(src) if src else builtin
+        kw = dict(causal=True, score_mod=mod, mod_params=params)
+        ws = torch.empty(fa.backward_workspace_bytes(fa.problem(q, k, **kw)), dtype=torch.uint8, device="cuda")
+        run_fwd = fa.plan_forward(q, k, v, out, lse, kv_splits=1, **kw)
+        run_bwd = fa.plan_backward(q, k, v, out, lse, do, *grads, ws, **kw)
+        run_fwd(); run_bwd()
+        settle(lambda i: (run_fwd(), run_bwd()), 0.2, torch)
+        ms_f = time_calls(lambda i: run_fwd(), reps, torch)
+        ms_fb = time_calls(lambda i: (run_fwd(), run_bwd()), reps, torch)
+        row[name] = {"forward_ms": round(ms_f, 4), "forward_TFLOP/s": round(flop_f / ms_f / 1e9, 1),
+                     "fwd_bwd_ms": round(ms_fb, 4), "fwd_bwd_TFLOP/s": round(3.5 * flop_f / ms_fb / 1e9, 1)}
+        torch.cuda.synchronize()
+        del run_fwd, run_bwd, ws
+        if src:
+            mod.close()
+    res[f"caller-defined score_mods f16 causal ({B},{H},{S},{D})"] = dict(row, flop_convention="causal pairs")
+    del q, k, v, do, out, lse, grads
+    torch.cuda.empty_cache()
+
     # Block sparsity: fp16 (8, 8, 8192, 64), causal, ALiBi, with a block mask
     # of a sliding window of 8 blocks (1024 keys).  Flops count only the pairs
     # the mask and the causal rule allow.
