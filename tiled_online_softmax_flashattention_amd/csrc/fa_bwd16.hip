@@ -516,8 +516,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
-  __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN : 4];   // q parity 0 / 1
-  __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN : 4];
+  __shared__ __attribute__((aligned(16))) float sB0[MASK ? 2 * BN + 4 : 4];   // q parity 0 / 1
+  __shared__ __attribute__((aligned(16))) float sB1[MASK ? 2 * BN + 4 : 4];
   __shared__ uint16_t sList[BLK ? kBlkMaxSeq / BN : 1];   // visited key tiles (block-sparse)
   __shared__ int sCnt[4];
 
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
           e1 = (kev ? a.odd_nat : a.even_nat) * inv_scale;
         }
         sB[tid] = keep ? e0 : kNegInf;
-        sB[BN + tid] = keep ? e1 : kNegInf;
+        sB[parity_row_off<BN>() + tid] = keep ? e1 : kNegInf;
       }
     }
   };
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     s = cinit;
     dp = dneg;
     if constexpr (MASK) {   // the row starts the accumulator (cinit is nonzero only for ALiBi)
-      const float* row = sB + ((qpos & 1) ? BN : 0) + 32 * t + 4 * hi;
+      const float* row = sB + ((qpos & 1) ? parity_row_off<BN>() : 0) + 32 * t + 4 * hi;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f32x4 m4 = *(const f32x4*)(row + 8 * u);

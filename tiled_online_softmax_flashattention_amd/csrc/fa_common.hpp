@@ -386,6 +386,16 @@ __device__ __forceinline__ BlockCoord block_coord(int i, int BH, int nblk, bool 
   return BlockCoord{x + 8 * (j / nblk), j % nblk};
 }
 
+// Per-key additive rows for queries of even and odd position (key mask and
+// checkerboard) share one LDS array: the odd row starts one row plus 16 bytes
+// in, so that in a 16-byte read, whose lanes hold queries of both parities,
+// the two rows' chunks fall in different banks (one row apart they would
+// share every bank).
+template <int BN>
+__device__ __forceinline__ constexpr int parity_row_off() {
+  return BN + 4;
+}
+
 // Order of a forward split over the key axis: query blocks longest first
 // (with causal, the last blocks: their chunks are full), the chunks of one
 // block next to each other, so that the longest pieces of work start first
