@@ -95,8 +95,8 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  *                       checker_odd (the workloads use +0.5 / -0.5).
  *  FA_MOD_CUSTOM:       s_ij = mod(scale * <q_i, k_j>, b, h, pos_i, j) with the
  *                       caller's device function (fa_score_mod_create); f16
- *                       and bf16 with head_dim 64 or 128, fa_forward and
- *                       fa_backward (fa_decode returns FA_ERR_UNSUPPORTED). */
+ *                       and bf16 with head_dim 64 or 128, every entry point
+ *                       (fp32 returns FA_ERR_UNSUPPORTED). */
 typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2, FA_MOD_CUSTOM = 3 } fa_mod_kind;
 
 /* A caller-defined score_mod compiled for the device (fa_score_mod_create). */
@@ -180,8 +180,9 @@ fa_status fa_forward_split_workspace_size(const fa_problem* p, size_t* bytes);
  * whole (enough query blocks, or too few keys per chunk to pay for the merge)
  * the call is exactly fa_forward.  Same outputs as fa_forward up to rounding.
  * The workspace (>= fa_forward_split_workspace_size bytes, 256-byte aligned)
- * is scratch; it may be NULL when that size is 0.  Not split: head_dim 512
- * and FA_MOD_CUSTOM (kv_splits > 1 gives FA_ERR_UNSUPPORTED for them). */
+ * is scratch; it may be NULL when that size is 0.  head_dim 512 is never
+ * split (kv_splits > 1 gives FA_ERR_UNSUPPORTED); with FA_MOD_CUSTOM the
+ * table keeps the forward whole and an explicit kv_splits > 1 splits it. */
 fa_status fa_forward_split(const fa_problem* p, const void* q, const void* k, const void* v,
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                            void* stream);
@@ -217,9 +218,10 @@ fa_status fa_decode_workspace_size(const fa_problem* p, size_t* bytes);
  * against seq_kv keys, split over the key axis into chunks whose partial
  * (max, sum, accumulator) are merged exactly.  The flaxattention page
  * (decoding benchmark and TODO list) singles this case out.  seq_q == 1 runs a
- * streaming kernel (one group of lanes per key); seq_q > 1 runs the forward
- * kernel of the dtype on each key chunk.  f16, bf16 and f32 with head_dim 64
- * or 128.  Same outputs as fa_forward. */
+ * streaming kernel (one group of lanes per key); seq_q > 1, and any seq_q
+ * with FA_MOD_CUSTOM, runs the forward kernel of the dtype (or of the
+ * caller's mod) on each key chunk, whose chunks are then whole 64-key tiles.
+ * f16, bf16 and f32 with head_dim 64 or 128.  Same outputs as fa_forward. */
 fa_status fa_decode(const fa_problem* p, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);

@@ -371,8 +371,11 @@ def test_forward_split_table_and_rules():
     assert ws(prob(seq_q=100, seq_kv=400, kv_splits=5)) == 2 * 4 * 100 * 4 * (64 + 2) * 4
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(head_dim=512, dtype=f32, kv_splits=4)),
                                                ctypes.byref(n)) == UNSUP
+    # a caller-defined mod is split only on request: the table keeps it whole
+    assert ws(prob(seq_q=4096, seq_kv=4096, batch=1, heads=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10])) == 0
+    assert ws(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], kv_splits=2)) == 2 * 4 * 100 * 2 * (64 + 2) * 4
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10],
-                                                                 kv_splits=4)), ctypes.byref(n)) == UNSUP
+                                                                 dtype=f32, kv_splits=4)), ctypes.byref(n)) == UNSUP
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(kv_splits=-1)), ctypes.byref(n)) == INVALID
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob()), None) == INVALID
 
@@ -412,4 +415,9 @@ def test_score_mod_create_compiles_and_reports_errors():
     # a custom mod needs its handle, and is refused for fp32
     assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM)) == INVALID
     assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32)) == UNSUP
-    assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10])) == UNSUP
+    assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32)) == UNSUP
+    # fa_decode takes a caller-defined mod in whole 64-key chunks (the forward's split kernel)
+    n = ctypes.c_size_t(0)
+    assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=1, seq_kv=1000, kv_splits=4, mod_kind=_lib.FA_MOD_CUSTOM,
+                                                           custom_mod=A[10])), ctypes.byref(n)) == _lib.FA_OK
+    assert n.value == 2 * 4 * 1 * 4 * (64 + 2) * 4   # ceil(1000 / 4) = 250 -> 256-key chunks, 4 of them

@@ -136,14 +136,71 @@ def test_custom_softcap_prefill_full_size(mods):
 
 
 def test_custom_mod_is_refused_where_it_is_not_built(mods):
-    """fa_decode and fp32 problems have no caller-defined score_mod path:
-    FA_ERR_UNSUPPORTED, nothing launched."""
-    q = torch.randn(1, 2, 1, 64, device="cuda", dtype=torch.float16)
-    k = torch.randn(1, 2, 100, 64, device="cuda", dtype=torch.float16)
+    """fp32 problems have no caller-defined score_mod path: FA_ERR_UNSUPPORTED,
+    nothing launched (forward and decode)."""
+    q = torch.randn(1, 2, 1, 64, device="cuda", dtype=torch.float32)
+    k = torch.randn(1, 2, 100, 64, device="cuda", dtype=torch.float32)
     p = torch.tensor([CAP], dtype=torch.float32, device="cuda")
     with pytest.raises(fa.FaError) as e:
         fa.decode(q, k, k, score_mod=mods["softcap"], mod_params=p)
     assert e.value.status == 2
     with pytest.raises(fa.FaError) as e:
-        fa.forward(q.float(), k.float(), k.float(), score_mod=mods["softcap"], mod_params=p)
+        fa.forward(q, k, k, score_mod=mods["softcap"], mod_params=p)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("dtype,D,Sq,Skv,causal,mask,n", [
+    ("f16", 64, 1, 5000, False, False, 0), ("bf16", 128, 1, 4100, True, True, 7), ("f16", 128, 16, 3000, True, False, 0),
+    ("bf16", 64, 64, 2500, False, True, 5)])
+def test_custom_softcap_decode(mods, dtype, D, Sq, Skv, causal, mask, n):
+    """fa_decode (and fa_decode_noalloc) with a caller-defined mod: one query
+    or a short block after a KV cache (query row i at key position
+    Skv - Sq + i), split over the keys, against the oracle."""
+    w = W.Workload("custom softcap decode", 403, 2, 3, Sq, Skv, D, dtype, causal=causal, key_mask=mask)
+    x = w.make()
+    x["q"] = (2.0 * x["q"].float()).to(x["q"].dtype)
+    dev = to_dev(x)
+    off = Skv - Sq
+    params = torch.tensor([CAP], dtype=torch.float32, device="cuda")
+    kw = dict(score_mod=mods["softcap"], mod_params=params, scale=w.scale, key_mask=dev.get("key_mask"),
+              q_offset=off, causal=causal)
+    say(f"[custom decode] {dtype} D{D} Sq={Sq} Skv={Skv} causal={causal} mask={mask} n={n}")
+    out, lse = fa.decode(dev["q"], dev["k"], dev["v"], kv_splits=n, **kw)
+    out2, lse2 = fa.decode_noalloc(dev["q"], dev["k"], dev["v"], **kw)
+    torch.cuda.synchronize()
+    okw = dict(scale=w.scale, causal=causal, q_offset=off, mod=oracle.MOD_CUSTOM,
+               custom=(softcap_np, softcap_grad_np),
+               key_mask=None if x.get("key_mask") is None else x["key_mask"].numpy())
+    o_r, lse_r = oracle.forward(x["q"], x["k"], x["v"], **okw)
+    check("o", out, o_r, dtype, "o")
+    check_lse(lse, lse_r)
+    check("o (no-allocation decode)", out2, o_r, dtype, "o")
+    check_lse(lse2, lse_r)
+
+
+@pytest.mark.parametrize("dtype,D,causal,blk,n", [("f16", 64, True, False, 3), ("bf16", 128, False, True, 5)])
+def test_custom_softcap_forward_split(mods, dtype, D, causal, blk, n):
+    """fa_forward_split with a caller-defined mod (an explicit chunk count:
+    the table keeps caller mods whole) against the oracle, and the backward
+    from its lse."""
+    Sq = Skv = 700
+    w = W.Workload("custom softcap split", 404, 2, 2, Sq, Skv, D, dtype, causal=causal)
+    x = w.make()
+    x["q"], x["k"] = (2.0 * x["q"].float()).to(x["q"].dtype), (2.0 * x["k"].float()).to(x["k"].dtype)
+    bm = W.bernoulli_block_mask(2, 2, Sq, Skv, 404, p_keep=0.7) if blk else None
+    dev = to_dev(x)
+    params = torch.tensor([CAP], dtype=torch.float32, device="cuda")
+    kw = dict(causal=causal, score_mod=mods["softcap"], mod_params=params, scale=w.scale,
+              block_mask=None if bm is None else bm.cuda())
+    say(f"[custom split] {dtype} D{D} causal={causal} blk={blk} n={n}")
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], kv_splits=n, **kw)
+    grads = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], **kw)
+    torch.cuda.synchronize()
+    okw = dict(scale=w.scale, causal=causal, mod=oracle.MOD_CUSTOM, custom=(softcap_np, softcap_grad_np),
+               block_mask=None if bm is None else bm.numpy() != 0)
+    o_r, lse_r = oracle.forward(x["q"], x["k"], x["v"], **okw)
+    g_r = oracle.backward(x["q"], x["k"], x["v"], x["dout"], **okw)
+    check("o", out, o_r, dtype, "o")
+    check_lse(lse, lse_r)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, g_r):
+        check(name, g, r, dtype, "grad")

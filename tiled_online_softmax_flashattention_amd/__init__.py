@@ -308,16 +308,17 @@ def decode(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=N
 
 
 def decode_noalloc(q, k, v, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None, checker=(0.5, -0.5),
-                   q_offset=0, causal=False, block_mask=None, out=None, lse=None):
+                   q_offset=0, causal=False, block_mask=None, out=None, lse=None, mod_params=None):
     """decode() through fa_decode_noalloc: no workspace, the library's fixed
     per-device scratch instead (for callers that cannot allocate at call time;
     pass out and lse to allocate nothing here either).  Calls that overlap on
     one device race on that scratch."""
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse)
-    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse)
+    _check_tensors(q, k, v, key_mask, alibi_slopes, block_mask, out, lse, mod_params)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
-                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask)
+                alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
+                mod_params=mod_params)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     lib = _lib.load()
@@ -385,16 +386,16 @@ def plan_backward(q, k, v, out, lse, dout, dq, dk, dv, workspace, *, causal=Fals
 
 
 def plan_decode(q, k, v, out, lse, workspace, *, key_mask=None, score_mod=None, scale=None, alibi_slopes=None,
-                checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None, kv_splits=0):
+                checker=(0.5, -0.5), q_offset=0, causal=False, block_mask=None, kv_splits=0, mod_params=None):
     key_mask, block_mask = _mask_u8(key_mask), _mask_u8(block_mask)
     _validate(q, k, v, key_mask=key_mask, alibi_slopes=alibi_slopes, block_mask=block_mask, out=out, lse=lse,
               workspace=workspace)
-    _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask)
+    _check_tensors(q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask, mod_params)
     p = problem(q, k, causal=causal, key_mask=key_mask, score_mod=score_mod, scale=scale,
                 alibi_slopes=alibi_slopes, checker=checker, q_offset=q_offset, block_mask=block_mask,
-                kv_splits=kv_splits)
+                kv_splits=kv_splits, mod_params=mod_params)
     lib = _lib.load()
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
             _stream(q))
     return _plan(lib.fa_decode, "fa_decode", args,
-                 (p, q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask))
+                 (p, q, k, v, out, lse, workspace, key_mask, alibi_slopes, block_mask, score_mod, mod_params))

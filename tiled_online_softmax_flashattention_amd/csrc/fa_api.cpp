@@ -169,7 +169,7 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
   } else {
     *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
   }
-  if (p->seq_q > 1) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
+  if (p->seq_q > 1 || p->mod_kind == FA_MOD_CUSTOM) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
   *n_split = (decode_kv_len(p) + *chunk - 1) / *chunk;
   return round_up((size_t)BH * (size_t)p->seq_q * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float),
                   256);
@@ -243,21 +243,29 @@ size_t forward_split_ws(const fa_problem* p, int* n_split, int* chunk) {
 // The forward over key chunks, then the merge of each row's partials, on a
 // validated problem with `ws` holding n_split partials per row (many_rows:
 // the forward's merge with several rows per workgroup; else the decode's).
-hipError_t split_forward_launch(const fa_problem* p, fa::AttnArgs a, int n_split, int chunk, void* ws,
-                                hipStream_t st, bool many_rows) {
+fa_status split_forward_launch(const fa_problem* p, fa::AttnArgs a, int n_split, int chunk, void* ws, hipStream_t st,
+                               bool many_rows) {
   const int D = (int)p->head_dim;
   const bool mask = p->key_mask != nullptr, causal = p->causal != 0;
   a.partial = (float*)ws;
   a.n_split = n_split;
   a.chunk = chunk;
   a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
-  hipError_t err;
-  if (p->dtype == FA_F32) err = fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true);
-  else err = fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal, mask, st, true);
-  if (err != hipSuccess) return err;
+  if (p->mod_kind == FA_MOD_CUSTOM) {
+    const unsigned grid = (unsigned)(a.n_qblocks * p->batch * p->heads * n_split);
+    const fa_status s = fa::custom_launch(p->custom_mod, 3, p->dtype, D, causal, mask, p->block_mask != nullptr, a,
+                                          grid, st);
+    if (s != FA_OK) return s;
+  } else {
+    const hipError_t err = p->dtype == FA_F32 ? fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true)
+                                              : fa::launch_fwd16(a, p->dtype == FA_BF16, D, p->mod_kind, causal,
+                                                                 mask, st, true);
+    if (err != hipSuccess) return FA_ERR_HIP;
+  }
   const int rows = (int)(p->batch * p->heads * p->seq_q);
-  return many_rows ? fa::launch_split_merge(a, p->dtype, D, rows, st)
-                   : fa::launch_decode_merge(a, p->dtype, D, rows, st);
+  const hipError_t err = many_rows ? fa::launch_split_merge(a, p->dtype, D, rows, st)
+                                   : fa::launch_decode_merge(a, p->dtype, D, rows, st);
+  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -297,7 +305,7 @@ fa_status fa_forward_split_workspace_size(const fa_problem* p, size_t* bytes) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
   if (!bytes) return FA_ERR_INVALID_ARGUMENT;
-  if (p->kv_splits > 1 && (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128)) return FA_ERR_UNSUPPORTED;
+  if (p->kv_splits > 1 && p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   int n_split, chunk;
   *bytes = forward_split_ws(p, &n_split, &chunk);
   return FA_OK;
@@ -307,7 +315,7 @@ fa_status fa_forward_split(const fa_problem* p, const void* q, const void* k, co
                            void* workspace, size_t workspace_bytes, void* stream) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
-  if (p->kv_splits > 1 && (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128)) return FA_ERR_UNSUPPORTED;
+  if (p->kv_splits > 1 && p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   int n_split, chunk;
   const size_t need = forward_split_ws(p, &n_split, &chunk);
   if (need == 0) return fa_forward(p, q, k, v, out, lse, stream);
@@ -323,8 +331,7 @@ fa_status fa_forward_split(const fa_problem* p, const void* q, const void* k, co
   a.v = v;
   a.o = out;
   a.lse = lse;
-  const hipError_t err = split_forward_launch(p, a, n_split, chunk, workspace, (hipStream_t)stream, true);
-  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return split_forward_launch(p, a, n_split, chunk, workspace, (hipStream_t)stream, true);
 }
 
 fa_status fa_backward_workspace_size(const fa_problem* p, size_t* bytes) {
@@ -425,7 +432,6 @@ fa_status validate_decode(const fa_problem* p, const void* q, const void* k, con
                           float* lse) {
   fa_status s = validate_problem(p);
   if (s != FA_OK) return s;
-  if (p->mod_kind == FA_MOD_CUSTOM) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxDecodeQ) return FA_ERR_INVALID_ARGUMENT;
   if (p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   if (!tensors_ok({q, k, v, out})) return FA_ERR_INVALID_ARGUMENT;
@@ -451,13 +457,11 @@ fa_status decode_launch(const fa_problem* p, const void* q, const void* k, const
   hipStream_t st = (hipStream_t)stream;
   const int D = (int)p->head_dim;
   const bool mask = p->key_mask != nullptr;
-  hipError_t err;
-  if (p->seq_q == 1) {
-    err = fa::launch_decode(a, p->dtype, D, p->mod_kind, mask, st);
-  } else {   // short query block: the forward split over the keys, then the merge
-    err = split_forward_launch(p, a, n_split, chunk, ws, st, false);
-  }
-  return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (p->seq_q == 1 && p->mod_kind != FA_MOD_CUSTOM)
+    return fa::launch_decode(a, p->dtype, D, p->mod_kind, mask, st) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  // a short query block, or a caller-defined score_mod (whose only key-split
+  // kernel is the forward's): the forward split over the keys, then the merge
+  return split_forward_launch(p, a, n_split, chunk, ws, st, false);
 }
 
 // Fixed device scratch of fa_decode_noalloc: the per-chunk partials live in

@@ -28,7 +28,11 @@ namespace fa {
 
 // ------------------------------------------------------------------ forward
 
-template <class T, int D, bool CAUSAL, bool MASK, bool BLK>
+// With SPLIT the workgroup covers one key chunk of its query block (the
+// order and chunking of the built-in split forward: split_coord, a.chunk
+// keys) and writes each row's unnormalised (accumulator, running max, sum)
+// to a.partial for the merge kernels.
+template <class T, int D, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false>
 __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
   constexpr int BM = 128, BN = 64;
   constexpr int QS = D / 16, DT = D / 32, TILE = BN * D;
@@ -45,8 +49,17 @@ __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const BlockCoord bc = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, CAUSAL);
-  const int bh = bc.bh, qb = CAUSAL ? a.n_qblocks - 1 - bc.blk : bc.blk;
+  int bh, qb, split = 0;
+  if constexpr (SPLIT) {
+    const SplitCoord c = split_coord(blockIdx.x, a.B * a.H, a.n_qblocks, a.n_split, CAUSAL);
+    bh = c.bh;
+    qb = c.qb;
+    split = c.split;
+  } else {
+    const BlockCoord bc = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, CAUSAL);
+    bh = bc.bh;
+    qb = CAUSAL ? a.n_qblocks - 1 - bc.blk : bc.blk;
+  }
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM, qw = q0 + 32 * wave, qi = qw + l32;
@@ -56,6 +69,16 @@ __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)bh * Sq * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)bh * Skv * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)bh * Skv * D;
+
+  const int kv_end = CAUSAL ? min(Skv, min(q0 + BM, Sq) + a.q_off) : Skv;
+  const int ntiles_all = (kv_end + BN - 1) / BN;
+  int t_lo = 0, t_hi = ntiles_all;
+  if constexpr (SPLIT) {
+    const int ct = a.chunk / BN;
+    t_lo = min(split * ct, ntiles_all);
+    t_hi = min(t_lo + ct, ntiles_all);
+    if (t_lo >= ntiles_all) return;   // past the block's last key: no row reads this partial
+  }
 
   u32x4 qf[QS];
   {
@@ -68,13 +91,12 @@ __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
     }
   }
 
-  const int kv_end = CAUSAL ? min(Skv, min(q0 + BM, Sq) + a.q_off) : Skv;
-  int ntiles = (kv_end + BN - 1) / BN;
+  int ntiles = t_hi - t_lo;
   if constexpr (BLK) {
     const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;
-    ntiles = compact_tiles(brow, 1, 1, 0, ntiles, sList, sCnt);
+    ntiles = compact_tiles(brow, 1, 1, t_lo, t_hi, sList, sCnt);
   }
-  auto kv_of = [&](int n) __attribute__((always_inline)) { return (BLK ? list_at(sList, n) : n) * BN; };
+  auto kv_of = [&](int n) __attribute__((always_inline)) { return (BLK ? list_at(sList, n) : t_lo + n) * BN; };
   auto load_tile = [&](int kv0, uint16_t* sK, uint16_t* sV, uint8_t* sM) __attribute__((always_inline)) {
     load_tile_lds<D, BN, SW_BOTH>(Kg, kv0, Skv, sK, wave, lane);
     load_tile_lds<D, BN, VSW>(Vg, kv0, Skv, sV, wave, lane);
@@ -157,6 +179,21 @@ __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
   if (n < ntiles) tile(n, sK0, sV0, sM0, sK1, sV1, sM1);
 
   const float l_tot = l_run + xor32(l_run);
+  if constexpr (SPLIT) {
+    if (qi < Sq) {
+      float* P = a.partial + (((size_t)bh * Sq + qi) * a.n_split + split) * (D + 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) P[32 * dt + 8 * (r >> 2) + 4 * hi + (r & 3)] = o[dt][r];
+      }
+      if (hi == 0) {
+        P[D] = l_tot > 0.f ? m_run : kNegInf;
+        P[D + 1] = l_tot;
+      }
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < Sq) {
     uint16_t* Og = (uint16_t*)a.o + ((size_t)bh * Sq + qi) * D;

@@ -24,7 +24,7 @@ struct fa_score_mod_s {
   std::mutex mu;
   struct Loaded {
     hipModule_t module;
-    hipFunction_t fn[3];   // forward, query pass, key/value pass
+    hipFunction_t fn[4];   // forward, query pass, key/value pass, forward over one key chunk
   };
   std::map<std::tuple<int, int, int, int, int, int>, Loaded> cache;   // device, dtype, D, causal, mask, block
 };
@@ -32,25 +32,25 @@ struct fa_score_mod_s {
 namespace fa {
 namespace {
 
-const char* kKernelNames[3] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv"};
+const char* kKernelNames[4] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv", "fa_custom_fwd_split"};
 
 // The translation unit: the caller's functions, then the kernel templates and
 // one instantiation of each pass for the configuration.
 std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, bool mask, bool blk) {
   const char* T = dtype == FA_BF16 ? "fa::BF16" : "fa::F16";
   const int lb = D == 64 ? 2 : 1;   // workgroups per CU the registers allow
-  char inst[1024];
   const char* tf[2] = {"false", "true"};
-  snprintf(inst, sizeof(inst),
-           "\n#include \"fa_custom.hpp\"\n"
-           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_fwd(const fa::AttnArgs a) "
-           "{ fa::fwd_custom<%s, %d, %s, %s, %s>(a); }\n"
-           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_dq(const fa::AttnArgs a) "
-           "{ fa::dq_custom<%s, %d, %s, %s, %s>(a); }\n"
-           "extern \"C\" __global__ __launch_bounds__(256, %d) void fa_custom_dkdv(const fa::AttnArgs a) "
-           "{ fa::dkdv_custom<%s, %d, %s, %s, %s>(a); }\n",
-           lb, T, D, tf[causal], tf[mask], tf[blk], lb, T, D, tf[causal], tf[mask], tf[blk], lb, T, D, tf[causal],
-           tf[mask], tf[blk]);
+  std::string inst = "\n#include \"fa_custom.hpp\"\n";
+  const char* kernels[4][2] = {{"fa_custom_fwd", "fwd_custom"}, {"fa_custom_dq", "dq_custom"},
+                               {"fa_custom_dkdv", "dkdv_custom"}, {"fa_custom_fwd_split", "fwd_custom"}};
+  for (int i = 0; i < 4; ++i) {
+    char line[512];
+    snprintf(line, sizeof(line),
+             "extern \"C\" __global__ __launch_bounds__(256, %d) void %s(const fa::AttnArgs a) "
+             "{ fa::%s<%s, %d, %s, %s, %s%s>(a); }\n",
+             lb, kernels[i][0], kernels[i][1], T, D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
+    inst += line;
+  }
   return user + "\n" + inst;
 }
 
@@ -135,7 +135,7 @@ fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causa
       if (code.empty()) return FA_ERR_COMPILE;
       fa_score_mod_s::Loaded l;
       if (hipModuleLoadData(&l.module, code.data()) != hipSuccess) return FA_ERR_HIP;
-      for (int i = 0; i < 3; ++i) {
+      for (int i = 0; i < 4; ++i) {
         if (hipModuleGetFunction(&l.fn[i], l.module, kKernelNames[i]) != hipSuccess) {
           hipModuleUnload(l.module);
           return FA_ERR_HIP;

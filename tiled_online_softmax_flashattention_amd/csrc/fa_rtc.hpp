@@ -12,7 +12,8 @@ namespace fa {
 fa_status custom_create(const char* source, fa_score_mod* out, char* log, size_t log_bytes);
 fa_status custom_destroy(fa_score_mod mod);
 
-// Launches pass 0 (forward), 1 (query pass) or 2 (key/value pass) of the
+// Launches pass 0 (forward), 1 (query pass), 2 (key/value pass) or 3 (the
+// forward over one key chunk per workgroup, writing partials) of the
 // configuration (dtype, D, causal, key mask, block mask) over `grid`
 // workgroups of 256 threads, compiling and loading it for the current device
 // on first use.
