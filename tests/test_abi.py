@@ -375,7 +375,8 @@ def test_forward_split_table_and_rules():
     assert ws(prob(seq_q=4096, seq_kv=4096, batch=1, heads=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10])) == 0
     assert ws(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], kv_splits=2)) == 2 * 4 * 100 * 2 * (64 + 2) * 4
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10],
-                                                                 dtype=f32, kv_splits=4)), ctypes.byref(n)) == UNSUP
+                                                                 dtype=f32, head_dim=512, kv_splits=4)),
+                                               ctypes.byref(n)) == UNSUP
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob(kv_splits=-1)), ctypes.byref(n)) == INVALID
     assert lib.fa_forward_split_workspace_size(ctypes.byref(prob()), None) == INVALID
 
@@ -412,10 +413,10 @@ def test_score_mod_create_compiles_and_reports_errors():
     assert not h2.value and b"error" in log.value
     assert lib.fa_score_mod_create(None, ctypes.byref(h2), None, 0) == INVALID
     assert lib.fa_score_mod_destroy(None) == INVALID
-    # a custom mod needs its handle, and is refused for fp32
+    # a custom mod needs its handle, and is refused at head_dim 512
     assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM)) == INVALID
-    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32)) == UNSUP
-    assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32)) == UNSUP
+    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32, head_dim=512)) == UNSUP
+    assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32, head_dim=512)) == UNSUP
     # fa_decode takes a caller-defined mod in whole 64-key chunks (the forward's split kernel)
     n = ctypes.c_size_t(0)
     assert lib.fa_decode_workspace_size(ctypes.byref(prob(seq_q=1, seq_kv=1000, kv_splits=4, mod_kind=_lib.FA_MOD_CUSTOM,

@@ -4,7 +4,8 @@ library at run time, forward and backward against the fp64 oracle with the
 same functions written in numpy.
 
 Bars as for the built-in mods: 16-bit max-abs-err / max|ref| <= 2e-2 (O) and
-5e-2 (gradients); lse within 1e-3 + 1e-5 |lse|.
+5e-2 (gradients); fp32 max-abs-err <= 1e-4 (O) and 1e-5 (gradients); lse
+within 1e-3 + 1e-5 |lse|.
 """
 import numpy as np
 import pytest
@@ -67,7 +68,9 @@ def run_custom(mod, params, w, inputs, *, q_offset=0, block_mask=None):
 
 CASES = [("f16", 64, False, False, False, 0), ("f16", 64, True, False, False, 0), ("bf16", 64, True, True, False, 0),
          ("f16", 128, False, True, False, 0), ("bf16", 128, True, False, True, 0), ("f16", 64, True, True, True, 37),
-         ("bf16", 64, False, False, True, 0), ("f16", 128, True, False, False, 90)]
+         ("bf16", 64, False, False, True, 0), ("f16", 128, True, False, False, 90),
+         ("f32", 64, True, False, False, 0), ("f32", 64, False, True, True, 0), ("f32", 128, True, True, False, 53),
+         ("f32", 128, False, False, True, 0)]
 
 
 @pytest.mark.parametrize("dtype,D,causal,mask,blk,off", CASES)
@@ -136,10 +139,10 @@ def test_custom_softcap_prefill_full_size(mods):
 
 
 def test_custom_mod_is_refused_where_it_is_not_built(mods):
-    """fp32 problems have no caller-defined score_mod path: FA_ERR_UNSUPPORTED,
-    nothing launched (forward and decode)."""
-    q = torch.randn(1, 2, 1, 64, device="cuda", dtype=torch.float32)
-    k = torch.randn(1, 2, 100, 64, device="cuda", dtype=torch.float32)
+    """fp32 at head_dim 512 has no caller-defined score_mod path:
+    FA_ERR_UNSUPPORTED, nothing launched (forward and decode)."""
+    q = torch.randn(1, 2, 1, 512, device="cuda", dtype=torch.float32)
+    k = torch.randn(1, 2, 100, 512, device="cuda", dtype=torch.float32)
     p = torch.tensor([CAP], dtype=torch.float32, device="cuda")
     with pytest.raises(fa.FaError) as e:
         fa.decode(q, k, k, score_mod=mods["softcap"], mod_params=p)
@@ -151,7 +154,7 @@ def test_custom_mod_is_refused_where_it_is_not_built(mods):
 
 @pytest.mark.parametrize("dtype,D,Sq,Skv,causal,mask,n", [
     ("f16", 64, 1, 5000, False, False, 0), ("bf16", 128, 1, 4100, True, True, 7), ("f16", 128, 16, 3000, True, False, 0),
-    ("bf16", 64, 64, 2500, False, True, 5)])
+    ("bf16", 64, 64, 2500, False, True, 5), ("f32", 64, 1, 3000, True, True, 0), ("f32", 128, 16, 2100, False, False, 3)])
 def test_custom_softcap_decode(mods, dtype, D, Sq, Skv, causal, mask, n):
     """fa_decode (and fa_decode_noalloc) with a caller-defined mod: one query
     or a short block after a KV cache (query row i at key position
@@ -178,7 +181,8 @@ def test_custom_softcap_decode(mods, dtype, D, Sq, Skv, causal, mask, n):
     check_lse(lse2, lse_r)
 
 
-@pytest.mark.parametrize("dtype,D,causal,blk,n", [("f16", 64, True, False, 3), ("bf16", 128, False, True, 5)])
+@pytest.mark.parametrize("dtype,D,causal,blk,n", [("f16", 64, True, False, 3), ("bf16", 128, False, True, 5),
+                                                  ("f32", 128, True, True, 4)])
 def test_custom_softcap_forward_split(mods, dtype, D, causal, blk, n):
     """fa_forward_split with a caller-defined mod (an explicit chunk count:
     the table keeps caller mods whole) against the oracle, and the backward

@@ -24,7 +24,8 @@ ARCH = "gfx950"
 SOURCES = ["fa_api.cpp", "fa_rtc.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_bwd16.hip", "fa_bwd32.hip",
            "fa_decode.hip"]
 # headers compiled again at run time (caller-defined score_mods), embedded as strings
-RTC_EMBED = (("kRtcCommon", "fa_common.hpp"), ("kRtcCustom", "fa_custom.hpp"))
+RTC_EMBED = (("kRtcCommon", "fa_common.hpp"), ("kRtcCustom", "fa_custom.hpp"), ("kRtcFwd32", "fa_fwd32.hip"),
+             ("kRtcBwd32", "fa_bwd32.hip"))
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

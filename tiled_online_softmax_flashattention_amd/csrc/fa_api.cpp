@@ -47,7 +47,7 @@ fa_status validate_problem(const fa_problem* p) {
   if (p->alibi_slopes && ((uintptr_t)p->alibi_slopes & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
   // caller-defined score_mods run the generic 16-bit kernels (head_dim 64, 128)
-  if (p->mod_kind == FA_MOD_CUSTOM && p->dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (p->mod_kind == FA_MOD_CUSTOM && p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 32-bit per (batch, head) slice
   if (p->batch * p->heads > kMaxI32 / 8) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;
@@ -253,8 +253,9 @@ fa_status split_forward_launch(const fa_problem* p, fa::AttnArgs a, int n_split,
   a.n_qblocks = (int)ceil_div(p->seq_q, block_q_fwd(p));
   if (p->mod_kind == FA_MOD_CUSTOM) {
     const unsigned grid = (unsigned)(a.n_qblocks * p->batch * p->heads * n_split);
-    const fa_status s = fa::custom_launch(p->custom_mod, 3, p->dtype, D, causal, mask, p->block_mask != nullptr, a,
-                                          grid, st);
+    const bool blk = p->block_mask != nullptr;
+    const fa_status s = fa::custom_launch(p->custom_mod, 3, p->dtype, D, causal, mask, blk, a, grid,
+                                          p->dtype == FA_F32 ? fa::fwd32_lds_bytes(D, blk) : 0, st);
     if (s != FA_OK) return s;
   } else {
     const hipError_t err = p->dtype == FA_F32 ? fa::launch_fwd32(a, D, p->mod_kind, causal, mask, st, true)
@@ -289,9 +290,12 @@ fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const vo
   a.lse = lse;
   a.n_qblocks = (int)nqb;
   hipStream_t st = (hipStream_t)stream;
-  if (p->mod_kind == FA_MOD_CUSTOM)
+  if (p->mod_kind == FA_MOD_CUSTOM) {
+    const bool blk = p->block_mask != nullptr;
     return fa::custom_launch(p->custom_mod, 0, p->dtype, (int)p->head_dim, p->causal != 0, p->key_mask != nullptr,
-                             p->block_mask != nullptr, a, (unsigned)(nqb * p->batch * p->heads), st);
+                             blk, a, (unsigned)(nqb * p->batch * p->heads),
+                             p->dtype == FA_F32 ? fa::fwd32_lds_bytes((int)p->head_dim, blk) : 0, st);
+  }
   hipError_t err;
   if (p->dtype == FA_F32)
     err = fa::launch_fwd32(a, (int)p->head_dim, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
@@ -391,14 +395,13 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
     if (err != hipSuccess) return FA_ERR_HIP;
     const bool causal = p->causal != 0, mask = p->key_mask != nullptr, blk = p->block_mask != nullptr;
     const unsigned bh = (unsigned)(p->batch * p->heads);
+    const size_t lds = f32 ? fa::bwd32_lds_bytes(D, blk) : 0;
     if (want_q) {
-      s = fa::custom_launch(p->custom_mod, 1, p->dtype, D, causal, mask, blk, a,
-                            (unsigned)ceil_div(p->seq_q, 128) * bh, st);
+      s = fa::custom_launch(p->custom_mod, 1, p->dtype, D, causal, mask, blk, a, (unsigned)nqb * bh, lds, st);
       if (s != FA_OK) return s;
     }
     if (want_kv)
-      s = fa::custom_launch(p->custom_mod, 2, p->dtype, D, causal, mask, blk, a,
-                            (unsigned)ceil_div(p->seq_kv, 128) * bh, st);
+      s = fa::custom_launch(p->custom_mod, 2, p->dtype, D, causal, mask, blk, a, (unsigned)nkb * bh, lds, st);
     return s;
   }
   if (f32) {   // fp32: preprocess kernel, then the passes

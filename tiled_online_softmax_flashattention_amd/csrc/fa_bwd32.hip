@@ -7,7 +7,16 @@
 // waves of a workgroup: each wave owns 128 dims of the register-resident rows
 // and accumulators, and the partial S and dP products are summed through LDS.
 #include "fa_common.hpp"
+#ifndef __HIPCC_RTC__
 #include "fa_launch.hpp"
+#endif
+
+// A caller-defined score_mod (the modified score of score = scale * q.k, and
+// its derivative in score), used by the MOD_CUSTOM instances below.  Defined
+// only in the units the library compiles at run time with the caller's
+// source, which are the only units that instantiate MOD_CUSTOM.
+__device__ float fa_score_mod(float score, int b, int h, int q_idx, int kv_idx, const float* params);
+__device__ float fa_score_mod_grad(float score, int b, int h, int q_idx, int kv_idx, const float* params);
 
 namespace fa {
 
@@ -51,9 +60,13 @@ __device__ __forceinline__ void stage32(float* dst, const float* g, int row0, in
 
 // With BLK only the query tiles whose 128 x 128 block is set in the block
 // mask are visited (a workgroup's keys lie in one block column).
+// MOD_CUSTOM (head_dim <= 128): P from the caller's fa_score_mod of the
+// scaled score and dS times its derivative fa_score_mod_grad; compiled only at
+// run time with the caller's source.
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
-__global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
+__device__ __forceinline__ void dkdv32_body(const AttnArgs& a) {
   using C = B32Cfg<D>;
+  static_assert(MOD != MOD_CUSTOM || C::DS == 1, "caller-defined mods are built for head_dim <= 128");
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
   constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
   constexpr int BKV = 32 * NG, BQ = 32;
@@ -177,11 +190,17 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
         float x = s[r] * a.scale_log2;
         if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kj - qi - off);
         if constexpr (MOD == MOD_CHECKERBOARD) x += ((r + off) & 1) ? cbo : cbe;
+        if constexpr (MOD == MOD_CUSTOM) x = fa_score_mod(s[r] * a.scale, b, h, qi + off, kj, a.mod_params) * kLog2e;
         float p = exp2_hw(x - l4[c]);
         if (!key_ok) p = 0.f;
         if (diag && kj > qi + off) p = 0.f;
+        if constexpr (MOD == MOD_CUSTOM) {
+          dp[r] = p != 0.f ? p * (dp[r] - d4[c]) * fa_score_mod_grad(s[r] * a.scale, b, h, qi + off, kj, a.mod_params)
+                           : 0.f;
+        } else {
+          dp[r] = p * (dp[r] - d4[c]);
+        }
         s[r] = p;
-        dp[r] = p * (dp[r] - d4[c]);
       }
     }
 
@@ -219,8 +238,9 @@ __global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
 
 // With BLK only the key tiles whose 128 x 128 block is set are visited.
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
-__global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
+__device__ __forceinline__ void dq32_body(const AttnArgs& a) {
   using C = B32Cfg<D>;
+  static_assert(MOD != MOD_CUSTOM || C::DS == 1, "caller-defined mods are built for head_dim <= 128");
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
   constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
   constexpr int BM = 32 * NG, BN = 32;
@@ -397,6 +417,7 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
         float x = s[r] * a.scale_log2;
         if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qpos);
         if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
+        if constexpr (MOD == MOD_CUSTOM) x = fa_score_mod(s[r] * a.scale, b, h, qpos, kv, a.mod_params) * kLog2e;
         float p = exp2_hw(x - lse2);
         if constexpr (MASK) {
           if (((mw >> (8 * c)) & 0xffu) == 0u) p = 0.f;
@@ -404,7 +425,12 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
           if (tail && kv >= Skv) p = 0.f;
         }
         if (diag && kv > qpos) p = 0.f;
-        dp[r] = p * (dp[r] - delta);
+        if constexpr (MOD == MOD_CUSTOM) {
+          dp[r] = p != 0.f ? p * (dp[r] - delta) * fa_score_mod_grad(s[r] * a.scale, b, h, qpos, kv, a.mod_params)
+                           : 0.f;
+        } else {
+          dp[r] = p * (dp[r] - delta);
+        }
       }
     }
 
@@ -432,6 +458,17 @@ __global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
             f32x4{dq[dt][4 * u] * sc, dq[dt][4 * u + 1] * sc, dq[dt][4 * u + 2] * sc, dq[dt][4 * u + 3] * sc};
     }
   }
+}
+
+#ifndef __HIPCC_RTC__
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+__global__ __launch_bounds__(256, 1) void dkdv32_kernel(const AttnArgs a) {
+  dkdv32_body<D, MOD, CAUSAL, MASK, BLK>(a);
+}
+
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+__global__ __launch_bounds__(256, 1) void dq32_kernel(const AttnArgs a) {
+  dq32_body<D, MOD, CAUSAL, MASK, BLK>(a);
 }
 
 template <class K>
@@ -479,6 +516,11 @@ static hipError_t launch_bwd32_d(const AttnArgs& a, int mod, bool causal, bool m
   }
 }
 
+size_t bwd32_lds_bytes(int D, bool blk) {
+  if (blk) return D == 512 ? B32Cfg<512>::lds_blk : D == 128 ? B32Cfg<128>::lds_blk : B32Cfg<64>::lds_blk;
+  return D == 512 ? B32Cfg<512>::lds : D == 128 ? B32Cfg<128>::lds : B32Cfg<64>::lds;
+}
+
 int bwd32_block_kv(int D) { return D >= 512 ? 32 : 128; }
 int bwd32_block_q(int D) { return D >= 512 ? 32 : 128; }
 
@@ -487,5 +529,7 @@ hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
   if (D == 128) return launch_bwd32_d<128>(a, mod, causal, mask, kv, qq, st);
   return launch_bwd32_d<512>(a, mod, causal, mask, kv, qq, st);
 }
+
+#endif  // !__HIPCC_RTC__
 
 }  // namespace fa

@@ -37,7 +37,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
-enum Mod { MOD_NONE = 0, MOD_ALIBI = 1, MOD_CHECKERBOARD = 2 };
+enum Mod { MOD_NONE = 0, MOD_ALIBI = 1, MOD_CHECKERBOARD = 2, MOD_CUSTOM = 3 };
 
 // Element tags for the 16-bit storage types.
 struct F16 {};

@@ -12,7 +12,16 @@
 // keeps Q (64 values) and the accumulator (64 values) per lane in registers
 // while a 32-key K tile and V tile (128 KiB together) sit in LDS.
 #include "fa_common.hpp"
+#ifndef __HIPCC_RTC__
 #include "fa_launch.hpp"
+#endif
+
+// A caller-defined score_mod (the modified score of score = scale * q.k, and
+// its derivative in score), used by the MOD_CUSTOM instances below.  Defined
+// only in the units the library compiles at run time with the caller's
+// source, which are the only units that instantiate MOD_CUSTOM.
+__device__ float fa_score_mod(float score, int b, int h, int q_idx, int kv_idx, const float* params);
+__device__ float fa_score_mod_grad(float score, int b, int h, int q_idx, int kv_idx, const float* params);
 
 namespace fa {
 
@@ -34,8 +43,10 @@ struct F32Cfg {
 // grid is (batch * heads) x query blocks x a.n_split key chunks of a.chunk
 // keys, and each workgroup writes its rows' unnormalised partial
 // (accumulator, running max, sum) to a.partial for the decode merge.
+// MOD_CUSTOM (head_dim <= 128): the caller's fa_score_mod on the scaled
+// score, before the masks; compiled only at run time with the caller's source.
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false>
-__global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
+__device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   using C = F32Cfg<D>;
   constexpr int DS = C::DS, BM = C::BM, BN = C::BN, P = C::P;
   constexpr int DSL = D / DS;          // dims per slice
@@ -55,6 +66,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = wave / DS, e = wave % DS;
   static_assert(!SPLIT || DS == 1, "the key split is built for head_dim <= 128");
+  static_assert(MOD != MOD_CUSTOM || DS == 1, "caller-defined mods are built for head_dim <= 128");
   const int BH = a.B * a.H;
   int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH, split = 0;
@@ -193,6 +205,7 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
         float x = s[r] * a.scale_log2;
         if constexpr (MOD == MOD_ALIBI) x += slope2 * (float)(kv - qpos);
         if constexpr (MOD == MOD_CHECKERBOARD) x += (r & 1) ? cb1 : cb0;
+        if constexpr (MOD == MOD_CUSTOM) x = fa_score_mod(s[r] * a.scale, b, h, qpos, kv, a.mod_params) * kLog2e;
         if constexpr (MASK) {
           if (((mw >> (8 * c)) & 0xffu) == 0u) x = kNegInf;
         } else {
@@ -271,6 +284,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   }
 }
 
+#ifndef __HIPCC_RTC__
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false>
+__global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
+  fwd32_body<D, MOD, CAUSAL, MASK, BLK, SPLIT>(a);
+}
+
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT>
 static hipError_t launch_one_blk(const AttnArgs& a, hipStream_t st) {
   auto kern = fwd32_kernel<D, MOD, CAUSAL, MASK, BLK, SPLIT>;
@@ -310,7 +329,8 @@ int fwd32_block_q(int D) {
   return D == 512 ? F32Cfg<512>::BM : D == 128 ? F32Cfg<128>::BM : F32Cfg<64>::BM;
 }
 
-size_t fwd32_lds_bytes(int D) {
+size_t fwd32_lds_bytes(int D, bool blk) {
+  if (blk) return D == 512 ? F32Cfg<512>::lds_blk : D == 128 ? F32Cfg<128>::lds_blk : F32Cfg<64>::lds_blk;
   return D == 512 ? F32Cfg<512>::lds : D == 128 ? F32Cfg<128>::lds : F32Cfg<64>::lds;
 }
 
@@ -321,5 +341,7 @@ hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
   if (D == 128) return launch_fwd32_d<128, false>(a, mod, causal, mask, st);
   return launch_fwd32_d<512, false>(a, mod, causal, mask, st);
 }
+
+#endif  // !__HIPCC_RTC__
 
 }  // namespace fa

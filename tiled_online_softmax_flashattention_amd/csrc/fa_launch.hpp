@@ -19,7 +19,7 @@ hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causa
 // query block is split over a.n_split key chunks of a.chunk keys (a multiple
 // of 32) whose partials go to a.partial, as launch_fwd16 does.
 int fwd32_block_q(int D);
-size_t fwd32_lds_bytes(int D);
+size_t fwd32_lds_bytes(int D, bool blk);   // dynamic LDS of a forward launch (with a block mask: blk)
 hipError_t launch_fwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, hipStream_t st,
                         bool split = false);
 
@@ -35,6 +35,7 @@ int bwd16_block_q();
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
                         bool want_kv, bool want_q, bool dq_atomic, hipStream_t st);
 int bwd32_block_kv(int D);
+size_t bwd32_lds_bytes(int D, bool blk);   // dynamic LDS of either fp32 backward pass
 int bwd32_block_q(int D);
 hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mask, bool want_kv, bool want_q,
                         hipStream_t st);

@@ -17,7 +17,7 @@
 #include "../../include/fa_mi355x.h"
 #include "fa_rtc.hpp"
 
-#include "fa_rtc_sources.inc"   // kRtcCommon, kRtcCustom
+#include "fa_rtc_sources.inc"   // kRtcCommon, kRtcCustom, kRtcFwd32, kRtcBwd32
 
 struct fa_score_mod_s {
   std::string source;
@@ -35,20 +35,34 @@ namespace {
 const char* kKernelNames[4] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv", "fa_custom_fwd_split"};
 
 // The translation unit: the caller's functions, then the kernel templates and
-// one instantiation of each pass for the configuration.
+// one instantiation of each pass for the configuration (16-bit: the generic
+// kernels of fa_custom.hpp; fp32: the library's fp32 kernels with MOD_CUSTOM).
 std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, bool mask, bool blk) {
+  const char* tf[2] = {"false", "true"};
+  const char* names[4] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv", "fa_custom_fwd_split"};
+  std::string inst;
+  char line[512];
+  if (dtype == FA_F32) {
+    inst = "\n#include \"fa_fwd32.hip\"\n#include \"fa_bwd32.hip\"\n";
+    const char* bodies[4] = {"fwd32_body", "dq32_body", "dkdv32_body", "fwd32_body"};
+    for (int i = 0; i < 4; ++i) {
+      snprintf(line, sizeof(line),
+               "extern \"C\" __global__ __launch_bounds__(256, 1) void %s(const fa::AttnArgs a) "
+               "{ fa::%s<%d, fa::MOD_CUSTOM, %s, %s, %s%s>(a); }\n",
+               names[i], bodies[i], D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
+      inst += line;
+    }
+    return user + "\n" + inst;
+  }
   const char* T = dtype == FA_BF16 ? "fa::BF16" : "fa::F16";
   const int lb = D == 64 ? 2 : 1;   // workgroups per CU the registers allow
-  const char* tf[2] = {"false", "true"};
-  std::string inst = "\n#include \"fa_custom.hpp\"\n";
-  const char* kernels[4][2] = {{"fa_custom_fwd", "fwd_custom"}, {"fa_custom_dq", "dq_custom"},
-                               {"fa_custom_dkdv", "dkdv_custom"}, {"fa_custom_fwd_split", "fwd_custom"}};
+  inst = "\n#include \"fa_custom.hpp\"\n";
+  const char* bodies[4] = {"fwd_custom", "dq_custom", "dkdv_custom", "fwd_custom"};
   for (int i = 0; i < 4; ++i) {
-    char line[512];
     snprintf(line, sizeof(line),
              "extern \"C\" __global__ __launch_bounds__(256, %d) void %s(const fa::AttnArgs a) "
              "{ fa::%s<%s, %d, %s, %s, %s%s>(a); }\n",
-             lb, kernels[i][0], kernels[i][1], T, D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
+             lb, names[i], bodies[i], T, D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
     inst += line;
   }
   return user + "\n" + inst;
@@ -58,9 +72,9 @@ std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, boo
 // empty vector with the compiler log in *log.
 std::vector<char> rtc_compile(const std::string& unit, const std::string& arch, std::string* log) {
   hiprtcProgram prog;
-  const char* headers[2] = {kRtcCommon, kRtcCustom};
-  const char* names[2] = {"fa_common.hpp", "fa_custom.hpp"};
-  if (hiprtcCreateProgram(&prog, unit.c_str(), "fa_score_mod.hip", 2, headers, names) != HIPRTC_SUCCESS) {
+  const char* headers[4] = {kRtcCommon, kRtcCustom, kRtcFwd32, kRtcBwd32};
+  const char* names[4] = {"fa_common.hpp", "fa_custom.hpp", "fa_fwd32.hip", "fa_bwd32.hip"};
+  if (hiprtcCreateProgram(&prog, unit.c_str(), "fa_score_mod.hip", 4, headers, names) != HIPRTC_SUCCESS) {
     *log = "hiprtcCreateProgram failed";
     return {};
   }
@@ -121,7 +135,7 @@ fa_status custom_destroy(fa_score_mod mod) {
 }
 
 fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causal, bool mask, bool blk,
-                        const AttnArgs& a, unsigned grid, hipStream_t st) {
+                        const AttnArgs& a, unsigned grid, size_t shared_bytes, hipStream_t st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
   const auto key = std::make_tuple(dev, dtype, D, (int)causal, (int)mask, (int)blk);
@@ -147,7 +161,8 @@ fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causa
   }
   AttnArgs args = a;
   void* params[] = {&args};
-  if (hipModuleLaunchKernel(fn, grid, 1, 1, 256, 1, 1, 0, st, params, nullptr) != hipSuccess) return FA_ERR_HIP;
+  if (hipModuleLaunchKernel(fn, grid, 1, 1, 256, 1, 1, (unsigned)shared_bytes, st, params, nullptr) != hipSuccess)
+    return FA_ERR_HIP;
   return FA_OK;
 }
 

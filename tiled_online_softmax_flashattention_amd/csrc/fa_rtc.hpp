@@ -15,9 +15,10 @@ fa_status custom_destroy(fa_score_mod mod);
 // Launches pass 0 (forward), 1 (query pass), 2 (key/value pass) or 3 (the
 // forward over one key chunk per workgroup, writing partials) of the
 // configuration (dtype, D, causal, key mask, block mask) over `grid`
-// workgroups of 256 threads, compiling and loading it for the current device
-// on first use.
+// workgroups of 256 threads with `shared_bytes` of dynamic LDS (the fp32
+// kernels'; 0 for the 16-bit ones), compiling and loading it for the current
+// device on first use.
 fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causal, bool mask, bool blk,
-                        const AttnArgs& a, unsigned grid, hipStream_t st);
+                        const AttnArgs& a, unsigned grid, size_t shared_bytes, hipStream_t st);
 
 }  // namespace fa
