@@ -55,14 +55,16 @@ std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, boo
     return user + "\n" + inst;
   }
   const char* T = dtype == FA_BF16 ? "fa::BF16" : "fa::F16";
-  const int lb = D == 64 ? 2 : 1;   // workgroups per CU the registers allow
+  // workgroups per CU the registers allow: the forward fits two at either
+  // head_dim (204 registers at 128), the backward passes at 128 one
+  const int lb[4] = {2, D == 64 ? 2 : 1, D == 64 ? 2 : 1, 2};
   inst = "\n#include \"fa_custom.hpp\"\n";
   const char* bodies[4] = {"fwd_custom", "dq_custom", "dkdv_custom", "fwd_custom"};
   for (int i = 0; i < 4; ++i) {
     snprintf(line, sizeof(line),
              "extern \"C\" __global__ __launch_bounds__(256, %d) void %s(const fa::AttnArgs a) "
              "{ fa::%s<%s, %d, %s, %s, %s%s>(a); }\n",
-             lb, names[i], bodies[i], T, D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
+             lb[i], names[i], bodies[i], T, D, tf[causal], tf[mask], tf[blk], i == 3 ? ", true" : "");
     inst += line;
   }
   return user + "\n" + inst;
