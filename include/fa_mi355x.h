@@ -94,9 +94,10 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
  *  FA_MOD_CHECKERBOARD: bias = checker_even when (pos_i + j) is even, otherwise
  *                       checker_odd (the workloads use +0.5 / -0.5).
  *  FA_MOD_CUSTOM:       s_ij = mod(scale * <q_i, k_j>, b, h, pos_i, j) with the
- *                       caller's device function (fa_score_mod_create); f16
- *                       and bf16 with head_dim 64 or 128, every entry point
- *                       (fp32 returns FA_ERR_UNSUPPORTED). */
+ *                       caller's device function (fa_score_mod_create); every
+ *                       dtype and head_dim, every entry point (fa_decode and
+ *                       the key split stop at head_dim 128 as for the
+ *                       built-in mods). */
 typedef enum { FA_MOD_NONE = 0, FA_MOD_ALIBI = 1, FA_MOD_CHECKERBOARD = 2, FA_MOD_CUSTOM = 3 } fa_mod_kind;
 
 /* A caller-defined score_mod compiled for the device (fa_score_mod_create). */

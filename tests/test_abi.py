@@ -413,9 +413,9 @@ def test_score_mod_create_compiles_and_reports_errors():
     assert not h2.value and b"error" in log.value
     assert lib.fa_score_mod_create(None, ctypes.byref(h2), None, 0) == INVALID
     assert lib.fa_score_mod_destroy(None) == INVALID
-    # a custom mod needs its handle, and is refused at head_dim 512
+    # a custom mod needs its handle; fa_decode and 16-bit kernels stop at head_dim 128
     assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM)) == INVALID
-    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32, head_dim=512)) == UNSUP
+    assert fwd(prob(mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F16, head_dim=512)) == UNSUP
     assert dec(prob(seq_q=1, mod_kind=_lib.FA_MOD_CUSTOM, custom_mod=A[10], dtype=_lib.FA_F32, head_dim=512)) == UNSUP
     # fa_decode takes a caller-defined mod in whole 64-key chunks (the forward's split kernel)
     n = ctypes.c_size_t(0)

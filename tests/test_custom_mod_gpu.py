@@ -139,8 +139,9 @@ def test_custom_softcap_prefill_full_size(mods):
 
 
 def test_custom_mod_is_refused_where_it_is_not_built(mods):
-    """fp32 at head_dim 512 has no caller-defined score_mod path:
-    FA_ERR_UNSUPPORTED, nothing launched (forward and decode)."""
+    """fa_decode and the split forward stop at head_dim 128: an fp32
+    head_dim 512 problem with a caller-defined mod is FA_ERR_UNSUPPORTED
+    there, nothing launched."""
     q = torch.randn(1, 2, 1, 512, device="cuda", dtype=torch.float32)
     k = torch.randn(1, 2, 100, 512, device="cuda", dtype=torch.float32)
     p = torch.tensor([CAP], dtype=torch.float32, device="cuda")
@@ -148,8 +149,29 @@ def test_custom_mod_is_refused_where_it_is_not_built(mods):
         fa.decode(q, k, k, score_mod=mods["softcap"], mod_params=p)
     assert e.value.status == 2
     with pytest.raises(fa.FaError) as e:
-        fa.forward(q, k, k, score_mod=mods["softcap"], mod_params=p)
+        fa.forward(q, k, k, score_mod=mods["softcap"], mod_params=p, kv_splits=2)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("causal,mask", [(True, False), (False, True)])
+def test_custom_softcap_f32_d512(mods, causal, mask):
+    """fp32 at head_dim 512 (the long-context kernels, dims split over four
+    waves) with the soft cap, forward and backward against the oracle."""
+    Sq, Skv = 80, 80 if causal else 130
+    w = W.Workload("custom softcap d512", 405, 1, 2, Sq, Skv, 512, "f32", causal=causal, key_mask=mask)
+    x = w.make()
+    x["q"], x["k"] = 2.0 * x["q"], 2.0 * x["k"]
+    say(f"[custom softcap] f32 D512 causal={causal} mask={mask}")
+    params = torch.tensor([CAP], dtype=torch.float32, device="cuda")
+    out, lse, (dq, dk, dv) = run_custom(mods["softcap"], params, w, x)
+    okw = dict(scale=w.scale, causal=causal, mod=oracle.MOD_CUSTOM, custom=(softcap_np, softcap_grad_np),
+               key_mask=None if x.get("key_mask") is None else x["key_mask"].numpy())
+    o_r, lse_r = oracle.forward(x["q"], x["k"], x["v"], **okw)
+    g_r = oracle.backward(x["q"], x["k"], x["v"], x["dout"], **okw)
+    check("o", out, o_r, "f32", "o")
+    check_lse(lse, lse_r)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), g_r):
+        check(name, g, r, "f32", "grad")
 
 
 @pytest.mark.parametrize("dtype,D,Sq,Skv,causal,mask,n", [

@@ -46,8 +46,6 @@ fa_status validate_problem(const fa_problem* p) {
   if (p->q_offset < 0) return FA_ERR_INVALID_ARGUMENT;
   if (p->alibi_slopes && ((uintptr_t)p->alibi_slopes & 3u)) return FA_ERR_INVALID_ARGUMENT;
   if (!head_dim_supported(p->dtype, p->head_dim)) return FA_ERR_UNSUPPORTED;
-  // caller-defined score_mods run the generic 16-bit kernels (head_dim 64, 128)
-  if (p->mod_kind == FA_MOD_CUSTOM && p->head_dim > 128) return FA_ERR_UNSUPPORTED;
   // index arithmetic inside the kernels is 32-bit per (batch, head) slice
   if (p->batch * p->heads > kMaxI32 / 8) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxI32 / p->head_dim || p->seq_kv > kMaxI32 / p->head_dim) return FA_ERR_UNSUPPORTED;

@@ -60,13 +60,12 @@ __device__ __forceinline__ void stage32(float* dst, const float* g, int row0, in
 
 // With BLK only the query tiles whose 128 x 128 block is set in the block
 // mask are visited (a workgroup's keys lie in one block column).
-// MOD_CUSTOM (head_dim <= 128): P from the caller's fa_score_mod of the
-// scaled score and dS times its derivative fa_score_mod_grad; compiled only at
-// run time with the caller's source.
+// MOD_CUSTOM: P from the caller's fa_score_mod of the scaled score and dS
+// times its derivative fa_score_mod_grad (at head_dim 512 after the partial
+// products are summed); compiled only at run time with the caller's source.
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __device__ __forceinline__ void dkdv32_body(const AttnArgs& a) {
   using C = B32Cfg<D>;
-  static_assert(MOD != MOD_CUSTOM || C::DS == 1, "caller-defined mods are built for head_dim <= 128");
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
   constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
   constexpr int BKV = 32 * NG, BQ = 32;
@@ -240,7 +239,6 @@ __device__ __forceinline__ void dkdv32_body(const AttnArgs& a) {
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 __device__ __forceinline__ void dq32_body(const AttnArgs& a) {
   using C = B32Cfg<D>;
-  static_assert(MOD != MOD_CUSTOM || C::DS == 1, "caller-defined mods are built for head_dim <= 128");
   constexpr int DS = C::DS, NG = C::NG, P = C::P;
   constexpr int DSL = D / DS, HS = DSL / 2, DT = DSL / 32;
   constexpr int BM = 32 * NG, BN = 32;

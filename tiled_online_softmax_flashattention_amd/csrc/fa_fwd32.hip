@@ -43,8 +43,9 @@ struct F32Cfg {
 // grid is (batch * heads) x query blocks x a.n_split key chunks of a.chunk
 // keys, and each workgroup writes its rows' unnormalised partial
 // (accumulator, running max, sum) to a.partial for the decode merge.
-// MOD_CUSTOM (head_dim <= 128): the caller's fa_score_mod on the scaled
-// score, before the masks; compiled only at run time with the caller's source.
+// MOD_CUSTOM: the caller's fa_score_mod on the scaled score (at head_dim 512
+// after the partial scores are summed), before the masks; compiled only at
+// run time with the caller's source.
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false>
 __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   using C = F32Cfg<D>;
@@ -66,7 +67,6 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int g = wave / DS, e = wave % DS;
   static_assert(!SPLIT || DS == 1, "the key split is built for head_dim <= 128");
-  static_assert(MOD != MOD_CUSTOM || DS == 1, "caller-defined mods are built for head_dim <= 128");
   const int BH = a.B * a.H;
   int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH, split = 0;

@@ -34,6 +34,10 @@ namespace {
 
 const char* kKernelNames[4] = {"fa_custom_fwd", "fa_custom_dq", "fa_custom_dkdv", "fa_custom_fwd_split"};
 
+// Kernels of a configuration: the forward, the two backward passes and the
+// forward over one key chunk; fp32 at head_dim 512 has no key split.
+int kernels_of(int dtype, int D) { return dtype == FA_F32 && D > 128 ? 3 : 4; }
+
 // The translation unit: the caller's functions, then the kernel templates and
 // one instantiation of each pass for the configuration (16-bit: the generic
 // kernels of fa_custom.hpp; fp32: the library's fp32 kernels with MOD_CUSTOM).
@@ -45,7 +49,7 @@ std::string rtc_unit(const std::string& user, int dtype, int D, bool causal, boo
   if (dtype == FA_F32) {
     inst = "\n#include \"fa_fwd32.hip\"\n#include \"fa_bwd32.hip\"\n";
     const char* bodies[4] = {"fwd32_body", "dq32_body", "dkdv32_body", "fwd32_body"};
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kernels_of(dtype, D); ++i) {
       snprintf(line, sizeof(line),
                "extern \"C\" __global__ __launch_bounds__(256, 1) void %s(const fa::AttnArgs a) "
                "{ fa::%s<%d, fa::MOD_CUSTOM, %s, %s, %s%s>(a); }\n",
@@ -151,7 +155,8 @@ fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causa
       if (code.empty()) return FA_ERR_COMPILE;
       fa_score_mod_s::Loaded l;
       if (hipModuleLoadData(&l.module, code.data()) != hipSuccess) return FA_ERR_HIP;
-      for (int i = 0; i < 4; ++i) {
+      l.fn[3] = nullptr;
+      for (int i = 0; i < kernels_of(dtype, D); ++i) {
         if (hipModuleGetFunction(&l.fn[i], l.module, kKernelNames[i]) != hipSuccess) {
           hipModuleUnload(l.module);
           return FA_ERR_HIP;
@@ -161,6 +166,7 @@ fa_status custom_launch(fa_score_mod mod, int pass, int dtype, int D, bool causa
     }
     fn = it->second.fn[pass];
   }
+  if (!fn) return FA_ERR_UNSUPPORTED;
   AttnArgs args = a;
   void* params[] = {&args};
   if (hipModuleLaunchKernel(fn, grid, 1, 1, 256, 1, 1, (unsigned)shared_bytes, st, params, nullptr) != hipSuccess)
