@@ -43,10 +43,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# The race-check library: the same sources with FA_DEBUG_BARRIERS (every
+# barrier and wait drains the wave's outstanding memory operations first); a
+# GPU test requires its results to equal the normal library's bit for bit.
+RACECHECK_OUT = os.path.join(PKG, "libfa_mi355x_racecheck.so")
+RACECHECK_BUILD = os.path.join(PKG, "_build_racecheck")
+
+
+def _compile(src: str, racecheck: bool = False) -> str:
+    out_dir = RACECHECK_BUILD if racecheck else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-DFA_DEBUG_BARRIERS"] if racecheck else []
+    cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -70,22 +79,33 @@ def write_rtc_sources() -> None:
             fh.write(new)
 
 
-def build(jobs: int = 0, verbose: bool = True) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    write_rtc_sources()
-    t0 = time.time()
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lhiprtc"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 0, verbose: bool = True, racecheck: bool = True) -> str:
+    """Compile every source and link the shared library (and, with
+    racecheck, the race-check library); returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(RACECHECK_BUILD, exist_ok=True)
+    write_rtc_sources()
+    t0 = time.time()
+    variants = [False, True] if racecheck else [False]
+    tasks = [(src, rc) for rc in variants for src in SOURCES]
+    jobs = jobs or min(len(tasks), os.cpu_count() or 4)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda t: _compile(*t), tasks))
+    _link(objs[:len(SOURCES)], OUT)
+    if racecheck:
+        _link(objs[len(SOURCES):], RACECHECK_OUT)
     if verbose:
-        print(f"built {OUT} in {time.time() - t0:.1f}s", file=sys.stderr)
+        print(f"built {OUT}" + (f" and {RACECHECK_OUT}" if racecheck else "") + f" in {time.time() - t0:.1f}s",
+              file=sys.stderr)
     return OUT
 
 

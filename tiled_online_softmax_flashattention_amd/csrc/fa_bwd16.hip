@@ -420,7 +420,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       barrier_lds();       // ... and every other wave's; tile n-1 is retired
     } else {
       wait_direct_loads();
-      __syncthreads();
+      sync_wg();
     }
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
     const int it = it_of(n);
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB, uint16_t* sKn, uint16_t* sVn,
                   float* sBn) __attribute__((always_inline)) {
     wait_direct_loads();   // this wave's loads of tile n are in LDS
-    __syncthreads();       // ... and every other wave's; tile n-1 is retired
+    sync_wg();       // ... and every other wave's; tile n-1 is retired
     if (n + 1 < ntiles) {
       load_tile_lds<D, BN, SW_BOTH>(Kg, kv_of(n + 1), Skv, sKn, wave, lane);
       load_tile_lds<D, BN, SW_BOTH>(Vg, kv_of(n + 1), Skv, sVn, wave, lane);

@@ -37,9 +37,9 @@ struct B32Cfg {
 template <int DS, bool TRAIL = true>
 __device__ __forceinline__ f32x16 slice_sum(f32x16 x, float* sS, int wave, int g, int lane) {
   slice_put(sS, x, wave, lane);
-  __syncthreads();
+  sync_wg();
   const f32x16 s = slice_gather<DS>(sS, g, lane);
-  if constexpr (TRAIL) __syncthreads();
+  if constexpr (TRAIL) sync_wg();
   return s;
 }
 
@@ -138,7 +138,7 @@ __device__ __forceinline__ void dkdv32_body(const AttnArgs& a) {
   }
   for (int n = 0; n < nvis; ++n) {
     const int q0 = (BLK ? list_at(sList, n) : qt0 + n) * BQ;
-    __syncthreads();
+    sync_wg();
     if constexpr (D * 4 % 1024 == 0) {   // head_dim 512: direct loads, one wait
       stage32_direct<D>(sQ, Qg, q0, Sq, wave, lane);
       stage32_direct<D>(sO, dOg, q0, Sq, wave, lane);
@@ -152,7 +152,7 @@ __device__ __forceinline__ void dkdv32_body(const AttnArgs& a) {
       sL[tid] = ok ? a.lse2[(size_t)bh * Sq + q0 + tid] : __builtin_inff();
       sDl[tid] = ok ? a.delta[(size_t)bh * Sq + q0 + tid] : 0.f;
     }
-    __syncthreads();
+    sync_wg();
     if (DS == 1 && CAUSAL && q0 + off + BQ - 1 < kw) continue;
 
     f32x16 s0 = zero16(), s1 = zero16(), p0 = zero16(), p1 = zero16();
@@ -352,7 +352,7 @@ __device__ __forceinline__ void dq32_body(const AttnArgs& a) {
       if constexpr (MASK) {
         if (tid < BN) sM[tid] = mb;
       }
-      __syncthreads();
+      sync_wg();
 #pragma unroll
       for (int kk = 0; kk < HS; kk += 4) {
         const f32x4 y = *(const f32x4*)(vrow + kk);
@@ -362,7 +362,7 @@ __device__ __forceinline__ void dq32_body(const AttnArgs& a) {
         p1 = mma_f32(y[3], of[kk + 3], p1);
       }
       wait_direct_loads();   // K_j landed
-      __syncthreads();       // and V_j is dead in every wave
+      sync_wg();       // and V_j is dead in every wave
       if (j + 1 < ntiles) stage32_direct<D, true>(sV, Vg, tile_kv(j + 1), Skv, wave, lane);
 #pragma unroll
       for (int kk = 0; kk < HS; kk += 4) {
@@ -373,14 +373,14 @@ __device__ __forceinline__ void dq32_body(const AttnArgs& a) {
         s1 = mma_f32(x[3], qf[kk + 3], s1);
       }
     } else {
-      __syncthreads();
+      sync_wg();
       rk.store(sK, tid);
       rv.store(sV, tid);
       if constexpr (MASK) {
         if (tid < BN) sM[tid] = mnext;
       }
       if (j + 1 < ntiles) fetch(tile_kv(j + 1));
-      __syncthreads();
+      sync_wg();
       if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
 #pragma unroll
       for (int kk = 0; kk < HS; kk += 4) {
@@ -440,7 +440,7 @@ __device__ __forceinline__ void dq32_body(const AttnArgs& a) {
       for (int dt = 0; dt < DT; ++dt) dq[dt] = mma_f32(krw[32 * dt], dp[t], dq[dt]);
     }
     if constexpr (PIPE) {
-      __syncthreads();   // K_j is dead in every wave
+      sync_wg();   // K_j is dead in every wave
       if (j + 1 < ntiles) stage32_direct<D, true>(sK, Kg, tile_kv(j + 1), Skv, wave, lane);
     }
   }

@@ -236,13 +236,35 @@ __device__ __forceinline__ void load_full_tile_lds(const uint16_t* g_row0, uint1
   }
 }
 
+// Race-check build (FA_DEBUG_BARRIERS): every workgroup barrier and every
+// wait for a wave's loads first drains all of the wave's outstanding memory
+// operations (vector loads and stores, direct loads into LDS, LDS accesses),
+// so nothing is in flight across a barrier.  The arithmetic is unchanged, so
+// results that differ from the normal build's mean that some wave reads LDS
+// before its writer (another wave, or its own load in flight) has finished.
+#ifdef FA_DEBUG_BARRIERS
+__device__ __forceinline__ void debug_drain() { __builtin_amdgcn_s_waitcnt(0); }
+#else
+__device__ __forceinline__ void debug_drain() {}
+#endif
+
+// Workgroup barrier with the release and acquire fences of __syncthreads.
+__device__ __forceinline__ void sync_wg() {
+  debug_drain();
+  __syncthreads();
+}
+
 // Wait until this wave's direct loads have landed (vmcnt(0)).
-__device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+__device__ __forceinline__ void wait_direct_loads() {
+  debug_drain();
+  __builtin_amdgcn_s_waitcnt(0x3f70);
+}
 // Wait until at most N (<= 63) of this wave's vector memory operations are in
 // flight (they complete in issue order, so the older ones have).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_le() {
   static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  debug_drain();
   __builtin_amdgcn_s_waitcnt(0x3f70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vmcnt_le16() { wait_vmcnt_le<16>(); }
@@ -253,6 +275,7 @@ __device__ __forceinline__ void wait_vmcnt_le16() { wait_vmcnt_le<16>(); }
 // loads still in flight; a caller that needs its direct loads in LDS waits
 // for them (vmcnt) first.
 __device__ __forceinline__ void barrier_lds() {
+  debug_drain();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -265,6 +288,7 @@ __device__ __forceinline__ void barrier_lds() {
 // clobber keeps the compiler from moving memory accesses across it.  The
 // caller must not read the buffers those loads write before waiting for them.
 __device__ __forceinline__ void barrier_lds_loads_in_flight() {
+  debug_drain();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -479,7 +503,7 @@ __device__ __forceinline__ int compact_tiles(const uint8_t* bytes, int stride, i
     const uint64_t bal = __builtin_amdgcn_ballot_w64(vis);
     const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
     if (lane == 0) cnt4[wave] = __builtin_popcountll(bal);
-    __syncthreads();
+    sync_wg();
     int before = total, sum = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -489,7 +513,7 @@ __device__ __forceinline__ int compact_tiles(const uint8_t* bytes, int stride, i
     }
     if (vis) list[before + below] = (uint16_t)t;
     total = __builtin_amdgcn_readfirstlane(total + sum);
-    __syncthreads();
+    sync_wg();
   }
   return total;
 }

@@ -162,7 +162,7 @@ __device__ __forceinline__ void fwd_custom(const AttnArgs& a) {
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const uint8_t* sM, uint16_t* sKn, uint16_t* sVn,
                   uint8_t* sMn) __attribute__((always_inline)) {
     wait_direct_loads();
-    __syncthreads();
+    sync_wg();
     if (n + 1 < ntiles) load_tile(kv_of(n + 1), sKn, sVn, sMn);
     if (qw < Sq) {
       const int kv0 = kv_of(n);
@@ -318,7 +318,7 @@ __device__ __forceinline__ void dq_custom(const AttnArgs& a) {
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const uint8_t* sM, uint16_t* sKn, uint16_t* sVn,
                   uint8_t* sMn) __attribute__((always_inline)) {
     wait_direct_loads();
-    __syncthreads();
+    sync_wg();
     if (n + 1 < ntiles) load_tile(kv_of(n + 1), sKn, sVn, sMn);
     const int kv0 = kv_of(n);
     half(kv0, 0, sK, sV, sM);
@@ -476,7 +476,7 @@ __device__ __forceinline__ void dkdv_custom(const AttnArgs& a) {
   auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
                   uint16_t* sOn, float* sLn, float* sDn) __attribute__((always_inline)) {
     wait_direct_loads();
-    __syncthreads();
+    sync_wg();
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
     const int it = it_of(n);
     half(it, 0, sQ, sO, sL, sD);

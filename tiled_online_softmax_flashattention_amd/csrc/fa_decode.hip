@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const AttnArgs a) {
       sPart[wave][D + 1] = st.l;
     }
   }
-  __syncthreads();
+  sync_wg();
   if (wave == 0 && grp == 0) {
     for (int w2 = 1; w2 < 4; ++w2) {
       float acc2[EPL];

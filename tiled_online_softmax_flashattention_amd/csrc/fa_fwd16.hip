@@ -339,7 +339,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB,
                   uint16_t* sKn, uint16_t* sVn, float* sBn) __attribute__((always_inline)) {
     wait_direct_loads();                   // this wave's loads of tile n are in LDS
-    __syncthreads();                       // ... and every other wave's; tile n-1 is retired
+    sync_wg();                       // ... and every other wave's; tile n-1 is retired
     if (n + 1 < ntiles) {
       load_tile(kv_of(n + 1), sKn, sVn);
       store_m(sBn);

@@ -143,7 +143,7 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   }
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = tile_kv(j);
-    __syncthreads();   // every wave is done with tile j-1 (its P V read V)
+    sync_wg();   // every wave is done with tile j-1 (its P V read V)
     if constexpr (PIPE) {
       uint8_t mb = 0;
       if constexpr (MASK) {   // issued before V_j, so the wait below covers it
@@ -168,7 +168,7 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
     if constexpr (MASK && !PIPE) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
     }
-    __syncthreads();
+    sync_wg();
     if (DS == 1 && CAUSAL && kv0 > qwp + 31) continue;
 
     f32x16 s0 = zero16(), s1 = zero16();
@@ -184,7 +184,7 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
     f32x16 s = s0 + s1;
     if constexpr (DS > 1) {
       slice_put(sS, s, wave, lane);
-      __syncthreads();   // every wave's partial scores are in: K_j is dead
+      sync_wg();   // every wave's partial scores are in: K_j is dead
       if constexpr (PIPE) {
         if (j + 1 < ntiles) stage32_direct<D, true>(sK, Kg, tile_kv(j + 1), Skv, wave, lane);
       }
@@ -240,7 +240,7 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
     if constexpr (PIPE) {   // V_j landed (K_{j+1} may be in flight) in every wave
       if (j + 1 < ntiles) wait_vmcnt_le16();
       else wait_direct_loads();
-      __syncthreads();
+      sync_wg();
     }
 
     // O^T += V^T P^T: step t pairs register t of the probabilities (key

@@ -87,7 +87,11 @@ std::vector<char> rtc_compile(const std::string& unit, const std::string& arch, 
   const std::string arch_opt = "--offload-arch=" + arch;
   // no packed fp32 VALU instructions, as in the library's own build
   const char* opts[] = {arch_opt.c_str(), "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-                        "-packed-fp32-ops"};
+                        "-packed-fp32-ops",
+#ifdef FA_DEBUG_BARRIERS
+                        "-DFA_DEBUG_BARRIERS",   // the race-check library's kernels drain at every barrier
+#endif
+  };
   const hiprtcResult r = hiprtcCompileProgram(prog, (int)(sizeof(opts) / sizeof(opts[0])), opts);
   size_t n = 0;
   hiprtcGetProgramLogSize(prog, &n);
