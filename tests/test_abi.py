@@ -38,6 +38,12 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     assert set(_lib.SIGNATURES) == declared_functions()
+    # the race-check build (FA_DEBUG_BARRIERS) exports the same interface
+    rc = ctypes.CDLL(os.path.join(os.path.dirname(_lib.LIB_PATH), "libfa_mi355x_racecheck.so"))
+    for name in declared_functions():
+        assert hasattr(rc, name), name
+    rc.fa_abi_version.restype = ctypes.c_int
+    assert rc.fa_abi_version() == _lib.FA_ABI_VERSION
 
 
 def test_abi_version_and_status_strings():
