@@ -173,11 +173,35 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
                   256);
 }
 
-// Workgroups of the forward resident on the device at once (256 CUs times
-// the workgroups per CU that the kernel's registers allow).
+// Compute units of the current device (MI355X: 256; fewer in a partitioned
+// mode), read once per device; 256 when no device answers (host-only use of
+// the workspace queries).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Workgroups of the forward resident on the device at once: its CUs times
+// the workgroups per CU that the kernel's registers allow.
 int64_t forward_slots(const fa_problem* p) {
-  if (p->dtype == FA_F32) return 256;
-  return p->head_dim == 64 ? 3 * 256 : 2 * 256;
+  const int64_t cus = device_cus();
+  if (p->dtype == FA_F32) return cus;
+  return p->head_dim == 64 ? 3 * cus : 2 * cus;
 }
 
 // Per-shape table of fa_forward_split (kv_splits = 0): how many key chunks,
