@@ -18,6 +18,29 @@ constexpr int64_t kMaxI32 = 2147483647;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Compute units of the current device (MI355X: 256; fewer in a partitioned
+// mode), read once per device; 256 when no device answers (host-only use of
+// the workspace queries).
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool head_dim_supported(int32_t dtype, int64_t d) {
@@ -165,35 +188,12 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
     const int len = decode_kv_len(p);
     *chunk = (len + p->kv_splits - 1) / p->kv_splits;
   } else {
-    *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk);
+    *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk, device_cus());
   }
   if (p->seq_q > 1 || p->mod_kind == FA_MOD_CUSTOM) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
   *n_split = (decode_kv_len(p) + *chunk - 1) / *chunk;
   return round_up((size_t)BH * (size_t)p->seq_q * (size_t)(*n_split) * (size_t)(p->head_dim + 2) * sizeof(float),
                   256);
-}
-
-// Compute units of the current device (MI355X: 256; fewer in a partitioned
-// mode), read once per device; 256 when no device answers (host-only use of
-// the workspace queries).
-int device_cus() {
-  static std::mutex mu;
-  static int cus[64] = {};
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return 256;
-  }
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cus[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-      (void)hipGetLastError();
-      n = 256;
-    }
-    cus[dev] = n;
-  }
-  return cus[dev];
 }
 
 // Workgroups of the forward resident on the device at once: its CUs times

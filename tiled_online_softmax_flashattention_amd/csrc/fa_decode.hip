@@ -341,11 +341,12 @@ hipError_t launch_split_merge(const AttnArgs& a, int dtype, int D, int rows, hip
   return launch_split_merge_t<F16>(a, D, rows, st);
 }
 
-int decode_choose_split(int BH, int Skv, int* chunk) {
-  // Aim for about 512 workgroups in total (two per CU; longer streams per
-  // workgroup measured faster than more, shorter chunks), with chunks of
-  // 256 .. 4096 keys (a multiple of 64 keys).
-  long long c = ((long long)Skv * BH + 511) / 512;
+int decode_choose_split(int BH, int Skv, int* chunk, int cus) {
+  // Aim for about two workgroups per CU in total (512 on MI355X; longer
+  // streams per workgroup measured faster than more, shorter chunks), with
+  // chunks of 256 .. 4096 keys (a multiple of 64 keys).
+  const long long wgs = 2LL * (cus > 0 ? cus : 256);
+  long long c = ((long long)Skv * BH + wgs - 1) / wgs;
   c = (c + 63) / 64 * 64;
   if (c < 256) c = 256;
   if (c > 4096) c = 4096;

@@ -41,7 +41,7 @@ hipError_t launch_bwd32(const AttnArgs& a, int D, int mod, bool causal, bool mas
                         hipStream_t st);
 
 // Split-KV decode and the merge of the partial (max, sum, accumulator).
-int decode_choose_split(int BH, int Skv, int* chunk);
+int decode_choose_split(int BH, int Skv, int* chunk, int cus);   // cus: the device's compute units
 hipError_t launch_decode(const AttnArgs& a, int dtype, int D, int mod, bool mask, hipStream_t st);
 // Merge of `rows` partial rows (a.n_split chunks each) into O and lse rows.
 hipError_t launch_decode_merge(const AttnArgs& a, int dtype, int D, int rows, hipStream_t st);
