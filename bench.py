@@ -70,12 +70,20 @@ def settle(fn, seconds: float, torch) -> int:
     return n
 
 
+COMMON_HEADER = "tiled_online_softmax_flashattention_amd/csrc/fa_common.hpp"
+
+
 def source_sha(path: str) -> str:
-    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()
+    """sha256 over a kernel's source file followed by the device header that
+    every kernel file includes."""
+    h = hashlib.sha256()
+    for p in (path, COMMON_HEADER):
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
 
 
 SOURCES = {"fwd16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
-           "dq16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
+           "dq16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_dq16.hip",
            "dkdv16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
            "bwd_pre_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
            "dq_convert_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd16.hip",
@@ -107,8 +115,9 @@ COPY_BYTES = 256 * 1024 * 1024    # the calibration copy of --counters
 #
 # The summaries under profiles/ come from rocprofv3 runs of this script and
 # are written by the summary modes below; each records the command that made
-# it and the sha256 of every kernel's source, and bench.py reports a figure
-# from them only while that source is unchanged.
+# it and the sha256 of every kernel's source (its file and the shared device
+# header), and bench.py reports a figure from them only while that source is
+# unchanged.
 
 
 def counters_pass() -> int:

@@ -73,6 +73,24 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
+// Registers 8u .. 8u+7 of a 32 x 32 accumulator rounded and packed: the
+// 16-bit operand fragment for keys (or queries) 16u .. 16u+15 of the block.
+template <class T>
+__device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
+  return u32x4{pack2<T>(x[8 * u + 0], x[8 * u + 1]), pack2<T>(x[8 * u + 2], x[8 * u + 3]),
+               pack2<T>(x[8 * u + 4], x[8 * u + 5]), pack2<T>(x[8 * u + 6], x[8 * u + 7])};
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Query tile of the 16-bit key/value pass.  The query pass, which runs
+// first, stores each row's lse2 with the query's ALiBi share relative to
+// this tile's start folded in.
+constexpr int kDkdvBQ = 64;
+
 template <class T>
 __device__ __forceinline__ float to_f32(uint16_t bits) {
   if constexpr (__is_same(T, F16)) {

@@ -49,10 +49,6 @@ namespace fa {
 
 constexpr float kSumLimit = 32768.0f;   // a half's row sum above this forces a max update
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
 // One 128-query block (qb) of one (batch, head) slice (bh).  With SPLIT the
 // block covers only key chunk `split` (a.chunk keys) and writes its
 // unnormalised partial (accumulator, running max, sum) to a.partial for the

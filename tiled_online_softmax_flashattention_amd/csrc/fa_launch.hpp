@@ -34,6 +34,9 @@ int bwd16_block_q();
 // pass (a.dq_acc, B*H*Sq*D floats) instead of the query pass.
 hipError_t launch_bwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
                         bool want_kv, bool want_q, bool dq_atomic, hipStream_t st);
+// The 16-bit dQ pass alone (separate mode; it also writes delta and lse2 for
+// the key/value pass).
+hipError_t launch_dq16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st);
 int bwd32_block_kv(int D);
 size_t bwd32_lds_bytes(int D, bool blk);   // dynamic LDS of either fp32 backward pass
 int bwd32_block_q(int D);
