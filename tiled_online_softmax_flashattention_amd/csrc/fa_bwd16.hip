@@ -288,15 +288,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       dpv = mma16<T>(lds_read16(sO + off), vf[kk], dpv);
     }
   };
-  // P = 0 for queries before the key (causal) and past seq_q, only on such halves
+  // P = 0 for queries before the key (causal), only on such halves.  Rows
+  // past seq_q need nothing here: their lse2 row entries are -inf (below).
   auto mask_scores = [&](int it, int mt, f32x16& sv) __attribute__((always_inline)) {
-    const int qs = it * BQ + 32 * mt;   // first query of the half
-    if (__builtin_amdgcn_ballot_w64((CAUSAL && qs + off < kj) || qs + 31 >= Sq) != 0) {
-      const int ql = qs + 4 * hi;   // query of register r: ql + 8 (r / 4) + r % 4
+    if constexpr (CAUSAL) {
+      const int qs = it * BQ + 32 * mt;   // first query of the half
+      if (__builtin_amdgcn_ballot_w64(qs + off < kj) != 0) {
+        const int ql = qs + 4 * hi;   // query of register r: ql + 8 (r / 4) + r % 4
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = ql + 8 * (r >> 2) + (r & 3);
-        if ((CAUSAL && q + off < kj) || q >= Sq) sv[r] = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int q = ql + 8 * (r >> 2) + (r & 3);
+          if (q + off < kj) sv[r] = kNegInf;
+        }
       }
     }
   };
@@ -390,59 +393,80 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
   };
 
+  // Both halves of a tile at head_dim 128.  In-order issue: the second
+  // half's score products and the first half's probabilities share one
+  // region, scheduled as MFMA / VALU alternation, and likewise the first
+  // half's dV, dK products and the second half's probabilities.  Without
+  // the causal rule nothing is masked here (rows past seq_q arrive masked
+  // in their lse2 row), so the whole schedule is straight-line code.
+  auto paired = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
+                    __attribute__((always_inline)) {
+    f32x16 sv0, dp0, sv1, dp1;
+    u32x4 pb0[2], db0[2], pb1[2], db1[2];
+    scores(0, sQ, sO, sL, sD, sv0, dp0);
+    if constexpr (!CAUSAL) {
+      // 8 row reads and 2 KS fragment reads feed 2 KS MFMAs: 12 reads up
+      // front, then one read ahead of each MFMA (the causal instances, at
+      // the 512-register limit, measured slower with it)
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {
+        if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      }
+    }
+    mask_scores(it, 0, sv0);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(1, sQ, sO, sL, sD, sv1, dp1);
+    probs(it, sv0, dp0, pb0, db0);
+    // the same reads, here with the first half's probabilities between the MFMAs
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mask_scores(it, 1, sv1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(0, pb0, db0, sQ, sO);
+    probs(it, sv1, dp1, pb1, db1);
+    // 2 transposing reads per MFMA: 8 up front, then 2 ahead of each MFMA
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      if (i < 4 * DT - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    products(1, pb1, db1, sQ, sO);
+  };
+
   // Visit n in the buffers of its parity; visit n+1 is requested into the
   // other buffers right after the barrier that retires visit n-1.
-  auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD, uint16_t* sQn,
+  auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, float* sL, const float* sD, uint16_t* sQn,
                   uint16_t* sOn, float* sLn, float* sDn) __attribute__((always_inline)) {
+    const int it = it_of(n);
     // this wave's loads of tile n are in LDS; in the atomic dQ mode the NA
     // atomics of tile n-1, issued after those loads, may still be in flight
     // (vector memory operations complete in issue order)
     if constexpr (DQA) {
       if (n == n0) wait_direct_loads();
       else wait_vmcnt_le<16 * NT>();
-      barrier_lds();       // ... and every other wave's; tile n-1 is retired
     } else {
       wait_direct_loads();
-      sync_wg();
     }
+    // Rows past seq_q (clamped copies of the last row) get -inf in place of
+    // -lse2 / c, so their P and dS are 0 without a per-score mask; wave 0,
+    // which loaded the row, writes it before the barrier publishes it.
+    if (wave == 0 && it * BQ + BQ > Sq && it * BQ + lane >= Sq) sL[lane] = kNegInf;
+    if constexpr (DQA) barrier_lds();   // ... and every other wave's; tile n-1 is retired
+    else sync_wg();
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
-    const int it = it_of(n);
     if (PAIRED && half_runs(it, 0) && half_runs(it, 1)) {
-      // In-order issue: the second half's score products and the first
-      // half's probabilities share one straight-line region, scheduled as
-      // MFMA / VALU alternation, and likewise the first half's dV, dK
-      // products and the second half's probabilities.
-      f32x16 sv0, dp0, sv1, dp1;
-      u32x4 pb0[2], db0[2], pb1[2], db1[2];
-      scores(0, sQ, sO, sL, sD, sv0, dp0);
-      mask_scores(it, 0, sv0);
-      __builtin_amdgcn_sched_barrier(0);
-      scores(1, sQ, sO, sL, sD, sv1, dp1);
-      probs(it, sv0, dp0, pb0, db0);
-      // 8 row reads and 2 KS fragment reads feed 2 KS MFMAs: the first 12
-      // reads up front, then one read ahead of each MFMA
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mask_scores(it, 1, sv1);
-      __builtin_amdgcn_sched_barrier(0);
-      products(0, pb0, db0, sQ, sO);
-      probs(it, sv1, dp1, pb1, db1);
-      // 2 transposing reads per MFMA: 8 up front, then 2 ahead of each MFMA
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 4 * DT; ++i) {
-        if (i < 4 * DT - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      products(1, pb1, db1, sQ, sO);
+      paired(it, sQ, sO, sL, sD);
     } else {
       half(it, 0, sQ, sO, sL, sD);
       __builtin_amdgcn_sched_barrier(0);   // the halves share registers
