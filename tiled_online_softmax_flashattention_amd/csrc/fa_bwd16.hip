@@ -192,6 +192,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       vf[kk] = *(const u32x4*)(Vg + off + 16 * kk);
     }
   }
+  if constexpr (D == 128 && !DQA) {   // one wave per SIMD: K and V fragments in AGPRs
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      keep_in_agprs(kf[kk]);
+      keep_in_agprs(vf[kk]);
+    }
+  }
   if constexpr (DQA) {   // K rows of the workgroup for the dQ products (visible after the first barrier)
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) lds_write16(sKd + tile_off<D, SW_TR>(32 * wave + l32, 16 * kk + 8 * hi), kf[kk]);

@@ -81,6 +81,13 @@ __device__ __forceinline__ u32x4 pack8(const f32x16& x, int u) {
                pack2<T>(x[8 * u + 4], x[8 * u + 5]), pack2<T>(x[8 * u + 6], x[8 * u + 7])};
 }
 
+// Place a loop-invariant MFMA operand in the accumulation registers (AGPRs).
+// MFMA reads its A and B operands from either register file; at one wave per
+// SIMD the accumulation file has room that the architectural one, holding
+// the addresses and the softmax arithmetic, lacks.  (An empty asm statement
+// with an AGPR operand: no instruction of its own.)
+__device__ __forceinline__ void keep_in_agprs(u32x4& x) { asm volatile("" : "+a"(x)); }
+
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;

@@ -100,6 +100,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     }
   }
 
+  if constexpr (D == 128) {   // one wave per SIMD: Q and dO fragments in AGPRs
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      keep_in_agprs(qf[kk]);
+      keep_in_agprs(of[kk]);
+    }
+  }
+
   float slope2 = 0.f;
   f32x16 cinit = zero16();
   if constexpr (MOD == MOD_ALIBI) {
