@@ -295,6 +295,47 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       dpv = mma16<T>(lds_read16(sO + off), vf[kk], dpv);
     }
   };
+  // The same products with the fragment reads software-pipelined by hand:
+  // the rows and the first AHEAD fragment pairs are requested up front, then
+  // each step's two MFMAs are followed by the reads of the pair AHEAD steps
+  // later (scheduling barriers keep the order, so AHEAD pairs stay in
+  // flight in registers of their own).
+  auto scores_pipelined = [&](int mt, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD,
+                              f32x16& sv, f32x16& dpv) __attribute__((always_inline)) {
+    constexpr int AHEAD = 4;
+    const float* lrow = sL + 32 * mt + 4 * hi;
+    const float* drow = sD + 32 * mt + 4 * hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
+      const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        sv[4 * u + cc] = l4[cc];
+        dpv[4 * u + cc] = d4[cc];
+      }
+    }
+    const int qr = 32 * mt + l32;
+    u32x4 fq[KS], fo[KS];
+#pragma unroll
+    for (int kk = 0; kk < AHEAD; ++kk) {
+      const int o = tile_off<D, SW_BOTH>(qr, 16 * kk + 8 * hi);
+      fq[kk] = lds_read16(sQ + o);
+      fo[kk] = lds_read16(sO + o);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      sv = mma16<T>(fq[kk], kf[kk], sv);
+      dpv = mma16<T>(fo[kk], vf[kk], dpv);
+      if (kk + AHEAD < KS) {
+        const int o = tile_off<D, SW_BOTH>(qr, 16 * (kk + AHEAD) + 8 * hi);
+        fq[kk + AHEAD] = lds_read16(sQ + o);
+        fo[kk + AHEAD] = lds_read16(sO + o);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // P = 0 for queries before the key (causal), only on such halves.  Rows
   // past seq_q need nothing here: their lse2 row entries are -inf (below).
   auto mask_scores = [&](int it, int mt, f32x16& sv) __attribute__((always_inline)) {
@@ -400,28 +441,125 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
   };
 
-  // Both halves of a tile at head_dim 128.  In-order issue: the second
-  // half's score products and the first half's probabilities share one
-  // region, scheduled as MFMA / VALU alternation, and likewise the first
-  // half's dV, dK products and the second half's probabilities.  Without
-  // the causal rule nothing is masked here (rows past seq_q arrive masked
-  // in their lse2 row), so the whole schedule is straight-line code.
+  // Both halves of a tile at head_dim 128 without the causal rule (nothing
+  // is masked: rows past seq_q arrive masked in their lse2 row), scheduled
+  // by hand as straight-line code.  Scheduling barriers fix the order; each
+  // MFMA's operands are requested AHEAD steps before it (a wait for LDS
+  // reads drains all of them while the tile loads are in flight, so the
+  // reads of later steps are issued after the MFMAs whose operands have
+  // arrived), and the VALU work of the other half sits between the MFMAs.
+  auto paired_nc = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
+                       __attribute__((always_inline)) {
+    constexpr int AHEAD = 4;
+    f32x16 sv0, dp0, sv1, dp1;
+    u32x4 pb0[2], db0[2], pb1[2], db1[2];
+    scores_pipelined(0, sQ, sO, sL, sD, sv0, dp0);
+
+    float lb = key_ok ? 0.f : kNegInf;
+    if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ - off) : kNegInf;
+    const float lb0 = lb + cb0, lb1 = lb + cb1;
+    auto prob = [&](f32x16& sv, f32x16& dpv, int r) __attribute__((always_inline)) {
+      const float p = exp2_hw(fmaf(sv[r], c, (r & 1) ? lb1 : lb0));
+      sv[r] = p;
+      dpv[r] *= p;
+    };
+
+    // second half's score products, first half's probabilities between them
+    {
+      const float* lrow = sL + 32 + 4 * hi;
+      const float* drow = sD + 32 + 4 * hi;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 l4 = *(const f32x4*)(lrow + 8 * u);
+        const f32x4 d4 = *(const f32x4*)(drow + 8 * u);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          sv1[4 * u + cc] = l4[cc];
+          dp1[4 * u + cc] = d4[cc];
+        }
+      }
+      const int qr = 32 + l32;
+      u32x4 fq[KS], fo[KS];
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk) {
+        const int o = tile_off<D, SW_BOTH>(qr, 16 * kk + 8 * hi);
+        fq[kk] = lds_read16(sQ + o);
+        fo[kk] = lds_read16(sO + o);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        sv1 = mma16<T>(fq[kk], kf[kk], sv1);
+        dp1 = mma16<T>(fo[kk], vf[kk], dp1);
+        if (kk + AHEAD < KS) {
+          const int o = tile_off<D, SW_BOTH>(qr, 16 * (kk + AHEAD) + 8 * hi);
+          fq[kk + AHEAD] = lds_read16(sQ + o);
+          fo[kk + AHEAD] = lds_read16(sO + o);
+        }
+        prob(sv0, dp0, 2 * kk);
+        prob(sv0, dp0, 2 * kk + 1);
+        if (kk == 3 || kk == 7) {
+          pb0[kk >> 2] = pack8<T>(sv0, kk >> 2);
+          db0[kk >> 2] = pack8<T>(dp0, kk >> 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS: MFMA i of a half uses the
+    // transposed fragment of query step u = i / (2 DT), dims 32 dt (dt =
+    // (i / 2) % DT), of dO (i even, for dV) or Q (i odd, for dK)
+    constexpr int NP = 4 * DT;
+    auto pfrag = [&](int mt, int i) __attribute__((always_inline)) {
+      const int u = i / (2 * DT), dt = (i / 2) % DT;
+      return read_a_tr_tile<D, SW_BOTH>((i & 1) ? sQ : sO, 32 * mt + 16 * u, 32 * dt, lane);
+    };
+    auto pmma = [&](int i, u32x4 af, const u32x4* pb, const u32x4* db) __attribute__((always_inline)) {
+      const int u = i / (2 * DT), dt = (i / 2) % DT;
+      if (i & 1) dk[dt] = mma16<T>(af, db[u], dk[dt]);
+      else dv[dt] = mma16<T>(af, pb[u], dv[dt]);
+    };
+    // first half's products, second half's probabilities between them
+    {
+      u32x4 af[NP];
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) af[i] = pfrag(0, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        pmma(i, af[i], pb0, db0);
+        if (i + AHEAD < NP) af[i + AHEAD] = pfrag(0, i + AHEAD);
+        prob(sv1, dp1, i);
+        if (i == 7 || i == 15) {
+          pb1[i >> 3] = pack8<T>(sv1, i >> 3);
+          db1[i >> 3] = pack8<T>(dp1, i >> 3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // second half's products
+    {
+      u32x4 af[NP];
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) af[i] = pfrag(1, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        pmma(i, af[i], pb1, db1);
+        if (i + AHEAD < NP) af[i + AHEAD] = pfrag(1, i + AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  // Both halves of a causal tile at head_dim 128.  In-order issue: the
+  // second half's score products and the first half's probabilities share
+  // one region, scheduled as MFMA / VALU alternation, and likewise the first
+  // half's dV, dK products and the second half's probabilities.
   auto paired = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
                     __attribute__((always_inline)) {
     f32x16 sv0, dp0, sv1, dp1;
     u32x4 pb0[2], db0[2], pb1[2], db1[2];
     scores(0, sQ, sO, sL, sD, sv0, dp0);
-    if constexpr (!CAUSAL) {
-      // 8 row reads and 2 KS fragment reads feed 2 KS MFMAs: 12 reads up
-      // front, then one read ahead of each MFMA (the causal instances, at
-      // the 512-register limit, measured slower with it)
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * KS; ++i) {
-        if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      }
-    }
     mask_scores(it, 0, sv0);
     __builtin_amdgcn_sched_barrier(0);
     scores(1, sQ, sO, sL, sD, sv1, dp1);
@@ -472,7 +610,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     if constexpr (DQA) barrier_lds();   // ... and every other wave's; tile n-1 is retired
     else sync_wg();
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
-    if (PAIRED && half_runs(it, 0) && half_runs(it, 1)) {
+    if (PAIRED && !CAUSAL) {
+      paired_nc(it, sQ, sO, sL, sD);
+    } else if (PAIRED && half_runs(it, 0) && half_runs(it, 1)) {
       paired(it, sQ, sO, sL, sD);
     } else {
       half(it, 0, sQ, sO, sL, sD);
