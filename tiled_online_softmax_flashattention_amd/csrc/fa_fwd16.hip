@@ -216,7 +216,23 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
         for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] = MOD == MOD_ALIBI ? cinit[4 * u + cc] + m4[cc] : m4[cc];
       }
     }
-    {
+    if constexpr (D == 128) {
+      // software-pipelined by hand: 4 fragments up front, then each MFMA
+      // followed by the read 4 steps ahead (scheduling barriers keep the
+      // order)
+      constexpr int AHEAD = 4;
+      const int kr = 32 * t + l32;
+      u32x4 kfr[QS];
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk) kfr[kk] = lds_read16(sK + tile_off<D, SW_BOTH>(kr, 16 * kk + 8 * hi));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < QS; ++kk) {
+        s = mma16<T>(kfr[kk], qf[kk], s);
+        if (kk + AHEAD < QS) kfr[kk + AHEAD] = lds_read16(sK + tile_off<D, SW_BOTH>(kr, 16 * (kk + AHEAD) + 8 * hi));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
       // every K fragment is requested (into its own registers) before the
       // first MFMA, so the LDS latency is paid once per half, not per MFMA
       const int kr = 32 * t + l32;
@@ -247,7 +263,10 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   // Keys 32t .. 32t+31 of tile n, held in (sK, sV, sB).
   auto half = [&](int n, int t, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
     const int k0 = kv_of(n) + 32 * t;   // first key of the half
-    if (CAUSAL && k0 > qwp + 31) return;   // every key follows every query of this wave
+    // every key follows every query of this wave: nothing to add (at head_dim
+    // 128 the half still runs, masked to P = 0: the early exit costs the
+    // causal instances more registers than they have)
+    if (CAUSAL && D == 64 && k0 > qwp + 31) return;
 
     f32x16 s = scores(t, k0, sK, sB);
     // per-lane exponent offset (ALiBi: bias of the half's first key)
