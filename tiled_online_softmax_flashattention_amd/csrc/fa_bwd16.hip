@@ -268,8 +268,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   // atomic dQ mode the half still runs, masked to P = 0, so its dS^T rows
   // of the LDS tile are zeros; such halves occur only in a key block's
   // first query tile)
+  // (at head_dim 128 every half runs: the paired schedule below has no room
+  // for a per-wave exit, whose registers spilled; the skipped halves are a
+  // few per key block)
   auto half_runs = [&](int it, int mt) __attribute__((always_inline)) {
-    return DQA || !CAUSAL || it * BQ + 32 * mt + off + 31 >= kw;
+    return DQA || !CAUSAL || D == 128 || it * BQ + 32 * mt + off + 31 >= kw;
   };
   // S' = Q K^T - lse2 / c and dP' = dO V^T - delta, queries as rows: the
   // accumulators start from the rows' stored values
@@ -441,19 +444,23 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     }
   };
 
-  // Both halves of a tile at head_dim 128 without the causal rule (nothing
-  // is masked: rows past seq_q arrive masked in their lse2 row), scheduled
-  // by hand as straight-line code.  Scheduling barriers fix the order; each
-  // MFMA's operands are requested AHEAD steps before it (a wait for LDS
-  // reads drains all of them while the tile loads are in flight, so the
-  // reads of later steps are issued after the MFMAs whose operands have
-  // arrived), and the VALU work of the other half sits between the MFMAs.
-  auto paired_nc = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
+  // Both halves of a tile at head_dim 128, scheduled by hand.  Scheduling
+  // barriers fix the order; each MFMA's operands are requested AHEAD steps
+  // before it (a wait for LDS reads drains all of them while the tile loads
+  // are in flight, so the reads of later steps are issued after the MFMAs
+  // whose operands have arrived), and the VALU work of the other half sits
+  // between the MFMAs: the second half's score products beside the first
+  // half's probabilities, the first half's dV, dK products beside the
+  // second half's.  The causal masking runs between the regions (rows past
+  // seq_q arrive masked in their lse2 row).
+  auto paired = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
                        __attribute__((always_inline)) {
     constexpr int AHEAD = 4;
     f32x16 sv0, dp0, sv1, dp1;
     u32x4 pb0[2], db0[2], pb1[2], db1[2];
     scores_pipelined(0, sQ, sO, sL, sD, sv0, dp0);
+    mask_scores(it, 0, sv0);
+    __builtin_amdgcn_sched_barrier(0);
 
     float lb = key_ok ? 0.f : kNegInf;
     if constexpr (MOD == MOD_ALIBI) lb = key_ok ? slope2 * (float)(kj - it * BQ - off) : kNegInf;
@@ -506,6 +513,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       }
     }
 
+    mask_scores(it, 1, sv1);
+    __builtin_amdgcn_sched_barrier(0);
+
     // dV^T += dO^T P and dK^T += Q^T dS: MFMA i of a half uses the
     // transposed fragment of query step u = i / (2 DT), dims 32 dt (dt =
     // (i / 2) % DT), of dO (i even, for dV) or Q (i odd, for dK)
@@ -551,44 +561,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
       }
     }
   };
-  // Both halves of a causal tile at head_dim 128.  In-order issue: the
-  // second half's score products and the first half's probabilities share
-  // one region, scheduled as MFMA / VALU alternation, and likewise the first
-  // half's dV, dK products and the second half's probabilities.
-  auto paired = [&](int it, const uint16_t* sQ, const uint16_t* sO, const float* sL, const float* sD)
-                    __attribute__((always_inline)) {
-    f32x16 sv0, dp0, sv1, dp1;
-    u32x4 pb0[2], db0[2], pb1[2], db1[2];
-    scores(0, sQ, sO, sL, sD, sv0, dp0);
-    mask_scores(it, 0, sv0);
-    __builtin_amdgcn_sched_barrier(0);
-    scores(1, sQ, sO, sL, sD, sv1, dp1);
-    probs(it, sv0, dp0, pb0, db0);
-    // the same reads, here with the first half's probabilities between the MFMAs
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      if (i < 2 * KS + 8 - 12) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mask_scores(it, 1, sv1);
-    __builtin_amdgcn_sched_barrier(0);
-    products(0, pb0, db0, sQ, sO);
-    probs(it, sv1, dp1, pb1, db1);
-    // 2 transposing reads per MFMA: 8 up front, then 2 ahead of each MFMA
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
-      if (i < 4 * DT - 4) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 3, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    products(1, pb1, db1, sQ, sO);
-  };
-
   // Visit n in the buffers of its parity; visit n+1 is requested into the
   // other buffers right after the barrier that retires visit n-1.
   auto tile = [&](int n, const uint16_t* sQ, const uint16_t* sO, float* sL, const float* sD, uint16_t* sQn,
@@ -610,9 +582,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     if constexpr (DQA) barrier_lds();   // ... and every other wave's; tile n-1 is retired
     else sync_wg();
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
-    if (PAIRED && !CAUSAL) {
-      paired_nc(it, sQ, sO, sL, sD);
-    } else if (PAIRED && half_runs(it, 0) && half_runs(it, 1)) {
+    if (PAIRED) {
       paired(it, sQ, sO, sL, sD);
     } else {
       half(it, 0, sQ, sO, sL, sD);
