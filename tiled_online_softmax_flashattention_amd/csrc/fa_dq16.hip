@@ -254,6 +254,146 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   // are computed (as in the key/value pass).
   constexpr bool PAIRED = D == 128;
 
+  // Both halves of a causal tile at head_dim 128, scheduled by hand (the
+  // non-causal instances measured 2 % faster with the compiler's schedule
+  // of the plain sequence below, which has no per-half branch for them).
+  // Scheduling barriers fix the order; each MFMA's operands are requested AHEAD steps
+  // before it (a wait for LDS reads drains all of them while the tile loads
+  // are in flight, so the reads of later steps are issued after the MFMAs
+  // whose operands have arrived), and the VALU work of the other half sits
+  // between the MFMAs: the second half's score products beside the first
+  // half's probabilities, the first half's dQ products beside the second
+  // half's.  Every half runs (a half wholly after the wave's queries is
+  // masked to P = 0): a per-wave exit costs registers this schedule lacks.
+  auto paired = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB) __attribute__((always_inline)) {
+    constexpr int AHEAD = 4;
+    f32x16 s0, dp0, s1, dp1;
+    auto start = [&](int t, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+      s = cinit;
+      dp = dneg;
+      if constexpr (MASK) {
+        const float* row = sB + ((qpos & 1) ? parity_row_off<BN>() : 0) + 32 * t + 4 * hi;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 m4 = *(const f32x4*)(row + 8 * u);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) s[4 * u + cc] = MOD == MOD_ALIBI ? cinit[4 * u + cc] + m4[cc] : m4[cc];
+        }
+      }
+    };
+    auto frag = [&](const uint16_t* tile, int t, int kk) __attribute__((always_inline)) {
+      return lds_read16(tile + tile_off<D, SW_BOTH>(32 * t + l32, 16 * kk + 8 * hi));
+    };
+    auto mask_half = [&](int t, f32x16& s) __attribute__((always_inline)) {
+      const int k0 = kv_of(n) + 32 * t;
+      int lim = 1 << 30;
+      if (CAUSAL && k0 + 31 > qwp) lim = qpos - k0;
+      if (!MASK && k0 + 32 > Skv) lim = min(lim, Skv - 1 - k0);
+      if (__builtin_amdgcn_ballot_w64(lim < 31) != 0) {
+        const int lim_l = lim - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pos = 8 * (r >> 2) + (r & 3);
+          if (pos > lim_l) s[r] = kNegInf;
+        }
+      }
+    };
+    auto nb_of = [&](int t) __attribute__((always_inline)) {
+      if constexpr (MOD == MOD_ALIBI) return slope2 * (float)(kv_of(n) + 32 * t - qpos) - lse2;
+      else return -lse2;
+    };
+    auto prob = [&](f32x16& s, f32x16& dp, float nb, int r) __attribute__((always_inline)) {
+      dp[r] *= exp2_hw(fmaf(s[r], c, nb));
+    };
+
+    // first half's score products
+    {
+      start(0, s0, dp0);
+      u32x4 kf[KS], vf[KS];
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk) {
+        kf[kk] = frag(sK, 0, kk);
+        vf[kk] = frag(sV, 0, kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s0 = mma16<T>(kf[kk], qf[kk], s0);
+        dp0 = mma16<T>(vf[kk], of[kk], dp0);
+        if (kk + AHEAD < KS) {
+          kf[kk + AHEAD] = frag(sK, 0, kk + AHEAD);
+          vf[kk + AHEAD] = frag(sV, 0, kk + AHEAD);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mask_half(0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    // second half's score products, first half's probabilities between them
+    {
+      const float nb0 = nb_of(0);
+      start(1, s1, dp1);
+      u32x4 kf[KS], vf[KS];
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk) {
+        kf[kk] = frag(sK, 1, kk);
+        vf[kk] = frag(sV, 1, kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s1 = mma16<T>(kf[kk], qf[kk], s1);
+        dp1 = mma16<T>(vf[kk], of[kk], dp1);
+        if (kk + AHEAD < KS) {
+          kf[kk + AHEAD] = frag(sK, 1, kk + AHEAD);
+          vf[kk + AHEAD] = frag(sV, 1, kk + AHEAD);
+        }
+        prob(s0, dp0, nb0, 2 * kk);
+        prob(s0, dp0, nb0, 2 * kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mask_half(1, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T += K^T dS^T: product i of a half uses key step u = i / DT and
+    // dims 32 (i % DT)
+    constexpr int NP = 2 * DT;
+    auto ktf = [&](int t, int i) __attribute__((always_inline)) {
+      return read_a_tr_tile<D, SW_BOTH>(sK, 32 * t + 16 * (i / DT), 32 * (i % DT), lane);
+    };
+    // first half's products, second half's probabilities between them
+    {
+      const float nb1 = nb_of(1);
+      const u32x4 db[2] = {pack8<T>(dp0, 0), pack8<T>(dp0, 1)};
+      u32x4 kt[NP];
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) kt[i] = ktf(0, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        dq[i % DT] = mma16<T>(kt[i], db[i / DT], dq[i % DT]);
+        if (i + AHEAD < NP) kt[i + AHEAD] = ktf(0, i + AHEAD);
+        prob(s1, dp1, nb1, 2 * i);
+        prob(s1, dp1, nb1, 2 * i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // second half's products
+    {
+      const u32x4 db[2] = {pack8<T>(dp1, 0), pack8<T>(dp1, 1)};
+      u32x4 kt[NP];
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) kt[i] = ktf(1, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        dq[i % DT] = mma16<T>(kt[i], db[i / DT], dq[i % DT]);
+        if (i + AHEAD < NP) kt[i + AHEAD] = ktf(1, i + AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   auto tile = [&](int n, const uint16_t* sK, const uint16_t* sV, const float* sB, uint16_t* sKn, uint16_t* sVn,
                   float* sBn) __attribute__((always_inline)) {
     wait_direct_loads();   // this wave's loads of tile n are in LDS
@@ -264,13 +404,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       store_m(sBn);
       load_m(kv_of(min(n + 2, ntiles - 1)));
     }
-    if constexpr (PAIRED) {
-      const bool r0 = half_runs(n, 0), r1 = half_runs(n, 1);
+    if constexpr (PAIRED && CAUSAL) {
+      paired(n, sK, sV, sB);
+    } else if constexpr (PAIRED) {   // both halves always run without the causal rule
       f32x16 s0, dp0, s1, dp1;
-      if (r0) scores(0, sK, sV, sB, s0, dp0);
-      if (r1) scores(1, sK, sV, sB, s1, dp1);
-      if (r0) finish(n, 0, s0, dp0, sK);
-      if (r1) finish(n, 1, s1, dp1, sK);
+      scores(0, sK, sV, sB, s0, dp0);
+      scores(1, sK, sV, sB, s1, dp1);
+      finish(n, 0, s0, dp0, sK);
+      finish(n, 1, s1, dp1, sK);
     } else {
       half(n, 0, sK, sV, sB);
       __builtin_amdgcn_sched_barrier(0);   // the halves share registers
