@@ -250,7 +250,7 @@ def test_decode_independent_of_split(gpu_lib):
     check_lse(l1, lse_ref)
 
 
-@pytest.mark.parametrize("dtype,Sq", [("f16", 1), ("bf16", 1), ("f32", 1), ("f16", 16), ("bf16", 16)])
+@pytest.mark.parametrize("dtype,Sq", [("f16", 1), ("bf16", 1), ("f32", 1), ("f16", 16), ("bf16", 16), ("f32", 16)])
 def test_decode_explicit_key_splits(gpu_lib, dtype, Sq):
     """The same decode split into 1, 2, 7 and the most (FA_MAX_KV_SPLITS
     requested) key chunks: every split against the oracle, and the splits
@@ -424,8 +424,8 @@ def test_decode_with_offset(gpu_lib, dtype, mod, off):
 # ------------------------------------------------------------------ short query blocks (split over keys)
 
 
-@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64)])
-@pytest.mark.parametrize("Sq,Skv", [(2, 300), (16, 5000), (33, 4100), (64, 700)])
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("Sq,Skv", [(2, 300), (16, 5000), (32, 2100), (33, 4100), (64, 700)])
 @pytest.mark.parametrize("causal,mod,mask", [(True, W.MOD_ALIBI, False), (True, W.MOD_NONE, True),
                                              (False, W.MOD_CHECKERBOARD, True), (False, W.MOD_NONE, False)])
 def test_decode_short_query_block(gpu_lib, dtype, D, Sq, Skv, causal, mod, mask):
