@@ -182,12 +182,15 @@ int decode_kv_len(const fa_problem* p) {
 
 // Split of the key axis and workspace bytes (one (D + 2)-float partial per
 // query row and chunk).
-// fp32 query blocks of at most 32 rows split over keys run one wave per
-// workgroup (the launcher's choice, mirrored here for the split sizes):
-// 8 such workgroups per CU at head_dim 64, 4 at 128 (their LDS).
-bool f32_short(const fa_problem* p) {
-  return p->dtype == FA_F32 && p->head_dim <= 128 && p->seq_q <= 32 && !p->block_mask &&
-         p->mod_kind != FA_MOD_CUSTOM;
+// fp32 query blocks of at most 64 rows split over keys run one wave per 32
+// rows in a workgroup (the launcher's choice, mirrored here for the split
+// sizes): 8 one-wave workgroups per CU at head_dim 64, 4 at 128 (their LDS),
+// 4 two-wave workgroups (registers at 64, LDS at 128).  Returns the
+// workgroups per CU, 0 outside that case.
+int f32_short(const fa_problem* p) {
+  if (p->dtype != FA_F32 || p->head_dim > 128 || p->seq_q > 64 || p->block_mask || p->mod_kind == FA_MOD_CUSTOM)
+    return 0;
+  return p->seq_q <= 32 && p->head_dim == 64 ? 8 : 4;
 }
 
 size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
@@ -196,9 +199,9 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
     const int len = decode_kv_len(p);
     *chunk = (len + p->kv_splits - 1) / p->kv_splits;
   } else {
-    // the chooser aims at two workgroups per CU; one-wave fp32 workgroups
-    // are a quarter (head_dim 64) or half (128) of one
-    const int scale = f32_short(p) ? (p->head_dim == 64 ? 4 : 2) : 1;
+    // the chooser aims at two workgroups per CU; of the small fp32 ones
+    // f32_short(p) fit a CU
+    const int scale = f32_short(p) ? f32_short(p) / 2 : 1;
     *n_split = fa::decode_choose_split(BH, decode_kv_len(p), chunk, device_cus() * scale);
   }
   if (p->seq_q > 1 || p->mod_kind == FA_MOD_CUSTOM) *chunk = (*chunk + 63) / 64 * 64;   // whole 64-key tiles of the forward
@@ -211,7 +214,7 @@ size_t decode_ws(const fa_problem* p, int* n_split, int* chunk) {
 // the workgroups per CU that the kernel's registers allow.
 int64_t forward_slots(const fa_problem* p) {
   const int64_t cus = device_cus();
-  if (f32_short(p)) return (p->head_dim == 64 ? 8 : 4) * cus;
+  if (f32_short(p)) return f32_short(p) * cus;
   if (p->dtype == FA_F32) return cus;
   return p->head_dim == 64 ? 3 * cus : 2 * cus;
 }

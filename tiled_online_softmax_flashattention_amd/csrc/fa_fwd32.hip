@@ -45,21 +45,21 @@ struct F32Cfg {
 // (accumulator, running max, sum) to a.partial for the decode merge.
 // MOD_CUSTOM: the caller's fa_score_mod on the scaled score (at head_dim 512
 // after the partial scores are summed), before the masks; compiled only at
-// run time with the caller's source.  ONE (split, head_dim <= 128, no block
-// mask): a workgroup of one wave and 32 queries, for query blocks of at most
-// 32 rows, whose other three waves would have no query; the device then holds
-// several such workgroups per CU.
-template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false, bool ONE = false>
+// run time with the caller's source.  WQ < 4 (split, head_dim <= 128, no
+// block mask): a workgroup of WQ waves and 32 WQ queries, for query blocks
+// of at most that many rows, whose other waves would have no query; the
+// device then holds several such workgroups per CU.
+template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT = false, int WQ = 4>
 __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   using C = F32Cfg<D>;
   constexpr int DS = C::DS, BN = C::BN, P = C::P;
-  constexpr int BM = ONE ? 32 : C::BM;
-  constexpr int NT = ONE ? 64 : 256;   // threads of the workgroup
+  constexpr int BM = WQ < 4 ? 32 * WQ : C::BM;
+  constexpr int NT = WQ < 4 ? 64 * WQ : 256;   // threads of the workgroup
   constexpr int DSL = D / DS;          // dims per slice
   constexpr int HS = DSL / 2;          // operand values per lane per product
   constexpr int DT = DSL / 32;         // 32-row tiles of the O^T slice
   constexpr int NCH = BN * D / 4 / NT;
-  static_assert(!ONE || (SPLIT && DS == 1 && !BLK), "one-wave workgroups: split, head_dim <= 128, dense");
+  static_assert(WQ == 4 || (SPLIT && DS == 1 && !BLK), "small workgroups: split, head_dim <= 128, dense");
 
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* sK = smem;
@@ -296,12 +296,12 @@ __global__ __launch_bounds__(256, 1) void fwd32_kernel(const AttnArgs a) {
   fwd32_body<D, MOD, CAUSAL, MASK, BLK, SPLIT>(a);
 }
 
-// Split forward of a query block of at most 32 rows: one wave per workgroup
-// (the second bound: waves per SIMD; 8 such workgroups fit a CU's LDS at
-// head_dim 64, 4 at 128).
-template <int D, int MOD, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(64, D == 64 ? 2 : 1) void fwd32_short_kernel(const AttnArgs a) {
-  fwd32_body<D, MOD, CAUSAL, MASK, false, true, true>(a);
+// Split forward of a query block of at most 32 WQ rows: WQ waves per
+// workgroup (the second bound: waves per SIMD; 8 such workgroups fit a CU's
+// LDS at head_dim 64, 4 at 128).
+template <int D, int MOD, bool CAUSAL, bool MASK, int WQ>
+__global__ __launch_bounds__(64 * WQ, D == 64 ? 2 : 1) void fwd32_short_kernel(const AttnArgs a) {
+  fwd32_body<D, MOD, CAUSAL, MASK, false, true, WQ>(a);
 }
 
 template <int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool SPLIT>
@@ -320,9 +320,12 @@ static hipError_t launch_one_blk(const AttnArgs& a, hipStream_t st) {
 template <int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t st) {
   if constexpr (SPLIT && D <= 128) {
-    if (!a.block_mask && a.Sq <= 32) {
+    if (!a.block_mask && a.Sq <= 64) {
       const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H) * (unsigned)a.n_split;
-      hipLaunchKernelGGL((fwd32_short_kernel<D, MOD, CAUSAL, MASK>), dim3(blocks), dim3(64), F32Cfg<D>::lds, st, a);
+      if (a.Sq <= 32)
+        hipLaunchKernelGGL((fwd32_short_kernel<D, MOD, CAUSAL, MASK, 1>), dim3(blocks), dim3(64), F32Cfg<D>::lds, st, a);
+      else
+        hipLaunchKernelGGL((fwd32_short_kernel<D, MOD, CAUSAL, MASK, 2>), dim3(blocks), dim3(128), F32Cfg<D>::lds, st, a);
       return hipGetLastError();
     }
   }
