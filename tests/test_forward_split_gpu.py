@@ -25,6 +25,10 @@ CASES = [
     ("f32", 64, True, W.MOD_ALIBI, False, False, 450, 450, 0, 3),
     ("f32", 128, False, W.MOD_NONE, True, True, 260, 700, 0, 4),
     ("f32", 64, True, W.MOD_CHECKERBOARD, True, False, 200, 900, 700, 6),
+    # query blocks of <= 32 and 33..64 rows: the one- and two-wave fp32 workgroups
+    ("f32", 64, False, W.MOD_ALIBI, True, False, 24, 3000, 0, 5),
+    ("f32", 128, True, W.MOD_NONE, False, False, 40, 5000, 4960, 7),
+    ("f32", 64, True, W.MOD_CHECKERBOARD, False, False, 64, 2000, 1936, 3),
 ]
 
 
