@@ -147,10 +147,41 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
   if constexpr (PIPE) {
     if (ntiles > 0) stage32_direct<D, true>(sK, Kg, tile_kv(0), Skv, wave, lane);
   }
+  // head_dim <= 128 with four waves: tile j+1 is read into registers while
+  // tile j is computed, and stored to LDS after the next barrier
+  constexpr bool PREF = !PIPE && WQ == 4;
+  f32x4 pk[PREF ? NCH : 1], pv[PREF ? NCH : 1];
+  uint8_t pmb = 0;
+  auto fetch = [&](int kv0) __attribute__((always_inline)) {
+    if constexpr (PREF) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        // rows past seq_kv: the last row (finite; its scores are masked to -inf)
+        const int c = tid + NT * i, row = c / (D / 4), ch = c % (D / 4), kv = min(kv0 + row, Skv - 1);
+        pk[i] = *(const f32x4*)(Kg + (size_t)kv * D + 4 * ch);
+        pv[i] = *(const f32x4*)(Vg + (size_t)kv * D + 4 * ch);
+      }
+      if constexpr (MASK) {
+        if (tid < BN) pmb = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
+      }
+    }
+  };
+  if (PREF && ntiles > 0) fetch(tile_kv(0));
   for (int j = 0; j < ntiles; ++j) {
     const int kv0 = tile_kv(j);
     sync_wg();   // every wave is done with tile j-1 (its P V read V)
-    if constexpr (PIPE) {
+    if constexpr (PREF) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int c = tid + NT * i, row = c / (D / 4), ch = c % (D / 4);
+        *(f32x4*)&sK[row * P + 4 * ch] = pk[i];
+        *(f32x4*)&sV[row * P + 4 * ch] = pv[i];
+      }
+      if constexpr (MASK) {
+        if (tid < BN) sM[tid] = pmb;
+      }
+      if (j + 1 < ntiles) fetch(tile_kv(j + 1));
+    } else if constexpr (PIPE) {
       uint8_t mb = 0;
       if constexpr (MASK) {   // issued before V_j, so the wait below covers it
         if (tid < BN) mb = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
@@ -171,7 +202,7 @@ __device__ __forceinline__ void fwd32_body(const AttnArgs& a) {
         *(f32x4*)&sV[row * P + 4 * ch] = vx;
       }
     }
-    if constexpr (MASK && !PIPE) {
+    if constexpr (MASK && !PIPE && !PREF) {
       if (tid < BN) sM[tid] = (kv0 + tid < Skv) ? a.key_mask[(size_t)b * Skv + kv0 + tid] : 0;
     }
     sync_wg();
