@@ -237,7 +237,9 @@ int64_t forward_slots(const fa_problem* p) {
 //    4 chunks vs 169 unsplit).
 //  * fp32 (one workgroup per CU, 4x the time per key): 2R chunks with causal,
 //    R without, when R >= 2 (1 x 1 x 8192 x 64 causal: 128 us at 16 chunks
-//    vs 816 unsplit).
+//    vs 816 unsplit).  fp32 blocks of at most 64 rows run in small
+//    workgroups, several per CU: one chunk per slot, R without the causal
+//    factor (8 x 8 x 16 x 64 after 32752 cached keys: 32 chunks).
 //  * Chunks of at least kMinSplitChunk keys (fp32: a quarter), so that the
 //    partials' write and merge stay small against the chunk's arithmetic.
 // Everything else (R < 2: the query blocks already fill the device, e.g.
@@ -249,10 +251,14 @@ constexpr int kMinSplitKeys = 4096;
 int forward_choose_split(const fa_problem* p, int len) {
   if (p->mod_kind == FA_MOD_CUSTOM || p->head_dim > 128 || len < kMinSplitKeys) return 1;
   const int64_t blocks = p->batch * p->heads * ceil_div(p->seq_q, block_q_fwd(p));
-  const int64_t R = (p->causal ? 2 : 1) * forward_slots(p) / blocks;
+  // fp32 blocks of at most 64 rows (small workgroups, usually after a KV
+  // cache, where the causal rule does not halve a block's keys): one chunk
+  // per free slot
+  const int64_t R = (p->causal && !f32_short(p) ? 2 : 1) * forward_slots(p) / blocks;
   if (R < 2) return 1;
   int64_t n;
-  if (p->dtype == FA_F32) n = p->causal ? 2 * R : R;
+  if (f32_short(p)) n = R;
+  else if (p->dtype == FA_F32) n = p->causal ? 2 * R : R;
   else if (!p->causal) n = R;
   else if (R >= 4) n = R - 1;
   else n = len >= (p->head_dim == 128 ? 16384 : 8192) ? 5 : 1;
