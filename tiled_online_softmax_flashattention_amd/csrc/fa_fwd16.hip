@@ -40,8 +40,10 @@
 // Causal: key tiles past the block's last query are never visited, tiles are
 // visited diagonal first (so the largest ALiBi scores set the maximum early;
 // non-causal ALiBi also visits the tiles from the last one down),
-// waves skip halves entirely past their own queries, and the per-score
-// comparison happens only on diagonal and ragged-tail halves.
+// at head_dim 64 waves skip halves entirely past their own queries (at 128
+// such halves run masked to P = 0, which needs fewer registers than the
+// exit), and the per-score comparison happens only on diagonal and
+// ragged-tail halves.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
