@@ -92,7 +92,10 @@ SOURCES = {"fwd16_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd1
            "dkdv32_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_bwd32.hip",
            "decode_split_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_decode.hip",
            "decode_merge_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_decode.hip",
-           "fwd16_split_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip"}
+           "fwd16_split_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
+           "fwd16_halves_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd16.hip",
+           "fwd32_short_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_fwd32.hip",
+           "split_merge_kernel": "tiled_online_softmax_flashattention_amd/csrc/fa_decode.hip"}
 
 
 def source_of(kernel_name: str):

@@ -14,7 +14,8 @@ import torch
 import oracle
 import tiled_online_softmax_flashattention_amd as fa
 import workloads as W
-from parity import check, check_case, check_lse, full_parity, oracle_kw, run_backward, run_forward, sampled_parity, say, to_dev
+from parity import (MOD_NAME, check, check_case, check_lse, full_parity, oracle_kw, run_backward, run_forward,
+                    sampled_parity, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +62,39 @@ def test_f32_d512_key_tile_edges(gpu_lib, Skv, mask):
 @pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128), ("f32", 64), ("f32", 512)])
 def test_ragged_causal_lengths(gpu_lib, S, dtype, D):
     full_parity(small(dtype, D, True, W.MOD_ALIBI, False, Sq=S, B=1, H=3, wid=101), strict=False)
+
+
+def forward_halves(B, H, Sq):
+    """Whether a causal 16-bit head_dim 64 forward of B x H slices of Sq
+    queries runs on 64-query blocks with two waves per 32 queries: B H
+    (ceil(Sq / 128) + 1) below the device's forward slots, three workgroups
+    per CU."""
+    return B * H * ((Sq + 127) // 128 + 1) < 3 * torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,off", [(2, 2, 200, 200, 0), (16, 16, 200, 200, 0), (1, 3, 700, 700, 0),
+                                           (8, 16, 520, 520, 0), (2, 3, 150, 301, 151), (16, 16, 150, 301, 151)])
+@pytest.mark.parametrize("dtype,mod,mask", [("f16", W.MOD_ALIBI, False), ("bf16", W.MOD_CHECKERBOARD, True),
+                                           ("f16", W.MOD_NONE, True)])
+def test_causal_d64_forward_layouts(gpu_lib, B, H, Sq, Skv, off, dtype, mod, mask):
+    """Causal head_dim 64: with few slices the forward takes 64-query blocks
+    whose waves each cover one key half of every tile (the two waves of a
+    query group merge their max, sum and accumulator at the end), with many
+    the 128-query blocks.  On MI355X's 256 CUs the 2 x 2, 1 x 3 and 2 x 3
+    shapes here take the first layout and the 16 x 16 and 8 x 16 shapes the
+    second; every output element against the oracle, with ragged tails and a
+    query offset on both sides."""
+    w = small(dtype, 64, False, mod, mask, Sq=Sq, Skv=Skv, B=B, H=H, wid=111)
+    inputs = w.make(with_dout=False)
+    say(f"[forward layout] {dtype} B{B} H{H} Sq{Sq} Skv{Skv} off{off} mod={mod} mask={mask} "
+        f"halves={forward_halves(B, H, Sq)}")
+    dev = to_dev(inputs)
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True, score_mod=MOD_NAME[mod], scale=w.scale,
+                          key_mask=dev.get("key_mask"), q_offset=off)
+    torch.cuda.synchronize()
+    okw = dict(scale=w.scale, causal=True, mod=mod, q_offset=off,
+               key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+    check_case(dtype, inputs, okw, out, lse)
 
 
 @pytest.mark.parametrize("Sq,Skv", [(1, 1), (1, 300), (300, 1), (5, 70), (129, 64), (64, 129)])

@@ -219,6 +219,22 @@ int64_t forward_slots(const fa_problem* p) {
   return p->head_dim == 64 ? 3 * cus : 2 * cus;
 }
 
+// Causal 16-bit head_dim 64 forward with 64-query blocks and two waves per
+// 32 queries (each one key half of every tile) when the 128-query blocks
+// leave the slots unbalanced.  Block b of a slice visits b + 1 key tiles of
+// 128, so the longest block exceeds a slot's share of the work when
+// r = B H (nqb + 1) / (2 slots) < 1; the halves pay from r < 1/2 (MI355X,
+// f16 causal ALiBi, same box: r = 0.08 1x1x16384: 231 -> 129 us; 0.34
+// 1x8x8192: 126 -> 93; 0.35 4x8x2048: 36.8 -> 28.1; 0.44 5x8x2048: 39.1 ->
+// 36.5; 0.52 3x8x4096: 78.3 -> 75.0; 0.53 6x8x2048: 42.2 both; 0.54
+// 8x8x1536: 33.4 -> 33.8; 0.71 8x8x2048: 50.7 -> 53.7 us).  A block mask
+// takes the same layout, so a mask with every block set gives the dense
+// result bit for bit.
+bool forward_halves(const fa_problem* p, int64_t nqb) {
+  if (p->dtype == FA_F32 || p->head_dim != 64 || !p->causal) return false;
+  return p->batch * p->heads * (nqb + 1) < forward_slots(p);
+}
+
 // Per-shape table of fa_forward_split (kv_splits = 0): how many key chunks,
 // from sweeps of the chunk count on MI355X over 16-bit and fp32 shapes with
 // 64 .. 1024 query blocks and 4096 .. 32768 keys.  R is the ratio of the
@@ -344,7 +360,7 @@ fa_status fa_forward(const fa_problem* p, const void* q, const void* k, const vo
     err = fa::launch_fwd32(a, (int)p->head_dim, p->mod_kind, p->causal != 0, p->key_mask != nullptr, st);
   else
     err = fa::launch_fwd16(a, p->dtype == FA_BF16, (int)p->head_dim, p->mod_kind, p->causal != 0,
-                           p->key_mask != nullptr, st);
+                           p->key_mask != nullptr, st, false, forward_halves(p, nqb));
   return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -16,6 +16,10 @@
 // per SIMD at head_dim 64 (two at 128): the matrix cores of a SIMD are kept
 // busy by the other waves while one wave works through its softmax (a wave's
 // own vector instructions overlap its MFMAs poorly on this chip).
+// Causal head_dim 64 with few query blocks per workgroup slot uses 64-query
+// blocks instead, two waves per 32 queries, each over one 32-key half of
+// every tile, merged through LDS at the end: the longest block then takes
+// half as long and the slots finish together (fwd16_halves_kernel).
 //
 // LDS layout: tiles are unpadded (key, dim) rows, because a direct load
 // writes 64 consecutive 16-byte chunks; the chunks of each K row are permuted
@@ -56,10 +60,13 @@ constexpr float kSumLimit = 32768.0f;   // a half's row sum above this forces a 
 // unnormalised partial (accumulator, running max, sum) to a.partial for the
 // exact merge of the decode path; otherwise it writes O and lse.  With BLK
 // only the key tiles whose 128 x 128 block is set in a.block_mask are visited
-// (the 128-query block is exactly one block row).
-template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT, bool BLK>
+// (the 128-query block is exactly one block row).  With HALVES the block
+// has 64 queries and two waves share each 32 of them: wave w takes queries
+// 32 (w & 1) .. +31 and key half w >> 1 of every tile, and the pair's
+// (max, sum, accumulator) are merged through LDS at the end.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool SPLIT, bool BLK, bool HALVES = false>
 __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, const int qb, const int split) {
-  constexpr int BM = 128;          // queries per workgroup
+  constexpr int BM = HALVES ? 64 : 128;   // queries per workgroup
   constexpr int BN = 64;           // keys per tile
   constexpr int QS = D / 16;       // MFMA steps of the q.k product
   constexpr int DT = D / 32;       // 32-row tiles of O^T
@@ -83,7 +90,7 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM;
-  const int qw = q0 + wave * 32;
+  const int qw = q0 + (HALVES ? wave & 1 : wave) * 32;
   const int qi = qw + l32;
   // positions among the keys (query row 0 sits at key position q_off)
   const int qwp = qw + a.q_off, qpos = qi + a.q_off;
@@ -363,9 +370,13 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
       load_m(kv_of(min(n + 2, ntiles - 1)));
     }
     if (qw < Sq) {   // a wave past the last query only loads its share of the tiles
-      half(n, 0, sK, sV, sB);
-      __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: their registers are shared
-      half(n, 1, sK, sV, sB);
+      if constexpr (HALVES) {
+        half(n, wave >> 1, sK, sV, sB);
+      } else {
+        half(n, 0, sK, sV, sB);
+        __builtin_amdgcn_sched_barrier(0);   // keep the halves apart: their registers are shared
+        half(n, 1, sK, sV, sB);
+      }
     }
   };
 
@@ -375,6 +386,36 @@ __device__ __forceinline__ void fwd16_block(const AttnArgs& a, const int bh, con
     tile(n + 1, sK1, sV1, sB1, sK0, sV0, sB0);
   }
   if (n < ntiles) tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
+
+  if constexpr (HALVES) {
+    // The wave of key half 1 hands its (max, sum, accumulator) to the wave of
+    // half 0 through the tile buffers (free once every wave is past its last
+    // tile); that wave rescales both to the larger max and adds them.
+    static_assert(TILE * sizeof(uint16_t) >= 16 * DT * 64 * sizeof(float), "merge buffer");
+    sync_wg();
+    float* xo = (float*)((wave & 1) ? sK1 : sK0);
+    float* xm = (float*)sV0 + 128 * (wave & 1);
+    if (wave >> 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(16 * dt + r) * 64 + lane] = o[dt][r];
+      xm[lane] = m_run;
+      xm[64 + lane] = l_run;
+    }
+    sync_wg();
+    if (wave >> 1) return;
+    const float mb = xm[lane], lb = xm[64 + lane];
+    const float m_new = fmaxf(m_run, mb);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float wa = exp2_hw(m_run - m_use), wb = exp2_hw(mb - m_use);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * wa + xo[(16 * dt + r) * 64 + lane] * wb;
+    l_run = l_run * wa + lb * wb;
+    m_run = m_new;
+  }
 
   const float l_tot = l_run + xor32(l_run);
   if constexpr (SPLIT) {
@@ -427,8 +468,27 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_split_kernel(const
   fwd16_block<T, D, MOD, CAUSAL, MASK, true, BLK>(a, c.bh, c.qb, c.split);
 }
 
+// Causal head_dim 64 with few query blocks per workgroup slot: 64-query
+// blocks, two waves per 32 queries (one key half each), longest first.  The
+// longest block then takes half the time while the total stays the same, so
+// the slots finish closer together.  a.n_qblocks counts 64-query blocks.
+template <class T, int MOD, bool MASK, bool BLK>
+__global__ __launch_bounds__(256, 3) void fwd16_halves_kernel(const AttnArgs a) {
+  const BlockCoord c = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, true);
+  fwd16_block<T, 64, MOD, true, MASK, false, BLK, true>(a, c.bh, a.n_qblocks - 1 - c.blk, 0);
+}
+
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
-static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st) {
+static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st, bool halves) {
+  if constexpr (D == 64 && CAUSAL) {
+    if (halves && !split) {
+      AttnArgs h = a;
+      h.n_qblocks = (a.Sq + 63) / 64;
+      hipLaunchKernelGGL((fwd16_halves_kernel<T, MOD, MASK, BLK>), dim3((unsigned)(h.n_qblocks * a.B * a.H)),
+                         dim3(256), 0, st, h);
+      return;
+    }
+  }
   const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H);
   if (split)
     hipLaunchKernelGGL((fwd16_split_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3(blocks * (unsigned)a.n_split),
@@ -438,42 +498,44 @@ static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st) {
 }
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
-static void launch_fwd16_blk(const AttnArgs& a, bool split, hipStream_t st) {
-  if (a.block_mask) launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, split, st);
-  else launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, split, st);
+static void launch_fwd16_blk(const AttnArgs& a, bool split, hipStream_t st, bool halves) {
+  if (a.block_mask) launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, true>(a, split, st, halves);
+  else launch_fwd16_inst<T, D, MOD, CAUSAL, MASK, false>(a, split, st, halves);
 }
 
 template <class T, int D, int MOD>
-static hipError_t launch_fwd16_mod(const AttnArgs& a, bool causal, bool mask, bool split, hipStream_t st) {
+static hipError_t launch_fwd16_mod(const AttnArgs& a, bool causal, bool mask, bool split, hipStream_t st,
+                                   bool halves) {
   if (causal) {
-    if (mask) launch_fwd16_blk<T, D, MOD, true, true>(a, split, st);
-    else launch_fwd16_blk<T, D, MOD, true, false>(a, split, st);
+    if (mask) launch_fwd16_blk<T, D, MOD, true, true>(a, split, st, halves);
+    else launch_fwd16_blk<T, D, MOD, true, false>(a, split, st, halves);
   } else {
-    if (mask) launch_fwd16_blk<T, D, MOD, false, true>(a, split, st);
-    else launch_fwd16_blk<T, D, MOD, false, false>(a, split, st);
+    if (mask) launch_fwd16_blk<T, D, MOD, false, true>(a, split, st, halves);
+    else launch_fwd16_blk<T, D, MOD, false, false>(a, split, st, halves);
   }
   return hipGetLastError();
 }
 
 template <class T, int D>
-static hipError_t launch_fwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool split, hipStream_t st) {
+static hipError_t launch_fwd16_d(const AttnArgs& a, int mod, bool causal, bool mask, bool split, hipStream_t st,
+                                 bool halves) {
   switch (mod) {
-    case MOD_ALIBI: return launch_fwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, split, st);
-    case MOD_CHECKERBOARD: return launch_fwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, split, st);
-    default: return launch_fwd16_mod<T, D, MOD_NONE>(a, causal, mask, split, st);
+    case MOD_ALIBI: return launch_fwd16_mod<T, D, MOD_ALIBI>(a, causal, mask, split, st, halves);
+    case MOD_CHECKERBOARD: return launch_fwd16_mod<T, D, MOD_CHECKERBOARD>(a, causal, mask, split, st, halves);
+    default: return launch_fwd16_mod<T, D, MOD_NONE>(a, causal, mask, split, st, halves);
   }
 }
 
 int fwd16_block_q(int) { return 128; }
 
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask, hipStream_t st,
-                        bool split) {
+                        bool split, bool halves) {
   if (bf16) {
-    return D == 64 ? launch_fwd16_d<BF16, 64>(a, mod, causal, mask, split, st)
-                   : launch_fwd16_d<BF16, 128>(a, mod, causal, mask, split, st);
+    return D == 64 ? launch_fwd16_d<BF16, 64>(a, mod, causal, mask, split, st, halves)
+                   : launch_fwd16_d<BF16, 128>(a, mod, causal, mask, split, st, halves);
   }
-  return D == 64 ? launch_fwd16_d<F16, 64>(a, mod, causal, mask, split, st)
-                 : launch_fwd16_d<F16, 128>(a, mod, causal, mask, split, st);
+  return D == 64 ? launch_fwd16_d<F16, 64>(a, mod, causal, mask, split, st, halves)
+                 : launch_fwd16_d<F16, 128>(a, mod, causal, mask, split, st, halves);
 }
 
 }  // namespace fa
