@@ -64,35 +64,40 @@ def test_ragged_causal_lengths(gpu_lib, S, dtype, D):
     full_parity(small(dtype, D, True, W.MOD_ALIBI, False, Sq=S, B=1, H=3, wid=101), strict=False)
 
 
-def forward_halves(B, H, Sq):
-    """Whether a causal 16-bit head_dim 64 forward of B x H slices of Sq
-    queries runs on 64-query blocks with two waves per 32 queries: B H
-    (ceil(Sq / 128) + 1) below the device's forward slots, three workgroups
-    per CU."""
-    return B * H * ((Sq + 127) // 128 + 1) < 3 * torch.cuda.get_device_properties(0).multi_processor_count
+def forward_halves(B, H, Sq, D, causal):
+    """Whether a 16-bit forward runs on 64-query blocks with two waves per 32
+    queries: with n 128-query blocks per slice and the device's forward slots
+    (3 workgroups per CU at head_dim 64, 2 at 128), causal when B H (n + 1)
+    is below the slots (1.2 times the slots at head_dim 128), otherwise when
+    2 B H n is at most the slots."""
+    n = (Sq + 127) // 128
+    slots = (3 if D == 64 else 2) * torch.cuda.get_device_properties(0).multi_processor_count
+    if not causal:
+        return 2 * B * H * n <= slots
+    return B * H * (n + 1) < slots if D == 64 else 5 * B * H * (n + 1) < 6 * slots
 
 
 @pytest.mark.parametrize("B,H,Sq,Skv,off", [(2, 2, 200, 200, 0), (16, 16, 200, 200, 0), (1, 3, 700, 700, 0),
-                                           (8, 16, 520, 520, 0), (2, 3, 150, 301, 151), (16, 16, 150, 301, 151)])
-@pytest.mark.parametrize("dtype,mod,mask", [("f16", W.MOD_ALIBI, False), ("bf16", W.MOD_CHECKERBOARD, True),
-                                           ("f16", W.MOD_NONE, True)])
-def test_causal_d64_forward_layouts(gpu_lib, B, H, Sq, Skv, off, dtype, mod, mask):
-    """Causal head_dim 64: with few slices the forward takes 64-query blocks
-    whose waves each cover one key half of every tile (the two waves of a
-    query group merge their max, sum and accumulator at the end), with many
-    the 128-query blocks.  On MI355X's 256 CUs the 2 x 2, 1 x 3 and 2 x 3
-    shapes here take the first layout and the 16 x 16 and 8 x 16 shapes the
+                                           (2, 3, 150, 301, 151), (16, 16, 150, 301, 151)])
+@pytest.mark.parametrize("D,causal", [(64, True), (64, False), (128, True), (128, False)])
+@pytest.mark.parametrize("dtype,mod,mask", [("f16", W.MOD_ALIBI, False), ("bf16", W.MOD_CHECKERBOARD, True)])
+def test_forward_layouts(gpu_lib, B, H, Sq, Skv, off, D, causal, dtype, mod, mask):
+    """With few blocks per workgroup slot the 16-bit forward takes 64-query
+    blocks whose waves each cover one key half of every tile (the two waves
+    of a query group merge their max, sum and accumulator at the end), with
+    many the 128-query blocks.  On MI355X's 256 CUs the 2 x 2, 1 x 3 and
+    2 x 3 shapes here take the first layout and the 16 x 16 shapes the
     second; every output element against the oracle, with ragged tails and a
     query offset on both sides."""
-    w = small(dtype, 64, False, mod, mask, Sq=Sq, Skv=Skv, B=B, H=H, wid=111)
+    w = small(dtype, D, False, mod, mask, Sq=Sq, Skv=Skv, B=B, H=H, wid=111)
     inputs = w.make(with_dout=False)
-    say(f"[forward layout] {dtype} B{B} H{H} Sq{Sq} Skv{Skv} off{off} mod={mod} mask={mask} "
-        f"halves={forward_halves(B, H, Sq)}")
+    say(f"[forward layout] {dtype} D{D} causal={causal} B{B} H{H} Sq{Sq} Skv{Skv} off{off} mod={mod} "
+        f"mask={mask} halves={forward_halves(B, H, Sq, D, causal)}")
     dev = to_dev(inputs)
-    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=True, score_mod=MOD_NAME[mod], scale=w.scale,
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], causal=causal, score_mod=MOD_NAME[mod], scale=w.scale,
                           key_mask=dev.get("key_mask"), q_offset=off)
     torch.cuda.synchronize()
-    okw = dict(scale=w.scale, causal=True, mod=mod, q_offset=off,
+    okw = dict(scale=w.scale, causal=causal, mod=mod, q_offset=off,
                key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
     check_case(dtype, inputs, okw, out, lse)
 

@@ -219,20 +219,33 @@ int64_t forward_slots(const fa_problem* p) {
   return p->head_dim == 64 ? 3 * cus : 2 * cus;
 }
 
-// Causal 16-bit head_dim 64 forward with 64-query blocks and two waves per
-// 32 queries (each one key half of every tile) when the 128-query blocks
-// leave the slots unbalanced.  Block b of a slice visits b + 1 key tiles of
-// 128, so the longest block exceeds a slot's share of the work when
-// r = B H (nqb + 1) / (2 slots) < 1; the halves pay from r < 1/2 (MI355X,
-// f16 causal ALiBi, same box: r = 0.08 1x1x16384: 231 -> 129 us; 0.34
-// 1x8x8192: 126 -> 93; 0.35 4x8x2048: 36.8 -> 28.1; 0.44 5x8x2048: 39.1 ->
-// 36.5; 0.52 3x8x4096: 78.3 -> 75.0; 0.53 6x8x2048: 42.2 both; 0.54
-// 8x8x1536: 33.4 -> 33.8; 0.71 8x8x2048: 50.7 -> 53.7 us).  A block mask
-// takes the same layout, so a mask with every block set gives the dense
-// result bit for bit.
+// 16-bit forward with 64-query blocks and two waves per 32 queries (each one
+// key half of every tile, merged at the end) when the 128-query blocks use
+// the device's workgroup slots badly.  Causal: block b of a slice visits
+// b + 1 key tiles of 128, so the longest block outlasts a slot's share of
+// the work when r = B H (nqb + 1) / (2 slots) < 1.  Not causal: the blocks
+// fill u = B H nqb / slots of the device.  The halves pay from r < 1/2 at
+// head_dim 64, r < 0.6 at 128 and u <= 1/2 (MI355X, same box, us):
+//  * causal f16 ALiBi, head_dim 64: r = 0.08 1x1x16384 231 -> 130; 0.34
+//    1x8x8192 126 -> 91; 0.35 4x8x2048 36.8 -> 28.1; 0.44 5x8x2048 39.1 ->
+//    36.5; 0.52 3x8x4096 78.3 -> 75.0; 0.53 6x8x2048 42.2 both; 0.54
+//    8x8x1536 33.4 -> 33.8; 0.71 8x8x2048 50.7 -> 53.7.
+//  * causal, head_dim 128: 0.13 1x1x16384 326 -> 201; 0.26 1x8x4096 88.1 ->
+//    61.9; 0.51 1x8x8192 200 -> 163; 0.53 4x8x2048 58.4 -> 52.6; 0.66
+//    5x8x2048 63.9 -> 68.1; 0.76 1x12x8192 238 -> 240; 1.06 8x8x2048 90.7 ->
+//    101.4.
+//  * not causal, head_dim 64 (f16 ALiBi): u = 0.17 1x1x16384 213 -> 129;
+//    0.33 1x8x4096 56.9 -> 48.9; 0.5 3x8x2048 41.6 -> 37.3; 0.67 2x8x4096
+//    86.2 -> 93.9; 0.83 5x8x2048 60.8 -> 61.0.  head_dim 128 (bf16
+//    checkerboard, key mask): 0.25 1x4x4096 94.1 -> 63.0; 0.5 1x8x4096 94.9
+//    -> 86.9; 0.75 3x8x2048 68.2 -> 74.8; 1.0 2x8x4096 141 -> 170.
+// A block mask takes the same layout, so a mask with every block set gives
+// the dense result bit for bit.
 bool forward_halves(const fa_problem* p, int64_t nqb) {
-  if (p->dtype == FA_F32 || p->head_dim != 64 || !p->causal) return false;
-  return p->batch * p->heads * (nqb + 1) < forward_slots(p);
+  if (p->dtype == FA_F32) return false;
+  const int64_t bh = p->batch * p->heads, slots = forward_slots(p);
+  if (!p->causal) return 2 * bh * nqb <= slots;
+  return p->head_dim == 64 ? bh * (nqb + 1) < slots : 5 * bh * (nqb + 1) < 6 * slots;
 }
 
 // Per-shape table of fa_forward_split (kv_splits = 0): how many key chunks,

@@ -16,10 +16,12 @@
 // per SIMD at head_dim 64 (two at 128): the matrix cores of a SIMD are kept
 // busy by the other waves while one wave works through its softmax (a wave's
 // own vector instructions overlap its MFMAs poorly on this chip).
-// Causal head_dim 64 with few query blocks per workgroup slot uses 64-query
-// blocks instead, two waves per 32 queries, each over one 32-key half of
-// every tile, merged through LDS at the end: the longest block then takes
-// half as long and the slots finish together (fwd16_halves_kernel).
+// With few query blocks per workgroup slot the forward uses 64-query blocks
+// instead, two waves per 32 queries, each over one 32-key half of every
+// tile, merged through LDS at the end (fwd16_halves_kernel): a causal
+// sequence's longest block then takes half as long, so the slots finish
+// together, and a device the 128-query blocks would leave half idle gets
+// twice the workgroups.
 //
 // LDS layout: tiles are unpadded (key, dim) rows, because a direct load
 // writes 64 consecutive 16-byte chunks; the chunks of each K row are permuted
@@ -468,26 +470,25 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_split_kernel(const
   fwd16_block<T, D, MOD, CAUSAL, MASK, true, BLK>(a, c.bh, c.qb, c.split);
 }
 
-// Causal head_dim 64 with few query blocks per workgroup slot: 64-query
-// blocks, two waves per 32 queries (one key half each), longest first.  The
-// longest block then takes half the time while the total stays the same, so
-// the slots finish closer together.  a.n_qblocks counts 64-query blocks.
-template <class T, int MOD, bool MASK, bool BLK>
-__global__ __launch_bounds__(256, 3) void fwd16_halves_kernel(const AttnArgs a) {
-  const BlockCoord c = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, true);
-  fwd16_block<T, 64, MOD, true, MASK, false, BLK, true>(a, c.bh, a.n_qblocks - 1 - c.blk, 0);
+// Few query blocks per workgroup slot: 64-query blocks, two waves per 32
+// queries (one key half each).  Causal: longest first; the longest block
+// then takes half the time while the total stays the same, so the slots
+// finish closer together.  Not causal: twice the workgroups on a device the
+// 128-query blocks leave half idle.  a.n_qblocks counts 64-query blocks.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd16_halves_kernel(const AttnArgs a) {
+  const BlockCoord c = block_coord(blockIdx.x, a.B * a.H, a.n_qblocks, CAUSAL);
+  fwd16_block<T, D, MOD, CAUSAL, MASK, false, BLK, true>(a, c.bh, CAUSAL ? a.n_qblocks - 1 - c.blk : c.blk, 0);
 }
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
 static void launch_fwd16_inst(const AttnArgs& a, bool split, hipStream_t st, bool halves) {
-  if constexpr (D == 64 && CAUSAL) {
-    if (halves && !split) {
-      AttnArgs h = a;
-      h.n_qblocks = (a.Sq + 63) / 64;
-      hipLaunchKernelGGL((fwd16_halves_kernel<T, MOD, MASK, BLK>), dim3((unsigned)(h.n_qblocks * a.B * a.H)),
-                         dim3(256), 0, st, h);
-      return;
-    }
+  if (halves && !split) {
+    AttnArgs h = a;
+    h.n_qblocks = (a.Sq + 63) / 64;
+    hipLaunchKernelGGL((fwd16_halves_kernel<T, D, MOD, CAUSAL, MASK, BLK>), dim3((unsigned)(h.n_qblocks * a.B * a.H)),
+                       dim3(256), 0, st, h);
+    return;
   }
   const unsigned blocks = (unsigned)(a.n_qblocks * a.B * a.H);
   if (split)

@@ -10,8 +10,8 @@ namespace fa {
 // 16-bit forward (f16 / bf16, head_dim 64 or 128).  With split, each query
 // block is split over a.n_split key chunks of a.chunk keys whose partials go
 // to a.partial (rows (bh, query) x chunks x (D + 2) floats) for
-// launch_decode_merge.  halves (causal head_dim 64, not split): 64-query
-// blocks with two waves per 32 queries, one key half each.
+// launch_decode_merge.  halves (not split): 64-query blocks with two waves
+// per 32 queries, one key half each.
 int fwd16_block_q(int D);
 hipError_t launch_fwd16(const AttnArgs& a, bool bf16, int D, int mod, bool causal, bool mask,
                         hipStream_t st, bool split = false, bool halves = false);
