@@ -102,6 +102,43 @@ def test_forward_layouts(gpu_lib, B, H, Sq, Skv, off, D, causal, dtype, mod, mas
     check_case(dtype, inputs, okw, out, lse)
 
 
+def backward_halves(B, H, n, D, causal):
+    """Whether a 16-bit dQ or dK/dV pass over n 128-row blocks per slice
+    (queries for dQ, keys for dK/dV) runs on 64-row blocks with two waves per
+    32 rows: with the passes' slots (2 workgroups per CU at head_dim 64, 1 at
+    128), causal when 5 B H (n + 1) is below 6 slots, otherwise when 2 B H n
+    is at most the slots."""
+    slots = (2 if D == 64 else 1) * torch.cuda.get_device_properties(0).multi_processor_count
+    return 5 * B * H * (n + 1) < 6 * slots if causal else 2 * B * H * n <= slots
+
+
+@pytest.mark.parametrize("B,H,Sq,Skv,off", [(2, 2, 200, 200, 0), (16, 16, 200, 200, 0), (2, 3, 150, 301, 151),
+                                           (16, 16, 150, 301, 151)])
+@pytest.mark.parametrize("D,causal", [(64, True), (64, False), (128, True), (128, False)])
+@pytest.mark.parametrize("dtype,mod,mask", [("f16", W.MOD_ALIBI, False), ("bf16", W.MOD_CHECKERBOARD, True)])
+def test_backward_layouts(gpu_lib, B, H, Sq, Skv, off, D, causal, dtype, mod, mask):
+    """With few blocks per workgroup slot the 16-bit dQ and dK/dV passes take
+    64-row blocks whose waves each cover one half of every tile (the two
+    waves of a row group add their sums at the end), with many the 128-row
+    blocks.  On MI355X's 256 CUs the 2 x 2 and 2 x 3 shapes here take the
+    first layout and the 16 x 16 shapes the second; forward and backward,
+    every output element against the oracle, with ragged tails and a query
+    offset on both sides."""
+    w = small(dtype, D, False, mod, mask, Sq=Sq, Skv=Skv, B=B, H=H, wid=112)
+    inputs = w.make()
+    say(f"[backward layout] {dtype} D{D} causal={causal} B{B} H{H} Sq{Sq} Skv{Skv} off{off} mod={mod} mask={mask} "
+        f"dq halves={backward_halves(B, H, (Sq + 127) // 128, D, causal)} "
+        f"dk/dv halves={backward_halves(B, H, (Skv + 127) // 128, D, causal)}")
+    dev = to_dev(inputs)
+    kw = dict(causal=causal, score_mod=MOD_NAME[mod], scale=w.scale, key_mask=dev.get("key_mask"), q_offset=off)
+    out, lse = fa.forward(dev["q"], dev["k"], dev["v"], **kw)
+    grads = fa.backward(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], dq_mode="separate", **kw)
+    torch.cuda.synchronize()
+    okw = dict(scale=w.scale, causal=causal, mod=mod, q_offset=off,
+               key_mask=None if inputs.get("key_mask") is None else inputs["key_mask"].numpy())
+    check_case(dtype, inputs, okw, out, lse, grads)
+
+
 @pytest.mark.parametrize("Sq,Skv", [(1, 1), (1, 300), (300, 1), (5, 70), (129, 64), (64, 129)])
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 def test_ragged_noncausal_shapes(gpu_lib, Sq, Skv, dtype):

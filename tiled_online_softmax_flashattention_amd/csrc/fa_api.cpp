@@ -248,6 +248,25 @@ bool forward_halves(const fa_problem* p, int64_t nqb) {
   return p->head_dim == 64 ? bh * (nqb + 1) < slots : 5 * bh * (nqb + 1) < 6 * slots;
 }
 
+// The 16-bit dQ and dK/dV passes on 64-row blocks (two waves per 32 rows,
+// each over one half of every tile, their sums added at the end) when the
+// 128-row blocks use the passes' workgroup slots badly: 2 per CU at head_dim
+// 64, 1 at 128; n = the pass's own 128-row blocks (queries for dQ, keys for
+// dK/dV).  Causal when r = B H (n + 1) / (2 slots) < 0.6, otherwise when
+// 2 B H n <= slots.  Measured on MI355X (both passes, f16 causal ALiBi or
+// bf16 checkerboard with a key mask, same box, us):
+//  * head_dim 64: r = 0.13 1x1x16384 517 -> 316; 0.27 2x8x2048 74.4 -> 55.0;
+//    0.51 1x8x8192 314 -> 276; 0.53 4x8x2048 89.4 -> 84.0; 1.06 8x8x2048
+//    145.6 -> 158.4.  Not causal: u = 0.5 1x8x4096 137.7 -> 131.5; 1.0
+//    2x8x4096 235.6 -> 257.1.
+//  * head_dim 128: r = 0.25 1x1x16384 912 -> 598; 0.52 1x8x4096 244 -> 188;
+//    1.03 2x8x4096 283 -> 356; 2.1 8x8x2048 324 -> 412.  Not causal: 0.5
+//    1x4x4096 220 -> 166; 1.0 1x8x4096 236 -> 305.
+bool backward_halves(const fa_problem* p, int64_t n) {
+  const int64_t bh = p->batch * p->heads, slots = (p->head_dim == 64 ? 2 : 1) * device_cus();
+  return p->causal ? 5 * bh * (n + 1) < 6 * slots : 2 * bh * n <= slots;
+}
+
 // Per-shape table of fa_forward_split (kv_splits = 0): how many key chunks,
 // from sweeps of the chunk count on MI355X over 16-bit and fp32 shapes with
 // 64 .. 1024 query blocks and 4096 .. 32768 keys.  R is the ratio of the
@@ -460,6 +479,10 @@ fa_status fa_backward(const fa_problem* p, const void* q, const void* k, const v
   a.lse2 = (float*)((char*)workspace + lay.lse2_off);
   a.dq_acc = atomic ? (float*)((char*)workspace + lay.dq_acc_off) : nullptr;
   a.n_qblocks = (int)nqb;
+  if (!f32 && p->mod_kind != FA_MOD_CUSTOM) {
+    a.dq_halves = backward_halves(p, ceil_div(p->seq_q, 128)) ? 1 : 0;
+    a.kv_halves = !atomic && backward_halves(p, ceil_div(p->seq_kv, 128)) ? 1 : 0;
+  }
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
   if (p->mod_kind == FA_MOD_CUSTOM) {   // preprocess (plain rows), then the run-time compiled passes

@@ -29,7 +29,9 @@
 // order of the atomic additions varies, so dQ is not bitwise repeatable.
 // The LDS tiles are unpadded rows with permuted 16-byte chunks (tswz), which
 // keeps both the row-fragment and the transposing reads free of bank
-// conflicts.
+// conflicts.  With few blocks per workgroup slot both passes run on 64-row
+// blocks instead, two waves per 32 rows, each over one half of every tile,
+// their sums added through LDS at the end (HALVES instances).
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -140,9 +142,13 @@ hipError_t launch_bwd_pre(const AttnArgs& a, int dtype, int D, hipStream_t st, i
 // (K, V, dK, dV and two score blocks) within the 256 of two waves per SIMD
 // at head_dim 64.  With BLK only the query tiles whose 128 x 128 block (row
 // tile / 2, this workgroup's 128 keys) is set in the block mask are visited.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool DQA>
+// With HALVES (not with DQA) the block has 64 keys and two waves share each
+// 32 of them: wave w takes keys 32 (w & 1) .. +31 and query half w >> 1 of
+// every tile, and the pair's dK, dV sums are added through LDS at the end.
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool DQA, bool HALVES = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const AttnArgs a) {
-  constexpr int BKV = 128;   // keys per workgroup (4 waves x 32)
+  static_assert(!(HALVES && DQA), "the atomic dQ mode keeps 128-key blocks");
+  constexpr int BKV = HALVES ? 64 : 128;   // keys per workgroup (4 waves x 32, or 2 x 32 twice)
   constexpr int BQ = kDkdvBQ;   // queries per tile
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = BQ * D;
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int k0 = kb * BKV;
-  const int kw = k0 + 32 * wave;
+  const int kw = k0 + 32 * (HALVES ? wave & 1 : wave);
   const int kj = kw + l32;            // this lane's key
   const float c = a.scale_log2;
 
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   // entry n of the list of tiles whose block is set.
   int n0 = qt0, n_end = nqt;
   if constexpr (BLK) {
-    const uint8_t* bcol = a.block_mask + (size_t)bh * a.bm_rows * a.bm_cols + kb;   // BKV = one block column
+    const uint8_t* bcol = a.block_mask + (size_t)bh * a.bm_rows * a.bm_cols + (k0 >> 7);   // one block column
     n0 = 0;
     n_end = compact_tiles(bcol, a.bm_cols, 1, qt0, nqt, sList, sCnt);   // 64-query tile t lies in block row t / 2
   }
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
   // products are issued first, and the first half's probabilities are
   // computed while the second half's products run (and its dV, dK products
   // while the second half's probabilities are computed).
-  constexpr bool PAIRED = D == 128 && !DQA;
+  constexpr bool PAIRED = D == 128 && !DQA && !HALVES;
 
   // Atomic dQ mode, after every wave has stored its dS^T of query tile it:
   // dQ_tile += dS K over the workgroup's 128 keys, as (64 queries x D) / 4
@@ -582,7 +588,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     if constexpr (DQA) barrier_lds();   // ... and every other wave's; tile n-1 is retired
     else sync_wg();
     if (n + 1 < n_end) load_tile(it_of(n + 1), sQn, sOn, sLn, sDn);
-    if (PAIRED) {
+    if constexpr (HALVES) {
+      half(it, wave >> 1, sQ, sO, sL, sD);
+    } else if (PAIRED) {
       paired(it, sQ, sO, sL, sD);
     } else {
       half(it, 0, sQ, sO, sL, sD);
@@ -602,6 +610,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv16_kernel(const Attn
     tile(n + 1, sQ1, sO1, sL1, sD1, sQ0, sO0, sL0, sD0);
   }
   if (n < n_end) tile(n, sQ0, sO0, sL0, sD0, sQ1, sO1, sL1, sD1);
+
+  if constexpr (HALVES) {
+    // the wave of query half 1 hands its dK, dV sums to the wave of half 0
+    // through the tile buffers (free once every wave is past its last tile)
+    static_assert(TILE * sizeof(uint16_t) >= 16 * DT * 64 * sizeof(float), "merge buffer");
+    sync_wg();
+    float* xk = (float*)((wave & 1) ? sQ1 : sQ0);
+    float* xv = (float*)((wave & 1) ? sO1 : sO0);
+    if (wave >> 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xk[(16 * dt + r) * 64 + lane] = dk[dt][r];
+          xv[(16 * dt + r) * 64 + lane] = dv[dt][r];
+        }
+    }
+    sync_wg();
+    if (wave >> 1) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[dt][r] += xk[(16 * dt + r) * 64 + lane];
+        dv[dt][r] += xv[(16 * dt + r) * 64 + lane];
+      }
+  }
 
   if (kj < Skv) {
     uint16_t* dKg = (uint16_t*)a.dk + ((size_t)bh * Skv + kj) * D;
@@ -666,7 +701,11 @@ static hipError_t launch_bwd16_inst(const AttnArgs& a, bool want_kv, bool want_q
     err = launch_bwd_pre(a, __is_same(T, BF16) ? 2 : 1, D, st, MOD == MOD_ALIBI ? 2 : 1);
   }
   if (err != hipSuccess || !want_kv) return err;
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK, false>), dim3(nkb * BH), dim3(256), 0, st, a);
+  if (a.kv_halves)
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK, false, true>), dim3((unsigned)((a.Skv + 63) / 64) * BH),
+                       dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, MOD, CAUSAL, MASK, BLK, false>), dim3(nkb * BH), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -499,6 +499,8 @@ struct AttnArgs {
   const uint8_t* block_mask;   // (B, H, bm_rows, bm_cols) bytes, 0 = block skipped; NULL = dense
   int bm_rows, bm_cols;        // ceil(Sq / kBlk), ceil(Skv / kBlk)
   const float* mod_params;     // caller-defined score_mod: its parameter array (device), or NULL
+  int dq_halves;               // 16-bit dQ pass: 64-query blocks, two waves per query group (host choice)
+  int kv_halves;               // 16-bit dK/dV pass: 64-key blocks, two waves per key group (host choice)
 };
 
 // ------------------------------------------------------------ block sparsity

@@ -24,10 +24,14 @@ namespace fa {
 // (K permuted for both of its reads: row fragments for S^T, transposed for
 // dQ), and per score one FMA and one exp give P = 2^(S' c + b - lse2).  With
 // BLK only the key tiles whose block (this workgroup's 128 queries, tile / 2)
-// is set in the block mask are visited.
-template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK>
+// is set in the block mask are visited.  With HALVES the block has 64
+// queries and two waves share each 32 of them: wave w takes queries
+// 32 (w & 1) .. +31 and key half w >> 1 of every tile, and the pair's dQ
+// sums are added through LDS at the end (a.n_qblocks counts 64-query
+// blocks then).
+template <class T, int D, int MOD, bool CAUSAL, bool MASK, bool BLK, bool HALVES = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnArgs a) {
-  constexpr int BM = 128;   // queries per workgroup
+  constexpr int BM = HALVES ? 64 : 128;   // queries per workgroup
   constexpr int BN = 64;    // keys per tile
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int TILE = BN * D;
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int b = bh / a.H, h = bh - b * a.H;
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qb * BM;
-  const int qw = q0 + 32 * wave;
+  const int qw = q0 + 32 * (HALVES ? wave & 1 : wave);
   const int qi = qw + l32;
   const int qwp = qw + a.q_off, qpos = qi + a.q_off;   // positions among the keys
   const float c = a.scale_log2;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
     const float lse = a.lse[(size_t)bh * Sq + min(qi, Sq - 1)];
     lse2 = (ok && lse != kNegInf) ? lse * kLog2e : __builtin_inff();   // empty rows and rows past seq_q: P = 0
     delta = ok ? dsum : 0.f;
-    if (ok && hi == 0) {
+    if (ok && hi == 0 && (!HALVES || wave < 2)) {
       // for the key/value pass, as it consumes them (see bwd_pre_kernel):
       // -delta, and -lse2 / c with the query's ALiBi share folded in
       float l2 = lse2;
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   const int kv_end = CAUSAL ? min(Skv, q0 + a.q_off + BM) : Skv;
   int ntiles = (kv_end + BN - 1) / BN;
   if constexpr (BLK) {
-    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + qb) * a.bm_cols;   // BM = one block row
+    const uint8_t* brow = a.block_mask + ((size_t)bh * a.bm_rows + (q0 >> 7)) * a.bm_cols;   // one block row
     ntiles = compact_tiles(brow, 1, 1, 0, ntiles, sList, sCnt);   // 64-key tile t lies in block t / 2
   }
   auto kv_of = [&](int n) __attribute__((always_inline)) {
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   // head_dim 128 runs one wave per SIMD: both halves' score products first,
   // so the second half's products run while the first half's probabilities
   // are computed (as in the key/value pass).
-  constexpr bool PAIRED = D == 128;
+  constexpr bool PAIRED = D == 128 && !HALVES;
 
   // Both halves of a causal tile at head_dim 128, scheduled by hand (the
   // non-causal instances measured 2 % faster with the compiler's schedule
@@ -404,7 +408,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
       store_m(sBn);
       load_m(kv_of(min(n + 2, ntiles - 1)));
     }
-    if constexpr (PAIRED && CAUSAL) {
+    if constexpr (HALVES) {
+      half(n, wave >> 1, sK, sV, sB);
+    } else if constexpr (PAIRED && CAUSAL) {
       paired(n, sK, sV, sB);
     } else if constexpr (PAIRED) {   // both halves always run without the causal rule
       f32x16 s0, dp0, s1, dp1;
@@ -433,6 +439,26 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
   }
   if (n < ntiles) tile(n, sK0, sV0, sB0, sK1, sV1, sB1);
 
+  if constexpr (HALVES) {
+    // the wave of key half 1 hands its dQ sums to the wave of half 0 through
+    // the tile buffers (free once every wave is past its last tile)
+    static_assert(TILE * sizeof(uint16_t) >= 16 * DT * 64 * sizeof(float), "merge buffer");
+    sync_wg();
+    float* xq = (float*)((wave & 1) ? sK1 : sK0);
+    if (wave >> 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xq[(16 * dt + r) * 64 + lane] = dq[dt][r];
+    }
+    sync_wg();
+    if (wave >> 1) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[dt][r] += xq[(16 * dt + r) * 64 + lane];
+  }
+
   if (qi < Sq) {
     uint16_t* dQg = (uint16_t*)a.dq + ((size_t)bh * Sq + qi) * D;
     const float sc = a.scale;
@@ -451,6 +477,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dq16_kernel(const AttnAr
 
 template <class T, int D, int MOD, bool CAUSAL, bool MASK>
 static hipError_t launch_dq16_inst(const AttnArgs& a, hipStream_t st) {
+  if (a.dq_halves) {
+    AttnArgs h = a;
+    h.n_qblocks = (a.Sq + 63) / 64;
+    const dim3 grid((unsigned)h.n_qblocks * (unsigned)(a.B * a.H));
+    if (a.block_mask)
+      hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK, true, true>), grid, dim3(256), 0, st, h);
+    else
+      hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK, false, true>), grid, dim3(256), 0, st, h);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)a.n_qblocks * (unsigned)(a.B * a.H);
   if (a.block_mask)
     hipLaunchKernelGGL((dq16_kernel<T, D, MOD, CAUSAL, MASK, true>), dim3(grid), dim3(256), 0, st, a);
