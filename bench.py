@@ -107,7 +107,7 @@ def source_of(kernel_name: str):
 
 
 # The headline's dominant kernel, as rocprofv3 names it.
-DKDV_PREFILL = "void fa::dkdv16_kernel<fa::F16, 64, 1, true, false, false, false>(fa::AttnArgs)"
+DKDV_PREFILL = "void fa::dkdv16_kernel<fa::F16, 64, 1, true, false, false, false, false>(fa::AttnArgs)"
 TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_trace_bench.json")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bench.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bench.json")
@@ -674,7 +674,7 @@ def main() -> int:
     dom_flops, dom_ms = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     full = {"dkdv16_kernel": DKDV_PREFILL,
-            "dq16_kernel": "void fa::dq16_kernel<fa::F16, 64, 1, true, false, false>(fa::AttnArgs)",
+            "dq16_kernel": "void fa::dq16_kernel<fa::F16, 64, 1, true, false, false, false>(fa::AttnArgs)",
             "fwd16_kernel": "void fa::fwd16_kernel<fa::F16, 64, 1, true, false, false>(fa::AttnArgs)"}[dom]
     traced_ns = _from_summary(TRACE_FILE, full, "average_ns")
     roofline = {"bound": "mfma", "kernel": full, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
