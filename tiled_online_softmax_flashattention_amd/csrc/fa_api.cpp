@@ -279,8 +279,15 @@ bool backward_halves(const fa_problem* p, int64_t n) {
 //    (1 x 1 x 32768 x 128: 421 us at 3 chunks, 588 at 4, 700 unsplit).
 //  * 16-bit, causal, 2 <= R < 4, long sequences (>= 16384 keys at head_dim
 //    128, >= 8192 at 64): 5 chunks, fine grains over several rounds
-//    (1 x 4 x 16384 x 128: 351 us vs 404 unsplit); shorter sequences stay
-//    whole (2 x 8 x 4096 x 128: 110 us unsplit, 117 at 2 chunks).
+//    (1 x 4 x 16384 x 128: 351 us vs 404 unsplit with 128-query blocks);
+//    shorter sequences stay whole (2 x 8 x 4096 x 128: 110 us unsplit, 117
+//    at 2 chunks).  At head_dim 64 the whole forward on 64-query halves
+//    (forward_halves) beats the 5 chunks where it applies: 2 x 4 x 8192: 93
+//    vs 114 us, 1 x 8 x 8192: 94 vs 115, 1 x 4 x 16384: 177 vs 198, 1 x 2 x
+//    32768: 389 vs 390; where it does not (1 x 3 x 32768, r = 0.50) the
+//    chunks stay (554 vs 588).  At head_dim 128 the chunks mostly still win
+//    over the halves (1 x 2 x 32768: 623 vs 703 us, 1 x 2 x 24576: 390 vs
+//    486, 1 x 3 x 16384: 284 vs 415; 1 x 4 x 16384: 332 vs 293).
 //  * 16-bit, not causal: R chunks when R >= 2 (1 x 2 x 8192 x 128: 90 us at
 //    4 chunks vs 169 unsplit).
 //  * fp32 (one workgroup per CU, 4x the time per key): 2R chunks with causal,
@@ -309,6 +316,7 @@ int forward_choose_split(const fa_problem* p, int len) {
   else if (p->dtype == FA_F32) n = p->causal ? 2 * R : R;
   else if (!p->causal) n = R;
   else if (R >= 4) n = R - 1;
+  else if (p->head_dim == 64 && forward_halves(p, ceil_div(p->seq_q, block_q_fwd(p)))) n = 1;
   else n = len >= (p->head_dim == 128 ? 16384 : 8192) ? 5 : 1;
   const int64_t most = len / (p->dtype == FA_F32 ? kMinSplitChunk / 4 : kMinSplitChunk);
   if (n > most) n = most;
