@@ -371,6 +371,14 @@ def test_forward_split_table_and_rules():
     big = ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1))
     assert big >= 2 * long_row and big % 256 == 0
     assert ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1, kv_splits=1)) == 0
+    # causal with 2 <= R < 4 (256 CUs without a GPU): at head_dim 64 the whole forward runs on 64-query halves
+    # where they apply (B H (n + 1) below the 768 slots) and the table keeps it whole; where they do not, and
+    # at head_dim 128, it splits in 5 chunks
+    assert ws(prob(batch=2, heads=4, seq_q=8192, seq_kv=8192, causal=1, mod_kind=1)) == 0
+    assert ws(prob(batch=1, heads=8, seq_q=8192, seq_kv=8192, causal=1, mod_kind=1)) == 0
+    assert ws(prob(batch=1, heads=3, seq_q=32768, seq_kv=32768, causal=1)) == 1 * 3 * 32768 * 5 * (64 + 2) * 4
+    assert ws(prob(batch=1, heads=4, seq_q=16384, seq_kv=16384, head_dim=128, causal=1)) == \
+        1 * 4 * 16384 * 5 * (128 + 2) * 4
     assert ws(prob(batch=1, heads=2, seq_q=16384, seq_kv=16384, head_dim=128, causal=1, kv_splits=4)) == \
         4 * long_row
     # chunks are whole 64-key tiles: 5 chunks of 80 keys become 128-key chunks, 4 in all
